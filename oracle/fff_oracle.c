@@ -1,0 +1,165 @@
+/*
+ * fff_oracle.c -- plain CPU reference for the Fast FeedForward (FFF) layer
+ * forward pass.  TEST INFRASTRUCTURE ONLY: the tests, the smoke check and the
+ * benchmark's CPU-baseline leg may load it; the HIP library never does, and
+ * the two share no code.
+ *
+ * Everything is float64.  Inputs arrive already widened (exactly) to double.
+ * Loops run in the plain textbook order (i ascending in every dot product).
+ *
+ * What is computed, and where it is stated:
+ *
+ *  - "Dynamic sparsity in tree-structured feed-forward layers at scale"
+ *    (gist.science explainer, section 2, Methodology): P parallel perfect
+ *    binary trees of depth D; per token one root-to-leaf path per tree; at
+ *    every node a linear projection of the input gives a logit whose sign
+ *    picks the child; only the nodes on the path are evaluated and their
+ *    outputs are summed.
+ *  - Same page, section 3.C: the nonlinearity (GELU) is applied per node,
+ *    before the outputs are summed (the FFF variant, not FFF-post).
+ *  - thelatestinai.com page of the same paper, Figure 1(c) caption: the tree
+ *    outputs are concatenated and passed through one final linear projection.
+ *  - Table 4 of that page (MLP-block sparsity 83% / 94% / 99% at depths
+ *    4 / 6 / 13) matches D+1 evaluated nodes out of 2^(D+1)-1, so every node
+ *    on the path, leaf included, contributes.
+ *
+ * Readings taken where the pages are silent (each is listed in the design
+ * notes):  node n computes a = x.w_n + b_n and contributes GELU(a) * v_n,
+ * v_n in R^h;  GELU is the tanh form 0.5 a (1 + tanh(sqrt(2/pi)(a + 0.044715
+ * a^3)));  a < 0 goes to the left child, anything else (0, -0, NaN) to the
+ * right;  nodes are numbered in heap order (children of n: 2n+1 left, 2n+2
+ * right);  tree p fills columns [p*h, (p+1)*h) of the concatenation and rows
+ * [p*h, (p+1)*h) of W_out;  there is no projection bias;  path_out holds the
+ * leaf index n - (2^D - 1), whose bit (D-1-l) is the level-l decision
+ * (1 = right).
+ *
+ * Near-tie threshold: for each visited node the oracle also records
+ * thr = 1e-4 * ||x_t||_2 * ||w_n||_2; a device path that takes the other
+ * branch at a node whose |a| <= thr is excused (and counted) by the tests.
+ */
+#include <math.h>
+#include <stddef.h>
+#include <stdint.h>
+#include <stdlib.h>
+
+#define FFFO_OK 0
+#define FFFO_BAD_ARG 1
+
+static double gelu_tanh(double a)
+{
+    const double k0 = 0.7978845608028654; /* sqrt(2/pi) */
+    const double k1 = 0.044715;
+    return 0.5 * a * (1.0 + tanh(k0 * (a + k1 * a * a * a)));
+}
+
+static double dot(const double *u, const double *v, int n)
+{
+    double s = 0.0;
+    for (int i = 0; i < n; ++i)
+        s += u[i] * v[i];
+    return s;
+}
+
+/*
+ * One token through one tree.  Walks root to leaf, adding GELU(a) * v_n for
+ * every visited node into acc[0..h).  If forced_leaf >= 0 the branch at each
+ * level is taken from that leaf's bits instead of the logit's sign.
+ * Returns the leaf index.
+ */
+static int32_t walk_tree(const double *xt, double xnorm, const double *Wp, const double *bp,
+                         const double *Vp, int d, int D, int h, int32_t forced_leaf,
+                         double *acc, double *rec_a, double *rec_thr, int32_t *rec_node)
+{
+    int64_t n = 0; /* heap index of the current node */
+    for (int j = 0; j < h; ++j)
+        acc[j] = 0.0;
+    for (int level = 0; level <= D; ++level) {
+        const double *w = Wp + n * (int64_t)d;
+        double a = dot(xt, w, d) + bp[n];
+        if (rec_a)
+            rec_a[level] = a;
+        if (rec_thr)
+            rec_thr[level] = 1e-4 * xnorm * sqrt(dot(w, w, d));
+        if (rec_node)
+            rec_node[level] = (int32_t)n;
+        double g = gelu_tanh(a);
+        const double *v = Vp + n * (int64_t)h;
+        for (int j = 0; j < h; ++j)
+            acc[j] += g * v[j];
+        if (level < D) {
+            int go_right;
+            if (forced_leaf >= 0)
+                go_right = (forced_leaf >> (D - 1 - level)) & 1;
+            else
+                go_right = !(a < 0.0);
+            n = 2 * n + 1 + go_right;
+        }
+    }
+    return (int32_t)(n - (((int64_t)1 << D) - 1));
+}
+
+/*
+ * fffo_forward: the whole layer for T tokens.
+ *
+ *   x [T,d], W [P,N,d], b [P,N], V [P,N,h], Wout [P*h,d]   (N = 2^(D+1)-1)
+ *   forced  [T,P] leaf indices, or NULL to route by sign
+ *   y       [T,d] out, or NULL to skip the projection
+ *   H       [T,P*h] out (the concatenated tree outputs), or NULL
+ *   path    [T,P] out (leaf indices), or NULL
+ *   rec_a, rec_thr, rec_node  [T,P,D+1] per-visit records, each may be NULL
+ *   nthreads  worker threads (<= 0: runtime default)
+ *
+ * Returns 0, or 1 for a bad shape.
+ */
+int fffo_forward(int64_t T, int d, int P, int D, int h,
+                 const double *x, const double *W, const double *b, const double *V,
+                 const double *Wout, const int32_t *forced,
+                 double *y, double *H, int32_t *path,
+                 double *rec_a, double *rec_thr, int32_t *rec_node, int nthreads)
+{
+    if (T < 0 || d <= 0 || P <= 0 || D < 0 || D > 24 || h <= 0)
+        return FFFO_BAD_ARG;
+    const int64_t N = ((int64_t)1 << (D + 1)) - 1;
+    const int64_t K = (int64_t)P * h;
+    const int L = D + 1;
+    if (nthreads <= 0)
+        nthreads = 1;
+
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nthreads)
+    for (int64_t t = 0; t < T; ++t) {
+        const double *xt = x + t * d;
+        double xnorm = sqrt(dot(xt, xt, d));
+        double *Ht = (double *)malloc(sizeof(double) * (size_t)K);
+        if (!Ht)
+            abort();
+        for (int p = 0; p < P; ++p) {
+            int64_t tp = t * P + p;
+            int32_t fl = forced ? forced[tp] : -1;
+            int32_t leaf = walk_tree(xt, xnorm, W + (int64_t)p * N * d, b + (int64_t)p * N,
+                                     V + (int64_t)p * N * h, d, D, h, fl, Ht + (int64_t)p * h,
+                                     rec_a ? rec_a + tp * L : NULL,
+                                     rec_thr ? rec_thr + tp * L : NULL,
+                                     rec_node ? rec_node + tp * L : NULL);
+            if (path)
+                path[tp] = leaf;
+        }
+        if (H)
+            for (int64_t k = 0; k < K; ++k)
+                H[t * K + k] = Ht[k];
+        if (y) {
+            /* y[t,c] = sum over k ascending of H[t,k] * Wout[k,c]; the k loop
+             * is outermost only so that Wout is read row by row. */
+            double *yt = y + t * d;
+            for (int c = 0; c < d; ++c)
+                yt[c] = 0.0;
+            for (int64_t k = 0; k < K; ++k) {
+                const double hk = Ht[k];
+                const double *wk = Wout + k * d;
+                for (int c = 0; c < d; ++c)
+                    yt[c] += hk * wk[c];
+            }
+        }
+        free(Ht);
+    }
+    return FFFO_OK;
+}

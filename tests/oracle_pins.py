@@ -1,0 +1,306 @@
+"""Pins for the CPU oracle: checks against things other than the oracle itself.
+
+Each ``pin_*`` function takes an oracle library handle (so the mutant test can
+run the same battery against deliberately broken copies) and raises
+AssertionError when the oracle disagrees with:
+
+* brute force over every root-to-leaf path of tiny trees, using the "masked"
+  formulation of the FFF explainer page (gist.science, section 2,
+  Implementation): all node logits computed densely, then the unique path
+  whose every decision agrees with its logit's sign selected as a mask;
+* hand-built weights whose routing is known in closed form;
+* the all-zero case (every logit exactly 0, so every decision is a tie);
+* a constant negative bias (every path goes to leaf 0; closed-form H);
+* the visit count against Table 4's MLP-block sparsity column and the
+  Figure 7 caption (tests/golden/table4_mlp_sparsity.txt);
+* depth 0, which the paper's Figure 5 caption calls the dense FF case, against
+  a dense one-hidden-layer MLP written with torch library routines;
+* forced paths against the brute-force masked sum along those paths;
+* invariances: positive rescaling of a node's (w, b), token and tree
+  permutation, linearity in V and W_out, batch invariance.
+
+GELU references come from ``torch.nn.functional.gelu(approximate="tanh")``
+in float64, a library implementation independent of the oracle's C code.
+"""
+from __future__ import annotations
+
+import os
+
+import numpy as np
+import torch
+
+import oracle
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def gelu_ref(a: np.ndarray) -> np.ndarray:
+    return torch.nn.functional.gelu(torch.from_numpy(np.asarray(a, dtype=np.float64)),
+                                    approximate="tanh").numpy()
+
+
+def rand_layer(rng, T, d, P, D, h):
+    N = (1 << (D + 1)) - 1
+    return dict(
+        x=rng.standard_normal((T, d)),
+        W_node=rng.standard_normal((P, N, d)) / np.sqrt(d),
+        b_node=0.1 * rng.standard_normal((P, N)),
+        V_node=rng.standard_normal((P, N, h)) / np.sqrt(h),
+        W_out=rng.standard_normal((P * h, d)) / np.sqrt(P * h),
+    )
+
+
+def ancestors_of_leaf(leaf: int, D: int):
+    """Heap ids of the nodes on the path to a leaf, root first (bottom-up walk)."""
+    n = leaf + (1 << D) - 1
+    nodes = [n]
+    while n > 0:
+        n = (n - 1) // 2
+        nodes.append(n)
+    return nodes[::-1]
+
+
+def brute_force(L, forced=None):
+    """Masked formulation: dense logits, enumerate all 2^D paths."""
+    x, W, b, V, Wo = L["x"], L["W_node"], L["b_node"], L["V_node"], L["W_out"]
+    T, d = x.shape
+    P, N, _ = W.shape
+    h = V.shape[2]
+    D = int(np.log2(N + 1)) - 1
+    A = np.einsum("td,pnd->tpn", x, W) + b[None, :, :]
+    G = gelu_ref(A)
+    path = np.zeros((T, P), dtype=np.int32)
+    H = np.zeros((T, P * h))
+    for t in range(T):
+        for p in range(P):
+            if forced is None:
+                ok = []
+                for leaf in range(1 << D):
+                    nodes = ancestors_of_leaf(leaf, D)
+                    good = True
+                    for lvl in range(D):
+                        child_is_right = nodes[lvl + 1] == 2 * nodes[lvl] + 2
+                        if child_is_right != (not (A[t, p, nodes[lvl]] < 0)):
+                            good = False
+                            break
+                    if good:
+                        ok.append(leaf)
+                assert len(ok) == 1, "exactly one path must agree with every sign"
+                leaf = ok[0]
+            else:
+                leaf = int(forced[t, p])
+            mask = np.zeros(N)
+            mask[ancestors_of_leaf(leaf, D)] = 1.0
+            path[t, p] = leaf
+            H[t, p * h:(p + 1) * h] = (mask * G[t, p]) @ V[p]
+    return path, H, H @ Wo
+
+
+def _close(a, b, rtol=1e-12, atol=1e-12):
+    np.testing.assert_allclose(a, b, rtol=rtol, atol=atol)
+
+
+def pin_brute_force(lib, n_cases=24):
+    rng = np.random.default_rng(1234)
+    shapes = [(7, 5, 3, 3, 4), (4, 8, 2, 5, 3), (9, 3, 1, 2, 6), (3, 16, 2, 4, 5), (5, 4, 3, 1, 2)]
+    for i in range(n_cases):
+        T, d, P, D, h = shapes[i % len(shapes)]
+        L = rand_layer(rng, T, d, P, D, h)
+        r = oracle.forward(**L, want_H=True, lib=lib, nthreads=2)
+        path, H, y = brute_force(L)
+        np.testing.assert_array_equal(r["path"], path)
+        _close(r["H"], H)
+        _close(r["y"], y)
+
+
+def pin_hand_routing(lib):
+    """x in {+-1}^(D+1), w_n = s_p * e_level(n), b = 0: every |a| = 1.
+
+    Then leaf = sum over l < D of [s_p * x_l > 0] * 2^(D-1-l) exactly, and with
+    V one-hot (v_n = e_n, h >= N) H[t, p*h + n] = GELU(s_p * x_level(n)) on the
+    visited nodes and 0 elsewhere.
+    """
+    D, P, T = 4, 3, 32
+    N = (1 << (D + 1)) - 1
+    d, h = D + 3, N + 2
+    rng = np.random.default_rng(7)
+    s = np.array([1.0, -1.0, 1.0])
+    x = np.zeros((T, d))
+    x[:, :D + 1] = rng.choice([-1.0, 1.0], size=(T, D + 1))
+    W = np.zeros((P, N, d))
+    for p in range(P):
+        for n in range(N):
+            level = int(np.floor(np.log2(n + 1)))
+            W[p, n, level] = s[p]
+    V = np.zeros((P, N, h))
+    for n in range(N):
+        V[:, n, n] = 1.0
+    b = np.zeros((P, N))
+    Wo = rng.standard_normal((P * h, d))
+    r = oracle.forward(x, W, b, V, Wo, want_H=True, lib=lib, nthreads=2)
+    g_pos, g_neg = gelu_ref(np.array([1.0, -1.0]))
+    for t in range(T):
+        for p in range(P):
+            bits = [(s[p] * x[t, lvl] > 0) for lvl in range(D + 1)]
+            leaf = sum(int(bits[lvl]) << (D - 1 - lvl) for lvl in range(D))
+            assert r["path"][t, p] == leaf
+            expect = np.zeros(h)
+            for lvl, n in enumerate(ancestors_of_leaf(leaf, D)):
+                expect[n] = g_pos if bits[lvl] else g_neg
+            _close(r["H"][t, p * h:(p + 1) * h], expect)
+    _close(r["y"], r["H"] @ Wo)
+
+
+def pin_zero_ties(lib):
+    """W = 0, b = 0: every logit is exactly 0 and goes right; GELU(0) = 0."""
+    T, d, P, D, h = 6, 5, 2, 3, 4
+    rng = np.random.default_rng(3)
+    L = rand_layer(rng, T, d, P, D, h)
+    L["W_node"][:] = 0.0
+    L["b_node"][:] = 0.0
+    r = oracle.forward(**L, want_H=True, lib=lib, nthreads=1)
+    assert (r["path"] == (1 << D) - 1).all()
+    assert (r["H"] == 0).all() and (r["y"] == 0).all()
+
+
+def pin_negative_bias(lib):
+    """W = 0, b = -beta: every path is leaf 0 (the leftmost spine) and
+    H_p = GELU(-beta) * sum over levels of V[p, 2^l - 1]."""
+    T, d, P, D, h = 5, 4, 3, 4, 6
+    beta = 0.75
+    rng = np.random.default_rng(4)
+    L = rand_layer(rng, T, d, P, D, h)
+    L["W_node"][:] = 0.0
+    L["b_node"][:] = -beta
+    r = oracle.forward(**L, want_H=True, lib=lib, nthreads=1)
+    assert (r["path"] == 0).all()
+    g = gelu_ref(np.array([-beta]))[0]
+    for p in range(P):
+        spine = sum(L["V_node"][p, (1 << lvl) - 1] for lvl in range(D + 1))
+        for t in range(T):
+            _close(r["H"][t, p * h:(p + 1) * h], g * spine)
+
+
+def read_table4():
+    rows = []
+    with open(os.path.join(GOLDEN, "table4_mlp_sparsity.txt")) as f:
+        for line in f:
+            line = line.split("#", 1)[0].strip()
+            if line:
+                depth, pct, mode = line.split()
+                rows.append((int(depth), int(pct), mode))
+    return rows
+
+
+def pin_visit_count_table4(lib):
+    """Evaluated nodes per (token, tree), counted from the oracle's records,
+    against the printed sparsity 1 - evaluated / nodes-per-tree."""
+    for depth, pct, mode in read_table4():
+        T, d, P, h = 3, 2, 1, 1
+        rng = np.random.default_rng(depth)
+        L = rand_layer(rng, T, d, P, depth, h)
+        r = oracle.forward(**L, want_y=False, want_records=True, lib=lib, nthreads=1)
+        evaluated = (r["rec_node"] >= 0).sum(axis=2)
+        assert (evaluated == evaluated[0, 0]).all()
+        nodes_per_tree = L["W_node"].shape[1]
+        sparsity = 100.0 * (1.0 - evaluated[0, 0] / nodes_per_tree)
+        got = int(np.floor(sparsity)) if mode == "floor" else int(np.floor(sparsity + 0.5))
+        assert got == pct, (depth, sparsity, pct)
+        # The recorded nodes form a root-to-leaf chain ending at the reported leaf.
+        for t in range(T):
+            chain = list(r["rec_node"][t, 0])
+            assert chain == ancestors_of_leaf(int(r["path"][t, 0]), depth)
+
+
+def pin_depth0_dense(lib):
+    """D = 0: one node per tree, so the layer is a dense MLP with P hidden
+    units: y = GELU(x W0^T + b0) M with M[p] = v_p W_out[p*h:(p+1)*h]."""
+    T, d, P, h = 11, 9, 5, 3
+    rng = np.random.default_rng(5)
+    L = rand_layer(rng, T, d, P, 0, h)
+    r = oracle.forward(**L, want_H=True, lib=lib, nthreads=1)
+    assert (r["path"] == 0).all()
+    xt = torch.from_numpy(L["x"])
+    W0 = torch.from_numpy(L["W_node"][:, 0, :])
+    b0 = torch.from_numpy(L["b_node"][:, 0])
+    hidden = torch.nn.functional.gelu(torch.nn.functional.linear(xt, W0, b0), approximate="tanh")
+    M = torch.stack([torch.from_numpy(L["V_node"][p, 0]) @ torch.from_numpy(
+        L["W_out"][p * h:(p + 1) * h]) for p in range(P)])
+    _close(r["y"], (hidden @ M).numpy(), rtol=1e-11, atol=1e-12)
+
+
+def pin_forced_paths(lib):
+    rng = np.random.default_rng(6)
+    T, d, P, D, h = 6, 7, 2, 3, 4
+    L = rand_layer(rng, T, d, P, D, h)
+    natural = oracle.forward(**L, want_H=True, lib=lib, nthreads=1)
+    same = oracle.forward(**L, forced=natural["path"], want_H=True, lib=lib, nthreads=1)
+    np.testing.assert_array_equal(same["path"], natural["path"])
+    _close(same["y"], natural["y"])
+    forced = rng.integers(0, 1 << D, size=(T, P)).astype(np.int32)
+    r = oracle.forward(**L, forced=forced, want_H=True, lib=lib, nthreads=1)
+    path, H, y = brute_force(L, forced=forced)
+    np.testing.assert_array_equal(r["path"], forced)
+    _close(r["H"], H)
+    _close(r["y"], y)
+
+
+def pin_invariants(lib):
+    rng = np.random.default_rng(8)
+    T, d, P, D, h = 10, 6, 3, 3, 4
+    L = rand_layer(rng, T, d, P, D, h)
+    base = oracle.forward(**L, want_H=True, lib=lib, nthreads=2)
+    # Only the sign of a logit routes: rescaling (w_n, b_n) by c > 0 keeps paths.
+    L2 = dict(L)
+    c = rng.uniform(0.1, 10.0, size=L["b_node"].shape)
+    L2["W_node"] = L["W_node"] * c[:, :, None]
+    L2["b_node"] = L["b_node"] * c
+    np.testing.assert_array_equal(oracle.forward(**L2, want_y=False, lib=lib)["path"], base["path"])
+    # Token permutation is equivariant.
+    perm = rng.permutation(T)
+    L3 = dict(L, x=L["x"][perm])
+    r3 = oracle.forward(**L3, lib=lib)
+    np.testing.assert_array_equal(r3["path"], base["path"][perm])
+    _close(r3["y"], base["y"][perm])
+    # Permuting trees together with W_out's row blocks leaves y unchanged.
+    tp = rng.permutation(P)
+    rows = np.concatenate([np.arange(p * h, (p + 1) * h) for p in tp])
+    L4 = dict(L, W_node=L["W_node"][tp], b_node=L["b_node"][tp], V_node=L["V_node"][tp],
+              W_out=L["W_out"][rows])
+    r4 = oracle.forward(**L4, lib=lib)
+    np.testing.assert_array_equal(r4["path"], base["path"][:, tp])
+    _close(r4["y"], base["y"], rtol=1e-11, atol=1e-12)
+    # H is linear in V; y is linear in W_out.
+    V2 = rng.standard_normal(L["V_node"].shape)
+    rv = oracle.forward(**dict(L, V_node=V2), want_H=True, lib=lib)
+    rs = oracle.forward(**dict(L, V_node=2.0 * L["V_node"] - 3.0 * V2), want_H=True, lib=lib)
+    _close(rs["H"], 2.0 * base["H"] - 3.0 * rv["H"], rtol=1e-10, atol=1e-11)
+    Wo2 = rng.standard_normal(L["W_out"].shape)
+    rw = oracle.forward(**dict(L, W_out=Wo2), lib=lib)
+    rsw = oracle.forward(**dict(L, W_out=L["W_out"] + 0.5 * Wo2), lib=lib)
+    _close(rsw["y"], base["y"] + 0.5 * rw["y"], rtol=1e-10, atol=1e-11)
+    # Batch invariance: one token alone gives its batched row.
+    for t in (0, T - 1):
+        r1 = oracle.forward(**dict(L, x=L["x"][t:t + 1]), lib=lib, nthreads=1)
+        np.testing.assert_array_equal(r1["path"][0], base["path"][t])
+        np.testing.assert_array_equal(r1["y"][0], base["y"][t])
+
+
+def pin_tie_threshold(lib):
+    """rec_thr = 1e-4 * ||x_t|| * ||w_n|| for each visited node."""
+    rng = np.random.default_rng(9)
+    T, d, P, D, h = 4, 6, 2, 2, 3
+    L = rand_layer(rng, T, d, P, D, h)
+    r = oracle.forward(**L, want_records=True, lib=lib, nthreads=1)
+    for t in range(T):
+        for p in range(P):
+            for lvl in range(D + 1):
+                n = r["rec_node"][t, p, lvl]
+                expect = 1e-4 * np.linalg.norm(L["x"][t]) * np.linalg.norm(L["W_node"][p, n])
+                _close(r["rec_thr"][t, p, lvl], expect)
+                _close(r["rec_a"][t, p, lvl], L["x"][t] @ L["W_node"][p, n] + L["b_node"][p, n])
+
+
+ALL_PINS = [pin_brute_force, pin_hand_routing, pin_zero_ties, pin_negative_bias,
+            pin_visit_count_table4, pin_depth0_dense, pin_forced_paths, pin_invariants,
+            pin_tie_threshold]
