@@ -1,0 +1,252 @@
+"""Benchmark of the FFF layer forward pass on one MI355X.
+
+One step = one fff_forward call (routing through every tree, the fused
+GELU*v accumulation into the concatenated buffer, the output projection)
+over one batch of synthetic tokens already resident in HBM.  The default
+workload is the OPT-1.3B-shaped depth-6 layer (T=16384, d=2048, P=32, D=6,
+h=128, bf16).  Input sets are rotated between steps so that the 256 MB
+Infinity Cache cannot serve a repeated call.
+
+Prints one JSON line: tokens/s, the dominant kernel's roofline (measured live
+with HIP events recorded by the library around that kernel, on the stream it
+is launched on) and the CPU oracle's throughput on a bounded token sample.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "FFF layer tokens/sec (bf16, OPT-1.3B d=6 shape) + % of HBM/MFMA roofline"
+PEAK_MFMA_BF16_TFLOPS = 2500.0
+PEAK_HBM_GBPS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="opt1p3b_d6")
+    ap.add_argument("--algo", default="auto")
+    ap.add_argument("--split-level", type=int, default=-1)
+    ap.add_argument("--rotate", type=int, default=0, help="input sets (0 = by footprint)")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="oracle sample budget")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+def algorithmic_work(s, U):
+    """Flops and bytes the method itself must do (not the work it avoids,
+    and not intermediate round trips): per visited node a length-d dot
+    product and an h-vector update, the projection, and one read of x, the
+    visited node rows, W_out, plus the writes of y and path_out."""
+    e = 2 if s.dtype == "bf16" else 4
+    flops_route = s.T * s.P * (s.D + 1) * 2 * (s.d + s.h)
+    flops_proj = 2 * s.T * s.P * s.h * s.d
+    bytes_alg = e * (2 * s.T * s.d + U * (s.d + s.h + 1) + s.P * s.h * s.d) + 4 * s.T * s.P
+    return flops_route, flops_proj, bytes_alg
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "sparse_tree_structured_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they
+    were taken on the current kernel sources (else None)."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as f:
+            data = json.load(f)
+    except (OSError, ValueError):
+        return None
+    ent = data.get(f"{kernel}@{workload}")
+    if not ent or ent.get("source_hash") != kernel_source_hash():
+        return None
+    return ent.get("bytes_per_launch")
+
+
+def cpu_baseline(inp, budget_s):
+    import numpy as np
+
+    import oracle
+
+    f = inp.as_f64()
+    threads = oracle.default_threads()
+    T = inp.shape.T
+
+    def timed(n):
+        t0 = time.perf_counter()
+        oracle.forward(f["x"][:n], f["W_node"], f["b_node"], f["V_node"], f["W_out"], nthreads=threads)
+        return time.perf_counter() - t0
+
+    pilot = min(T, max(threads, 16))
+    tp = timed(pilot)
+    n = int(min(T, max(pilot, pilot * budget_s / max(tp, 1e-6))))
+    dt = timed(n) if n > pilot else tp
+    cpu = "unknown"
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    cpu = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"value": n / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"first {n} of {T} tokens of the same workload (seed 0), full forward "
+                      f"(routing + projection) in float64, {dt:.2f} s wall on {cpu}",
+            "seconds": dt}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
+              "(the layer shards by tokens with no communication, see the design notes)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import sparse_tree_structured_amd as fff
+    from sparse_tree_structured_amd.hiprt import Event
+    import workloads
+
+    dev = torch.device("cuda:0")
+    shape, opts = workloads.WORKLOADS[args.workload]
+    footprint = (shape.T * shape.d + shape.P * shape.N * (shape.d + shape.h + 1)
+                 + shape.P * shape.h * shape.d) * (2 if shape.dtype == "bf16" else 4)
+    rotate = args.rotate or max(2, -(-600_000_000 // max(footprint, 1)))
+    rotate = min(rotate, 64)
+
+    def upload(inp):
+        out = []
+        for k in ("x", "W_node", "b_node", "V_node", "W_out"):
+            a = getattr(inp, k)
+            t = torch.from_numpy(a.view(np.int16)).view(torch.bfloat16) if shape.dtype == "bf16" \
+                else torch.from_numpy(a)
+            out.append(t.to(dev))
+        return out
+
+    inp0 = workloads.make_inputs(shape, seed=0, **opts)
+    sets = [upload(inp0)] + [upload(workloads.make_inputs(shape, seed=s, **opts))
+                             for s in range(1, rotate)]
+    torch.cuda.synchronize()
+
+    plan = fff.make_plan(args.algo, args.split_level)
+    fshape = fff.shape_of(sets[0][0], sets[0][1], sets[0][3])
+    if plan.algo == fff.ALGO_AUTO:
+        plan = fff.plan_default(fshape)
+    ws, nbytes = fff.alloc_workspace(fshape, plan, dev)
+    y = torch.empty((shape.T, shape.d), dtype=sets[0][0].dtype, device=dev)
+    path = torch.empty((shape.T, shape.P), dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step(i, ev=None):
+        x, W, b, V, Wo = sets[i % rotate]
+        fff.forward(x, W, b, V, Wo, algo=plan.algo, split_level=plan.split_level, workspace=ws,
+                    y=y, path_out=path, stream=stream, events=ev)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    evs = [(Event(), Event(), Event()) for _ in range(args.steps)]
+    sev = [fff.StageEvents(a.ptr, b.ptr, c.ptr) for a, b, c in evs]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i, sev[i])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+
+    route_ms = [a.elapsed_ms(b) for a, b, _ in evs]
+    proj_ms = [b.elapsed_ms(c) for _, b, c in evs]
+    fwd_ms = [a.elapsed_ms(c) for a, _, c in evs]
+
+    # Distinct visited (tree, node) pairs for the algorithmic byte count,
+    # from the device's own paths on input set 0.
+    step(0)
+    torch.cuda.synchronize()
+    leaves = path.cpu().numpy().astype(np.int64)
+    visited = set()
+    for p in range(shape.P):
+        for lf in np.unique(leaves[:, p]):
+            n = int(lf) + (1 << shape.D) - 1
+            while True:
+                visited.add((p, n))
+                if n == 0:
+                    break
+                n = (n - 1) // 2
+    U = len(visited)
+    f_route, f_proj, b_alg = algorithmic_work(shape, U)
+    ms_step = 1e3 * elapsed / args.steps
+    tokens_per_s = shape.T * args.steps / elapsed
+
+    fused = plan.algo == fff.ALGO_DECODE
+    if fused:
+        t_dom = float(np.mean(fwd_ms)) * 1e-3
+        achieved = b_alg / t_dom / 1e9
+        roof = {"bound": "hbm", "kernel": "decode_fused", "achieved": achieved,
+                "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": achieved / PEAK_HBM_GBPS,
+                "traffic": measured_traffic("decode_fused", args.workload),
+                "per_launch": {"bytes": b_alg, "avg_us": t_dom * 1e6}}
+    else:
+        t_dom = float(np.mean(proj_ms)) * 1e-3
+        achieved = f_proj / t_dom / 1e12
+        roof = {"bound": "mfma", "kernel": "proj_mfma", "achieved": achieved,
+                "peak": PEAK_MFMA_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": achieved / PEAK_MFMA_BF16_TFLOPS,
+                "traffic": measured_traffic("proj_mfma", args.workload),
+                "per_launch": {"flops": f_proj, "avg_us": t_dom * 1e6}}
+
+    t_roof = max(b_alg / (PEAK_HBM_GBPS * 1e9), (f_route + f_proj) / (PEAK_MFMA_BF16_TFLOPS * 1e12))
+    out = {
+        "metric": METRIC,
+        "value": tokens_per_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if shape.dtype == "bf16" else "f32",
+        "data": "synthetic (seeded Gaussian inputs and random-init weights of the named shape)",
+        "config": {"workload": args.workload, "T": shape.T, "d": shape.d, "P": shape.P,
+                   "D": shape.D, "h": shape.h, "algo": fff.algo_name(plan.algo),
+                   "split_level": plan.split_level, "rotated_sets": rotate,
+                   "parallelism": "none (1 GPU)"},
+        "roofline": roof,
+        "layer": {"F_alg": f_route + f_proj, "B_alg": b_alg, "U": U,
+                  "t_roof_us": t_roof * 1e6, "roof_frac": t_roof / (ms_step * 1e-3),
+                  "route_us": float(np.mean(route_ms)) * 1e3,
+                  "proj_us": float(np.mean(proj_ms)) * 1e3,
+                  "forward_us_median": float(np.median(fwd_ms)) * 1e3,
+                  "forward_us_p10": float(np.percentile(fwd_ms, 10)) * 1e3,
+                  "forward_us_p90": float(np.percentile(fwd_ms, 90)) * 1e3},
+        "host": platform.node(),
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(inp0, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

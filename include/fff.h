@@ -1,0 +1,170 @@
+/*
+ * fff.h -- C ABI of the Fast FeedForward (FFF) layer forward pass on AMD
+ * Instinct MI355X (gfx950).
+ *
+ * The operation
+ * -------------
+ * "Dynamic sparsity in tree-structured feed-forward layers at scale": the
+ * explainer page (gist.science, section 2, Methodology) describes an FFF
+ * layer as P parallel perfect binary trees of depth D in which each token
+ * follows one root-to-leaf path per tree, the sign of a per-node linear logit
+ * choosing the branch, and only the visited nodes' outputs are summed; the
+ * paper's own page (thelatestinai.com, Figure 1(c) caption) concatenates the
+ * P tree outputs and applies one final linear projection; section 3.C of the
+ * explainer puts the GELU before the summation.  With N = 2^(D+1) - 1 nodes
+ * per tree, for every token x (a row of x[T,d]) and tree p:
+ *
+ *     n = 0 (root);  acc = 0 (h values)
+ *     for level = 0 .. D:
+ *         a    = x . W_node[p,n,:] + b_node[p,n]
+ *         acc += GELU(a) * V_node[p,n,:]
+ *         if level < D:  n = 2n+1 if a < 0 else 2n+2
+ *     path_out[t,p] = n - (2^D - 1)            (leaf index)
+ *     H[t, p*h : (p+1)*h] = acc
+ *     y[t,:] = H[t,:] . W_out                  (no bias)
+ *
+ * Readings fixed here where the pages are silent: GELU is the tanh form
+ * 0.5 a (1 + tanh(sqrt(2/pi) (a + 0.044715 a^3))); a logit of exactly 0 (or
+ * -0, or NaN) goes right; nodes are numbered in heap order; tree p owns
+ * columns [p*h, (p+1)*h) of H and rows [p*h, (p+1)*h) of W_out; bit (D-1-l)
+ * of a leaf index is the level-l decision, 1 = right.
+ *
+ * Layout and precision
+ * --------------------
+ * Every tensor is dense, row-major and of one dtype (FFF_DTYPE_F32 or
+ * FFF_DTYPE_BF16):  x[T,d]  W_node[P,N,d]  b_node[P,N]  V_node[P,N,h]
+ * W_out[P*h,d]  y[T,d].  path_out[T,P] is int32.  Logits, GELU and sums are
+ * computed in fp32; for bf16 the concatenated tree outputs are rounded to
+ * bf16 once (they feed the projection's matrix cores) and y is rounded to
+ * bf16 (nearest even).
+ *
+ * Ownership, streams and errors
+ * -----------------------------
+ * All tensor and workspace pointers are device pointers owned by the caller.
+ * The library allocates no memory and keeps no state between calls; calls
+ * that use distinct workspaces may run concurrently.  Work is enqueued on
+ * `stream` (0 = the null stream) and the call returns without waiting;
+ * faults inside kernels surface at the caller's next synchronisation.
+ * Arguments are validated on the host before any HIP call: on a validation
+ * error nothing is enqueued.  Launch failures return FFF_ERROR_HIP.
+ */
+#ifndef FFF_H
+#define FFF_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FFF_MAX_DEPTH 20
+
+typedef enum fff_dtype {
+    FFF_DTYPE_F32 = 0,
+    FFF_DTYPE_BF16 = 1
+} fff_dtype_t;
+
+typedef enum fff_status {
+    FFF_SUCCESS = 0,
+    FFF_ERROR_INVALID_VALUE = 1, /* bad shape, null or misaligned pointer */
+    FFF_ERROR_NOT_SUPPORTED = 2, /* unknown dtype, or a plan the shape cannot take */
+    FFF_ERROR_WORKSPACE = 3,     /* workspace missing or smaller than required */
+    FFF_ERROR_HIP = 4            /* a HIP launch or runtime call failed */
+} fff_status_t;
+
+/* Layer shape.  N = 2^(D+1) - 1 is implied.  Limits: T >= 0, d, P, h >= 1,
+ * 0 <= D <= FFF_MAX_DEPTH, T < 2^31, and every tensor below 2^40 elements. */
+typedef struct fff_shape {
+    int64_t T;     /* tokens */
+    int32_t d;     /* model width */
+    int32_t P;     /* parallel trees */
+    int32_t D;     /* depth: D+1 nodes visited per path */
+    int32_t h;     /* output width of one node */
+    int32_t dtype; /* fff_dtype_t */
+} fff_shape_t;
+
+/* Algorithms.  AUTO picks by shape; the others force one (for tests and
+ * measurement).  GENERIC takes any shape and dtype.  PREFILL needs bf16,
+ * d % 64 == 0, h % 64 == 0 and (P*h) % 64 == 0.  DECODE needs bf16,
+ * d % 256 == 0, h % 64 == 0 and T <= 64. */
+typedef enum fff_algo {
+    FFF_ALGO_AUTO = 0,
+    FFF_ALGO_GENERIC = 1,
+    FFF_ALGO_PREFILL = 2,
+    FFF_ALGO_DECODE = 3
+} fff_algo_t;
+
+typedef struct fff_plan {
+    int32_t algo;        /* fff_algo_t */
+    int32_t split_level; /* PREFILL: levels 0..k-1 evaluated as one dense
+                            matrix product, the rest per token bucket;
+                            -1 = choose by shape; ignored by other algos */
+} fff_plan_t;
+
+/* Optional events recorded on `stream` at stage boundaries (each may be
+ * NULL): `start` before the first kernel, `routed` once the concatenated tree
+ * outputs are complete, `done` after the projection.  Algorithms that fuse
+ * routing and projection record `routed` together with `done`. */
+typedef struct fff_stage_events {
+    hipEvent_t start;
+    hipEvent_t routed;
+    hipEvent_t done;
+} fff_stage_events_t;
+
+/* Fill *plan with the choice FFF_ALGO_AUTO makes for this shape. */
+fff_status_t fff_plan_default(const fff_shape_t *shape, fff_plan_t *plan);
+
+/* Workspace bytes the plan needs (plan NULL = the default plan).  The size
+ * depends only on the shape and plan. */
+fff_status_t fff_workspace_size(const fff_shape_t *shape, const fff_plan_t *plan, size_t *bytes);
+
+/*
+ * The whole layer: y = concat_p(tree outputs) . W_out, and path_out.
+ *   x, W_node, b_node, V_node, W_out  inputs (device, dtype, 16-byte aligned
+ *                                     except b_node: element aligned)
+ *   y          output [T,d] (device, dtype, 16-byte aligned)
+ *   path_out   output [T,P] int32 leaf indices, or NULL to skip
+ *   workspace  device scratch of at least fff_workspace_size() bytes,
+ *              256-byte aligned; may be NULL when that size is 0
+ *   plan       NULL = default plan
+ *   events     NULL = no events
+ * T == 0 is a no-op that returns FFF_SUCCESS without touching any pointer.
+ */
+fff_status_t fff_forward(const fff_shape_t *shape, const fff_plan_t *plan,
+                         const void *x, const void *W_node, const void *b_node,
+                         const void *V_node, const void *W_out, void *y, int32_t *path_out,
+                         void *workspace, size_t workspace_bytes, hipStream_t stream,
+                         const fff_stage_events_t *events);
+
+/*
+ * Routing only: the concatenated tree outputs H[T, P*h] (dtype) and
+ * path_out, without the projection.  Same rules as fff_forward; `H` is a
+ * caller buffer (16-byte aligned).  Uses the same workspace size.
+ */
+fff_status_t fff_route(const fff_shape_t *shape, const fff_plan_t *plan,
+                       const void *x, const void *W_node, const void *b_node,
+                       const void *V_node, void *H, int32_t *path_out,
+                       void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Projection only: y[T,d] = H[T,K] . W_out[K,d] with K = P*h, fp32
+ * accumulation, output rounded to dtype.  `algo` selects the kernel family
+ * (AUTO, GENERIC, or PREFILL for the matrix-core kernel).  Needs no workspace.
+ */
+fff_status_t fff_project(const fff_shape_t *shape, int32_t algo, const void *H,
+                         const void *W_out, void *y, hipStream_t stream);
+
+/* Static, human-readable text for a status code. */
+const char *fff_status_string(fff_status_t status);
+
+/* Static name of an algorithm ("auto", "generic", "prefill", "decode"). */
+const char *fff_algo_name(int32_t algo);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FFF_H */

@@ -1,0 +1,234 @@
+"""Python binding of the FFF forward-pass library (libfff.so, C ABI in
+include/fff.h).
+
+Argument marshalling only: every step of the layer runs in the library's HIP
+kernels.  Torch tensors supply device memory and the current stream.  If the
+library has not been built this module raises on first use; there is no
+fallback implementation.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIBRARY = os.path.join(_PKG, "libfff.so")
+
+# fff_dtype_t
+DTYPE_F32 = 0
+DTYPE_BF16 = 1
+# fff_status_t
+SUCCESS = 0
+ERROR_INVALID_VALUE = 1
+ERROR_NOT_SUPPORTED = 2
+ERROR_WORKSPACE = 3
+ERROR_HIP = 4
+# fff_algo_t
+ALGO_AUTO = 0
+ALGO_GENERIC = 1
+ALGO_PREFILL = 2
+ALGO_DECODE = 3
+ALGOS = {"auto": ALGO_AUTO, "generic": ALGO_GENERIC, "prefill": ALGO_PREFILL, "decode": ALGO_DECODE}
+MAX_DEPTH = 20
+
+
+class Shape(ctypes.Structure):
+    _fields_ = [("T", ctypes.c_int64), ("d", ctypes.c_int32), ("P", ctypes.c_int32),
+                ("D", ctypes.c_int32), ("h", ctypes.c_int32), ("dtype", ctypes.c_int32)]
+
+
+class Plan(ctypes.Structure):
+    _fields_ = [("algo", ctypes.c_int32), ("split_level", ctypes.c_int32)]
+
+
+class StageEvents(ctypes.Structure):
+    _fields_ = [("start", ctypes.c_void_p), ("routed", ctypes.c_void_p), ("done", ctypes.c_void_p)]
+
+
+class FFFError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {status_string(status)} (status {status})")
+
+
+EXPORTS = ("fff_plan_default", "fff_workspace_size", "fff_forward", "fff_route", "fff_project",
+           "fff_status_string", "fff_algo_name")
+
+_lib: Optional[ctypes.CDLL] = None
+
+
+def load_library(path: Optional[str] = None) -> ctypes.CDLL:
+    """Load libfff.so; raises if it is missing (build it with build.py)."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or LIBRARY
+    if not os.path.exists(p):
+        raise ImportError(f"{p} is missing: build it with `python sparse_tree_structured_amd/build.py` "
+                          "(or __graft_entry__.build()); there is no fallback path")
+    lib = ctypes.CDLL(p)
+    vp, sz = ctypes.c_void_p, ctypes.c_size_t
+    SP, PP = ctypes.POINTER(Shape), ctypes.POINTER(Plan)
+    lib.fff_plan_default.argtypes = [SP, PP]
+    lib.fff_workspace_size.argtypes = [SP, PP, ctypes.POINTER(sz)]
+    lib.fff_forward.argtypes = [SP, PP, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp,
+                                ctypes.POINTER(StageEvents)]
+    lib.fff_route.argtypes = [SP, PP, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.fff_project.argtypes = [SP, ctypes.c_int32, vp, vp, vp, vp]
+    lib.fff_status_string.argtypes = [ctypes.c_int]
+    lib.fff_status_string.restype = ctypes.c_char_p
+    lib.fff_algo_name.argtypes = [ctypes.c_int32]
+    lib.fff_algo_name.restype = ctypes.c_char_p
+    for name in ("fff_plan_default", "fff_workspace_size", "fff_forward", "fff_route", "fff_project"):
+        getattr(lib, name).restype = ctypes.c_int
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load_library().fff_status_string(int(status)).decode()
+
+
+def algo_name(algo: int) -> str:
+    return load_library().fff_algo_name(int(algo)).decode()
+
+
+def make_shape(T: int, d: int, P: int, D: int, h: int, dtype: int) -> Shape:
+    return Shape(int(T), int(d), int(P), int(D), int(h), int(dtype))
+
+
+def make_plan(algo=ALGO_AUTO, split_level: int = -1) -> Plan:
+    if isinstance(algo, str):
+        algo = ALGOS[algo]
+    return Plan(int(algo), int(split_level))
+
+
+def plan_default(shape: Shape) -> Plan:
+    p = Plan()
+    st = load_library().fff_plan_default(ctypes.byref(shape), ctypes.byref(p))
+    if st != SUCCESS:
+        raise FFFError(st, "fff_plan_default")
+    return p
+
+
+def workspace_size(shape: Shape, plan: Optional[Plan] = None) -> int:
+    n = ctypes.c_size_t()
+    st = load_library().fff_workspace_size(ctypes.byref(shape),
+                                           ctypes.byref(plan) if plan is not None else None,
+                                           ctypes.byref(n))
+    if st != SUCCESS:
+        raise FFFError(st, "fff_workspace_size")
+    return int(n.value)
+
+
+# ---- torch-facing helpers (device memory and streams only) ----
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.float32:
+        return DTYPE_F32
+    if t.dtype == torch.bfloat16:
+        return DTYPE_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def shape_of(x, W_node, V_node) -> Shape:
+    T, d = x.shape
+    P, N, d2 = W_node.shape
+    h = V_node.shape[2]
+    D = N.bit_length() - 1
+    if d2 != d or (1 << (D + 1)) - 1 != N:
+        raise ValueError("W_node must be [P, 2^(D+1)-1, d]")
+    return make_shape(T, d, P, D, h, _dtype_code(x))
+
+
+def _check(tensors, dtype, device):
+    for t in tensors:
+        if t.dtype != dtype or t.device != device or not t.is_contiguous():
+            raise ValueError("all tensors must be contiguous, on one device, of one dtype")
+
+
+def _stream_handle(stream) -> int:
+    torch = _torch()
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return int(s.cuda_stream)
+
+
+def alloc_workspace(shape: Shape, plan: Optional[Plan], device):
+    torch = _torch()
+    n = workspace_size(shape, plan)
+    # torch's caching allocator returns blocks aligned to at least 512 bytes.
+    return torch.empty(max(n, 1), dtype=torch.uint8, device=device), n
+
+
+def forward(x, W_node, b_node, V_node, W_out, *, algo=ALGO_AUTO, split_level: int = -1,
+            want_path: bool = True, workspace=None, y=None, path_out=None, stream=None,
+            events: Optional[StageEvents] = None) -> Tuple[object, Optional[object]]:
+    """y = FFF(x); returns (y, path_out[T,P] int32 or None)."""
+    torch = _torch()
+    shape = shape_of(x, W_node, V_node)
+    _check([x, W_node, b_node, V_node, W_out], x.dtype, x.device)
+    plan = make_plan(algo, split_level)
+    if workspace is None:
+        workspace, nbytes = alloc_workspace(shape, plan, x.device)
+    else:
+        nbytes = workspace.numel() * workspace.element_size()
+    if y is None:
+        y = torch.empty((shape.T, shape.d), dtype=x.dtype, device=x.device)
+    if want_path and path_out is None:
+        path_out = torch.empty((shape.T, shape.P), dtype=torch.int32, device=x.device)
+    st = load_library().fff_forward(
+        ctypes.byref(shape), ctypes.byref(plan), x.data_ptr(), W_node.data_ptr(), b_node.data_ptr(),
+        V_node.data_ptr(), W_out.data_ptr(), y.data_ptr(),
+        path_out.data_ptr() if path_out is not None else None,
+        workspace.data_ptr(), nbytes, _stream_handle(stream),
+        ctypes.byref(events) if events is not None else None)
+    if st != SUCCESS:
+        raise FFFError(st, "fff_forward")
+    return y, path_out
+
+
+def route(x, W_node, b_node, V_node, *, algo=ALGO_AUTO, split_level: int = -1, stream=None):
+    """Routing only: returns (H[T, P*h], path_out[T,P])."""
+    torch = _torch()
+    shape = shape_of(x, W_node, V_node)
+    _check([x, W_node, b_node, V_node], x.dtype, x.device)
+    plan = make_plan(algo, split_level)
+    workspace, nbytes = alloc_workspace(shape, plan, x.device)
+    H = torch.empty((shape.T, shape.P * shape.h), dtype=x.dtype, device=x.device)
+    path = torch.empty((shape.T, shape.P), dtype=torch.int32, device=x.device)
+    st = load_library().fff_route(ctypes.byref(shape), ctypes.byref(plan), x.data_ptr(),
+                                  W_node.data_ptr(), b_node.data_ptr(), V_node.data_ptr(),
+                                  H.data_ptr(), path.data_ptr(), workspace.data_ptr(), nbytes,
+                                  _stream_handle(stream))
+    if st != SUCCESS:
+        raise FFFError(st, "fff_route")
+    return H, path
+
+
+def project(H, W_out, *, algo=ALGO_AUTO, stream=None, y=None):
+    """y = H . W_out (fp32 accumulation)."""
+    torch = _torch()
+    T, K = H.shape
+    K2, d = W_out.shape
+    if K2 != K:
+        raise ValueError("H and W_out disagree on K")
+    _check([H, W_out], H.dtype, H.device)
+    # K = P*h with P=1, h=K describes the product for the library.
+    shape = make_shape(T, d, 1, 0, K, _dtype_code(H))
+    if y is None:
+        y = torch.empty((T, d), dtype=H.dtype, device=H.device)
+    if isinstance(algo, str):
+        algo = ALGOS[algo]
+    st = load_library().fff_project(ctypes.byref(shape), int(algo), H.data_ptr(), W_out.data_ptr(),
+                                    y.data_ptr(), _stream_handle(stream))
+    if st != SUCCESS:
+        raise FFFError(st, "fff_project")
+    return y

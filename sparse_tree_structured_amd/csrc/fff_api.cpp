@@ -1,0 +1,257 @@
+// C ABI of the FFF forward pass: host-side validation, planning, workspace
+// carving and kernel launches.  Validation runs before any HIP call, so every
+// error path is testable without a GPU.
+#include <hip/hip_runtime.h>
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/fff.h"
+#include "launch.hpp"
+
+namespace {
+
+using fff::Dims;
+
+constexpr int64_t kMaxElems = int64_t(1) << 40;
+constexpr size_t kWsAlign = 256;
+
+bool mul_ok(int64_t a, int64_t b, int64_t limit) { return a == 0 || b <= limit / a; }
+
+fff_status_t check_shape(const fff_shape_t* s, Dims* out) {
+  if (!s) return FFF_ERROR_INVALID_VALUE;
+  if (s->dtype != FFF_DTYPE_F32 && s->dtype != FFF_DTYPE_BF16) return FFF_ERROR_NOT_SUPPORTED;
+  if (s->T < 0 || s->T > INT32_MAX || s->d <= 0 || s->P <= 0 || s->h <= 0 || s->D < 0 ||
+      s->D > FFF_MAX_DEPTH || s->d > (1 << 22))
+    return FFF_ERROR_INVALID_VALUE;
+  Dims d;
+  d.T = s->T;
+  d.d = s->d;
+  d.P = s->P;
+  d.D = s->D;
+  d.h = s->h;
+  d.dtype = s->dtype;
+  d.N = (int64_t(1) << (s->D + 1)) - 1;
+  d.K = int64_t(s->P) * s->h;
+  d.esize = s->dtype == FFF_DTYPE_F32 ? 4 : 2;
+  // Every tensor must stay below 2^40 elements, and T*P below 2^31.
+  if (!mul_ok(d.T, d.d, kMaxElems) || !mul_ok(int64_t(d.P) * d.N, d.d, kMaxElems) ||
+      !mul_ok(int64_t(d.P) * d.N, d.h, kMaxElems) || !mul_ok(d.K, d.d, kMaxElems) ||
+      !mul_ok(d.T, d.K, kMaxElems) || !mul_ok(d.T, int64_t(d.P) * (d.D + 1), kMaxElems) ||
+      d.T * d.P > INT32_MAX || d.K > INT32_MAX)
+    return FFF_ERROR_INVALID_VALUE;
+  *out = d;
+  return FFF_SUCCESS;
+}
+
+bool prefill_fits(const Dims& s) {
+  return s.dtype == FFF_DTYPE_BF16 && s.d % 64 == 0 && s.h % 64 == 0 && s.K % 64 == 0;
+}
+
+fff_status_t resolve_plan(const Dims& s, const fff_plan_t* in, fff_plan_t* out) {
+  fff_plan_t p;
+  p.algo = in ? in->algo : FFF_ALGO_AUTO;
+  p.split_level = in ? in->split_level : -1;
+  if (p.algo == FFF_ALGO_AUTO) p.algo = prefill_fits(s) ? FFF_ALGO_PREFILL : FFF_ALGO_GENERIC;
+  switch (p.algo) {
+    case FFF_ALGO_GENERIC:
+      p.split_level = 0;
+      break;
+    case FFF_ALGO_PREFILL:
+      if (!prefill_fits(s)) return FFF_ERROR_NOT_SUPPORTED;
+      p.split_level = 0;
+      break;
+    case FFF_ALGO_DECODE:
+      return FFF_ERROR_NOT_SUPPORTED;
+    default:
+      return FFF_ERROR_INVALID_VALUE;
+  }
+  *out = p;
+  return FFF_SUCCESS;
+}
+
+// Workspace carve-up.  Offsets are multiples of kWsAlign.
+struct Layout {
+  size_t logits = 0, leaf = 0, H = 0;  // offsets
+  size_t total = 0;
+};
+
+size_t align_up(size_t v) { return (v + kWsAlign - 1) / kWsAlign * kWsAlign; }
+
+Layout layout_for(const Dims& s, const fff_plan_t& p) {
+  (void)p;
+  Layout L;
+  size_t off = 0;
+  L.logits = off;
+  off = align_up(off + size_t(s.T) * s.P * (s.D + 1) * sizeof(float));
+  L.leaf = off;
+  off = align_up(off + size_t(s.T) * s.P * sizeof(int32_t));
+  L.H = off;
+  off = align_up(off + size_t(s.T) * size_t(s.K) * s.esize);
+  L.total = off;
+  return L;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+fff_status_t hip_status(hipError_t e) { return e == hipSuccess ? FFF_SUCCESS : FFF_ERROR_HIP; }
+
+fff_status_t record(hipEvent_t ev, hipStream_t st) {
+  if (!ev) return FFF_SUCCESS;
+  return hip_status(hipEventRecord(ev, st));
+}
+
+// Routing stage into H (caller or workspace buffer).
+fff_status_t run_route(const Dims& s, const fff_plan_t& p, const Layout& L, const void* x,
+                       const void* W, const void* b, const void* V, void* H, int32_t* path_out,
+                       char* ws, hipStream_t st) {
+  (void)p;
+  float* logits = reinterpret_cast<float*>(ws + L.logits);
+  int32_t* leaf = reinterpret_cast<int32_t*>(ws + L.leaf);
+  hipError_t e = fff::launch_route_generic(s, x, W, b, logits, path_out, leaf, st);
+  if (e != hipSuccess) return FFF_ERROR_HIP;
+  e = fff::launch_hbuild_generic(s, logits, leaf, V, H, st);
+  return hip_status(e);
+}
+
+fff_status_t run_project(const Dims& s, int32_t algo, const void* H, const void* Wout, void* y,
+                         hipStream_t st) {
+  hipError_t e;
+  if (algo != FFF_ALGO_GENERIC && fff::project_mfma_supported(s))
+    e = fff::launch_project_mfma(s, H, Wout, y, st);
+  else
+    e = fff::launch_project_generic(s, H, Wout, y, st);
+  return hip_status(e);
+}
+
+fff_status_t check_inputs(const Dims& s, const void* x, const void* W, const void* b,
+                          const void* V) {
+  if (!x || !W || !b || !V) return FFF_ERROR_INVALID_VALUE;
+  if (!aligned(x, 16) || !aligned(W, 16) || !aligned(V, 16) || !aligned(b, s.esize))
+    return FFF_ERROR_INVALID_VALUE;
+  return FFF_SUCCESS;
+}
+
+}  // namespace
+
+extern "C" {
+
+fff_status_t fff_plan_default(const fff_shape_t* shape, fff_plan_t* plan) {
+  Dims s;
+  fff_status_t st = check_shape(shape, &s);
+  if (st != FFF_SUCCESS) return st;
+  if (!plan) return FFF_ERROR_INVALID_VALUE;
+  return resolve_plan(s, nullptr, plan);
+}
+
+fff_status_t fff_workspace_size(const fff_shape_t* shape, const fff_plan_t* plan, size_t* bytes) {
+  Dims s;
+  fff_status_t st = check_shape(shape, &s);
+  if (st != FFF_SUCCESS) return st;
+  if (!bytes) return FFF_ERROR_INVALID_VALUE;
+  fff_plan_t p;
+  st = resolve_plan(s, plan, &p);
+  if (st != FFF_SUCCESS) return st;
+  *bytes = s.T == 0 ? 0 : layout_for(s, p).total;
+  return FFF_SUCCESS;
+}
+
+fff_status_t fff_forward(const fff_shape_t* shape, const fff_plan_t* plan, const void* x,
+                         const void* W_node, const void* b_node, const void* V_node,
+                         const void* W_out, void* y, int32_t* path_out, void* workspace,
+                         size_t workspace_bytes, hipStream_t stream,
+                         const fff_stage_events_t* events) {
+  Dims s;
+  fff_status_t st = check_shape(shape, &s);
+  if (st != FFF_SUCCESS) return st;
+  fff_plan_t p;
+  st = resolve_plan(s, plan, &p);
+  if (st != FFF_SUCCESS) return st;
+  if (s.T == 0) return FFF_SUCCESS;
+  st = check_inputs(s, x, W_node, b_node, V_node);
+  if (st != FFF_SUCCESS) return st;
+  if (!W_out || !y || !aligned(W_out, 16) || !aligned(y, 16) ||
+      (path_out && !aligned(path_out, 4)))
+    return FFF_ERROR_INVALID_VALUE;
+  const Layout L = layout_for(s, p);
+  if (L.total > 0 && (!workspace || workspace_bytes < L.total)) return FFF_ERROR_WORKSPACE;
+  if (workspace && !aligned(workspace, kWsAlign)) return FFF_ERROR_INVALID_VALUE;
+
+  char* ws = static_cast<char*>(workspace);
+  void* H = ws + L.H;
+  if (events && (st = record(events->start, stream)) != FFF_SUCCESS) return st;
+  st = run_route(s, p, L, x, W_node, b_node, V_node, H, path_out, ws, stream);
+  if (st != FFF_SUCCESS) return st;
+  if (events && (st = record(events->routed, stream)) != FFF_SUCCESS) return st;
+  st = run_project(s, p.algo, H, W_out, y, stream);
+  if (st != FFF_SUCCESS) return st;
+  if (events && (st = record(events->done, stream)) != FFF_SUCCESS) return st;
+  return FFF_SUCCESS;
+}
+
+fff_status_t fff_route(const fff_shape_t* shape, const fff_plan_t* plan, const void* x,
+                       const void* W_node, const void* b_node, const void* V_node, void* H,
+                       int32_t* path_out, void* workspace, size_t workspace_bytes,
+                       hipStream_t stream) {
+  Dims s;
+  fff_status_t st = check_shape(shape, &s);
+  if (st != FFF_SUCCESS) return st;
+  fff_plan_t p;
+  st = resolve_plan(s, plan, &p);
+  if (st != FFF_SUCCESS) return st;
+  if (s.T == 0) return FFF_SUCCESS;
+  st = check_inputs(s, x, W_node, b_node, V_node);
+  if (st != FFF_SUCCESS) return st;
+  if (!H || !aligned(H, 16) || (path_out && !aligned(path_out, 4))) return FFF_ERROR_INVALID_VALUE;
+  const Layout L = layout_for(s, p);
+  if (L.total > 0 && (!workspace || workspace_bytes < L.total)) return FFF_ERROR_WORKSPACE;
+  if (workspace && !aligned(workspace, kWsAlign)) return FFF_ERROR_INVALID_VALUE;
+  return run_route(s, p, L, x, W_node, b_node, V_node, H, path_out, static_cast<char*>(workspace),
+                   stream);
+}
+
+fff_status_t fff_project(const fff_shape_t* shape, int32_t algo, const void* H, const void* W_out,
+                         void* y, hipStream_t stream) {
+  Dims s;
+  fff_status_t st = check_shape(shape, &s);
+  if (st != FFF_SUCCESS) return st;
+  if (algo != FFF_ALGO_AUTO && algo != FFF_ALGO_GENERIC && algo != FFF_ALGO_PREFILL)
+    return FFF_ERROR_INVALID_VALUE;
+  if (algo == FFF_ALGO_PREFILL && !fff::project_mfma_supported(s)) return FFF_ERROR_NOT_SUPPORTED;
+  if (s.T == 0) return FFF_SUCCESS;
+  if (!H || !W_out || !y || !aligned(H, 16) || !aligned(W_out, 16) || !aligned(y, 16))
+    return FFF_ERROR_INVALID_VALUE;
+  return run_project(s, algo, H, W_out, y, stream);
+}
+
+const char* fff_status_string(fff_status_t status) {
+  switch (status) {
+    case FFF_SUCCESS:
+      return "success";
+    case FFF_ERROR_INVALID_VALUE:
+      return "invalid value (shape, null or misaligned pointer)";
+    case FFF_ERROR_NOT_SUPPORTED:
+      return "not supported (dtype or plan)";
+    case FFF_ERROR_WORKSPACE:
+      return "workspace missing or too small";
+    case FFF_ERROR_HIP:
+      return "HIP runtime or launch error";
+  }
+  return "unknown status";
+}
+
+const char* fff_algo_name(int32_t algo) {
+  switch (algo) {
+    case FFF_ALGO_AUTO:
+      return "auto";
+    case FFF_ALGO_GENERIC:
+      return "generic";
+    case FFF_ALGO_PREFILL:
+      return "prefill";
+    case FFF_ALGO_DECODE:
+      return "decode";
+  }
+  return "unknown";
+}
+
+}  // extern "C"

@@ -1,0 +1,39 @@
+// Host-side launchers of the gfx950 kernels.  Each enqueues its kernel(s) on
+// `stream` and returns hipGetLastError().  Shapes have been validated by the
+// C-ABI layer before any of these is called.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace fff {
+
+struct Dims {
+  int64_t T;
+  int d, P, D, h;
+  int dtype;  // fff_dtype_t
+  int64_t N;  // 2^(D+1) - 1
+  int64_t K;  // P * h
+  size_t esize;
+};
+
+// ---- generic path: any shape, fp32 or bf16 ----
+// Per (token, tree) logits of the visited nodes -> logits[T,P,D+1] (fp32) and
+// path_out (may be null).
+hipError_t launch_route_generic(const Dims& s, const void* x, const void* W, const void* b,
+                                float* logits, int32_t* path_out, int32_t* leaf_ws,
+                                hipStream_t st);
+// H[t, p*h + j] = sum over levels of GELU(a_l) * V[p, n_l, j].
+hipError_t launch_hbuild_generic(const Dims& s, const float* logits, const int32_t* leaf_ws,
+                                 const void* V, void* H, hipStream_t st);
+// y = H . W_out with fp32 accumulation.
+hipError_t launch_project_generic(const Dims& s, const void* H, const void* Wout, void* y,
+                                  hipStream_t st);
+
+// ---- matrix-core projection (bf16, K % 64 == 0, d % 64 == 0) ----
+bool project_mfma_supported(const Dims& s);
+hipError_t launch_project_mfma(const Dims& s, const void* H, const void* Wout, void* y,
+                               hipStream_t st);
+
+}  // namespace fff

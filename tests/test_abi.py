@@ -1,0 +1,131 @@
+"""The C-ABI library on the CPU: it loads, exports what include/fff.h
+declares, and its host-side validation returns the documented codes before
+any HIP call (only error paths and T=0 are exercised here; no kernel runs)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import sparse_tree_structured_amd as fff
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fff.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(fff.LIBRARY):
+        from sparse_tree_structured_amd import build
+        build.build()
+    return fff.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fff_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert set(names) == set(fff.EXPORTS)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings(lib):
+    for code in range(5):
+        assert fff.status_string(code)
+    assert fff.status_string(99) == "unknown status"
+    assert [fff.algo_name(a) for a in range(4)] == ["auto", "generic", "prefill", "decode"]
+
+
+def _shape(**kw):
+    base = dict(T=64, d=64, P=2, D=3, h=32, dtype=fff.DTYPE_BF16)
+    base.update(kw)
+    return fff.make_shape(**base)
+
+
+FAKE = 0x10000  # an aligned, never-dereferenced address: validation fails first
+
+
+def _forward(lib, shape, plan=None, ptrs=None, path=FAKE, ws=FAKE, ws_bytes=1 << 40):
+    p = dict(x=FAKE, W=FAKE, b=FAKE, V=FAKE, Wo=FAKE, y=FAKE)
+    p.update(ptrs or {})
+    return lib.fff_forward(ctypes.byref(shape), ctypes.byref(plan) if plan else None, p["x"], p["W"],
+                           p["b"], p["V"], p["Wo"], p["y"], path, ws, ws_bytes, None, None)
+
+
+@pytest.mark.parametrize("kw", [dict(T=-1), dict(d=0), dict(P=0), dict(h=0), dict(D=-1),
+                                dict(D=fff.MAX_DEPTH + 1), dict(T=1 << 31), dict(d=(1 << 22) + 1),
+                                dict(T=1 << 30, P=4)])
+def test_bad_shapes(lib, kw):
+    assert _forward(lib, _shape(**kw)) == fff.ERROR_INVALID_VALUE
+    n = ctypes.c_size_t()
+    assert lib.fff_workspace_size(ctypes.byref(_shape(**kw)), None, ctypes.byref(n)) == \
+        fff.ERROR_INVALID_VALUE
+
+
+def test_unknown_dtype(lib):
+    assert _forward(lib, _shape(dtype=7)) == fff.ERROR_NOT_SUPPORTED
+
+
+def test_null_shape_and_outputs(lib):
+    n = ctypes.c_size_t()
+    assert lib.fff_workspace_size(None, None, ctypes.byref(n)) == fff.ERROR_INVALID_VALUE
+    assert lib.fff_workspace_size(ctypes.byref(_shape()), None, None) == fff.ERROR_INVALID_VALUE
+    assert lib.fff_plan_default(ctypes.byref(_shape()), None) == fff.ERROR_INVALID_VALUE
+
+
+@pytest.mark.parametrize("which", ["x", "W", "b", "V", "Wo", "y"])
+def test_null_pointers(lib, which):
+    assert _forward(lib, _shape(), ptrs={which: None}) == fff.ERROR_INVALID_VALUE
+
+
+@pytest.mark.parametrize("which", ["x", "W", "V", "Wo", "y"])
+def test_misaligned_pointers(lib, which):
+    assert _forward(lib, _shape(), ptrs={which: FAKE + 2}) == fff.ERROR_INVALID_VALUE
+
+
+def test_misaligned_bias_and_path(lib):
+    assert _forward(lib, _shape(dtype=fff.DTYPE_F32), ptrs={"b": FAKE + 2}) == fff.ERROR_INVALID_VALUE
+    assert _forward(lib, _shape(), path=FAKE + 2) == fff.ERROR_INVALID_VALUE
+
+
+def test_workspace_checks(lib):
+    s = _shape()
+    need = fff.workspace_size(s)
+    assert need > 0
+    assert _forward(lib, s, ws_bytes=need - 1) == fff.ERROR_WORKSPACE
+    assert _forward(lib, s, ws=None) == fff.ERROR_WORKSPACE
+    assert _forward(lib, s, ws=FAKE + 16) == fff.ERROR_INVALID_VALUE
+
+
+def test_zero_tokens_is_a_noop(lib):
+    s = _shape(T=0)
+    assert fff.workspace_size(s) == 0
+    nulls = dict(x=None, W=None, b=None, V=None, Wo=None, y=None)
+    assert _forward(lib, s, ptrs=nulls, path=None, ws=None, ws_bytes=0) == fff.SUCCESS
+    assert lib.fff_project(ctypes.byref(s), fff.ALGO_AUTO, None, None, None, None) == fff.SUCCESS
+
+
+def test_plans(lib):
+    p = fff.plan_default(_shape(dtype=fff.DTYPE_F32))
+    assert p.algo == fff.ALGO_GENERIC
+    p = fff.plan_default(_shape(T=16384, d=2048, P=32, D=6, h=128))
+    assert p.algo in (fff.ALGO_PREFILL, fff.ALGO_DECODE)
+    # PREFILL needs bf16 and 64-aligned widths.
+    bad = fff.make_plan(fff.ALGO_PREFILL)
+    assert _forward(lib, _shape(dtype=fff.DTYPE_F32), plan=bad) == fff.ERROR_NOT_SUPPORTED
+    assert _forward(lib, _shape(d=72), plan=bad) == fff.ERROR_NOT_SUPPORTED
+    assert _forward(lib, _shape(), plan=fff.make_plan(9)) == fff.ERROR_INVALID_VALUE
+
+
+def test_project_validation(lib):
+    s = _shape()
+    assert lib.fff_project(ctypes.byref(s), 7, FAKE, FAKE, FAKE, None) == fff.ERROR_INVALID_VALUE
+    assert lib.fff_project(ctypes.byref(s), fff.ALGO_AUTO, None, FAKE, FAKE, None) == \
+        fff.ERROR_INVALID_VALUE
+    assert lib.fff_project(ctypes.byref(_shape(dtype=fff.DTYPE_F32)), fff.ALGO_PREFILL, FAKE, FAKE,
+                           FAKE, None) == fff.ERROR_NOT_SUPPORTED

@@ -1,0 +1,163 @@
+"""Parity of the HIP path with the CPU oracle, through the C ABI, on the GPU.
+
+Paths: every token, bit-exact except counted near-ties.  y: every token for
+the small workloads, sampled tokens (including the first and last) at full
+size; tolerance 1e-4 for fp32 and 2e-2 for bf16 (max elementwise relative
+error with the denominator floored at the row RMS).
+"""
+import functools
+
+import numpy as np
+import pytest
+import torch
+
+import workloads
+from gpu_helpers import check, run, sample_rows, to_device, to_f64
+
+pytestmark = pytest.mark.gpu
+
+needs_gpu = pytest.mark.skipif(not torch.cuda.is_available(), reason="no GPU")
+
+
+@functools.lru_cache(maxsize=None)
+def wl(name):
+    return workloads.workload(name)
+
+
+ALL = ["tiny", "gpt125m", "opt1p3b_d4", "opt1p3b_d6", "decode_skew_t1", "decode_skew_t8",
+       "decode_skew_t64"]
+
+
+@needs_gpu
+@pytest.mark.parametrize("name", ALL)
+def test_workload_default_plan(name):
+    inp = wl(name)
+    y, path = run(inp)
+    sample = None if inp.shape.T <= 1024 else sample_rows(inp.shape.T)
+    r = check(inp, y, path, sample=sample)
+    print(name, r)
+
+
+@needs_gpu
+@pytest.mark.parametrize("name", ["tiny", "gpt125m", "decode_skew_t64"])
+def test_workload_generic(name):
+    inp = wl(name)
+    y, path = run(inp, algo="generic")
+    sample = None if inp.shape.T <= 1024 else sample_rows(inp.shape.T, n=32)
+    check(inp, y, path, sample=sample)
+
+
+SHAPES = [
+    # T, d, P, D, h, dtype
+    (1, 64, 1, 0, 64, "bf16"),
+    (1000, 128, 3, 4, 64, "bf16"),     # ragged T
+    (333, 192, 2, 7, 128, "bf16"),
+    (77, 64, 4, 10, 64, "bf16"),       # deep trees
+    (50, 37, 3, 3, 5, "bf16"),         # odd widths -> generic
+    (50, 37, 3, 3, 5, "f32"),
+    (129, 96, 5, 2, 24, "f32"),
+    (1, 1, 1, 0, 1, "f32"),
+    (257, 256, 2, 6, 64, "bf16"),
+]
+
+
+@needs_gpu
+@pytest.mark.parametrize("shape", SHAPES, ids=[str(s) for s in SHAPES])
+def test_shape_sweep(shape):
+    T, d, P, D, h, dt = shape
+    inp = workloads.random_inputs(T, d, P, D, h, dt, seed=3, unit_rms_x=True)
+    y, path = run(inp)
+    check(inp, y, path)
+
+
+@needs_gpu
+def test_zero_weights_route_right():
+    inp = workloads.random_inputs(100, 128, 2, 5, 64, "bf16", seed=1)
+    inp.W_node[:] = 0
+    inp.b_node[:] = 0
+    y, path = run(inp)
+    assert (path == (1 << 5) - 1).all()
+    assert (y == 0).all()
+
+
+@needs_gpu
+def test_hand_built_routing():
+    # w_n = s_p * e_level(n), x in {+-1}: leaf bits are [s_p x_l > 0].
+    D, P, T, d, h = 5, 2, 256, 64, 64
+    inp = workloads.random_inputs(T, d, P, D, h, "bf16", seed=2)
+    N = (1 << (D + 1)) - 1
+    rng = np.random.default_rng(0)
+    xs = rng.choice([-1.0, 1.0], size=(T, D + 1))
+    x = np.zeros((T, d))
+    x[:, :D + 1] = xs
+    W = np.zeros((P, N, d))
+    s = np.array([1.0, -1.0])
+    for n in range(N):
+        W[:, n, int(np.log2(n + 1))] = s
+    inp.x[:] = workloads.round_to_bf16_bits(x)
+    inp.W_node[:] = workloads.round_to_bf16_bits(W)
+    inp.b_node[:] = 0
+    y, path = run(inp)
+    for p in range(P):
+        leaf = np.zeros(T, dtype=np.int64)
+        for lvl in range(D):
+            leaf |= (s[p] * xs[:, lvl] > 0).astype(np.int64) << (D - 1 - lvl)
+        np.testing.assert_array_equal(path[:, p], leaf)
+    check(inp, y, path)
+
+
+@needs_gpu
+def test_deterministic():
+    inp = wl("gpt125m")
+    y1, p1 = run(inp)
+    y2, p2 = run(inp)
+    np.testing.assert_array_equal(p1, p2)
+    np.testing.assert_array_equal(y1, y2)
+
+
+@needs_gpu
+def test_batch_invariance_decode():
+    paths = {}
+    for T in (1, 8, 64):
+        _, paths[T] = run(wl(f"decode_skew_t{T}"))
+    np.testing.assert_array_equal(paths[8], paths[64][:8])
+    np.testing.assert_array_equal(paths[1], paths[64][:1])
+
+
+@needs_gpu
+def test_empty_leaves_in_skewed_workload():
+    _, path = run(wl("decode_skew_t64"))
+    used = np.zeros((path.shape[1], 64), dtype=bool)
+    for p in range(path.shape[1]):
+        used[p, path[:, p]] = True
+    empty = 1.0 - used.mean()
+    assert empty > 0.3, empty  # the raised biases starve whole subtrees
+
+
+@needs_gpu
+def test_zero_tokens():
+    import sparse_tree_structured_amd as fff
+    inp = workloads.random_inputs(0, 64, 2, 3, 64, "bf16")
+    T = to_device(inp)
+    y, path = fff.forward(T["x"], T["W_node"], T["b_node"], T["V_node"], T["W_out"])
+    torch.cuda.synchronize()
+    assert y.shape == (0, 64) and path.shape == (0, 2)
+
+
+@needs_gpu
+@pytest.mark.parametrize("M,K,N", [(16384, 4096, 2048), (1000, 1024, 768), (1, 64, 8), (129, 192, 72)])
+def test_projection_matches_fp64(M, K, N):
+    import sparse_tree_structured_amd as fff
+    g = torch.Generator().manual_seed(M + K + N)
+    H = torch.randn(M, K, generator=g).to(torch.bfloat16)
+    Wo = (torch.randn(K, N, generator=g) / K ** 0.5).to(torch.bfloat16)
+    rows = sample_rows(M, n=64)
+    ref = H[rows].double() @ Wo.double()
+    for algo in ("prefill", "generic"):
+        if algo == "prefill" and K % 64:
+            continue
+        y = fff.project(H.cuda(), Wo.cuda(), algo=algo)
+        torch.cuda.synchronize()
+        got = to_f64(y)[rows]
+        err = np.abs(got - ref.numpy()) / np.maximum(np.abs(ref.numpy()), 1e-2)
+        assert err.max() < 2e-2, (algo, err.max())
