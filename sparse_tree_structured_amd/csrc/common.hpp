@@ -16,10 +16,10 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
 
 // fp32 -> bf16, round to nearest even; NaN stays a (quiet) NaN.
 __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return static_cast<uint16_t>(u >> 16);
+  const uint32_t u = __float_as_uint(f);
+  const uint32_t rounded = (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+  const uint32_t quiet_nan = (u >> 16) | 0x40u;
+  return static_cast<uint16_t>(((u & 0x7fffffffu) > 0x7f800000u) ? quiet_nan : rounded);
 }
 
 // Two bf16 in one dword: low half is the lower index.

@@ -45,8 +45,12 @@ fff_status_t check_shape(const fff_shape_t* s, Dims* out) {
 }
 
 bool prefill_fits(const Dims& s) {
-  return s.dtype == FFF_DTYPE_BF16 && s.d % 64 == 0 && s.h % 64 == 0 && s.K % 64 == 0;
+  return s.dtype == FFF_DTYPE_BF16 && s.d % 64 == 0 && s.h % 64 == 0 && s.K % 64 == 0 &&
+         fff::route_top_supported(s, s.D + 1);
 }
+
+// Levels evaluated by the dense top-level product.
+int default_split(const Dims& s) { return s.D + 1; }
 
 fff_status_t resolve_plan(const Dims& s, const fff_plan_t* in, fff_plan_t* out) {
   fff_plan_t p;
@@ -59,7 +63,8 @@ fff_status_t resolve_plan(const Dims& s, const fff_plan_t* in, fff_plan_t* out) 
       break;
     case FFF_ALGO_PREFILL:
       if (!prefill_fits(s)) return FFF_ERROR_NOT_SUPPORTED;
-      p.split_level = 0;
+      if (p.split_level < 0) p.split_level = default_split(s);
+      if (p.split_level != s.D + 1) return FFF_ERROR_NOT_SUPPORTED;
       break;
     case FFF_ALGO_DECODE:
       return FFF_ERROR_NOT_SUPPORTED;
@@ -71,6 +76,10 @@ fff_status_t resolve_plan(const Dims& s, const fff_plan_t* in, fff_plan_t* out) 
 }
 
 // Workspace carve-up.  Offsets are multiples of kWsAlign.
+//   logits  per (token, tree) fp32 logits of the densely evaluated levels
+//           (all D+1 levels on the generic path)
+//   leaf    per (token, tree) int32 node state
+//   H       concatenated tree outputs [T, P*h] in the layer dtype
 struct Layout {
   size_t logits = 0, leaf = 0, H = 0;  // offsets
   size_t total = 0;
@@ -79,11 +88,11 @@ struct Layout {
 size_t align_up(size_t v) { return (v + kWsAlign - 1) / kWsAlign * kWsAlign; }
 
 Layout layout_for(const Dims& s, const fff_plan_t& p) {
-  (void)p;
+  const int levels = p.algo == FFF_ALGO_PREFILL ? p.split_level : s.D + 1;
   Layout L;
   size_t off = 0;
   L.logits = off;
-  off = align_up(off + size_t(s.T) * s.P * (s.D + 1) * sizeof(float));
+  off = align_up(off + size_t(s.T) * s.P * levels * sizeof(float));
   L.leaf = off;
   off = align_up(off + size_t(s.T) * s.P * sizeof(int32_t));
   L.H = off;
@@ -105,10 +114,16 @@ fff_status_t record(hipEvent_t ev, hipStream_t st) {
 fff_status_t run_route(const Dims& s, const fff_plan_t& p, const Layout& L, const void* x,
                        const void* W, const void* b, const void* V, void* H, int32_t* path_out,
                        char* ws, hipStream_t st) {
-  (void)p;
   float* logits = reinterpret_cast<float*>(ws + L.logits);
   int32_t* leaf = reinterpret_cast<int32_t*>(ws + L.leaf);
-  hipError_t e = fff::launch_route_generic(s, x, W, b, logits, path_out, leaf, st);
+  hipError_t e;
+  if (p.algo == FFF_ALGO_PREFILL) {
+    e = fff::launch_route_top(s, p.split_level, x, W, b, logits, leaf, st);
+    if (e != hipSuccess) return FFF_ERROR_HIP;
+    e = fff::launch_hbuild(s, logits, leaf, V, H, path_out, st);
+    return hip_status(e);
+  }
+  e = fff::launch_route_generic(s, x, W, b, logits, path_out, leaf, st);
   if (e != hipSuccess) return FFF_ERROR_HIP;
   e = fff::launch_hbuild_generic(s, logits, leaf, V, H, st);
   return hip_status(e);

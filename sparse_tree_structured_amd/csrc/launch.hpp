@@ -36,4 +36,15 @@ bool project_mfma_supported(const Dims& s);
 hipError_t launch_project_mfma(const Dims& s, const void* H, const void* Wout, void* y,
                                hipStream_t st);
 
+// ---- prefill routing (bf16) ----
+// Dense evaluation of tree levels 0..L-1 (L <= 8) with the walk over them:
+// rec_logit[p][t][l] (fp32) and rec_next[p][t] (heap id at level L, or the
+// leaf when L = D+1).
+bool route_top_supported(const Dims& s, int L);
+hipError_t launch_route_top(const Dims& s, int L, const void* x, const void* W, const void* b,
+                            float* rec_logit, int32_t* rec_next, hipStream_t st);
+// H and path_out from fully routed records (L = D+1).
+hipError_t launch_hbuild(const Dims& s, const float* rec_logit, const int32_t* rec_next,
+                         const void* V, void* H, int32_t* path_out, hipStream_t st);
+
 }  // namespace fff
