@@ -37,6 +37,7 @@ def parse():
     ap.add_argument("--workload", default="opt1p3b_d6")
     ap.add_argument("--algo", default="auto")
     ap.add_argument("--split-level", type=int, default=-1)
+    ap.add_argument("--chunk-tokens", type=int, default=0)
     ap.add_argument("--rotate", type=int, default=0, help="input sets (0 = by footprint)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="oracle sample budget")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -124,7 +125,6 @@ def main():
     import torch
 
     import sparse_tree_structured_amd as fff
-    from sparse_tree_structured_amd.hiprt import Event
     import workloads
 
     dev = torch.device("cuda:0")
@@ -148,10 +148,8 @@ def main():
                              for s in range(1, rotate)]
     torch.cuda.synchronize()
 
-    plan = fff.make_plan(args.algo, args.split_level)
     fshape = fff.shape_of(sets[0][0], sets[0][1], sets[0][3])
-    if plan.algo == fff.ALGO_AUTO:
-        plan = fff.plan_default(fshape)
+    plan = fff.resolve_plan(fshape, fff.make_plan(args.algo, args.split_level, args.chunk_tokens))
     ws, nbytes = fff.alloc_workspace(fshape, plan, dev)
     y = torch.empty((shape.T, shape.d), dtype=sets[0][0].dtype, device=dev)
     path = torch.empty((shape.T, shape.P), dtype=torch.int32, device=dev)
@@ -159,25 +157,32 @@ def main():
 
     def step(i, ev=None):
         x, W, b, V, Wo = sets[i % rotate]
-        fff.forward(x, W, b, V, Wo, algo=plan.algo, split_level=plan.split_level, workspace=ws,
-                    y=y, path_out=path, stream=stream, events=ev)
+        fff.forward(x, W, b, V, Wo, algo=plan.algo, split_level=plan.split_level,
+                    chunk_tokens=plan.chunk_tokens, workspace=ws, y=y, path_out=path, stream=stream,
+                    events=ev)
 
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
 
-    evs = [(Event(), Event(), Event()) for _ in range(args.steps)]
-    sev = [fff.StageEvents(a.ptr, b.ptr, c.ptr) for a, b, c in evs]
+    # HIP events (torch-created, so profilers see ordinary events) that the
+    # library records on `stream` around its stages.  Record each once so the
+    # underlying event exists before its handle is passed on.
+    evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in range(args.steps)]
+    for trio in evs:
+        for e in trio:
+            e.record(stream)
     torch.cuda.synchronize()
+    sev = [fff.StageEvents(a.cuda_event, b.cuda_event, c.cuda_event) for a, b, c in evs]
     t0 = time.perf_counter()
     for i in range(args.steps):
         step(i, sev[i])
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
 
-    route_ms = [a.elapsed_ms(b) for a, b, _ in evs]
-    proj_ms = [b.elapsed_ms(c) for _, b, c in evs]
-    fwd_ms = [a.elapsed_ms(c) for a, _, c in evs]
+    route_ms = [a.elapsed_time(b) for a, b, _ in evs]
+    proj_ms = [b.elapsed_time(c) for _, b, c in evs]
+    fwd_ms = [a.elapsed_time(c) for a, _, c in evs]
 
     # Distinct visited (tree, node) pairs for the algorithmic byte count,
     # from the device's own paths on input set 0.
@@ -231,7 +236,8 @@ def main():
         "data": "synthetic (seeded Gaussian inputs and random-init weights of the named shape)",
         "config": {"workload": args.workload, "T": shape.T, "d": shape.d, "P": shape.P,
                    "D": shape.D, "h": shape.h, "algo": fff.algo_name(plan.algo),
-                   "split_level": plan.split_level, "rotated_sets": rotate,
+                   "split_level": plan.split_level, "chunk_tokens": plan.chunk_tokens,
+                   "rotated_sets": rotate,
                    "parallelism": "none (1 GPU)"},
         "roofline": roof,
         "layer": {"F_alg": f_route + f_proj, "B_alg": b_alg, "U": U,

@@ -88,7 +88,8 @@ typedef struct fff_shape {
 
 /* Algorithms.  AUTO picks by shape; the others force one (for tests and
  * measurement).  GENERIC takes any shape and dtype.  PREFILL needs bf16,
- * d % 64 == 0, h % 64 == 0 and (P*h) % 64 == 0.  DECODE needs bf16,
+ * d % 64 == 0, h % 64 == 0 and either 2^(D+1) <= 256 (every level dense) or
+ * a split level k with 2^k <= 256 and D-k <= 3.  DECODE needs bf16,
  * d % 256 == 0, h % 64 == 0 and T <= 64. */
 typedef enum fff_algo {
     FFF_ALGO_AUTO = 0,
@@ -98,10 +99,16 @@ typedef enum fff_algo {
 } fff_algo_t;
 
 typedef struct fff_plan {
-    int32_t algo;        /* fff_algo_t */
-    int32_t split_level; /* PREFILL: levels 0..k-1 evaluated as one dense
-                            matrix product, the rest per token bucket;
-                            -1 = choose by shape; ignored by other algos */
+    int32_t algo;         /* fff_algo_t */
+    int32_t split_level;  /* PREFILL: levels 0..k-1 are evaluated as one dense
+                             matrix product over all tokens; levels k..D (at
+                             most 4 of them) per bucket of tokens sharing a
+                             level-k node.  k = D+1 evaluates every level
+                             densely.  -1 = choose by shape; ignored by other
+                             algorithms */
+    int32_t chunk_tokens; /* PREFILL with k <= D: tokens per bucketing chunk
+                             (each chunk's x rows are reused from one XCD's
+                             L2 across all trees); 0 = choose by shape */
 } fff_plan_t;
 
 /* Optional events recorded on `stream` at stage boundaries (each may be
@@ -116,6 +123,11 @@ typedef struct fff_stage_events {
 
 /* Fill *plan with the choice FFF_ALGO_AUTO makes for this shape. */
 fff_status_t fff_plan_default(const fff_shape_t *shape, fff_plan_t *plan);
+
+/* Copy *in to *out with every 'choose by shape' field (algo AUTO,
+ * split_level -1, chunk_tokens 0) replaced by the value the library would
+ * use.  FFF_ERROR_NOT_SUPPORTED if the shape cannot run the requested plan. */
+fff_status_t fff_plan_resolve(const fff_shape_t *shape, const fff_plan_t *in, fff_plan_t *out);
 
 /* Workspace bytes the plan needs (plan NULL = the default plan).  The size
  * depends only on the shape and plan. */

@@ -39,7 +39,8 @@ class Shape(ctypes.Structure):
 
 
 class Plan(ctypes.Structure):
-    _fields_ = [("algo", ctypes.c_int32), ("split_level", ctypes.c_int32)]
+    _fields_ = [("algo", ctypes.c_int32), ("split_level", ctypes.c_int32),
+                ("chunk_tokens", ctypes.c_int32)]
 
 
 class StageEvents(ctypes.Structure):
@@ -52,8 +53,8 @@ class FFFError(RuntimeError):
         super().__init__(f"{what}: {status_string(status)} (status {status})")
 
 
-EXPORTS = ("fff_plan_default", "fff_workspace_size", "fff_forward", "fff_route", "fff_project",
-           "fff_status_string", "fff_algo_name")
+EXPORTS = ("fff_plan_default", "fff_plan_resolve", "fff_workspace_size", "fff_forward",
+           "fff_route", "fff_project", "fff_status_string", "fff_algo_name")
 
 _lib: Optional[ctypes.CDLL] = None
 
@@ -71,6 +72,7 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     vp, sz = ctypes.c_void_p, ctypes.c_size_t
     SP, PP = ctypes.POINTER(Shape), ctypes.POINTER(Plan)
     lib.fff_plan_default.argtypes = [SP, PP]
+    lib.fff_plan_resolve.argtypes = [SP, PP, PP]
     lib.fff_workspace_size.argtypes = [SP, PP, ctypes.POINTER(sz)]
     lib.fff_forward.argtypes = [SP, PP, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp,
                                 ctypes.POINTER(StageEvents)]
@@ -80,7 +82,8 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.fff_status_string.restype = ctypes.c_char_p
     lib.fff_algo_name.argtypes = [ctypes.c_int32]
     lib.fff_algo_name.restype = ctypes.c_char_p
-    for name in ("fff_plan_default", "fff_workspace_size", "fff_forward", "fff_route", "fff_project"):
+    for name in ("fff_plan_default", "fff_plan_resolve", "fff_workspace_size", "fff_forward",
+                 "fff_route", "fff_project"):
         getattr(lib, name).restype = ctypes.c_int
     if path is None:
         _lib = lib
@@ -99,10 +102,10 @@ def make_shape(T: int, d: int, P: int, D: int, h: int, dtype: int) -> Shape:
     return Shape(int(T), int(d), int(P), int(D), int(h), int(dtype))
 
 
-def make_plan(algo=ALGO_AUTO, split_level: int = -1) -> Plan:
+def make_plan(algo=ALGO_AUTO, split_level: int = -1, chunk_tokens: int = 0) -> Plan:
     if isinstance(algo, str):
         algo = ALGOS[algo]
-    return Plan(int(algo), int(split_level))
+    return Plan(int(algo), int(split_level), int(chunk_tokens))
 
 
 def plan_default(shape: Shape) -> Plan:
@@ -111,6 +114,15 @@ def plan_default(shape: Shape) -> Plan:
     if st != SUCCESS:
         raise FFFError(st, "fff_plan_default")
     return p
+
+
+def resolve_plan(shape: Shape, plan: Plan) -> Plan:
+    """The plan as the library would run it ('choose by shape' fields filled in)."""
+    out = Plan()
+    st = load_library().fff_plan_resolve(ctypes.byref(shape), ctypes.byref(plan), ctypes.byref(out))
+    if st != SUCCESS:
+        raise FFFError(st, "fff_plan_resolve")
+    return out
 
 
 def workspace_size(shape: Shape, plan: Optional[Plan] = None) -> int:
@@ -169,13 +181,13 @@ def alloc_workspace(shape: Shape, plan: Optional[Plan], device):
 
 
 def forward(x, W_node, b_node, V_node, W_out, *, algo=ALGO_AUTO, split_level: int = -1,
-            want_path: bool = True, workspace=None, y=None, path_out=None, stream=None,
-            events: Optional[StageEvents] = None) -> Tuple[object, Optional[object]]:
+            chunk_tokens: int = 0, want_path: bool = True, workspace=None, y=None, path_out=None,
+            stream=None, events: Optional[StageEvents] = None) -> Tuple[object, Optional[object]]:
     """y = FFF(x); returns (y, path_out[T,P] int32 or None)."""
     torch = _torch()
     shape = shape_of(x, W_node, V_node)
     _check([x, W_node, b_node, V_node, W_out], x.dtype, x.device)
-    plan = make_plan(algo, split_level)
+    plan = make_plan(algo, split_level, chunk_tokens)
     if workspace is None:
         workspace, nbytes = alloc_workspace(shape, plan, x.device)
     else:
@@ -195,12 +207,13 @@ def forward(x, W_node, b_node, V_node, W_out, *, algo=ALGO_AUTO, split_level: in
     return y, path_out
 
 
-def route(x, W_node, b_node, V_node, *, algo=ALGO_AUTO, split_level: int = -1, stream=None):
+def route(x, W_node, b_node, V_node, *, algo=ALGO_AUTO, split_level: int = -1,
+          chunk_tokens: int = 0, stream=None):
     """Routing only: returns (H[T, P*h], path_out[T,P])."""
     torch = _torch()
     shape = shape_of(x, W_node, V_node)
     _check([x, W_node, b_node, V_node], x.dtype, x.device)
-    plan = make_plan(algo, split_level)
+    plan = make_plan(algo, split_level, chunk_tokens)
     workspace, nbytes = alloc_workspace(shape, plan, x.device)
     H = torch.empty((shape.T, shape.P * shape.h), dtype=x.dtype, device=x.device)
     path = torch.empty((shape.T, shape.P), dtype=torch.int32, device=x.device)

@@ -44,27 +44,50 @@ fff_status_t check_shape(const fff_shape_t* s, Dims* out) {
   return FFF_SUCCESS;
 }
 
-bool prefill_fits(const Dims& s) {
-  return s.dtype == FFF_DTYPE_BF16 && s.d % 64 == 0 && s.h % 64 == 0 && s.K % 64 == 0 &&
-         fff::route_top_supported(s, s.D + 1);
+// Split levels the prefill algorithm can take for this shape.
+bool split_ok(const Dims& s, int k) {
+  if (k == s.D + 1) return fff::route_top_supported(s, k);
+  return k >= 1 && k <= s.D && fff::route_top_supported(s, k) && fff::deep_supported(s, k);
 }
 
-// Levels evaluated by the dense top-level product.
-int default_split(const Dims& s) { return s.D + 1; }
+// Every level dense whenever the tile fits a whole tree (2^(D+1) <= 256):
+// on MI355X the bucketed deep levels gather each token's x row once per tree
+// with little L2 reuse and measure slower than the dense product for the
+// shapes up to depth 7.  Deeper trees evaluate their last four levels per
+// token bucket.
+int default_split(const Dims& s) {
+  if (split_ok(s, s.D + 1)) return s.D + 1;
+  const int k = s.D - 3 > 1 ? s.D - 3 : 1;
+  return split_ok(s, k) ? k : -1;
+}
+
+bool prefill_fits(const Dims& s) {
+  return s.dtype == FFF_DTYPE_BF16 && s.d % 64 == 0 && s.h % 64 == 0 && s.K % 64 == 0 &&
+         default_split(s) > 0;
+}
 
 fff_status_t resolve_plan(const Dims& s, const fff_plan_t* in, fff_plan_t* out) {
   fff_plan_t p;
   p.algo = in ? in->algo : FFF_ALGO_AUTO;
   p.split_level = in ? in->split_level : -1;
+  p.chunk_tokens = in ? in->chunk_tokens : 0;
   if (p.algo == FFF_ALGO_AUTO) p.algo = prefill_fits(s) ? FFF_ALGO_PREFILL : FFF_ALGO_GENERIC;
   switch (p.algo) {
     case FFF_ALGO_GENERIC:
       p.split_level = 0;
+      p.chunk_tokens = 0;
       break;
     case FFF_ALGO_PREFILL:
       if (!prefill_fits(s)) return FFF_ERROR_NOT_SUPPORTED;
       if (p.split_level < 0) p.split_level = default_split(s);
-      if (p.split_level != s.D + 1) return FFF_ERROR_NOT_SUPPORTED;
+      if (!split_ok(s, p.split_level)) return FFF_ERROR_NOT_SUPPORTED;
+      if (p.chunk_tokens < 0) return FFF_ERROR_INVALID_VALUE;
+      if (p.split_level <= s.D) {
+        if (p.chunk_tokens == 0) p.chunk_tokens = static_cast<int32_t>(fff::deep_chunk(s));
+        if (p.chunk_tokens > s.T) p.chunk_tokens = static_cast<int32_t>(s.T > 0 ? s.T : 1);
+      } else {
+        p.chunk_tokens = 0;
+      }
       break;
     case FFF_ALGO_DECODE:
       return FFF_ERROR_NOT_SUPPORTED;
@@ -76,27 +99,44 @@ fff_status_t resolve_plan(const Dims& s, const fff_plan_t* in, fff_plan_t* out) 
 }
 
 // Workspace carve-up.  Offsets are multiples of kWsAlign.
-//   logits  per (token, tree) fp32 logits of the densely evaluated levels
+//   logits  per (tree, token) fp32 logits of the densely evaluated levels
 //           (all D+1 levels on the generic path)
-//   leaf    per (token, tree) int32 node state
+//   leaf    per (tree, token) int32 node state
+//   perm    per (tree, token) int32 token ids grouped by bucket (prefill, k <= D)
+//   offs    per (chunk, tree) bucket offsets, 2^k + 1 int32 each
 //   H       concatenated tree outputs [T, P*h] in the layer dtype
+//   WT      W_out transposed to [d, P*h] for the direct-to-LDS projection
+//           (prefill, large products only)
 struct Layout {
-  size_t logits = 0, leaf = 0, H = 0;  // offsets
+  size_t logits = 0, leaf = 0, perm = 0, offs = 0, H = 0, WT = 0;  // offsets
+  bool use_wt = false;
   size_t total = 0;
 };
 
 size_t align_up(size_t v) { return (v + kWsAlign - 1) / kWsAlign * kWsAlign; }
 
 Layout layout_for(const Dims& s, const fff_plan_t& p) {
-  const int levels = p.algo == FFF_ALGO_PREFILL ? p.split_level : s.D + 1;
+  const bool prefill = p.algo == FFF_ALGO_PREFILL;
+  const int levels = prefill ? p.split_level : s.D + 1;
+  const bool deep = prefill && p.split_level <= s.D;
   Layout L;
   size_t off = 0;
   L.logits = off;
   off = align_up(off + size_t(s.T) * s.P * levels * sizeof(float));
   L.leaf = off;
   off = align_up(off + size_t(s.T) * s.P * sizeof(int32_t));
+  L.perm = off;
+  if (deep) off = align_up(off + size_t(s.T) * s.P * sizeof(int32_t));
+  L.offs = off;
+  if (deep) {
+    const size_t nchunks = (size_t(s.T) + p.chunk_tokens - 1) / p.chunk_tokens;
+    off = align_up(off + nchunks * s.P * ((size_t(1) << p.split_level) + 1) * sizeof(int32_t));
+  }
   L.H = off;
   off = align_up(off + size_t(s.T) * size_t(s.K) * s.esize);
+  L.WT = off;
+  L.use_wt = prefill && fff::project_direct_supported(s);
+  if (L.use_wt) off = align_up(off + size_t(s.d) * size_t(s.K) * s.esize);
   L.total = off;
   return L;
 }
@@ -118,10 +158,16 @@ fff_status_t run_route(const Dims& s, const fff_plan_t& p, const Layout& L, cons
   int32_t* leaf = reinterpret_cast<int32_t*>(ws + L.leaf);
   hipError_t e;
   if (p.algo == FFF_ALGO_PREFILL) {
-    e = fff::launch_route_top(s, p.split_level, x, W, b, logits, leaf, st);
+    const int k = p.split_level;
+    e = fff::launch_route_top(s, k, x, W, b, logits, leaf, st);
     if (e != hipSuccess) return FFF_ERROR_HIP;
-    e = fff::launch_hbuild(s, logits, leaf, V, H, path_out, st);
-    return hip_status(e);
+    if (k == s.D + 1) return hip_status(fff::launch_hbuild(s, logits, leaf, V, H, path_out, st));
+    int32_t* perm = reinterpret_cast<int32_t*>(ws + L.perm);
+    int32_t* offs = reinterpret_cast<int32_t*>(ws + L.offs);
+    e = fff::launch_bucket(s, k, leaf, perm, offs, p.chunk_tokens, st);
+    if (e != hipSuccess) return FFF_ERROR_HIP;
+    return hip_status(fff::launch_deep(s, k, x, W, b, V, logits, perm, offs, H, path_out,
+                                       p.chunk_tokens, st));
   }
   e = fff::launch_route_generic(s, x, W, b, logits, path_out, leaf, st);
   if (e != hipSuccess) return FFF_ERROR_HIP;
@@ -157,6 +203,14 @@ fff_status_t fff_plan_default(const fff_shape_t* shape, fff_plan_t* plan) {
   if (st != FFF_SUCCESS) return st;
   if (!plan) return FFF_ERROR_INVALID_VALUE;
   return resolve_plan(s, nullptr, plan);
+}
+
+fff_status_t fff_plan_resolve(const fff_shape_t* shape, const fff_plan_t* in, fff_plan_t* out) {
+  Dims s;
+  fff_status_t st = check_shape(shape, &s);
+  if (st != FFF_SUCCESS) return st;
+  if (!in || !out) return FFF_ERROR_INVALID_VALUE;
+  return resolve_plan(s, in, out);
 }
 
 fff_status_t fff_workspace_size(const fff_shape_t* shape, const fff_plan_t* plan, size_t* bytes) {
@@ -195,10 +249,17 @@ fff_status_t fff_forward(const fff_shape_t* shape, const fff_plan_t* plan, const
   char* ws = static_cast<char*>(workspace);
   void* H = ws + L.H;
   if (events && (st = record(events->start, stream)) != FFF_SUCCESS) return st;
+  // The projection's transposed W_out is prepared first, so that the
+  // projection stage is the matrix product alone.
+  if (L.use_wt && fff::launch_transpose(W_out, ws + L.WT, s.K, s.d, stream) != hipSuccess)
+    return FFF_ERROR_HIP;
   st = run_route(s, p, L, x, W_node, b_node, V_node, H, path_out, ws, stream);
   if (st != FFF_SUCCESS) return st;
   if (events && (st = record(events->routed, stream)) != FFF_SUCCESS) return st;
-  st = run_project(s, p.algo, H, W_out, y, stream);
+  if (L.use_wt)
+    st = hip_status(fff::launch_project_direct(s, H, ws + L.WT, y, stream));
+  else
+    st = run_project(s, p.algo, H, W_out, y, stream);
   if (st != FFF_SUCCESS) return st;
   if (events && (st = record(events->done, stream)) != FFF_SUCCESS) return st;
   return FFF_SUCCESS;

@@ -100,6 +100,101 @@ struct WoutTransposeLoader {
   }
 };
 
+// y tile store from the transposed-block accumulators: lane holds y row
+// (m-block i, lane % 32) and, for g = 0..3, the four consecutive columns
+// 8g + 4*(lane/32) + 0..3 of n-block j -> one 8-byte store each.
+template <class C>
+__device__ __forceinline__ void store_y_tile(const f32x16_t (&acc)[C::kTm][C::kTn],
+                                             uint16_t* __restrict__ y, int M, int Nc, int m0,
+                                             int n0) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x / kWave;
+  const int wm = wave / C::kWavesN;
+  const int wn = wave % C::kWavesN;
+  const int row_base = m0 + wm * C::WM + (lane & 31);
+#pragma unroll
+  for (int i = 0; i < C::kTm; ++i) {
+    const int row = row_base + i * 32;
+    if (row >= M) continue;
+    uint16_t* yrow = y + static_cast<size_t>(row) * Nc;
+#pragma unroll
+    for (int j = 0; j < C::kTn; ++j) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int col = n0 + wn * C::WN + j * 32 + g * 8 + (lane >> 5) * 4;
+        if (col < Nc) {
+          const uint2 v = make_uint2(pack_bf16x2(acc[i][j][4 * g], acc[i][j][4 * g + 1]),
+                                     pack_bf16x2(acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]));
+          *reinterpret_cast<uint2*>(yrow + col) = v;
+        }
+      }
+    }
+  }
+}
+
+// y = H . W_out with W_out supplied transposed (WT[d][K], K-contiguous), both
+// operands loaded straight into LDS by the multi-stage main loop.
+template <class C>
+__global__ __launch_bounds__(C::kThreads) void proj_direct_kernel(
+    const uint16_t* __restrict__ H, const uint16_t* __restrict__ WT, uint16_t* __restrict__ y,
+    int M, int K, int Nc, int tiles_n) {
+  extern __shared__ __align__(16) unsigned char lds[];
+  const int logical = xcd_logical_tile(blockIdx.x, gridDim.x);
+  const int tn = logical % tiles_n;
+  const int tm = logical / tiles_n;
+  const int m0 = tm * C::BM;
+  const int n0 = tn * C::BN;
+  auto a_row = [&](int i) {
+    const int r = m0 + i < M ? m0 + i : M - 1;
+    return H + static_cast<size_t>(r) * K;
+  };
+  auto b_row = [&](int j) {
+    const int c = n0 + j < Nc ? n0 + j : Nc - 1;
+    return WT + static_cast<size_t>(c) * K;
+  };
+  f32x16_t acc[C::kTm][C::kTn];
+  gemm_mainloop_direct<C>(acc, lds, K, a_row, b_row);
+  store_y_tile<C>(acc, y, M, Nc, m0, n0);
+}
+
+// WT[n][k] = W[k][n] for a [K x Nc] bf16 matrix, 64 x 64 tiles through LDS.
+__global__ __launch_bounds__(256) void transpose_kernel(const uint16_t* __restrict__ W,
+                                                        uint16_t* __restrict__ WT, int K, int Nc) {
+  __shared__ uint16_t tile[64][64 + 2];
+  const int k0 = blockIdx.y * 64;
+  const int n0 = blockIdx.x * 64;
+  const int t = threadIdx.x;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int r = t / 8 + 32 * i;  // k within tile
+    const int c8 = (t % 8) * 8;    // n within tile
+    if (k0 + r < K && n0 + c8 < Nc) {
+      const uint4 v = ldg16(W + static_cast<size_t>(k0 + r) * Nc + n0 + c8);
+      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        tile[r][c8 + 2 * e] = static_cast<uint16_t>(w[e] & 0xffffu);
+        tile[r][c8 + 2 * e + 1] = static_cast<uint16_t>(w[e] >> 16);
+      }
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int rn = t / 8 + 32 * i;  // n within tile
+    const int k8 = (t % 8) * 8;     // k within tile
+    if (n0 + rn < Nc && k0 + k8 < K) {
+      uint32_t w[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        w[e] = static_cast<uint32_t>(tile[k8 + 2 * e][rn]) |
+               (static_cast<uint32_t>(tile[k8 + 2 * e + 1][rn]) << 16);
+      *reinterpret_cast<uint4*>(WT + static_cast<size_t>(n0 + rn) * K + k0 + k8) =
+          make_uint4(w[0], w[1], w[2], w[3]);
+    }
+  }
+}
+
 template <class C>
 __global__ __launch_bounds__(C::kThreads) void proj_mfma_kernel(
     const uint16_t* __restrict__ H, const uint16_t* __restrict__ Wout, uint16_t* __restrict__ y,
@@ -130,27 +225,7 @@ __global__ __launch_bounds__(C::kThreads) void proj_mfma_kernel(
   f32x16_t acc[C::kTm][C::kTn];
   gemm_mainloop<C>(acc, smem, K, la, lb);
 
-  // Lane holds y row (m-block i, lane % 32) and, for g = 0..3, the four
-  // consecutive columns 8g + 4*(lane/32) + 0..3 of n-block j.
-  const int row_base = m0 + wm * C::WM + (lane & 31);
-#pragma unroll
-  for (int i = 0; i < C::kTm; ++i) {
-    const int row = row_base + i * 32;
-    if (row >= M) continue;
-    uint16_t* yrow = y + static_cast<size_t>(row) * Nc;
-#pragma unroll
-    for (int j = 0; j < C::kTn; ++j) {
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int col = n0 + wn * C::WN + j * 32 + g * 8 + (lane >> 5) * 4;
-        if (col < Nc) {
-          const uint2 v = make_uint2(pack_bf16x2(acc[i][j][4 * g], acc[i][j][4 * g + 1]),
-                                     pack_bf16x2(acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]));
-          *reinterpret_cast<uint2*>(yrow + col) = v;
-        }
-      }
-    }
-  }
+  store_y_tile<C>(acc, y, M, Nc, m0, n0);
 }
 
 template <class C>
@@ -175,6 +250,7 @@ hipError_t launch_cfg(const Dims& s, const void* H, const void* Wout, void* y, h
 
 using BigTile = TileCfg<256, 256, 64, 128, 128>;
 using SmallTile = TileCfg<128, 128, 64, 64, 64>;
+using BigDirect = DirectCfg<256, 256, 128, 64, 4>;
 
 }  // namespace
 
@@ -189,6 +265,37 @@ hipError_t launch_project_mfma(const Dims& s, const void* H, const void* Wout, v
   const int64_t big_tiles = ((s.T + 255) / 256) * ((s.d + 255) / 256);
   if (big_tiles >= 256) return launch_cfg<BigTile>(s, H, Wout, y, st);
   return launch_cfg<SmallTile>(s, H, Wout, y, st);
+}
+
+bool project_direct_supported(const Dims& s) {
+  return project_mfma_supported(s) && s.K % 32 == 0 &&
+         ((s.T + 255) / 256) * ((s.d + 255) / 256) >= 256;
+}
+
+hipError_t launch_transpose(const void* W, void* WT, int64_t K, int Nc, hipStream_t st) {
+  transpose_kernel<<<dim3((Nc + 63) / 64, static_cast<unsigned>((K + 63) / 64)), dim3(256), 0, st>>>(
+      static_cast<const uint16_t*>(W), static_cast<uint16_t*>(WT), static_cast<int>(K), Nc);
+  return hipGetLastError();
+}
+
+hipError_t launch_project_direct(const Dims& s, const void* H, const void* WT, void* y,
+                                 hipStream_t st) {
+  using C = BigDirect;
+  const int tiles_m = static_cast<int>((s.T + C::BM - 1) / C::BM);
+  const int tiles_n = (s.d + C::BN - 1) / C::BN;
+  auto kern = proj_direct_kernel<C>;
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       static_cast<int>(C::kLdsBytes));
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  kern<<<dim3(tiles_m * tiles_n), dim3(C::kThreads), C::kLdsBytes, st>>>(
+      static_cast<const uint16_t*>(H), static_cast<const uint16_t*>(WT), static_cast<uint16_t*>(y),
+      static_cast<int>(s.T), static_cast<int>(s.K), s.d, tiles_n);
+  return hipGetLastError();
 }
 
 }  // namespace fff

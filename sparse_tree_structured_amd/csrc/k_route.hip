@@ -62,46 +62,24 @@ struct NodeRowLoader {
   __device__ __forceinline__ void store(uint16_t* lds, int ld) const { rl.store(lds, ld, tid); }
 };
 
+// Walk epilogue shared by the top-level kernels.  acc holds the tile's
+// logits without bias (transposed-block layout of mfma_tile.hpp); `lg` is
+// LDS of at least WM * (BN + 4) floats, free for reuse.
 template <class C>
-__global__ __launch_bounds__(C::kThreads) void route_top_kernel(
-    const uint16_t* __restrict__ x, const uint16_t* __restrict__ W, const uint16_t* __restrict__ b,
-    float* __restrict__ rec_logit, int32_t* __restrict__ rec_next, int T, int d, int P, int D,
-    int L, int64_t N, int tiles_n) {
-  extern __shared__ __align__(16) uint16_t smem[];
-  const int logical = xcd_logical_tile(blockIdx.x, gridDim.x);
-  const int tn = logical % tiles_n;
-  const int tm = logical / tiles_n;
-  const int m0 = tm * C::BM;
-  const int n0 = tn * C::BN;
+__device__ __forceinline__ void top_walk_epilogue(const f32x16_t (&acc)[C::kTm][C::kTn], float* lg,
+                                                  const uint16_t* __restrict__ b,
+                                                  float* __restrict__ rec_logit,
+                                                  int32_t* __restrict__ rec_next, int T, int P,
+                                                  int D, int L, int64_t N, int m0, int n0) {
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = tid / kWave;
   const int wm = wave / C::kWavesN;
   const int wn = wave % C::kWavesN;
-
-  XLoader<C> la;
-  la.x = x;
-  la.d = d;
-  la.T = T;
-  la.m0 = m0;
-  la.tid = tid;
-  NodeRowLoader<C> lb;
-  lb.W = W;
-  lb.d = d;
-  lb.P = P;
-  lb.L = L;
-  lb.n0 = n0;
-  lb.tid = tid;
-  lb.N = N;
-  f32x16_t acc[C::kTm][C::kTn];
-  gemm_mainloop<C>(acc, smem, d, la, lb);
-
-  // Epilogue in two halves of 128 token rows (the fp32 tile of one half,
-  // 128 x BN, fits in the LDS freed by the main loop).
-  constexpr int kRows = C::WM;  // token rows per half
+  // Two passes of WM token rows each (the fp32 tile of one pass, WM x BN,
+  // fits in the LDS freed by the main loop).
+  constexpr int kRows = C::WM;
   constexpr int kPitch = C::BN + 4;
-  static_assert(kRows * kPitch * 4 <= C::kLdsBytes, "logit tile must fit in LDS");
-  float* lg = reinterpret_cast<float*>(smem);
   const int cpt = 1 << L;
   const int tpt = C::BN >> L;  // trees per tile
   const int p_base = n0 >> L;
@@ -141,6 +119,73 @@ __global__ __launch_bounds__(C::kThreads) void route_top_kernel(
     }
     __syncthreads();
   }
+}
+
+template <class C>
+constexpr size_t top_lds_bytes() {
+  return C::kLdsBytes > size_t(C::WM) * (C::BN + 4) * 4 ? C::kLdsBytes
+                                                        : size_t(C::WM) * (C::BN + 4) * 4;
+}
+
+template <class C>
+__global__ __launch_bounds__(C::kThreads) void route_top_kernel(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ W, const uint16_t* __restrict__ b,
+    float* __restrict__ rec_logit, int32_t* __restrict__ rec_next, int T, int d, int P, int D,
+    int L, int64_t N, int tiles_n) {
+  extern __shared__ __align__(16) uint16_t smem[];
+  const int logical = xcd_logical_tile(blockIdx.x, gridDim.x);
+  const int tn = logical % tiles_n;
+  const int tm = logical / tiles_n;
+  const int m0 = tm * C::BM;
+  const int n0 = tn * C::BN;
+  XLoader<C> la;
+  la.x = x;
+  la.d = d;
+  la.T = T;
+  la.m0 = m0;
+  la.tid = threadIdx.x;
+  NodeRowLoader<C> lb;
+  lb.W = W;
+  lb.d = d;
+  lb.P = P;
+  lb.L = L;
+  lb.n0 = n0;
+  lb.tid = threadIdx.x;
+  lb.N = N;
+  f32x16_t acc[C::kTm][C::kTn];
+  gemm_mainloop<C>(acc, smem, d, la, lb);
+  top_walk_epilogue<C>(acc, reinterpret_cast<float*>(smem), b, rec_logit, rec_next, T, P, D, L, N,
+                       m0, n0);
+}
+
+// Same product through the direct-to-LDS multi-stage main loop.
+template <class C>
+__global__ __launch_bounds__(C::kThreads) void route_top_direct_kernel(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ W, const uint16_t* __restrict__ b,
+    float* __restrict__ rec_logit, int32_t* __restrict__ rec_next, int T, int d, int P, int D,
+    int L, int64_t N, int tiles_n) {
+  extern __shared__ __align__(16) unsigned char lds[];
+  const int logical = xcd_logical_tile(blockIdx.x, gridDim.x);
+  const int tn = logical % tiles_n;
+  const int tm = logical / tiles_n;
+  const int m0 = tm * C::BM;
+  const int n0 = tn * C::BN;
+  const int cmask = (1 << L) - 1;
+  auto a_row = [&](int i) {
+    const int r = m0 + i < T ? m0 + i : T - 1;
+    return x + static_cast<size_t>(r) * d;
+  };
+  auto b_row = [&](int j) {
+    const int gc = n0 + j;
+    const int p = gc >> L;
+    const int n = gc & cmask;
+    const bool used = p < P && n < cmask;
+    return W + (used ? (static_cast<int64_t>(p) * N + n) * d : 0);
+  };
+  f32x16_t acc[C::kTm][C::kTn];
+  gemm_mainloop_direct<C>(acc, lds, d, a_row, b_row);
+  top_walk_epilogue<C>(acc, reinterpret_cast<float*>(lds), b, rec_logit, rec_next, T, P, D, L, N,
+                       m0, n0);
 }
 
 // H for fully routed paths (L = D+1).  One workgroup per token: first the
@@ -194,6 +239,38 @@ __global__ __launch_bounds__(256) void hbuild_kernel(const float* __restrict__ r
   }
 }
 
+template <class C, bool kDirect>
+hipError_t launch_top_cfg(const Dims& s, int L, const void* x, const void* W, const void* b,
+                          float* rec_logit, int32_t* rec_next, hipStream_t st) {
+  const int tiles_m = static_cast<int>((s.T + C::BM - 1) / C::BM);
+  const int64_t cols = static_cast<int64_t>(s.P) << L;
+  const int tiles_n = static_cast<int>((cols + C::BN - 1) / C::BN);
+  void (*kern)(const uint16_t*, const uint16_t*, const uint16_t*, float*, int32_t*, int, int, int,
+               int, int, int64_t, int);
+  if constexpr (kDirect)
+    kern = route_top_direct_kernel<C>;
+  else
+    kern = route_top_kernel<C>;
+  const size_t lds = top_lds_bytes<C>();
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       static_cast<int>(lds));
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  kern<<<dim3(tiles_m * tiles_n), dim3(C::kThreads), lds, st>>>(
+      static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(W),
+      static_cast<const uint16_t*>(b), rec_logit, rec_next, static_cast<int>(s.T), s.d, s.P, s.D,
+      L, s.N, tiles_n);
+  return hipGetLastError();
+}
+
+using MidTile = TileCfg<128, 256, 64, 64, 128>;
+using SmallTile = TileCfg<64, 256, 64, 64, 64>;
+using TopDirect = DirectCfg<256, 256, 128, 64, 4>;
+
 }  // namespace
 
 bool route_top_supported(const Dims& s, int L) {
@@ -203,24 +280,14 @@ bool route_top_supported(const Dims& s, int L) {
 
 hipError_t launch_route_top(const Dims& s, int L, const void* x, const void* W, const void* b,
                             float* rec_logit, int32_t* rec_next, hipStream_t st) {
-  using C = TopTile;
-  const int tiles_m = static_cast<int>((s.T + C::BM - 1) / C::BM);
-  const int64_t cols = static_cast<int64_t>(s.P) << L;
-  const int tiles_n = static_cast<int>((cols + C::BN - 1) / C::BN);
-  auto kern = route_top_kernel<C>;
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       static_cast<int>(C::kLdsBytes));
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
-  kern<<<dim3(tiles_m * tiles_n), dim3(C::kThreads), C::kLdsBytes, st>>>(
-      static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(W),
-      static_cast<const uint16_t*>(b), rec_logit, rec_next, static_cast<int>(s.T), s.d, s.P, s.D,
-      L, s.N, tiles_n);
-  return hipGetLastError();
+  // Enough tiles to cover the 256 compute units: shrink the token tile when
+  // the column count is small (few trees or few levels).
+  const int64_t tiles_n = ((static_cast<int64_t>(s.P) << L) + TopTile::BN - 1) / TopTile::BN;
+  if (((s.T + 255) / 256) * tiles_n >= 256)
+    return launch_top_cfg<TopDirect, true>(s, L, x, W, b, rec_logit, rec_next, st);
+  if (((s.T + 127) / 128) * tiles_n >= 256)
+    return launch_top_cfg<MidTile, false>(s, L, x, W, b, rec_logit, rec_next, st);
+  return launch_top_cfg<SmallTile, false>(s, L, x, W, b, rec_logit, rec_next, st);
 }
 
 hipError_t launch_hbuild(const Dims& s, const float* rec_logit, const int32_t* rec_next,

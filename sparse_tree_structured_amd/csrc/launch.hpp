@@ -36,6 +36,12 @@ bool project_mfma_supported(const Dims& s);
 hipError_t launch_project_mfma(const Dims& s, const void* H, const void* Wout, void* y,
                                hipStream_t st);
 
+// Multi-stage direct-to-LDS projection; W_out supplied transposed (WT[d][K]).
+bool project_direct_supported(const Dims& s);
+hipError_t launch_transpose(const void* W, void* WT, int64_t K, int Nc, hipStream_t st);
+hipError_t launch_project_direct(const Dims& s, const void* H, const void* WT, void* y,
+                                 hipStream_t st);
+
 // ---- prefill routing (bf16) ----
 // Dense evaluation of tree levels 0..L-1 (L <= 8) with the walk over them:
 // rec_logit[p][t][l] (fp32) and rec_next[p][t] (heap id at level L, or the
@@ -46,5 +52,15 @@ hipError_t launch_route_top(const Dims& s, int L, const void* x, const void* W, 
 // H and path_out from fully routed records (L = D+1).
 hipError_t launch_hbuild(const Dims& s, const float* rec_logit, const int32_t* rec_next,
                          const void* V, void* H, int32_t* path_out, hipStream_t st);
+
+// Deep levels k..D per token bucket (bf16; D-k <= 3).
+bool deep_supported(const Dims& s, int k);
+size_t deep_chunk(const Dims& s);  // default tokens per bucket chunk
+hipError_t launch_bucket(const Dims& s, int k, const int32_t* rec_next, int32_t* perm,
+                         int32_t* offs, int chunk, hipStream_t st);
+hipError_t launch_deep(const Dims& s, int k, const void* x, const void* W, const void* b,
+                       const void* V, const float* rec_logit, const int32_t* perm,
+                       const int32_t* offs, void* H, int32_t* path_out, int chunk,
+                       hipStream_t st);
 
 }  // namespace fff

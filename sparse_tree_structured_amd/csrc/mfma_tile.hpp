@@ -137,6 +137,174 @@ __device__ __forceinline__ void gemm_mainloop(f32x16_t (&acc)[C::kTm][C::kTn], u
   }
 }
 
+// ---------------------------------------------------------------------------
+// Direct-to-LDS main loop (both operands K-contiguous).
+//
+// Each K step of 32 lives in one of kStages LDS buffers; the buffers are
+// filled with global_load_lds_dwordx4 (16 bytes per lane straight into LDS,
+// no register staging), kStages-1 steps ahead of the matrix-core work.  One
+// wave-wide load fills 1 KB = 16 rows x 64 bytes.  A row's four 16-byte
+// chunks are stored XOR-swizzled, chunk c of row r at slot c ^ f(r) with
+// f(r) = (r >> 2) & 3.  The operand reads (32 consecutive rows, one chunk per
+// half wavefront) are then free of LDS bank conflicts; this choice was
+// measured with the SQ_LDS_BANK_CONFLICT counter on gfx950, where other
+// XOR patterns that look conflict-free on paper give 2-way conflicts.
+// ---------------------------------------------------------------------------
+template <int BM_, int BN_, int WM_, int WN_, int STAGES_>
+struct DirectCfg {
+  static constexpr int BM = BM_, BN = BN_, BK = 32, WM = WM_, WN = WN_;
+  static constexpr int kStages = STAGES_;
+  static constexpr int kWavesM = BM / WM;
+  static constexpr int kWavesN = BN / WN;
+  static constexpr int kWaves = kWavesM * kWavesN;
+  static constexpr int kThreads = kWaves * kWave;
+  static constexpr int kTm = WM / 32;
+  static constexpr int kTn = WN / 32;
+  static constexpr int kRowBytes = BK * 2;  // 64
+  static constexpr int kStageBytes = (BM + BN) * kRowBytes;
+  static constexpr size_t kLdsBytes = size_t(kStages) * kStageBytes;
+  static constexpr int kALoads = BM / 16 / kWaves;  // wave-wide loads per stage
+  static constexpr int kBLoads = BN / 16 / kWaves;
+  static_assert(BM % (16 * kWaves) == 0 && BN % (16 * kWaves) == 0, "rows split over waves");
+  static_assert(WM % 32 == 0 && WN % 32 == 0, "MFMA block shape");
+};
+
+__device__ __forceinline__ int lds_swz(int r) { return (r >> 2) & 3; }
+
+// Wait until at most n vector-memory operations of this wave are in flight
+// (lgkm and exp counters left unconstrained).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// Issue the loads of one K step (k0) into stage buffer `buf` for ROWS rows
+// starting at LDS byte offset `base`.  row_ptr(i) gives row i's start.
+template <class C, int ROWS, class RowPtr>
+__device__ __forceinline__ void direct_load_rows(unsigned char* lds, int base, const RowPtr& row_ptr,
+                                                 int k0, int wave, int lane) {
+  constexpr int kLoads = ROWS / 16 / C::kWaves;
+#pragma unroll
+  for (int j = 0; j < kLoads; ++j) {
+    const int r0 = (wave * kLoads + j) * 16;
+    const int r = r0 + (lane >> 2);
+    const int chunk = (lane & 3) ^ lds_swz(r);
+    const uint16_t* g = row_ptr(r) + k0 + chunk * 8;
+    __builtin_amdgcn_global_load_lds(g, lds + base + r0 * C::kRowBytes, 16, 0, 0);
+  }
+}
+
+// Operand fragments of one 16-wide k sub-step (kk = 0 or 1) of a stage.
+template <class C>
+struct Frags {
+  bf16x8_t a[C::kTm], b[C::kTn];
+};
+
+template <class C>
+__device__ __forceinline__ void read_frags(Frags<C>& f, const unsigned char* stage, int kk, int wm,
+                                           int wn, int lane) {
+  const unsigned char* As = stage;
+  const unsigned char* Bs = stage + C::BM * C::kRowBytes;
+  const int lrow = lane & 31;
+  const int chunk = kk * 2 + (lane >> 5);
+#pragma unroll
+  for (int i = 0; i < C::kTm; ++i) {
+    const int r = wm * C::WM + i * 32 + lrow;
+    f.a[i] = *reinterpret_cast<const bf16x8_t*>(As + r * C::kRowBytes + ((chunk ^ lds_swz(r)) << 4));
+  }
+#pragma unroll
+  for (int j = 0; j < C::kTn; ++j) {
+    const int r = wn * C::WN + j * 32 + lrow;
+    f.b[j] = *reinterpret_cast<const bf16x8_t*>(Bs + r * C::kRowBytes + ((chunk ^ lds_swz(r)) << 4));
+  }
+}
+
+template <class C>
+__device__ __forceinline__ void mma_frags(f32x16_t (&acc)[C::kTm][C::kTn], const Frags<C>& f) {
+#pragma unroll
+  for (int i = 0; i < C::kTm; ++i)
+#pragma unroll
+    for (int j = 0; j < C::kTn; ++j)
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[j], f.a[i], acc[i][j], 0, 0, 0);
+}
+
+// Workgroup barrier that does not drain the loads still in flight for later
+// stages (__syncthreads() would).  The empty asm statements keep the
+// compiler from moving memory operations across it.
+__device__ __forceinline__ void stage_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Full K loop (K % 32 == 0).  a_row(i), i < BM, and b_row(j), j < BN, return
+// K-contiguous row starts (already clamped to valid memory).
+//
+// Schedule of iteration ks (stage buffer ks % S):
+//   read fragments (ks, kk=1)            -- LDS reads overlap the MFMAs below
+//   MFMAs on fragments (ks, kk=0)
+//   wait for stage ks+1's loads; barrier; issue the loads of stage ks+S-1
+//   read fragments (ks+1, kk=0)
+//   MFMAs on fragments (ks, kk=1)
+// so every fragment is read one MFMA group (16 MFMAs) before its use and the
+// loads of a stage are issued S-2 iterations before it is needed.
+template <class C, class ARow, class BRow>
+__device__ __forceinline__ void gemm_mainloop_direct(f32x16_t (&acc)[C::kTm][C::kTn],
+                                                     unsigned char* lds, int K, const ARow& a_row,
+                                                     const BRow& b_row) {
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = tid / kWave;
+  const int wm = wave / C::kWavesN;
+  const int wn = wave % C::kWavesN;
+  constexpr int S = C::kStages;
+  static_assert(S == 4, "wait counts below assume four stages");
+  constexpr int kPerStage = C::kALoads + C::kBLoads;  // loads per wave per stage
+  zero_acc<C>(acc);
+  const int nk = K / C::BK;
+  auto issue = [&](int ks) {
+    const int base = (ks % S) * C::kStageBytes;
+    direct_load_rows<C, C::BM>(lds, base, a_row, ks * C::BK, wave, lane);
+    direct_load_rows<C, C::BN>(lds, base + C::BM * C::kRowBytes, b_row, ks * C::BK, wave, lane);
+  };
+#pragma unroll
+  for (int s = 0; s < S - 1; ++s)
+    if (s < nk) issue(s);
+  // Stage 0 ready: at most stages 1 and 2 still in flight.
+  if (nk >= 3)
+    wait_vmcnt<2 * kPerStage>();
+  else if (nk == 2)
+    wait_vmcnt<kPerStage>();
+  else
+    wait_vmcnt<0>();
+  stage_barrier();
+  Frags<C> f0, f1;
+  read_frags<C>(f0, lds, 0, wm, wn, lane);
+  for (int ks = 0; ks < nk; ++ks) {
+    const unsigned char* cur = lds + (ks % S) * C::kStageBytes;
+    read_frags<C>(f1, cur, 1, wm, wn, lane);
+    asm volatile("" ::: "memory");  // keep these reads ahead of the MFMAs below
+    mma_frags<C>(acc, f0);
+    if (ks + 1 < nk) {
+      // Stage ks+1 ready: at most stage ks+2 still in flight.
+      if (ks + 2 < nk)
+        wait_vmcnt<kPerStage>();
+      else
+        wait_vmcnt<0>();
+      stage_barrier();  // also: every wave is done with stage ks-1's buffer
+      if (ks + S - 1 < nk) issue(ks + S - 1);
+    }
+    // Unconditional (after the last stage it reads a stale buffer and the
+    // values go unused), so the wait before the MFMAs below can leave these
+    // eight reads in flight on every path.
+    read_frags<C>(f0, lds + ((ks + 1) % S) * C::kStageBytes, 0, wm, wn, lane);
+    asm volatile("" ::: "memory");
+    mma_frags<C>(acc, f1);
+  }
+  __syncthreads();
+}
+
 // XCD-aware tile order: hardware sends workgroup b to XCD b % 8.  Each XCD
 // gets a contiguous range of logical tiles (row-panel major), so operand
 // panels are fetched from HBM about once per XCD and the tiles an XCD runs

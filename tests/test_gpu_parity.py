@@ -161,3 +161,47 @@ def test_projection_matches_fp64(M, K, N):
         got = to_f64(y)[rows]
         err = np.abs(got - ref.numpy()) / np.maximum(np.abs(ref.numpy()), 1e-2)
         assert err.max() < 2e-2, (algo, err.max())
+
+
+SPLITS = [
+    # workload, split level k, chunk tokens (0 = auto)
+    ("opt1p3b_d6", 3, 0),
+    ("opt1p3b_d6", 7, 0),      # every level dense
+    ("opt1p3b_d6", 4, 0),
+    ("opt1p3b_d6", 3, 1000),   # chunks that do not divide T
+    ("opt1p3b_d4", 1, 0),
+    ("opt1p3b_d4", 5, 0),
+    ("gpt125m", 2, 0),
+    ("gpt125m", 3, 256),
+    ("gpt125m", 6, 0),
+    ("decode_skew_t64", 3, 16),
+    ("decode_skew_t8", 6, 0),
+]
+
+
+@needs_gpu
+@pytest.mark.parametrize("name,k,chunk", SPLITS, ids=[f"{n}-k{k}-c{c}" for n, k, c in SPLITS])
+def test_prefill_split_levels(name, k, chunk):
+    import sparse_tree_structured_amd as fff
+    inp = wl(name)
+    T = to_device(inp)
+    print(f"[gpu] {name} k={k} chunk={chunk}", flush=True)
+    y, path = fff.forward(T["x"], T["W_node"], T["b_node"], T["V_node"], T["W_out"],
+                          algo="prefill", split_level=k, chunk_tokens=chunk)
+    torch.cuda.synchronize()
+    sample = None if inp.shape.T <= 1024 else sample_rows(inp.shape.T, n=48)
+    check(inp, to_f64(y), path.cpu().numpy(), sample=sample)
+
+
+@needs_gpu
+def test_route_matches_forward_h():
+    # fff_route exposes H; projecting it must give fff_forward's y exactly.
+    import sparse_tree_structured_amd as fff
+    inp = wl("gpt125m")
+    T = to_device(inp)
+    H, path = fff.route(T["x"], T["W_node"], T["b_node"], T["V_node"])
+    y2 = fff.project(H, T["W_out"])
+    y, path1 = fff.forward(T["x"], T["W_node"], T["b_node"], T["V_node"], T["W_out"])
+    torch.cuda.synchronize()
+    assert torch.equal(path, path1)
+    assert torch.equal(y, y2)
