@@ -188,55 +188,117 @@ __global__ __launch_bounds__(C::kThreads) void route_top_direct_kernel(
                        m0, n0);
 }
 
-// H for fully routed paths (L = D+1).  One workgroup per token: first the
-// P*(D+1) GELU values and node ids into LDS, then each thread forms 8
-// consecutive outputs (one 16-byte store) of the token's H row.
+// H for fully routed paths (L = D+1).  One workgroup per (tile of kHbTok
+// tokens, tree p): the tree's v rows are staged in LDS once (widened to fp32
+// when they fit in 32 KB, else kept bf16) and reused by every token of the
+// tile (the top levels' rows are shared by all of them); the tile's GELU(a)
+// values and leaves come from the routing records.  Each thread then forms
+// 16 consecutive outputs of
+//     H[t, p*h : (p+1)*h] = sum over l of GELU(a_l) * V_node[p, n_l, :]
+// (GELU before the sum: explainer section 3.C) as two 16-byte stores; the
+// h/16 threads of a token write its 2h-byte segment contiguously.  The work
+// is vector-ALU bound: the depth and the chunk count per token are template
+// parameters (all per-level reads issue together; index math is shifts).
+constexpr int kHbTok = 256;
+
+template <bool F32>
+__device__ __forceinline__ void load_v16(const unsigned char* vs, size_t elem, float (&v)[16]) {
+  if constexpr (F32) {
+    const float4* src = reinterpret_cast<const float4*>(vs + elem * 4);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float4 f = src[q];
+      v[4 * q] = f.x;
+      v[4 * q + 1] = f.y;
+      v[4 * q + 2] = f.z;
+      v[4 * q + 3] = f.w;
+    }
+  } else {
+    const uint4* src = reinterpret_cast<const uint4*>(vs + elem * 2);
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const uint4 u = src[q];
+      v[8 * q] = bf16lo(u.x);
+      v[8 * q + 1] = bf16hi(u.x);
+      v[8 * q + 2] = bf16lo(u.y);
+      v[8 * q + 3] = bf16hi(u.y);
+      v[8 * q + 4] = bf16lo(u.z);
+      v[8 * q + 5] = bf16hi(u.z);
+      v[8 * q + 6] = bf16lo(u.w);
+      v[8 * q + 7] = bf16hi(u.w);
+    }
+  }
+}
+
+template <int LEVELS, int HSHIFT, bool F32>
 __global__ __launch_bounds__(256) void hbuild_kernel(const float* __restrict__ rec_logit,
                                                      const int32_t* __restrict__ rec_next,
                                                      const uint16_t* __restrict__ V,
                                                      uint16_t* __restrict__ H,
                                                      int32_t* __restrict__ path_out, int T, int P,
-                                                     int D, int h, int64_t N) {
-  extern __shared__ float gl[];  // [P][D+1] GELU values, then [P] leaf heap ids
-  int32_t* leaf = reinterpret_cast<int32_t*>(gl + P * (D + 1));
-  const int t = blockIdx.x;
-  const int L = D + 1;
-  for (int i = threadIdx.x; i < P * L; i += blockDim.x) {
-    const int p = i / L;
-    const int l = i - p * L;
-    gl[i] = gelu_tanh(rec_logit[(static_cast<int64_t>(p) * T + t) * L + l]);
+                                                     int64_t N) {
+  constexpr int L = LEVELS;
+  constexpr int D = LEVELS - 1;
+  constexpr int h = 16 << HSHIFT;     // node output width
+  constexpr int kChunks = 1 << HSHIFT;  // 16-output chunks per token
+  constexpr int kEsz = F32 ? 4 : 2;
+  extern __shared__ __align__(16) unsigned char hb_lds[];
+  const int p = blockIdx.y;
+  const int t0 = blockIdx.x * kHbTok;
+  const int ntok = min(kHbTok, T - t0);
+  unsigned char* vs = hb_lds;                                               // N x h
+  float* gl = reinterpret_cast<float*>(hb_lds + size_t(N) * h * kEsz);     // kHbTok x L
+  int32_t* leaf = reinterpret_cast<int32_t*>(gl + kHbTok * L);             // kHbTok
+  const uint16_t* Vp = V + static_cast<int64_t>(p) * N * h;
+  for (int e = threadIdx.x; e < static_cast<int>(N) * (h / 8); e += blockDim.x) {
+    const uint4 v = ldg16(Vp + static_cast<size_t>(e) * 8);
+    if constexpr (F32) {
+      float4* dst = reinterpret_cast<float4*>(vs + static_cast<size_t>(e) * 32);
+      dst[0] = make_float4(bf16lo(v.x), bf16hi(v.x), bf16lo(v.y), bf16hi(v.y));
+      dst[1] = make_float4(bf16lo(v.z), bf16hi(v.z), bf16lo(v.w), bf16hi(v.w));
+    } else {
+      *reinterpret_cast<uint4*>(vs + static_cast<size_t>(e) * 16) = v;
+    }
   }
-  for (int p = threadIdx.x; p < P; p += blockDim.x) {
-    const int32_t n = rec_next[static_cast<int64_t>(p) * T + t];
-    leaf[p] = n;
-    if (path_out) path_out[static_cast<int64_t>(t) * P + p] = n - ((1 << D) - 1);
+  const float* rl = rec_logit + (static_cast<int64_t>(p) * T + t0) * L;
+  for (int i = threadIdx.x; i < ntok * L; i += blockDim.x) gl[i] = gelu_tanh(rl[i]);
+  for (int i = threadIdx.x; i < ntok; i += blockDim.x) {
+    const int32_t n = rec_next[static_cast<int64_t>(p) * T + t0 + i];
+    leaf[i] = n;
+    if (path_out) path_out[static_cast<int64_t>(t0 + i) * P + p] = n - ((1 << D) - 1);
   }
   __syncthreads();
-  const int chunks = h / 8;
-  uint16_t* Ht = H + static_cast<int64_t>(t) * P * h;
-  for (int c = threadIdx.x; c < P * chunks; c += blockDim.x) {
-    const int p = c / chunks;
-    const int j0 = (c - p * chunks) * 8;
-    const int32_t lf = leaf[p];
-    const uint16_t* Vp = V + static_cast<int64_t>(p) * N * h + j0;
-    float acc[8] = {};
+  uint16_t* Hp = H + static_cast<int64_t>(p) * h;
+  for (int e = threadIdx.x; e < (ntok << HSHIFT); e += blockDim.x) {
+    const int i = e >> HSHIFT;
+    const int j0 = (e & (kChunks - 1)) * 16;
+    const int32_t lf = leaf[i];
+    const float* g = gl + i * L;
+    float acc[16];
+#pragma unroll
+    for (int q = 0; q < 16; ++q) acc[q] = 0.0f;
+#pragma unroll
     for (int l = 0; l < L; ++l) {
-      const int64_t n = ((lf + 1) >> (D - l)) - 1;  // ancestor of the leaf at level l
-      const float g = gl[p * L + l];
-      const uint4 v = ldg16(Vp + n * h);
-      acc[0] += g * bf16lo(v.x);
-      acc[1] += g * bf16hi(v.x);
-      acc[2] += g * bf16lo(v.y);
-      acc[3] += g * bf16hi(v.y);
-      acc[4] += g * bf16lo(v.z);
-      acc[5] += g * bf16hi(v.z);
-      acc[6] += g * bf16lo(v.w);
-      acc[7] += g * bf16hi(v.w);
+      const int n = ((lf + 1) >> (D - l)) - 1;  // ancestor of the leaf at level l
+      float v[16];
+      load_v16<F32>(vs, static_cast<size_t>(n) * h + j0, v);
+      const float gg = g[l];
+#pragma unroll
+      for (int q = 0; q < 16; ++q) acc[q] += gg * v[q];
     }
-    *reinterpret_cast<uint4*>(Ht + p * h + j0) =
-        make_uint4(pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]),
-                   pack_bf16x2(acc[4], acc[5]), pack_bf16x2(acc[6], acc[7]));
+    uint4* dst = reinterpret_cast<uint4*>(Hp + static_cast<int64_t>(t0 + i) * P * h + j0);
+    dst[0] = make_uint4(pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]),
+                        pack_bf16x2(acc[4], acc[5]), pack_bf16x2(acc[6], acc[7]));
+    dst[1] = make_uint4(pack_bf16x2(acc[8], acc[9]), pack_bf16x2(acc[10], acc[11]),
+                        pack_bf16x2(acc[12], acc[13]), pack_bf16x2(acc[14], acc[15]));
   }
+}
+
+bool hbuild_f32(const Dims& s) { return size_t(s.N) * s.h * 4 <= 32 * 1024; }
+
+size_t hbuild_lds_bytes(const Dims& s) {
+  return size_t(s.N) * s.h * (hbuild_f32(s) ? 4 : 2) + size_t(kHbTok) * (s.D + 1) * 4 +
+         kHbTok * 4;
 }
 
 template <class C, bool kDirect>
@@ -271,11 +333,14 @@ using MidTile = TileCfg<128, 256, 64, 64, 128>;
 using SmallTile = TileCfg<64, 256, 64, 64, 64>;
 using TopDirect = DirectCfg<256, 256, 128, 64, 4>;
 
+
 }  // namespace
+
+bool hbuild_supported(const Dims& s);
 
 bool route_top_supported(const Dims& s, int L) {
   return s.dtype == 1 && s.d % TopTile::BK == 0 && s.h % 8 == 0 && L >= 1 && L <= s.D + 1 &&
-         (1 << L) <= TopTile::BN && int64_t(s.P) * (s.D + 2) * 4 <= 65536;
+         (1 << L) <= TopTile::BN && (L <= s.D || hbuild_supported(s));
 }
 
 hipError_t launch_route_top(const Dims& s, int L, const void* x, const void* W, const void* b,
@@ -290,13 +355,65 @@ hipError_t launch_route_top(const Dims& s, int L, const void* x, const void* W, 
   return launch_top_cfg<SmallTile, false>(s, L, x, W, b, rec_logit, rec_next, st);
 }
 
+namespace {
+template <int LEVELS, int HSHIFT, bool F32>
+hipError_t launch_hbuild_l(const Dims& s, const float* rec_logit, const int32_t* rec_next,
+                           const void* V, void* H, int32_t* path_out, hipStream_t st) {
+  const size_t lds = hbuild_lds_bytes(s);
+  auto kern = hbuild_kernel<LEVELS, HSHIFT, F32>;
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  const dim3 grid(static_cast<unsigned>((s.T + kHbTok - 1) / kHbTok), static_cast<unsigned>(s.P));
+  kern<<<grid, dim3(256), lds, st>>>(rec_logit, rec_next, static_cast<const uint16_t*>(V),
+                                     static_cast<uint16_t*>(H), path_out, static_cast<int>(s.T),
+                                     s.P, s.N);
+  return hipGetLastError();
+}
+
+template <int LEVELS, int HSHIFT>
+hipError_t launch_hbuild_h(const Dims& s, const float* rec_logit, const int32_t* rec_next,
+                           const void* V, void* H, int32_t* path_out, hipStream_t st) {
+  if (hbuild_f32(s))
+    return launch_hbuild_l<LEVELS, HSHIFT, true>(s, rec_logit, rec_next, V, H, path_out, st);
+  return launch_hbuild_l<LEVELS, HSHIFT, false>(s, rec_logit, rec_next, V, H, path_out, st);
+}
+
+template <int LEVELS>
+hipError_t launch_hbuild_d(const Dims& s, const float* rec_logit, const int32_t* rec_next,
+                           const void* V, void* H, int32_t* path_out, hipStream_t st) {
+  switch (s.h) {
+    case 64: return launch_hbuild_h<LEVELS, 2>(s, rec_logit, rec_next, V, H, path_out, st);
+    case 128: return launch_hbuild_h<LEVELS, 3>(s, rec_logit, rec_next, V, H, path_out, st);
+    case 256: return launch_hbuild_h<LEVELS, 4>(s, rec_logit, rec_next, V, H, path_out, st);
+    case 512: return launch_hbuild_h<LEVELS, 5>(s, rec_logit, rec_next, V, H, path_out, st);
+    default: return hipErrorInvalidValue;  // hbuild_supported() excludes other widths
+  }
+}
+}  // namespace
+
+bool hbuild_supported(const Dims& s) {
+  return s.D + 1 <= 8 && (s.h == 64 || s.h == 128 || s.h == 256 || s.h == 512) &&
+         hbuild_lds_bytes(s) <= 160 * 1024;
+}
+
 hipError_t launch_hbuild(const Dims& s, const float* rec_logit, const int32_t* rec_next,
                          const void* V, void* H, int32_t* path_out, hipStream_t st) {
-  const size_t lds = static_cast<size_t>(s.P) * (s.D + 1) * sizeof(float) + s.P * sizeof(int32_t);
-  hbuild_kernel<<<dim3(static_cast<unsigned>(s.T)), dim3(256), lds, st>>>(
-      rec_logit, rec_next, static_cast<const uint16_t*>(V), static_cast<uint16_t*>(H), path_out,
-      static_cast<int>(s.T), s.P, s.D, s.h, s.N);
-  return hipGetLastError();
+  switch (s.D + 1) {
+    case 1: return launch_hbuild_d<1>(s, rec_logit, rec_next, V, H, path_out, st);
+    case 2: return launch_hbuild_d<2>(s, rec_logit, rec_next, V, H, path_out, st);
+    case 3: return launch_hbuild_d<3>(s, rec_logit, rec_next, V, H, path_out, st);
+    case 4: return launch_hbuild_d<4>(s, rec_logit, rec_next, V, H, path_out, st);
+    case 5: return launch_hbuild_d<5>(s, rec_logit, rec_next, V, H, path_out, st);
+    case 6: return launch_hbuild_d<6>(s, rec_logit, rec_next, V, H, path_out, st);
+    case 7: return launch_hbuild_d<7>(s, rec_logit, rec_next, V, H, path_out, st);
+    case 8: return launch_hbuild_d<8>(s, rec_logit, rec_next, V, H, path_out, st);
+    default: return hipErrorInvalidValue;  // the dense path covers D+1 <= 8 only
+  }
 }
 
 }  // namespace fff

@@ -58,6 +58,8 @@ SHAPES = [
     (129, 96, 5, 2, 24, "f32"),
     (1, 1, 1, 0, 1, "f32"),
     (257, 256, 2, 6, 64, "bf16"),
+    (100, 128, 2, 3, 512, "bf16"),     # wide nodes: H built by a separate pass
+    (300, 512, 40, 2, 64, "bf16"),     # trees that do not fill the last tile
 ]
 
 
