@@ -348,7 +348,7 @@ hipError_t launch_route_top(const Dims& s, int L, const void* x, const void* W, 
   // Enough tiles to cover the 256 compute units: shrink the token tile when
   // the column count is small (few trees or few levels).
   const int64_t tiles_n = ((static_cast<int64_t>(s.P) << L) + TopTile::BN - 1) / TopTile::BN;
-  if (((s.T + 255) / 256) * tiles_n >= 256)
+  if ((1 << L) <= TopDirect::BN && ((s.T + 255) / 256) * tiles_n >= 256)
     return launch_top_cfg<TopDirect, true>(s, L, x, W, b, rec_logit, rec_next, st);
   if (((s.T + 127) / 128) * tiles_n >= 256)
     return launch_top_cfg<MidTile, false>(s, L, x, W, b, rec_logit, rec_next, st);

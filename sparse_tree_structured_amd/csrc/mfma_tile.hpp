@@ -179,6 +179,20 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
+// Wait until at most min(later, MAXLATER) stages of PER loads each are in
+// flight (the immediate of s_waitcnt must be a compile-time constant).
+template <int PER, int MAXLATER>
+__device__ __forceinline__ void wait_stages(int later) {
+  if constexpr (MAXLATER <= 0) {
+    wait_vmcnt<0>();
+  } else {
+    if (later >= MAXLATER)
+      wait_vmcnt<MAXLATER * PER>();
+    else
+      wait_stages<PER, MAXLATER - 1>(later);
+  }
+}
+
 // Issue the loads of one K step (k0) into stage buffer `buf` for ROWS rows
 // starting at LDS byte offset `base`.  row_ptr(i) gives row i's start.
 template <class C, int ROWS, class RowPtr>
@@ -259,7 +273,7 @@ __device__ __forceinline__ void gemm_mainloop_direct(f32x16_t (&acc)[C::kTm][C::
   const int wm = wave / C::kWavesN;
   const int wn = wave % C::kWavesN;
   constexpr int S = C::kStages;
-  static_assert(S == 4, "wait counts below assume four stages");
+  static_assert(S >= 3 && S <= 6, "wait counts below cover three to six stages");
   constexpr int kPerStage = C::kALoads + C::kBLoads;  // loads per wave per stage
   zero_acc<C>(acc);
   const int nk = K / C::BK;
@@ -271,13 +285,8 @@ __device__ __forceinline__ void gemm_mainloop_direct(f32x16_t (&acc)[C::kTm][C::
 #pragma unroll
   for (int s = 0; s < S - 1; ++s)
     if (s < nk) issue(s);
-  // Stage 0 ready: at most stages 1 and 2 still in flight.
-  if (nk >= 3)
-    wait_vmcnt<2 * kPerStage>();
-  else if (nk == 2)
-    wait_vmcnt<kPerStage>();
-  else
-    wait_vmcnt<0>();
+  // Stage 0 ready: at most stages 1 .. S-2 still in flight.
+  wait_stages<kPerStage, S - 2>(nk - 1);
   stage_barrier();
   Frags<C> f0, f1;
   read_frags<C>(f0, lds, 0, wm, wn, lane);
@@ -287,11 +296,8 @@ __device__ __forceinline__ void gemm_mainloop_direct(f32x16_t (&acc)[C::kTm][C::
     asm volatile("" ::: "memory");  // keep these reads ahead of the MFMAs below
     mma_frags<C>(acc, f0);
     if (ks + 1 < nk) {
-      // Stage ks+1 ready: at most stage ks+2 still in flight.
-      if (ks + 2 < nk)
-        wait_vmcnt<kPerStage>();
-      else
-        wait_vmcnt<0>();
+      // Stage ks+1 ready: at most stages ks+2 .. ks+S-2 still in flight.
+      wait_stages<kPerStage, S - 3>(nk - 2 - ks);
       stage_barrier();  // also: every wave is done with stage ks-1's buffer
       if (ks + S - 1 < nk) issue(ks + S - 1);
     }
