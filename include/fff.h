@@ -89,8 +89,10 @@ typedef struct fff_shape {
 /* Algorithms.  AUTO picks by shape; the others force one (for tests and
  * measurement).  GENERIC takes any shape and dtype.  PREFILL needs bf16,
  * d % 64 == 0, h % 64 == 0 and either 2^(D+1) <= 256 (every level dense) or
- * a split level k with 2^k <= 256 and D-k <= 3.  DECODE needs bf16,
- * d % 256 == 0, h % 64 == 0 and T <= 64. */
+ * a split level k with 2^k <= 256 and D-k <= 3.  DECODE (one kernel for
+ * the whole layer, routing overlapped with the stream of W_out) needs bf16,
+ * 1 <= T <= 64, d % 128 == 0, d <= 2048, h % 8 == 0, h <= 512,
+ * P*h % 512 == 0 and D <= 15; AUTO takes it whenever the shape allows. */
 typedef enum fff_algo {
     FFF_ALGO_AUTO = 0,
     FFF_ALGO_GENERIC = 1,
@@ -129,8 +131,9 @@ fff_status_t fff_plan_default(const fff_shape_t *shape, fff_plan_t *plan);
  * use.  FFF_ERROR_NOT_SUPPORTED if the shape cannot run the requested plan. */
 fff_status_t fff_plan_resolve(const fff_shape_t *shape, const fff_plan_t *in, fff_plan_t *out);
 
-/* Workspace bytes the plan needs (plan NULL = the default plan).  The size
- * depends only on the shape and plan. */
+/* Workspace bytes the plan needs (plan NULL = the default plan), enough for
+ * both fff_forward and fff_route under that plan.  The size depends only on
+ * the shape and plan. */
 fff_status_t fff_workspace_size(const fff_shape_t *shape, const fff_plan_t *plan, size_t *bytes);
 
 /*
@@ -154,7 +157,9 @@ fff_status_t fff_forward(const fff_shape_t *shape, const fff_plan_t *plan,
 /*
  * Routing only: the concatenated tree outputs H[T, P*h] (dtype) and
  * path_out, without the projection.  Same rules as fff_forward; `H` is a
- * caller buffer (16-byte aligned).  Uses the same workspace size.
+ * caller buffer (16-byte aligned).  Uses the same workspace size.  Runs a
+ * staged algorithm: AUTO picks PREFILL or GENERIC, and DECODE (which fuses
+ * the projection) returns FFF_ERROR_NOT_SUPPORTED.
  */
 fff_status_t fff_route(const fff_shape_t *shape, const fff_plan_t *plan,
                        const void *x, const void *W_node, const void *b_node,

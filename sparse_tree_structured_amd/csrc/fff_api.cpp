@@ -66,12 +66,20 @@ bool prefill_fits(const Dims& s) {
          default_split(s) > 0;
 }
 
-fff_status_t resolve_plan(const Dims& s, const fff_plan_t* in, fff_plan_t* out) {
+// `staged`: the plan is for fff_route, which needs the routing stage on its
+// own; AUTO then never picks the fused decode kernel.
+fff_status_t resolve_plan(const Dims& s, const fff_plan_t* in, fff_plan_t* out,
+                          bool staged = false) {
   fff_plan_t p;
   p.algo = in ? in->algo : FFF_ALGO_AUTO;
   p.split_level = in ? in->split_level : -1;
   p.chunk_tokens = in ? in->chunk_tokens : 0;
-  if (p.algo == FFF_ALGO_AUTO) p.algo = prefill_fits(s) ? FFF_ALGO_PREFILL : FFF_ALGO_GENERIC;
+  if (p.algo == FFF_ALGO_AUTO) {
+    if (!staged && fff::decode_supported(s))
+      p.algo = FFF_ALGO_DECODE;
+    else
+      p.algo = prefill_fits(s) ? FFF_ALGO_PREFILL : FFF_ALGO_GENERIC;
+  }
   switch (p.algo) {
     case FFF_ALGO_GENERIC:
       p.split_level = 0;
@@ -90,7 +98,10 @@ fff_status_t resolve_plan(const Dims& s, const fff_plan_t* in, fff_plan_t* out) 
       }
       break;
     case FFF_ALGO_DECODE:
-      return FFF_ERROR_NOT_SUPPORTED;
+      if (staged || !fff::decode_supported(s)) return FFF_ERROR_NOT_SUPPORTED;
+      p.split_level = 0;
+      p.chunk_tokens = 0;
+      break;
     default:
       return FFF_ERROR_INVALID_VALUE;
   }
@@ -116,6 +127,11 @@ struct Layout {
 size_t align_up(size_t v) { return (v + kWsAlign - 1) / kWsAlign * kWsAlign; }
 
 Layout layout_for(const Dims& s, const fff_plan_t& p) {
+  if (p.algo == FFF_ALGO_DECODE) {  // the decode kernel carves its own
+    Layout L;
+    L.total = fff::decode_workspace(s);
+    return L;
+  }
   const bool prefill = p.algo == FFF_ALGO_PREFILL;
   const int levels = prefill ? p.split_level : s.D + 1;
   const bool deep = prefill && p.split_level <= s.D;
@@ -221,7 +237,14 @@ fff_status_t fff_workspace_size(const fff_shape_t* shape, const fff_plan_t* plan
   fff_plan_t p;
   st = resolve_plan(s, plan, &p);
   if (st != FFF_SUCCESS) return st;
-  *bytes = s.T == 0 ? 0 : layout_for(s, p).total;
+  size_t n = layout_for(s, p).total;
+  // The same plan given to fff_route may resolve to a staged algorithm.
+  fff_plan_t pr;
+  if (resolve_plan(s, plan, &pr, true) == FFF_SUCCESS) {
+    const size_t nr = layout_for(s, pr).total;
+    if (nr > n) n = nr;
+  }
+  *bytes = s.T == 0 ? 0 : n;
   return FFF_SUCCESS;
 }
 
@@ -249,6 +272,14 @@ fff_status_t fff_forward(const fff_shape_t* shape, const fff_plan_t* plan, const
   char* ws = static_cast<char*>(workspace);
   void* H = ws + L.H;
   if (events && (st = record(events->start, stream)) != FFF_SUCCESS) return st;
+  if (p.algo == FFF_ALGO_DECODE) {
+    st = hip_status(fff::launch_decode(s, x, W_node, b_node, V_node, W_out, y, path_out, ws,
+                                       stream));
+    if (st != FFF_SUCCESS) return st;
+    if (events && (st = record(events->routed, stream)) != FFF_SUCCESS) return st;
+    if (events && (st = record(events->done, stream)) != FFF_SUCCESS) return st;
+    return FFF_SUCCESS;
+  }
   // The projection's transposed W_out is prepared first, so that the
   // projection stage is the matrix product alone.
   if (L.use_wt && fff::launch_transpose(W_out, ws + L.WT, s.K, s.d, stream) != hipSuccess)
@@ -273,7 +304,7 @@ fff_status_t fff_route(const fff_shape_t* shape, const fff_plan_t* plan, const v
   fff_status_t st = check_shape(shape, &s);
   if (st != FFF_SUCCESS) return st;
   fff_plan_t p;
-  st = resolve_plan(s, plan, &p);
+  st = resolve_plan(s, plan, &p, true);
   if (st != FFF_SUCCESS) return st;
   if (s.T == 0) return FFF_SUCCESS;
   st = check_inputs(s, x, W_node, b_node, V_node);

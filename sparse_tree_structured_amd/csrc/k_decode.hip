@@ -1,0 +1,589 @@
+// Decode-shaped FFF forward (T <= 64 tokens) on gfx950: the whole layer in
+// one launch.
+//
+// At decode sizes the layer is bound by reading W_out (P*h x d) and by the
+// chain of dependent node evaluations down each tree (explainer page,
+// section 2: one root-to-leaf path per tree, the sign of each visited node's
+// logit choosing the child).  The launch holds two kinds of workgroups,
+// routing ones first (lower block ids), and overlaps the two:
+//
+//  routing     item = (tree p, up to 16 tokens).  The walk proceeds in
+//              rounds.  A round evaluates, below every distinct node the
+//              item's tokens sit on, the subtree of the next rl levels (rl
+//              chosen so that at most 16 node rows are read), as one
+//              16-row x 16-token product on the matrix cores with the model
+//              width split over the four waves (each wave keeps its slice of
+//              the token rows in registers for all rounds).  The round's V
+//              rows arrive in the same round trip.  The tokens walk the
+//              subtree (a < 0 goes left) and add GELU(a) * v_n of each
+//              visited node to their H row (GELU before the sum: section
+//              3.C).  H[t, p*h:(p+1)*h] (workspace, bf16 as in the prefill
+//              path) and path_out are written, then the item is counted as
+//              done for the K chunks its columns fall in.
+//  projection  item = (K chunk of 512 rows, 64 output columns).  The
+//              workgroup reads its W_out block into LDS transposed ([n][k])
+//              at once, waits until every routing item of its K chunk is
+//              counted, forms the partial y block H[:, chunk] . block on the
+//              matrix cores and writes it to the workspace.  The last of the
+//              chunk partials of a column slice to arrive sums them in chunk
+//              order and writes y in bf16.
+//
+// Workgroups hand data to each other through the workspace with device-
+// coherent (sc1) 16-byte buffer loads and stores, which do not stay in one
+// XCD's L2, so no L2 write-back or invalidation is needed: a writer waits
+// until its stores have completed, then publishes.  A routing item publishes
+// by storing the call's epoch into its own slot; a column slice counts its
+// arrived partials in a word tagged with the epoch (high 40 bits) over the
+// count (low 24 bits).  A slot or word that does not carry the current epoch
+// counts as not done, so nothing needs clearing between calls or before the
+// first one.  Epochs come from a per-process counter started at a random
+// point.  A projection workgroup only waits on routing workgroups, which
+// have lower block ids, never wait themselves and are all resident (the
+// grid is capped at what the device holds at once); the wait is also
+// bounded.
+#include <atomic>
+#include <chrono>
+#include <random>
+
+#include "common.hpp"
+#include "launch.hpp"
+#include "mfma_tile.hpp"
+
+namespace fff {
+namespace {
+
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kDecThreads = 256;
+constexpr int kDecWaves = kDecThreads / kWave;
+constexpr int kDecTok = 16;      // tokens per routing item (one MFMA column block)
+constexpr int kKc = 512;         // K rows per projection item
+constexpr int kColSlice = 64;    // output columns per projection item
+constexpr int kMaxRows = 16;     // node rows per routing round (one MFMA row block)
+constexpr int kMaxLevels = 16;   // D + 1
+constexpr int kMaxD = 2048;      // model width: 16 k-steps per wave slice
+constexpr int kMaxH = 512;       // node output width: 4 H pieces per thread
+constexpr int kWtPitch = kKc + 8;
+constexpr int kTagShift = 24;
+constexpr uint64_t kCountMask = (uint64_t(1) << kTagShift) - 1;
+constexpr uint64_t kEpochMask = (uint64_t(1) << 40) - 1;
+constexpr int kSpinLimit = 1 << 22;
+
+struct DecodeArgs {
+  const uint16_t* x;
+  const uint16_t* W;
+  const uint16_t* b;
+  const uint16_t* V;
+  const uint16_t* Wout;
+  uint16_t* y;
+  int32_t* path_out;
+  uint16_t* H;       // workspace [T, K] bf16
+  float* partial;    // workspace [K / kKc, T, d] fp32
+  uint64_t* done;    // workspace [routing items] epoch of the call that routed it
+  uint64_t* arrive;  // workspace [d / kColSlice] partials per column slice (tagged)
+  uint64_t epoch;
+  int T, d, P, D, h, K;
+  int64_t N;
+  int n_route_wg, n_proj_wg;
+};
+
+__device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
+
+__device__ __forceinline__ uint32_t pack_lo(uint32_t a, uint32_t b) {
+  return __builtin_amdgcn_perm(b, a, 0x05040100u);
+}
+__device__ __forceinline__ uint32_t pack_hi(uint32_t a, uint32_t b) {
+  return __builtin_amdgcn_perm(b, a, 0x07060302u);
+}
+__device__ __forceinline__ uint32_t word(const uint4& q, int i) {
+  return i == 0 ? q.x : (i == 1 ? q.y : (i == 2 ? q.z : q.w));
+}
+
+// Heap id of local node j (heap order within the subtree) of the subtree
+// rooted at global node r.
+__device__ __forceinline__ int64_t sub_global(int64_t r, int j) {
+  const int lvl = 31 - __clz(j + 1);
+  return ((r + 1) << lvl) - 1 + (j - ((1 << lvl) - 1));
+}
+
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+constexpr int kSc1 = 16;  // buffer cache policy: device scope (sc1)
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_of(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
+}
+__device__ __forceinline__ uint4 coherent_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kSc1));
+}
+__device__ __forceinline__ void coherent_store16(__amdgpu_buffer_rsrc_t r, uint32_t off, uint4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v), r, off, 0, kSc1);
+}
+
+// Adds one to an epoch-tagged count (agent scope; the caller has waited for
+// its data stores); returns the new count.
+__device__ uint64_t tagged_add(uint64_t* w, uint64_t epoch) {
+  uint64_t old = __hip_atomic_load(w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  for (;;) {
+    const uint64_t nw = (old >> kTagShift) == epoch ? old + 1 : (epoch << kTagShift) | 1;
+    if (__hip_atomic_compare_exchange_strong(w, &old, nw, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                             __HIP_MEMORY_SCOPE_AGENT))
+      return nw & kCountMask;
+  }
+}
+
+// One wave waits (bounded) until slots [first, first + n) all hold `epoch`.
+__device__ void wait_slots(const uint64_t* done, int first, int n, uint64_t epoch) {
+  const int lane = threadIdx.x & (kWave - 1);
+  for (int it = 0; it < kSpinLimit; ++it) {
+    bool ok = true;
+    for (int i = lane; i < n; i += kWave)
+      ok &= __hip_atomic_load(done + first + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == epoch;
+    if (__all(ok)) break;
+    __builtin_amdgcn_s_sleep(1);
+  }
+}
+
+// LDS: the two roles overlay one allocation.
+struct ProjLds {
+  static constexpr size_t wt = 0;  // [64][kWtPitch] bf16
+  static constexpr size_t total = size_t(kColSlice) * kWtPitch * 2;
+};
+struct RouteLds {
+  static constexpr size_t part = 0;                                   // [4 waves][16][16] f32
+  static constexpr size_t vc = part + size_t(kDecWaves) * 256 * 4;    // [16 rows][h] bf16
+  static constexpr size_t bias = vc + size_t(kMaxRows) * kMaxH * 2;   // [16] f32
+  static constexpr size_t rows = bias + kMaxRows * 4;                 // [16] i32 node ids
+  static constexpr size_t troot = rows + kMaxRows * 4;                // [16] i32 root of token
+  static constexpr size_t cur = troot + kDecTok * 4;                  // [16] i32 node of token
+  static constexpr size_t roots = cur + kDecTok * 4;                  // [16] i32
+  static constexpr size_t gsm = roots + kDecTok * 4;                  // [16][4] f32 GELU(a)
+  static constexpr size_t rsm = gsm + kDecTok * 4 * 4;                // [16][4] i32 row
+  static constexpr size_t leaf = rsm + kDecTok * 4 * 4;               // [16] i32
+  static constexpr size_t meta = leaf + kDecTok * 4;                  // R, rl
+  static constexpr size_t total = meta + 16;
+};
+constexpr size_t kDecLds = ProjLds::total > RouteLds::total ? ProjLds::total : RouteLds::total;
+
+// One routing round's plan, made by wave 0 (lane m < nt is token m): the
+// distinct current nodes of the item's tokens, the subtree depth rl, and the
+// node rows to evaluate (subtree of root i at rows i*S .. i*S+S-1 in local
+// heap order, S = 2^rl - 1).
+__device__ void plan_round(unsigned char* lds, int nt, int levels_left) {
+  int32_t* rows = reinterpret_cast<int32_t*>(lds + RouteLds::rows);
+  int32_t* troot = reinterpret_cast<int32_t*>(lds + RouteLds::troot);
+  const int32_t* cur = reinterpret_cast<const int32_t*>(lds + RouteLds::cur);
+  int32_t* roots = reinterpret_cast<int32_t*>(lds + RouteLds::roots);
+  int32_t* meta = reinterpret_cast<int32_t*>(lds + RouteLds::meta);
+  const int m = threadIdx.x & (kWave - 1);
+  const int c = m < nt ? cur[m] : -1 - m;  // lanes past nt match nobody
+  int f = m;                               // lowest lane on the same node
+  for (int k = kDecTok - 1; k >= 0; --k)
+    if (__shfl(c, k) == c) f = k < f ? k : f;
+  const uint64_t firsts = __ballot(m < nt && f == m);
+  const int n = __popcll(firsts);
+  const int rank = __popcll(firsts & ((uint64_t(1) << f) - 1));
+  if (m < nt) {
+    troot[m] = rank;
+    if (f == m) roots[rank] = c;
+  }
+  int rl = levels_left < 4 ? levels_left : 4;
+  while (rl > 1 && n * ((1 << rl) - 1) > kMaxRows) --rl;
+  const int S = (1 << rl) - 1;
+  // LDS operations of one wave complete in order: roots[] is written above.
+  if (m < n * S) rows[m] = static_cast<int32_t>(sub_global(roots[m / S], m % S));
+  if (m == 0) {
+    meta[0] = n * S;
+    meta[1] = rl;
+  }
+}
+
+// Routing of one item: tree p, tokens [t0, t0 + nt).
+__device__ void route_item(const DecodeArgs& a, unsigned char* lds, int item, int p, int t0,
+                           int nt) {
+  float* part = reinterpret_cast<float*>(lds + RouteLds::part);
+  uint16_t* vc = reinterpret_cast<uint16_t*>(lds + RouteLds::vc);
+  float* bias = reinterpret_cast<float*>(lds + RouteLds::bias);
+  const int32_t* rows = reinterpret_cast<const int32_t*>(lds + RouteLds::rows);
+  const int32_t* troot = reinterpret_cast<const int32_t*>(lds + RouteLds::troot);
+  int32_t* cur = reinterpret_cast<int32_t*>(lds + RouteLds::cur);
+  float* gsm = reinterpret_cast<float*>(lds + RouteLds::gsm);
+  int32_t* rsm = reinterpret_cast<int32_t*>(lds + RouteLds::rsm);
+  int32_t* leaf = reinterpret_cast<int32_t*>(lds + RouteLds::leaf);
+  const int32_t* meta = reinterpret_cast<const int32_t*>(lds + RouteLds::meta);
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = tid / kWave;
+  const int j = lane & 15;  // node row of the block (A) / token (B)
+  const int q = lane >> 4;  // 8-wide k group within each 32-wide step
+  const int klen = a.d / kDecWaves;
+  const int nsteps = klen / 32;  // <= 16
+  const int hc = a.h / 8;
+  const uint16_t* Wp = a.W + static_cast<int64_t>(p) * a.N * a.d;
+  const uint16_t* bp = a.b + static_cast<int64_t>(p) * a.N;
+  const uint16_t* Vp = a.V + static_cast<int64_t>(p) * a.N * a.h;
+
+  // This wave's slice of the token rows, kept for every round (rows past
+  // nt repeat the last token; their results are not used).
+  uint4 xf[16];
+  {
+    const uint16_t* xrow = a.x + static_cast<int64_t>(t0 + (j < nt ? j : nt - 1)) * a.d +
+                           wave * klen + q * 8;
+#pragma unroll
+    for (int u = 0; u < 16; ++u)
+      if (u < nsteps) xf[u] = ldg16(xrow + u * 32);
+  }
+  float hacc[4][8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int c = 0; c < 8; ++c) hacc[i][c] = 0.0f;
+
+  __syncthreads();  // LDS of a previous item is no longer read
+  if (wave == 0) {
+    if (lane < nt) cur[lane] = 0;  // every token starts at the root
+    plan_round(lds, nt, a.D + 1);
+  }
+  __syncthreads();
+
+  for (int lev = 0; lev <= a.D;) {
+    const int R = meta[0];
+    const int rl = meta[1];
+    const int S = (1 << rl) - 1;
+    // Node rows (lane row j; rows past R repeat row 0, unused).
+    uint4 wf[16];
+    {
+      const int64_t node = rows[j < R ? j : 0];
+      const uint16_t* wrow = Wp + node * a.d + wave * klen + q * 8;
+#pragma unroll
+      for (int u = 0; u < 16; ++u)
+        if (u < nsteps) wf[u] = ldg16(wrow + u * 32);
+    }
+    // V rows and biases of the round's nodes.
+    uint4 vr[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e = tid + i * kDecThreads;
+      if (e < R * hc) {
+        const int r = e / hc;
+        vr[i] = ldg16(Vp + static_cast<int64_t>(rows[r]) * a.h + (e - r * hc) * 8);
+      }
+    }
+    float bv = 0.0f;
+    if (tid < R) bv = bf16_to_f32(bp[rows[tid]]);
+
+    f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int u = 0; u < 16; ++u)
+      if (u < nsteps)
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(wf[u]), as_bf16x8(xf[u]), acc, 0, 0, 0);
+    // acc[r] = this wave's partial logit of row 4q + r for token j.
+#pragma unroll
+    for (int r = 0; r < 4; ++r) part[(wave * 16 + 4 * q + r) * 16 + j] = acc[r];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e = tid + i * kDecThreads;
+      if (e < R * hc) {
+        const int r = e / hc;
+        *reinterpret_cast<uint4*>(vc + r * a.h + (e - r * hc) * 8) = vr[i];
+      }
+    }
+    if (tid < R) bias[tid] = bv;
+    __syncthreads();
+
+    if (tid < nt) {  // walk of token tid through its subtree
+      const int m = tid;
+      const int base = troot[m] * S;
+      int jj = 0;
+      float lg = 0.0f;
+      int32_t nd = 0;
+      for (int lv = 0; lv < rl; ++lv) {
+        const int row = base + jj;
+        float s = 0.0f;
+#pragma unroll
+        for (int w = 0; w < kDecWaves; ++w) s += part[(w * 16 + row) * 16 + m];
+        lg = s + bias[row];
+        nd = rows[row];
+        gsm[m * 4 + lv] = gelu_tanh(lg);
+        rsm[m * 4 + lv] = row;
+        jj = 2 * jj + 1 + go_right(lg);
+      }
+      cur[m] = 2 * nd + 1 + go_right(lg);
+      leaf[m] = nd;
+    }
+    __syncthreads();
+
+    // H pieces (token m, 8 columns) of this thread: add the round's terms.
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e = tid + i * kDecThreads;
+      const int m = e / hc;
+      if (m < nt) {
+        const int c0 = (e - m * hc) * 8;
+        for (int lv = 0; lv < rl; ++lv) {
+          const float g = gsm[m * 4 + lv];
+          const uint4 v = *reinterpret_cast<const uint4*>(vc + rsm[m * 4 + lv] * a.h + c0);
+          hacc[i][0] += g * bf16lo(v.x);
+          hacc[i][1] += g * bf16hi(v.x);
+          hacc[i][2] += g * bf16lo(v.y);
+          hacc[i][3] += g * bf16hi(v.y);
+          hacc[i][4] += g * bf16lo(v.z);
+          hacc[i][5] += g * bf16hi(v.z);
+          hacc[i][6] += g * bf16lo(v.w);
+          hacc[i][7] += g * bf16hi(v.w);
+        }
+      }
+    }
+    lev += rl;
+    if (lev <= a.D && wave == 0) plan_round(lds, nt, a.D + 1 - lev);
+    __syncthreads();
+  }
+
+  const __amdgpu_buffer_rsrc_t hbuf = buffer_of(a.H, uint32_t(a.T) * a.K * 2);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int e = tid + i * kDecThreads;
+    const int m = e / hc;
+    if (m < nt) {
+      const int c0 = (e - m * hc) * 8;
+      coherent_store16(hbuf, uint32_t((t0 + m) * a.K + p * a.h + c0) * 2,
+                       make_uint4(pack_bf16x2(hacc[i][0], hacc[i][1]),
+                                  pack_bf16x2(hacc[i][2], hacc[i][3]),
+                                  pack_bf16x2(hacc[i][4], hacc[i][5]),
+                                  pack_bf16x2(hacc[i][6], hacc[i][7])));
+    }
+  }
+  if (a.path_out && tid < nt)
+    a.path_out[static_cast<int64_t>(t0 + tid) * a.P + p] = leaf[tid] - ((1 << a.D) - 1);
+
+  // Publish the item once every thread's H stores have completed.
+  wait_vmcnt<0>();
+  __syncthreads();
+  if (tid == 0)
+    __hip_atomic_store(a.done + item, a.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// W_out block (K chunk kc, column slice cs) into LDS as wt[n][k].  A thread
+// takes 4(k) x 8(n) pieces; eight lanes cover one 128-byte row segment.  All
+// loads of a thread are issued before the first LDS write.
+__device__ void load_wout_block(const DecodeArgs& a, unsigned char* lds, int kc, int cs) {
+  uint16_t* wt = reinterpret_cast<uint16_t*>(lds + ProjLds::wt);
+  constexpr int kNb = kColSlice / 8;
+  constexpr int kPieces = (kKc / 4) * kNb;
+  constexpr int kPer = kPieces / kDecThreads;
+  static_assert(kPieces % kDecThreads == 0, "pieces split evenly");
+  uint4 r[kPer][4];
+#pragma unroll
+  for (int u = 0; u < kPer; ++u) {
+    const int c = threadIdx.x + u * kDecThreads;
+    const int nb = c % kNb;
+    const int kb = c / kNb;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      r[u][i] = ldg16(a.Wout + static_cast<size_t>(kc * kKc + kb * 4 + i) * a.d + cs * kColSlice +
+                      nb * 8);
+  }
+#pragma unroll
+  for (int u = 0; u < kPer; ++u) {
+    const int c = threadIdx.x + u * kDecThreads;
+    const int nb = c % kNb;
+    const int kb = c / kNb;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint2 even = make_uint2(pack_lo(word(r[u][0], q), word(r[u][1], q)),
+                                    pack_lo(word(r[u][2], q), word(r[u][3], q)));
+      const uint2 odd = make_uint2(pack_hi(word(r[u][0], q), word(r[u][1], q)),
+                                   pack_hi(word(r[u][2], q), word(r[u][3], q)));
+      *reinterpret_cast<uint2*>(wt + (nb * 8 + 2 * q) * kWtPitch + kb * 4) = even;
+      *reinterpret_cast<uint2*>(wt + (nb * 8 + 2 * q + 1) * kWtPitch + kb * 4) = odd;
+    }
+  }
+}
+
+// Projection item (kc, cs): partial[kc][t][cs*64 + c] = H[t, chunk] . block.
+// Wave w takes token block w (T <= 64) and all four 16-column groups.
+__device__ void project_item(const DecodeArgs& a, unsigned char* lds, int kc, int cs) {
+  const uint16_t* wt = reinterpret_cast<const uint16_t*>(lds + ProjLds::wt);
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x / kWave;
+  const int n = lane & 15;  // column in a group (A row) / token in the block (B column)
+  const int q = lane >> 4;
+  const int tb = wave * 16;
+  if (tb >= a.T) return;
+  const int t = tb + n < a.T ? tb + n : a.T - 1;
+  const __amdgpu_buffer_rsrc_t hbuf = buffer_of(a.H, uint32_t(a.T) * a.K * 2);
+  const uint32_t hoff = uint32_t(t * a.K + kc * kKc + q * 8) * 2;
+  uint4 hf[kKc / 32];
+#pragma unroll
+  for (int s = 0; s < kKc / 32; ++s) hf[s] = coherent_load16(hbuf, hoff + s * 64);
+  const __amdgpu_buffer_rsrc_t pbuf = buffer_of(a.partial, uint32_t(a.K / kKc) * a.T * a.d * 4);
+#pragma unroll
+  for (int cg = 0; cg < kColSlice / 16; ++cg) {
+    const uint16_t* wrow = wt + (cg * 16 + n) * kWtPitch + q * 8;
+    f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int s = 0; s < kKc / 32; ++s) {
+      const uint4 wv = *reinterpret_cast<const uint4*>(wrow + s * 32);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(wv), as_bf16x8(hf[s]), acc, 0, 0, 0);
+    }
+    // acc[r]: column cg*16 + 4q + r, token tb + n.
+    if (tb + n < a.T)
+      coherent_store16(pbuf,
+                       uint32_t((kc * a.T + tb + n) * a.d + cs * kColSlice + cg * 16 + q * 4) * 4,
+                       make_uint4(__float_as_uint(acc[0]), __float_as_uint(acc[1]),
+                                  __float_as_uint(acc[2]), __float_as_uint(acc[3])));
+  }
+}
+
+// y columns of slice cs: sum of the K-chunk partials in chunk order.
+__device__ void reduce_slice(const DecodeArgs& a, int cs) {
+  const int nkc = a.K / kKc;
+  const __amdgpu_buffer_rsrc_t pbuf = buffer_of(a.partial, uint32_t(nkc) * a.T * a.d * 4);
+  for (int e = threadIdx.x; e < a.T * (kColSlice / 4); e += kDecThreads) {
+    const int t = e / (kColSlice / 4);
+    const int c = cs * kColSlice + (e - t * (kColSlice / 4)) * 4;
+    float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll 8
+    for (int kc = 0; kc < nkc; ++kc) {
+      const uint4 v = coherent_load16(pbuf, uint32_t((kc * a.T + t) * a.d + c) * 4);
+      s.x += __uint_as_float(v.x);
+      s.y += __uint_as_float(v.y);
+      s.z += __uint_as_float(v.z);
+      s.w += __uint_as_float(v.w);
+    }
+    *reinterpret_cast<uint2*>(a.y + static_cast<int64_t>(t) * a.d + c) =
+        make_uint2(pack_bf16x2(s.x, s.y), pack_bf16x2(s.z, s.w));
+  }
+}
+
+__global__ __launch_bounds__(kDecThreads, 2) void decode_kernel(DecodeArgs a) {
+  extern __shared__ __align__(16) unsigned char lds[];
+  __shared__ int last;
+  const int per_tree = (a.T + kDecTok - 1) / kDecTok;
+  const int g = blockIdx.x;
+  if (g < a.n_route_wg) {
+    for (int it = g; it < a.P * per_tree; it += a.n_route_wg) {
+      const int p = it / per_tree;
+      const int t0 = (it - p * per_tree) * kDecTok;
+      route_item(a, lds, it, p, t0, min(kDecTok, a.T - t0));
+    }
+    return;
+  }
+  const int nkc = a.K / kKc;
+  const int nproj = nkc * (a.d / kColSlice);
+  for (int it = g - a.n_route_wg; it < nproj; it += a.n_proj_wg) {
+    const int kc = it % nkc;
+    const int cs = it / nkc;
+    __syncthreads();  // LDS of a previous item is no longer read
+    load_wout_block(a, lds, kc, cs);
+    if (threadIdx.x < kWave) {
+      // Routing items (consecutive ids) of the trees whose columns overlap
+      // this K chunk.
+      const int p_lo = kc * kKc / a.h;
+      int p_hi = (kc * kKc + kKc - 1) / a.h;
+      if (p_hi > a.P - 1) p_hi = a.P - 1;
+      wait_slots(a.done, p_lo * per_tree, (p_hi - p_lo + 1) * per_tree, a.epoch);
+    }
+    __syncthreads();
+    project_item(a, lds, kc, cs);
+    wait_vmcnt<0>();  // this thread's partial stores have completed
+    __syncthreads();
+    if (threadIdx.x == 0) last = tagged_add(a.arrive + cs, a.epoch) == uint64_t(nkc);
+    __syncthreads();
+    if (last) reduce_slice(a, cs);
+  }
+}
+
+struct DeviceInfo {
+  int cus = 0, per_cu = 0;
+  bool ready = false;
+};
+
+size_t up256(size_t v) { return (v + 255) / 256 * 256; }
+
+// Per-call epochs: distinct within a process, and starting from a random
+// point so that words left by other processes do not match.
+uint64_t next_epoch() {
+  static std::atomic<uint64_t> counter{[] {
+    std::random_device rd;
+    const uint64_t t = static_cast<uint64_t>(
+        std::chrono::steady_clock::now().time_since_epoch().count());
+    return (uint64_t(rd()) << 32) ^ uint64_t(rd()) ^ (t * 0x9E3779B97F4A7C15ull);
+  }()};
+  uint64_t e = counter.fetch_add(1, std::memory_order_relaxed) & kEpochMask;
+  return e ? e : 1;
+}
+
+}  // namespace
+
+bool decode_supported(const Dims& s) {
+  // Buffer offsets (bytes) of the workspace arrays stay below 2^31.
+  return s.dtype == 1 && s.T >= 1 && s.T <= 64 && s.d % 128 == 0 && s.d <= kMaxD &&
+         s.h % 8 == 0 && s.h <= kMaxH && s.K % kKc == 0 && s.D + 1 <= kMaxLevels &&
+         s.K <= (int64_t(1) << 20);
+}
+
+size_t decode_workspace(const Dims& s) {
+  const size_t items = size_t(s.P) * ((s.T + kDecTok - 1) / kDecTok);
+  return up256(items * 8) + up256(size_t(s.d / kColSlice) * 8) + up256(size_t(s.T) * s.K * 2) +
+         up256(size_t(s.K / kKc) * s.T * s.d * 4);
+}
+
+hipError_t launch_decode(const Dims& s, const void* x, const void* W, const void* b,
+                         const void* V, const void* Wout, void* y, int32_t* path_out, void* ws,
+                         hipStream_t st) {
+  DecodeArgs a;
+  a.x = static_cast<const uint16_t*>(x);
+  a.W = static_cast<const uint16_t*>(W);
+  a.b = static_cast<const uint16_t*>(b);
+  a.V = static_cast<const uint16_t*>(V);
+  a.Wout = static_cast<const uint16_t*>(Wout);
+  a.y = static_cast<uint16_t*>(y);
+  a.path_out = path_out;
+  char* w = static_cast<char*>(ws);
+  a.done = reinterpret_cast<uint64_t*>(w);
+  w += up256(size_t(s.P) * ((s.T + kDecTok - 1) / kDecTok) * 8);
+  a.arrive = reinterpret_cast<uint64_t*>(w);
+  w += up256(size_t(s.d / kColSlice) * 8);
+  a.H = reinterpret_cast<uint16_t*>(w);
+  w += up256(size_t(s.T) * s.K * 2);
+  a.partial = reinterpret_cast<float*>(w);
+  a.T = static_cast<int>(s.T);
+  a.d = s.d;
+  a.P = s.P;
+  a.D = s.D;
+  a.h = s.h;
+  a.K = static_cast<int>(s.K);
+  a.N = s.N;
+
+  // Per-device residency limit, queried once per device.
+  static DeviceInfo info[64];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  DeviceInfo& di = info[dev];
+  if (!di.ready) {
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(decode_kernel),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, int(kDecLds));
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&di.cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e == hipSuccess)
+      e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&di.per_cu, decode_kernel, kDecThreads, kDecLds);
+    if (e != hipSuccess) return e;
+    if (di.cus < 1 || di.per_cu < 1) return hipErrorInvalidConfiguration;
+    di.ready = true;
+  }
+  // Grid no larger than what the device holds at once; items beyond it are
+  // looped over.  Routing gets at most half of the slots.
+  const int cap = di.cus * di.per_cu;
+  const int nroute = s.P * static_cast<int>((s.T + kDecTok - 1) / kDecTok);
+  const int nproj = static_cast<int>(s.K / kKc) * (s.d / kColSlice);
+  a.n_route_wg = nroute < cap / 2 ? nroute : cap / 2;
+  a.n_proj_wg = nproj < cap - a.n_route_wg ? nproj : cap - a.n_route_wg;
+  if (a.n_route_wg < 1 || a.n_proj_wg < 1) return hipErrorInvalidConfiguration;
+  a.epoch = next_epoch();
+  hipLaunchKernelGGL(decode_kernel, dim3(a.n_route_wg + a.n_proj_wg), dim3(kDecThreads), kDecLds,
+                     st, a);
+  return hipGetLastError();
+}
+
+}  // namespace fff

@@ -63,4 +63,12 @@ hipError_t launch_deep(const Dims& s, int k, const void* x, const void* W, const
                        const int32_t* offs, void* H, int32_t* path_out, int chunk,
                        hipStream_t st);
 
+// ---- decode (bf16, 1 <= T <= 64): one cooperative kernel for the layer ----
+// Workspace: H [T,K] bf16, fp32 K-chunk partials of y, per-slice counters.
+bool decode_supported(const Dims& s);
+size_t decode_workspace(const Dims& s);
+hipError_t launch_decode(const Dims& s, const void* x, const void* W, const void* b,
+                         const void* V, const void* Wout, void* y, int32_t* path_out, void* ws,
+                         hipStream_t st);
+
 }  // namespace fff

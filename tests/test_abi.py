@@ -129,3 +129,37 @@ def test_project_validation(lib):
         fff.ERROR_INVALID_VALUE
     assert lib.fff_project(ctypes.byref(_shape(dtype=fff.DTYPE_F32)), fff.ALGO_PREFILL, FAKE, FAKE,
                            FAKE, None) == fff.ERROR_NOT_SUPPORTED
+
+
+def test_decode_plans(lib):
+    dec = dict(d=2048, P=32, D=6, h=128)
+    for T in (1, 8, 64):
+        assert fff.plan_default(_shape(T=T, **dec)).algo == fff.ALGO_DECODE
+    # More than 64 tokens, fp32, or widths the kernel does not take: staged.
+    assert fff.plan_default(_shape(T=65, **dec)).algo == fff.ALGO_PREFILL
+    assert fff.plan_default(_shape(T=8, **dict(dec, d=2304))).algo == fff.ALGO_PREFILL
+    assert fff.plan_default(_shape(T=8, **dict(dec, h=120))).algo == fff.ALGO_GENERIC
+    assert fff.plan_default(_shape(T=8, dtype=fff.DTYPE_F32, **dec)).algo == fff.ALGO_GENERIC
+    forced = fff.make_plan("decode")
+    for kw in (dict(T=65), dict(T=8, d=192), dict(T=8, d=2176), dict(T=8, D=16), dict(T=8, h=1024),
+               dict(T=8, P=3, h=128), dict(T=8, dtype=fff.DTYPE_F32)):
+        s = _shape(**dict(dec, **kw))
+        assert _forward(lib, s, plan=forced) == fff.ERROR_NOT_SUPPORTED, kw
+    r = fff.resolve_plan(_shape(T=8, **dec), forced)
+    assert r.algo == fff.ALGO_DECODE and r.split_level == 0 and r.chunk_tokens == 0
+
+
+def test_decode_workspace_covers_route(lib):
+    # fff_route never runs the fused kernel: AUTO resolves to a staged
+    # algorithm there, and the size reported for AUTO covers both.
+    s = _shape(T=8, d=2048, P=32, D=6, h=128)
+    auto = fff.workspace_size(s)
+    dec = fff.workspace_size(s, fff.make_plan("decode"))
+    pre = fff.workspace_size(s, fff.make_plan("prefill"))
+    assert auto >= dec > 0 and auto >= pre > 0
+    # 8 chunk counts + 32 slice counts (64-bit, each rounded up to 256 bytes),
+    # H [8, 4096] bf16, 8 K-chunk partials [8, 8, 2048] fp32.
+    assert dec == 256 + 256 + 8 * 4096 * 2 + 8 * 8 * 2048 * 4
+    st = lib.fff_route(ctypes.byref(s), ctypes.byref(fff.make_plan("decode")), FAKE, FAKE, FAKE,
+                       FAKE, FAKE, FAKE, FAKE, 1 << 40, None)
+    assert st == fff.ERROR_NOT_SUPPORTED

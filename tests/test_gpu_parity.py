@@ -207,3 +207,64 @@ def test_route_matches_forward_h():
     torch.cuda.synchronize()
     assert torch.equal(path, path1)
     assert torch.equal(y, y2)
+
+
+DECODE_SHAPES = [
+    # T, d, P, D, h (bf16)
+    (1, 256, 2, 0, 256),       # a single level
+    (5, 256, 4, 3, 128),       # ragged T
+    (17, 512, 8, 5, 64),       # a second token group holding one token
+    (64, 2048, 32, 6, 128),    # unskewed: later rounds see up to 16 distinct nodes
+    (33, 768, 4, 9, 128),      # three rounds
+    (40, 256, 320, 3, 8),      # more routing items than workgroups
+    (3, 256, 1, 15, 512),      # deepest tree the kernel takes
+    (64, 1024, 16, 7, 64),
+    (8, 128, 4, 2, 128),       # narrowest model width
+    (12, 256, 8, 4, 192),      # trees straddling K-chunk boundaries
+]
+
+
+@needs_gpu
+@pytest.mark.parametrize("shape", DECODE_SHAPES, ids=[str(s) for s in DECODE_SHAPES])
+def test_decode_shapes(shape):
+    T, d, P, D, h = shape
+    inp = workloads.random_inputs(T, d, P, D, h, "bf16", seed=5, unit_rms_x=True)
+    y, path = run(inp, algo="decode")
+    check(inp, y, path)
+
+
+@needs_gpu
+@pytest.mark.parametrize("name", ["decode_skew_t1", "decode_skew_t8", "decode_skew_t64"])
+def test_decode_matches_prefill(name):
+    inp = wl(name)
+    yd, pd = run(inp, algo="decode")
+    yp, pp = run(inp, algo="prefill")
+    np.testing.assert_array_equal(pd, pp)
+    # Same bf16 H on both paths; the projections differ only in fp32
+    # summation order before the final rounding.
+    assert np.abs(yd - yp).max() <= 2e-2 * np.sqrt(np.mean(yp ** 2))
+
+
+@needs_gpu
+def test_decode_workspace_reuse():
+    # One workspace over calls of different sizes: the arrival counters are
+    # reset inside each call; results repeat bit for bit.
+    import sparse_tree_structured_amd as fff
+    big = workloads.random_inputs(64, 512, 8, 4, 64, "bf16", seed=8, unit_rms_x=True)
+    Tb = to_device(big)
+    shape = fff.shape_of(Tb["x"], Tb["W_node"], Tb["V_node"])
+    ws, _ = fff.alloc_workspace(shape, fff.make_plan("decode"), Tb["x"].device)
+    outs = []
+    for T in (64, 7, 64):
+        x = Tb["x"][:T].contiguous()
+        print(f"[gpu] decode reuse T={T}", flush=True)
+        y, path = fff.forward(x, Tb["W_node"], Tb["b_node"], Tb["V_node"], Tb["W_out"],
+                              algo="decode", workspace=ws)
+        y2, _ = fff.forward(x, Tb["W_node"], Tb["b_node"], Tb["V_node"], Tb["W_out"],
+                            algo="decode", want_path=False)
+        torch.cuda.synchronize()
+        assert torch.equal(y, y2)
+        outs.append((to_f64(y), path.cpu().numpy()))
+    np.testing.assert_array_equal(outs[0][0], outs[2][0])
+    np.testing.assert_array_equal(outs[0][1][:7], outs[1][1])
+    check(big, outs[0][0], outs[0][1])
