@@ -91,7 +91,7 @@ typedef struct fff_shape {
  * d % 64 == 0, h % 64 == 0 and either 2^(D+1) <= 256 (every level dense) or
  * a split level k with 2^k <= 256 and D-k <= 3.  DECODE (one kernel for
  * the whole layer, routing overlapped with the stream of W_out) needs bf16,
- * 1 <= T <= 64, d % 128 == 0, d <= 2048, h % 8 == 0, h <= 512,
+ * 1 <= T <= 64, d % 128 == 0, d <= 2048, h % 8 == 0, h <= 256,
  * P*h % 512 == 0 and D <= 15; AUTO takes it whenever the shape allows. */
 typedef enum fff_algo {
     FFF_ALGO_AUTO = 0,

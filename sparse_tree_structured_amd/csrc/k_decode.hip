@@ -14,29 +14,29 @@
 //              16-row x 16-token product on the matrix cores with the model
 //              width split over the four waves (each wave keeps its slice of
 //              the token rows in registers for all rounds).  The round's V
-//              rows arrive in the same round trip.  The tokens walk the
-//              subtree (a < 0 goes left) and add GELU(a) * v_n of each
-//              visited node to their H row (GELU before the sum: section
-//              3.C).  H[t, p*h:(p+1)*h] (workspace, bf16 as in the prefill
-//              path) and path_out are written, then the item is counted as
-//              done for the K chunks its columns fall in.
+//              rows and biases arrive in the same round trip.  Wave 0 sums
+//              the four partial logits, walks the tokens through the subtree
+//              (a < 0 goes left) and plans the next round; the GELU(a) * v_n
+//              terms of the visited nodes (GELU before the sum: section 3.C)
+//              are added to the token's H row while the next round's loads
+//              are in flight.  H[t, p*h:(p+1)*h] (workspace, bf16 as in the
+//              prefill path) and path_out are written, then the item is
+//              published.
 //  projection  item = (K chunk of 512 rows, 64 output columns).  The
-//              workgroup reads its W_out block into LDS transposed ([n][k])
-//              at once, waits until every routing item of its K chunk is
-//              counted, forms the partial y block H[:, chunk] . block on the
-//              matrix cores and writes it to the workspace.  The last of the
-//              chunk partials of a column slice to arrive sums them in chunk
+//              workgroup streams its W_out block into LDS transposed
+//              ([n][k]), waits until the routing items of the trees in its K
+//              chunk are published, forms the partial y block H[:, chunk] .
+//              block on the matrix cores and writes it to the workspace; the
+//              last partial of a column slice to arrive sums them in chunk
 //              order and writes y in bf16.
 //
 // Workgroups hand data to each other through the workspace with device-
 // coherent (sc1) 16-byte buffer loads and stores, which do not stay in one
 // XCD's L2, so no L2 write-back or invalidation is needed: a writer waits
-// until its stores have completed, then publishes.  A routing item publishes
-// by storing the call's epoch into its own slot; a column slice counts its
-// arrived partials in a word tagged with the epoch (high 40 bits) over the
-// count (low 24 bits).  A slot or word that does not carry the current epoch
-// counts as not done, so nothing needs clearing between calls or before the
-// first one.  Epochs come from a per-process counter started at a random
+// until its stores have completed, then publishes by storing the call's
+// epoch into a slot of its own (routing items; split-K partials).  A slot
+// that does not hold the current epoch counts as not done, so nothing needs
+// clearing between calls or before the first one.  Epochs come from a per-process counter started at a random
 // point.  A projection workgroup only waits on routing workgroups, which
 // have lower block ids, never wait themselves and are all resident (the
 // grid is capped at what the device holds at once); the wait is also
@@ -53,21 +53,22 @@ namespace fff {
 namespace {
 
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kDecThreads = 256;
 constexpr int kDecWaves = kDecThreads / kWave;
-constexpr int kDecTok = 16;      // tokens per routing item (one MFMA column block)
-constexpr int kKc = 512;         // K rows per projection item
-constexpr int kColSlice = 64;    // output columns per projection item
-constexpr int kMaxRows = 16;     // node rows per routing round (one MFMA row block)
-constexpr int kMaxLevels = 16;   // D + 1
-constexpr int kMaxD = 2048;      // model width: 16 k-steps per wave slice
-constexpr int kMaxH = 512;       // node output width: 4 H pieces per thread
+constexpr int kDecTok = 16;       // tokens per routing item (one MFMA column block)
+constexpr int kKc = 512;          // projection: K rows per item
+constexpr int kColSlice = 64;     // projection: output columns per item
+constexpr int kMaxRows = 16;      // node rows per routing round (one MFMA row block)
+constexpr int kMaxLevels = 16;    // D + 1
+constexpr int kMaxD = 2048;       // model width: 16 k-steps per wave slice
+constexpr int kMaxH = 256;        // node output width: 2 H pieces per thread
+constexpr int kHPieces = kDecTok * (kMaxH / 8) / kDecThreads;
 constexpr int kWtPitch = kKc + 8;
-constexpr int kTagShift = 24;
-constexpr uint64_t kCountMask = (uint64_t(1) << kTagShift) - 1;
 constexpr uint64_t kEpochMask = (uint64_t(1) << 40) - 1;
 constexpr int kSpinLimit = 1 << 22;
+constexpr int kSc1 = 16;  // buffer cache policy: device scope (sc1)
 
 struct DecodeArgs {
   const uint16_t* x;
@@ -80,7 +81,7 @@ struct DecodeArgs {
   uint16_t* H;       // workspace [T, K] bf16
   float* partial;    // workspace [K / kKc, T, d] fp32
   uint64_t* done;    // workspace [routing items] epoch of the call that routed it
-  uint64_t* arrive;  // workspace [d / kColSlice] partials per column slice (tagged)
+  uint64_t* arrive;  // workspace [d / kColSlice][K / kKc] epoch of the call whose partial arrived
   uint64_t epoch;
   int T, d, P, D, h, K;
   int64_t N;
@@ -106,29 +107,24 @@ __device__ __forceinline__ int64_t sub_global(int64_t r, int j) {
   return ((r + 1) << lvl) - 1 + (j - ((1 << lvl) - 1));
 }
 
-typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
-constexpr int kSc1 = 16;  // buffer cache policy: device scope (sc1)
-
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_of(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
+}
+// Plain buffer loads.  A lane whose offset is kOob (past every buffer's
+// size) gets zeros, so loads need no per-lane branch: branches around loads
+// make the compiler wait for all outstanding loads where they join.
+constexpr uint32_t kOob = 0x80000000u;
+__device__ __forceinline__ uint4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+__device__ __forceinline__ uint16_t buffer_load2(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
 }
 __device__ __forceinline__ uint4 coherent_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kSc1));
 }
 __device__ __forceinline__ void coherent_store16(__amdgpu_buffer_rsrc_t r, uint32_t off, uint4 v) {
   __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v), r, off, 0, kSc1);
-}
-
-// Adds one to an epoch-tagged count (agent scope; the caller has waited for
-// its data stores); returns the new count.
-__device__ uint64_t tagged_add(uint64_t* w, uint64_t epoch) {
-  uint64_t old = __hip_atomic_load(w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  for (;;) {
-    const uint64_t nw = (old >> kTagShift) == epoch ? old + 1 : (epoch << kTagShift) | 1;
-    if (__hip_atomic_compare_exchange_strong(w, &old, nw, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
-                                             __HIP_MEMORY_SCOPE_AGENT))
-      return nw & kCountMask;
-  }
 }
 
 // One wave waits (bounded) until slots [first, first + n) all hold `epoch`.
@@ -149,51 +145,45 @@ struct ProjLds {
   static constexpr size_t total = size_t(kColSlice) * kWtPitch * 2;
 };
 struct RouteLds {
-  static constexpr size_t part = 0;                                   // [4 waves][16][16] f32
-  static constexpr size_t vc = part + size_t(kDecWaves) * 256 * 4;    // [16 rows][h] bf16
-  static constexpr size_t bias = vc + size_t(kMaxRows) * kMaxH * 2;   // [16] f32
-  static constexpr size_t rows = bias + kMaxRows * 4;                 // [16] i32 node ids
-  static constexpr size_t troot = rows + kMaxRows * 4;                // [16] i32 root of token
-  static constexpr size_t cur = troot + kDecTok * 4;                  // [16] i32 node of token
-  static constexpr size_t roots = cur + kDecTok * 4;                  // [16] i32
-  static constexpr size_t gsm = roots + kDecTok * 4;                  // [16][4] f32 GELU(a)
-  static constexpr size_t rsm = gsm + kDecTok * 4 * 4;                // [16][4] i32 row
-  static constexpr size_t leaf = rsm + kDecTok * 4 * 4;               // [16] i32
-  static constexpr size_t meta = leaf + kDecTok * 4;                  // R, rl
+  static constexpr size_t part = 0;                                 // [3 waves][16][16] f32
+  static constexpr size_t lgs = part + 3 * 256 * 4;                 // [16 rows][16 tok] f32 logit
+  static constexpr size_t vc = lgs + 256 * 4;                       // [2][16 rows][h] bf16
+  static constexpr size_t rows = vc + 2 * size_t(kMaxRows) * kMaxH * 2;  // [16] i32 node ids
+  static constexpr size_t roots = rows + kMaxRows * 4;              // [16] i32
+  static constexpr size_t rsm = roots + kDecTok * 4;                // [16 tok][4] i32 row
+  static constexpr size_t meta = rsm + kDecTok * 4 * 4;             // R, rl
   static constexpr size_t total = meta + 16;
 };
 constexpr size_t kDecLds = ProjLds::total > RouteLds::total ? ProjLds::total : RouteLds::total;
 
-// One routing round's plan, made by wave 0 (lane m < nt is token m): the
-// distinct current nodes of the item's tokens, the subtree depth rl, and the
-// node rows to evaluate (subtree of root i at rows i*S .. i*S+S-1 in local
-// heap order, S = 2^rl - 1).
-__device__ void plan_round(unsigned char* lds, int nt, int levels_left) {
-  int32_t* rows = reinterpret_cast<int32_t*>(lds + RouteLds::rows);
-  int32_t* troot = reinterpret_cast<int32_t*>(lds + RouteLds::troot);
-  const int32_t* cur = reinterpret_cast<const int32_t*>(lds + RouteLds::cur);
-  int32_t* roots = reinterpret_cast<int32_t*>(lds + RouteLds::roots);
-  int32_t* meta = reinterpret_cast<int32_t*>(lds + RouteLds::meta);
-  const int m = threadIdx.x & (kWave - 1);
-  const int c = m < nt ? cur[m] : -1 - m;  // lanes past nt match nobody
-  int f = m;                               // lowest lane on the same node
-  for (int k = kDecTok - 1; k >= 0; --k)
-    if (__shfl(c, k) == c) f = k < f ? k : f;
-  const uint64_t firsts = __ballot(m < nt && f == m);
-  const int n = __popcll(firsts);
-  const int rank = __popcll(firsts & ((uint64_t(1) << f) - 1));
-  if (m < nt) {
-    troot[m] = rank;
-    if (f == m) roots[rank] = c;
-  }
-  int rl = levels_left < 4 ? levels_left : 4;
-  while (rl > 1 && n * ((1 << rl) - 1) > kMaxRows) --rl;
-  const int S = (1 << rl) - 1;
-  // LDS operations of one wave complete in order: roots[] is written above.
-  if (m < n * S) rows[m] = static_cast<int32_t>(sub_global(roots[m / S], m % S));
-  if (m == 0) {
-    meta[0] = n * S;
-    meta[1] = rl;
+// Adds one round's GELU(a) * v_n terms to the thread's H pieces (token m,
+// eight columns c0..c0+7; piece i is thread + 256 i).  rsm holds the rows
+// token m visited this round, lgs the round's logits [row][token].
+__device__ __forceinline__ void add_h_terms(const unsigned char* lds, const uint16_t* vcb, int rl,
+                                            int nt, int h, float (&hacc)[kHPieces][8]) {
+  const float* lgs = reinterpret_cast<const float*>(lds + RouteLds::lgs);
+  const int32_t* rsm = reinterpret_cast<const int32_t*>(lds + RouteLds::rsm);
+  const int hc = h / 8;
+#pragma unroll
+  for (int i = 0; i < kHPieces; ++i) {
+    const int e = threadIdx.x + i * kDecThreads;
+    const int m = e / hc;
+    if (m < nt) {
+      const int c0 = (e - m * hc) * 8;
+      for (int lv = 0; lv < rl; ++lv) {
+        const int row = rsm[m * 4 + lv];
+        const float g = gelu_tanh(lgs[row * 16 + m]);
+        const uint4 v = *reinterpret_cast<const uint4*>(vcb + row * h + c0);
+        hacc[i][0] += g * bf16lo(v.x);
+        hacc[i][1] += g * bf16hi(v.x);
+        hacc[i][2] += g * bf16lo(v.y);
+        hacc[i][3] += g * bf16hi(v.y);
+        hacc[i][4] += g * bf16lo(v.z);
+        hacc[i][5] += g * bf16hi(v.z);
+        hacc[i][6] += g * bf16lo(v.w);
+        hacc[i][7] += g * bf16hi(v.w);
+      }
+    }
   }
 }
 
@@ -201,15 +191,12 @@ __device__ void plan_round(unsigned char* lds, int nt, int levels_left) {
 __device__ void route_item(const DecodeArgs& a, unsigned char* lds, int item, int p, int t0,
                            int nt) {
   float* part = reinterpret_cast<float*>(lds + RouteLds::part);
+  float* lgs = reinterpret_cast<float*>(lds + RouteLds::lgs);
   uint16_t* vc = reinterpret_cast<uint16_t*>(lds + RouteLds::vc);
-  float* bias = reinterpret_cast<float*>(lds + RouteLds::bias);
-  const int32_t* rows = reinterpret_cast<const int32_t*>(lds + RouteLds::rows);
-  const int32_t* troot = reinterpret_cast<const int32_t*>(lds + RouteLds::troot);
-  int32_t* cur = reinterpret_cast<int32_t*>(lds + RouteLds::cur);
-  float* gsm = reinterpret_cast<float*>(lds + RouteLds::gsm);
+  int32_t* rows = reinterpret_cast<int32_t*>(lds + RouteLds::rows);
+  int32_t* roots = reinterpret_cast<int32_t*>(lds + RouteLds::roots);
   int32_t* rsm = reinterpret_cast<int32_t*>(lds + RouteLds::rsm);
-  int32_t* leaf = reinterpret_cast<int32_t*>(lds + RouteLds::leaf);
-  const int32_t* meta = reinterpret_cast<const int32_t*>(lds + RouteLds::meta);
+  int32_t* meta = reinterpret_cast<int32_t*>(lds + RouteLds::meta);
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = tid / kWave;
@@ -218,129 +205,156 @@ __device__ void route_item(const DecodeArgs& a, unsigned char* lds, int item, in
   const int klen = a.d / kDecWaves;
   const int nsteps = klen / 32;  // <= 16
   const int hc = a.h / 8;
-  const uint16_t* Wp = a.W + static_cast<int64_t>(p) * a.N * a.d;
-  const uint16_t* bp = a.b + static_cast<int64_t>(p) * a.N;
-  const uint16_t* Vp = a.V + static_cast<int64_t>(p) * a.N * a.h;
+  const int vc_stride = kMaxRows * a.h;
+  const __amdgpu_buffer_rsrc_t xbuf = buffer_of(a.x, uint32_t(a.T) * a.d * 2);
+  const __amdgpu_buffer_rsrc_t wbuf =
+      buffer_of(a.W + static_cast<int64_t>(p) * a.N * a.d, uint32_t(a.N) * a.d * 2);
+  const __amdgpu_buffer_rsrc_t bbuf = buffer_of(a.b + static_cast<int64_t>(p) * a.N, uint32_t(a.N) * 2);
+  const __amdgpu_buffer_rsrc_t vbuf =
+      buffer_of(a.V + static_cast<int64_t>(p) * a.N * a.h, uint32_t(a.N) * a.h * 2);
 
   // This wave's slice of the token rows, kept for every round (rows past
-  // nt repeat the last token; their results are not used).
+  // nt repeat the last token; their results are not used; k steps past the
+  // width load zeros).
   uint4 xf[16];
   {
-    const uint16_t* xrow = a.x + static_cast<int64_t>(t0 + (j < nt ? j : nt - 1)) * a.d +
-                           wave * klen + q * 8;
+    const uint32_t xoff = uint32_t((t0 + (j < nt ? j : nt - 1)) * a.d + wave * klen + q * 8) * 2;
 #pragma unroll
-    for (int u = 0; u < 16; ++u)
-      if (u < nsteps) xf[u] = ldg16(xrow + u * 32);
+    for (int u = 0; u < 16; ++u) xf[u] = buffer_load16(xbuf, u < nsteps ? xoff + u * 64 : kOob);
   }
-  float hacc[4][8];
+  float hacc[kHPieces][8];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < kHPieces; ++i)
 #pragma unroll
     for (int c = 0; c < 8; ++c) hacc[i][c] = 0.0f;
 
+  // Round 1 evaluates the top subtree, the same for every token: its rows
+  // are heap ids 0 .. S-1.  Wave 0 keeps, in lane j, token j's current node,
+  // the index of its subtree root in this round, and its last visited node.
+  int rl = a.D + 1 < 4 ? a.D + 1 : 4;
+  int R = (1 << rl) - 1;
+  int cur = 0, troot = 0, last_node = 0;
+  int prev_rl = 0, buf = 0;
   __syncthreads();  // LDS of a previous item is no longer read
-  if (wave == 0) {
-    if (lane < nt) cur[lane] = 0;  // every token starts at the root
-    plan_round(lds, nt, a.D + 1);
-  }
-  __syncthreads();
 
-  for (int lev = 0; lev <= a.D;) {
-    const int R = meta[0];
-    const int rl = meta[1];
+  for (int lev = 0;;) {
     const int S = (1 << rl) - 1;
-    // Node rows (lane row j; rows past R repeat row 0, unused).
+    // Node rows (row j of the block; rows past R repeat row 0, unused), the
+    // round's V rows, and the biases of rows 4q .. 4q+3 (wave 0).
     uint4 wf[16];
     {
-      const int64_t node = rows[j < R ? j : 0];
-      const uint16_t* wrow = Wp + node * a.d + wave * klen + q * 8;
+      const int r = j < R ? j : 0;
+      const int node = lev == 0 ? r : rows[r];
+      const uint32_t woff = uint32_t(node * a.d + wave * klen + q * 8) * 2;
 #pragma unroll
-      for (int u = 0; u < 16; ++u)
-        if (u < nsteps) wf[u] = ldg16(wrow + u * 32);
+      for (int u = 0; u < 16; ++u) wf[u] = buffer_load16(wbuf, u < nsteps ? woff + u * 64 : kOob);
     }
-    // V rows and biases of the round's nodes.
-    uint4 vr[4];
+    uint4 vr[kHPieces];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < kHPieces; ++i) {
       const int e = tid + i * kDecThreads;
-      if (e < R * hc) {
-        const int r = e / hc;
-        vr[i] = ldg16(Vp + static_cast<int64_t>(rows[r]) * a.h + (e - r * hc) * 8);
-      }
+      const int r = e / hc < R ? e / hc : R - 1;
+      const int node = lev == 0 ? r : rows[r];
+      vr[i] = buffer_load16(vbuf, e < R * hc ? uint32_t(node * a.h + (e - r * hc) * 8) * 2 : kOob);
     }
-    float bv = 0.0f;
-    if (tid < R) bv = bf16_to_f32(bp[rows[tid]]);
+    // Raw bias bits of rows 4q .. 4q+3 (used by wave 0), converted only
+    // after the MFMA so that nothing waits on these loads before then.
+    uint16_t braw[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int row = 4 * q + r < R ? 4 * q + r : 0;
+      braw[r] = buffer_load2(bbuf, 4 * q + r < R ? uint32_t(lev == 0 ? row : rows[row]) * 2 : kOob);
+    }
+    // The previous round's H terms, while these loads are in flight.
+    if (prev_rl) add_h_terms(lds, vc + (buf ^ 1) * vc_stride, prev_rl, nt, a.h, hacc);
 
+    // k steps past the width have zero operands.
     f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int u = 0; u < 16; ++u)
-      if (u < nsteps)
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(wf[u]), as_bf16x8(xf[u]), acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(wf[u]), as_bf16x8(xf[u]), acc, 0, 0, 0);
     // acc[r] = this wave's partial logit of row 4q + r for token j.
+    if (wave != 0) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) part[(wave * 16 + 4 * q + r) * 16 + j] = acc[r];
+      for (int r = 0; r < 4; ++r) part[((wave - 1) * 16 + 4 * q + r) * 16 + j] = acc[r];
+    }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < kHPieces; ++i) {
       const int e = tid + i * kDecThreads;
       if (e < R * hc) {
         const int r = e / hc;
-        *reinterpret_cast<uint4*>(vc + r * a.h + (e - r * hc) * 8) = vr[i];
+        *reinterpret_cast<uint4*>(vc + buf * vc_stride + r * a.h + (e - r * hc) * 8) = vr[i];
       }
     }
-    if (tid < R) bias[tid] = bv;
     __syncthreads();
 
-    if (tid < nt) {  // walk of token tid through its subtree
-      const int m = tid;
-      const int base = troot[m] * S;
-      int jj = 0;
-      float lg = 0.0f;
-      int32_t nd = 0;
+    if (wave == 0) {
+      // Logits (partials summed in wave order); the sign of row 4q + r for
+      // token j becomes bit 16q + j of ballot r.
+      uint64_t right[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = 4 * q + r;
+        const float lg = acc[r] + part[(0 * 16 + row) * 16 + j] + part[(1 * 16 + row) * 16 + j] +
+                         part[(2 * 16 + row) * 16 + j] + bf16_to_f32(braw[r]);
+        lgs[row * 16 + j] = lg;
+        right[r] = __ballot(go_right(lg));
+      }
+      // Walk of token j through its subtree (the four lanes of token j do
+      // the same walk; lane q == 0 records the visited rows).
+      const int base = troot * S;
+      int jj = 0, row = 0, bit = 0;
       for (int lv = 0; lv < rl; ++lv) {
-        const int row = base + jj;
-        float s = 0.0f;
-#pragma unroll
-        for (int w = 0; w < kDecWaves; ++w) s += part[(w * 16 + row) * 16 + m];
-        lg = s + bias[row];
-        nd = rows[row];
-        gsm[m * 4 + lv] = gelu_tanh(lg);
-        rsm[m * 4 + lv] = row;
-        jj = 2 * jj + 1 + go_right(lg);
+        row = base + jj;
+        const int sel = row & 3;
+        const uint64_t m = sel == 0 ? right[0] : sel == 1 ? right[1] : sel == 2 ? right[2] : right[3];
+        bit = static_cast<int>((m >> ((row >> 2) * 16 + j)) & 1);
+        if (q == 0 && j < nt) rsm[j * 4 + lv] = row;
+        jj = 2 * jj + 1 + bit;
       }
-      cur[m] = 2 * nd + 1 + go_right(lg);
-      leaf[m] = nd;
-    }
-    __syncthreads();
-
-    // H pieces (token m, 8 columns) of this thread: add the round's terms.
+      last_node = lev == 0 ? row : rows[row];
+      cur = 2 * last_node + 1 + bit;
+      if (lev + rl <= a.D) {
+        // Plan of the next round: distinct current nodes of the tokens
+        // (lanes 0..nt-1 hold tokens 0..nt-1), the depth of the subtrees
+        // below them, and their rows (subtree of root i at rows
+        // i*S' .. i*S'+S'-1).  Every lane of token j finds the same root.
+        int f = -1;  // lowest token with the same node
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int e = tid + i * kDecThreads;
-      const int m = e / hc;
-      if (m < nt) {
-        const int c0 = (e - m * hc) * 8;
-        for (int lv = 0; lv < rl; ++lv) {
-          const float g = gsm[m * 4 + lv];
-          const uint4 v = *reinterpret_cast<const uint4*>(vc + rsm[m * 4 + lv] * a.h + c0);
-          hacc[i][0] += g * bf16lo(v.x);
-          hacc[i][1] += g * bf16hi(v.x);
-          hacc[i][2] += g * bf16lo(v.y);
-          hacc[i][3] += g * bf16hi(v.y);
-          hacc[i][4] += g * bf16lo(v.z);
-          hacc[i][5] += g * bf16hi(v.z);
-          hacc[i][6] += g * bf16lo(v.w);
-          hacc[i][7] += g * bf16hi(v.w);
+        for (int k = 0; k < kDecTok; ++k) {
+          const int ck = __builtin_amdgcn_readlane(cur, k);
+          if (k < nt && f < 0 && ck == cur) f = k;
+        }
+        const uint64_t firsts = __ballot(lane < nt && f == lane);
+        const int n = __popcll(firsts);
+        const int rank = f < 0 ? 0 : __popcll(firsts & ((uint64_t(1) << f) - 1));
+        if (lane < nt && f == lane) roots[rank] = cur;
+        troot = j < nt ? rank : 0;
+        int nrl = a.D + 1 - (lev + rl);
+        nrl = nrl < 4 ? nrl : 4;
+        while (nrl > 1 && n * ((1 << nrl) - 1) > kMaxRows) --nrl;
+        const int nS = (1 << nrl) - 1;
+        // LDS operations of one wave complete in order: roots[] is written.
+        if (lane < n * nS) rows[lane] = static_cast<int32_t>(sub_global(roots[lane / nS], lane % nS));
+        if (lane == 0) {
+          meta[0] = n * nS;
+          meta[1] = nrl;
         }
       }
     }
-    lev += rl;
-    if (lev <= a.D && wave == 0) plan_round(lds, nt, a.D + 1 - lev);
     __syncthreads();
+    lev += rl;
+    prev_rl = rl;
+    buf ^= 1;
+    if (lev > a.D) break;
+    R = meta[0];
+    rl = meta[1];
   }
+  add_h_terms(lds, vc + (buf ^ 1) * vc_stride, prev_rl, nt, a.h, hacc);
 
   const __amdgpu_buffer_rsrc_t hbuf = buffer_of(a.H, uint32_t(a.T) * a.K * 2);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < kHPieces; ++i) {
     const int e = tid + i * kDecThreads;
     const int m = e / hc;
     if (m < nt) {
@@ -352,10 +366,10 @@ __device__ void route_item(const DecodeArgs& a, unsigned char* lds, int item, in
                                   pack_bf16x2(hacc[i][6], hacc[i][7])));
     }
   }
-  if (a.path_out && tid < nt)
-    a.path_out[static_cast<int64_t>(t0 + tid) * a.P + p] = leaf[tid] - ((1 << a.D) - 1);
+  if (a.path_out && wave == 0 && q == 0 && j < nt)
+    a.path_out[static_cast<int64_t>(t0 + j) * a.P + p] = last_node - ((1 << a.D) - 1);
 
-  // Publish the item once every thread's H stores have completed.
+  // Publish the item once every thread's stores have completed.
   wait_vmcnt<0>();
   __syncthreads();
   if (tid == 0)
@@ -363,45 +377,41 @@ __device__ void route_item(const DecodeArgs& a, unsigned char* lds, int item, in
 }
 
 // W_out block (K chunk kc, column slice cs) into LDS as wt[n][k].  A thread
-// takes 4(k) x 8(n) pieces; eight lanes cover one 128-byte row segment.  All
-// loads of a thread are issued before the first LDS write.
+// takes 4(k) x 8(n) pieces (four 16-byte row loads, byte permutes, eight
+// 8-byte LDS writes); eight lanes cover one 128-byte row segment.
 __device__ void load_wout_block(const DecodeArgs& a, unsigned char* lds, int kc, int cs) {
   uint16_t* wt = reinterpret_cast<uint16_t*>(lds + ProjLds::wt);
   constexpr int kNb = kColSlice / 8;
   constexpr int kPieces = (kKc / 4) * kNb;
   constexpr int kPer = kPieces / kDecThreads;
   static_assert(kPieces % kDecThreads == 0, "pieces split evenly");
-  uint4 r[kPer][4];
-#pragma unroll
+  const __amdgpu_buffer_rsrc_t obuf = buffer_of(a.Wout, uint32_t(a.K) * a.d * 2);
+  // One piece per thread at a time: the blocks of all projection
+  // workgroups together are the whole of W_out, and issuing them in
+  // batches keeps the memory queues short for the routing loads.
   for (int u = 0; u < kPer; ++u) {
     const int c = threadIdx.x + u * kDecThreads;
     const int nb = c % kNb;
     const int kb = c / kNb;
+    uint4 r[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      r[u][i] = ldg16(a.Wout + static_cast<size_t>(kc * kKc + kb * 4 + i) * a.d + cs * kColSlice +
-                      nb * 8);
-  }
-#pragma unroll
-  for (int u = 0; u < kPer; ++u) {
-    const int c = threadIdx.x + u * kDecThreads;
-    const int nb = c % kNb;
-    const int kb = c / kNb;
+      r[i] = buffer_load16(obuf, uint32_t((kc * kKc + kb * 4 + i) * a.d + cs * kColSlice + nb * 8) * 2);
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const uint2 even = make_uint2(pack_lo(word(r[u][0], q), word(r[u][1], q)),
-                                    pack_lo(word(r[u][2], q), word(r[u][3], q)));
-      const uint2 odd = make_uint2(pack_hi(word(r[u][0], q), word(r[u][1], q)),
-                                   pack_hi(word(r[u][2], q), word(r[u][3], q)));
+      const uint2 even = make_uint2(pack_lo(word(r[0], q), word(r[1], q)),
+                                    pack_lo(word(r[2], q), word(r[3], q)));
+      const uint2 odd = make_uint2(pack_hi(word(r[0], q), word(r[1], q)),
+                                   pack_hi(word(r[2], q), word(r[3], q)));
       *reinterpret_cast<uint2*>(wt + (nb * 8 + 2 * q) * kWtPitch + kb * 4) = even;
       *reinterpret_cast<uint2*>(wt + (nb * 8 + 2 * q + 1) * kWtPitch + kb * 4) = odd;
     }
   }
 }
 
-// Projection item (kc, cs): partial[kc][t][cs*64 + c] = H[t, chunk] . block.
-// Wave w takes token block w (T <= 64) and all four 16-column groups.
-__device__ void project_item(const DecodeArgs& a, unsigned char* lds, int kc, int cs) {
+// Partial product of item (kc, cs): partial[kc][t][cs*64 + c].  Wave w takes
+// token block w (T <= 64) and all four 16-column groups.
+__device__ void project_split(const DecodeArgs& a, unsigned char* lds, int kc, int cs) {
   const uint16_t* wt = reinterpret_cast<const uint16_t*>(lds + ProjLds::wt);
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
@@ -409,12 +419,12 @@ __device__ void project_item(const DecodeArgs& a, unsigned char* lds, int kc, in
   const int q = lane >> 4;
   const int tb = wave * 16;
   if (tb >= a.T) return;
-  const int t = tb + n < a.T ? tb + n : a.T - 1;
+  // Token columns past T are zero (no load).
   const __amdgpu_buffer_rsrc_t hbuf = buffer_of(a.H, uint32_t(a.T) * a.K * 2);
-  const uint32_t hoff = uint32_t(t * a.K + kc * kKc + q * 8) * 2;
+  const uint32_t hoff = uint32_t((tb + n) * a.K + kc * kKc + q * 8) * 2;
   uint4 hf[kKc / 32];
 #pragma unroll
-  for (int s = 0; s < kKc / 32; ++s) hf[s] = coherent_load16(hbuf, hoff + s * 64);
+  for (int s = 0; s < kKc / 32; ++s) hf[s] = coherent_load16(hbuf, tb + n < a.T ? hoff + s * 64 : kOob);
   const __amdgpu_buffer_rsrc_t pbuf = buffer_of(a.partial, uint32_t(a.K / kKc) * a.T * a.d * 4);
 #pragma unroll
   for (int cg = 0; cg < kColSlice / 16; ++cg) {
@@ -459,18 +469,20 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_kernel(DecodeArgs a) {
   extern __shared__ __align__(16) unsigned char lds[];
   __shared__ int last;
   const int per_tree = (a.T + kDecTok - 1) / kDecTok;
+  const int nroute = a.P * per_tree;
   const int g = blockIdx.x;
   if (g < a.n_route_wg) {
-    for (int it = g; it < a.P * per_tree; it += a.n_route_wg) {
+    for (int it = g; it < nroute; it += a.n_route_wg) {
       const int p = it / per_tree;
       const int t0 = (it - p * per_tree) * kDecTok;
       route_item(a, lds, it, p, t0, min(kDecTok, a.T - t0));
     }
     return;
   }
+  const int j = g - a.n_route_wg;
   const int nkc = a.K / kKc;
   const int nproj = nkc * (a.d / kColSlice);
-  for (int it = g - a.n_route_wg; it < nproj; it += a.n_proj_wg) {
+  for (int it = j; it < nproj; it += a.n_proj_wg) {
     const int kc = it % nkc;
     const int cs = it / nkc;
     __syncthreads();  // LDS of a previous item is no longer read
@@ -484,10 +496,24 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_kernel(DecodeArgs a) {
       wait_slots(a.done, p_lo * per_tree, (p_hi - p_lo + 1) * per_tree, a.epoch);
     }
     __syncthreads();
-    project_item(a, lds, kc, cs);
-    wait_vmcnt<0>();  // this thread's partial stores have completed
+    project_split(a, lds, kc, cs);
+    // Arrival: store this chunk's slot once the partial stores have
+    // completed, wait for that store, then read the slice's slots.  The
+    // workgroup whose slot store completes last sees every slot set; more
+    // than one may, and each then writes the same y values.
+    wait_vmcnt<0>();
     __syncthreads();
-    if (threadIdx.x == 0) last = tagged_add(a.arrive + cs, a.epoch) == uint64_t(nkc);
+    if (threadIdx.x < kWave) {
+      uint64_t* slots = a.arrive + static_cast<int64_t>(cs) * nkc;
+      if (threadIdx.x == 0)
+        __hip_atomic_store(slots + kc, a.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      wait_vmcnt<0>();
+      bool ok = true;
+      for (int i = threadIdx.x; i < nkc; i += kWave)
+        ok &= __hip_atomic_load(slots + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == a.epoch;
+      ok = __all(ok);
+      if (threadIdx.x == 0) last = ok;
+    }
     __syncthreads();
     if (last) reduce_slice(a, cs);
   }
@@ -516,16 +542,17 @@ uint64_t next_epoch() {
 }  // namespace
 
 bool decode_supported(const Dims& s) {
-  // Buffer offsets (bytes) of the workspace arrays stay below 2^31.
+  // Every buffer the kernel addresses (one tree's W_node or V_node rows,
+  // W_out, the workspace arrays) stays below 2^31 bytes.
   return s.dtype == 1 && s.T >= 1 && s.T <= 64 && s.d % 128 == 0 && s.d <= kMaxD &&
          s.h % 8 == 0 && s.h <= kMaxH && s.K % kKc == 0 && s.D + 1 <= kMaxLevels &&
-         s.K <= (int64_t(1) << 20);
+         s.K * s.d < (int64_t(1) << 30);
 }
 
 size_t decode_workspace(const Dims& s) {
   const size_t items = size_t(s.P) * ((s.T + kDecTok - 1) / kDecTok);
-  return up256(items * 8) + up256(size_t(s.d / kColSlice) * 8) + up256(size_t(s.T) * s.K * 2) +
-         up256(size_t(s.K / kKc) * s.T * s.d * 4);
+  return up256(items * 8) + up256(size_t(s.T) * s.K * 2) +
+         up256(size_t(s.d / kColSlice) * (s.K / kKc) * 8) + up256(size_t(s.K / kKc) * s.T * s.d * 4);
 }
 
 hipError_t launch_decode(const Dims& s, const void* x, const void* W, const void* b,
@@ -539,13 +566,14 @@ hipError_t launch_decode(const Dims& s, const void* x, const void* W, const void
   a.Wout = static_cast<const uint16_t*>(Wout);
   a.y = static_cast<uint16_t*>(y);
   a.path_out = path_out;
+  const int nroute = s.P * static_cast<int>((s.T + kDecTok - 1) / kDecTok);
   char* w = static_cast<char*>(ws);
   a.done = reinterpret_cast<uint64_t*>(w);
-  w += up256(size_t(s.P) * ((s.T + kDecTok - 1) / kDecTok) * 8);
-  a.arrive = reinterpret_cast<uint64_t*>(w);
-  w += up256(size_t(s.d / kColSlice) * 8);
+  w += up256(size_t(nroute) * 8);
   a.H = reinterpret_cast<uint16_t*>(w);
   w += up256(size_t(s.T) * s.K * 2);
+  a.arrive = reinterpret_cast<uint64_t*>(w);
+  w += up256(size_t(s.d / kColSlice) * (s.K / kKc) * 8);
   a.partial = reinterpret_cast<float*>(w);
   a.T = static_cast<int>(s.T);
   a.d = s.d;
@@ -575,11 +603,10 @@ hipError_t launch_decode(const Dims& s, const void* x, const void* W, const void
   // Grid no larger than what the device holds at once; items beyond it are
   // looped over.  Routing gets at most half of the slots.
   const int cap = di.cus * di.per_cu;
-  const int nroute = s.P * static_cast<int>((s.T + kDecTok - 1) / kDecTok);
   const int nproj = static_cast<int>(s.K / kKc) * (s.d / kColSlice);
   a.n_route_wg = nroute < cap / 2 ? nroute : cap / 2;
   a.n_proj_wg = nproj < cap - a.n_route_wg ? nproj : cap - a.n_route_wg;
-  if (a.n_route_wg < 1 || a.n_proj_wg < 1) return hipErrorInvalidConfiguration;
+  if (a.n_proj_wg < 1) return hipErrorInvalidConfiguration;
   a.epoch = next_epoch();
   hipLaunchKernelGGL(decode_kernel, dim3(a.n_route_wg + a.n_proj_wg), dim3(kDecThreads), kDecLds,
                      st, a);

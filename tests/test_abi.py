@@ -141,7 +141,7 @@ def test_decode_plans(lib):
     assert fff.plan_default(_shape(T=8, **dict(dec, h=120))).algo == fff.ALGO_GENERIC
     assert fff.plan_default(_shape(T=8, dtype=fff.DTYPE_F32, **dec)).algo == fff.ALGO_GENERIC
     forced = fff.make_plan("decode")
-    for kw in (dict(T=65), dict(T=8, d=192), dict(T=8, d=2176), dict(T=8, D=16), dict(T=8, h=1024),
+    for kw in (dict(T=65), dict(T=8, d=192), dict(T=8, d=2176), dict(T=8, D=16), dict(T=8, h=512),
                dict(T=8, P=3, h=128), dict(T=8, dtype=fff.DTYPE_F32)):
         s = _shape(**dict(dec, **kw))
         assert _forward(lib, s, plan=forced) == fff.ERROR_NOT_SUPPORTED, kw
@@ -157,9 +157,9 @@ def test_decode_workspace_covers_route(lib):
     dec = fff.workspace_size(s, fff.make_plan("decode"))
     pre = fff.workspace_size(s, fff.make_plan("prefill"))
     assert auto >= dec > 0 and auto >= pre > 0
-    # 8 chunk counts + 32 slice counts (64-bit, each rounded up to 256 bytes),
-    # H [8, 4096] bf16, 8 K-chunk partials [8, 8, 2048] fp32.
-    assert dec == 256 + 256 + 8 * 4096 * 2 + 8 * 8 * 2048 * 4
+    # 32 routing-item slots (64-bit, rounded up to 256 bytes), H [8, 4096]
+    # bf16, 32 x 8 arrival slots and 8 K-chunk partials of y [8, 2048] fp32.
+    assert dec == 256 + 8 * 4096 * 2 + 32 * 8 * 8 + 8 * 8 * 2048 * 4
     st = lib.fff_route(ctypes.byref(s), ctypes.byref(fff.make_plan("decode")), FAKE, FAKE, FAKE,
                        FAKE, FAKE, FAKE, FAKE, 1 << 40, None)
     assert st == fff.ERROR_NOT_SUPPORTED

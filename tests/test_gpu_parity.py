@@ -217,7 +217,7 @@ DECODE_SHAPES = [
     (64, 2048, 32, 6, 128),    # unskewed: later rounds see up to 16 distinct nodes
     (33, 768, 4, 9, 128),      # three rounds
     (40, 256, 320, 3, 8),      # more routing items than workgroups
-    (3, 256, 1, 15, 512),      # deepest tree the kernel takes
+    (3, 256, 2, 15, 256),      # deepest tree and widest node output the kernel takes
     (64, 1024, 16, 7, 64),
     (8, 128, 4, 2, 128),       # narrowest model width
     (12, 256, 8, 4, 192),      # trees straddling K-chunk boundaries
