@@ -64,7 +64,7 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     ip = ctypes.POINTER(ctypes.c_int32)
     lib.fffo_forward.restype = ctypes.c_int
     lib.fffo_forward.argtypes = [ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_int,
-                                 ctypes.c_int, dp, dp, dp, dp, dp, ip, dp, dp, ip, dp, dp,
+                                 ctypes.c_int, ctypes.c_int, dp, dp, dp, dp, dp, ip, dp, dp, ip, dp, dp,
                                  ip, ctypes.c_int]
     _LIBS[path] = lib
     return lib
@@ -93,13 +93,15 @@ def _iptr(a: Optional[np.ndarray]):
 
 def forward(x: np.ndarray, W_node: np.ndarray, b_node: np.ndarray, V_node: np.ndarray,
             W_out: np.ndarray, forced: Optional[np.ndarray] = None, want_y: bool = True,
-            want_H: bool = False, want_records: bool = False,
+            want_H: bool = False, want_records: bool = False, variant: int = 0,
             nthreads: Optional[int] = None, lib: Optional[ctypes.CDLL] = None) -> Dict[str, np.ndarray]:
     """Run the oracle.
 
     Arrays are float64 (widened exactly from the storage dtype):
     x [T,d], W_node [P,N,d], b_node [P,N], V_node [P,N,h], W_out [P*h,d].
     ``forced`` [T,P] int32 leaf indices walks those paths instead of routing.
+    ``variant`` 0 is FFF (GELU on each node's logit before the sum), 1 is
+    FFF-post (GELU applied once to each tree's summed h-vector).
 
     Returns a dict with ``path`` [T,P] int32, and as requested ``y`` [T,d],
     ``H`` [T,P*h], and the per-visit records ``rec_a``, ``rec_thr`` (float64)
@@ -132,8 +134,8 @@ def forward(x: np.ndarray, W_node: np.ndarray, b_node: np.ndarray, V_node: np.nd
         forced = np.ascontiguousarray(forced, dtype=np.int32)
         if forced.shape != (T, P):
             raise ValueError("forced must be [T,P]")
-    rc = lib.fffo_forward(T, d, P, D, h, _dptr(x), _dptr(W_node), _dptr(b_node), _dptr(V_node),
-                          _dptr(W_out), _iptr(forced), _dptr(out.get("y")), _dptr(out.get("H")),
+    rc = lib.fffo_forward(T, d, P, D, h, int(variant), _dptr(x), _dptr(W_node), _dptr(b_node),
+                          _dptr(V_node), _dptr(W_out), _iptr(forced), _dptr(out.get("y")), _dptr(out.get("H")),
                           _iptr(out["path"]), _dptr(out.get("rec_a")), _dptr(out.get("rec_thr")),
                           _iptr(out.get("rec_node")), int(nthreads or default_threads()))
     if rc != 0:

@@ -15,8 +15,12 @@
  *    every node a linear projection of the input gives a logit whose sign
  *    picks the child; only the nodes on the path are evaluated and their
  *    outputs are summed.
- *  - Same page, section 3.C: the nonlinearity (GELU) is applied per node,
- *    before the outputs are summed (the FFF variant, not FFF-post).
+ *  - Same page, section 3.C: two placements of the nonlinearity.  In FFF
+ *    (variant 0) GELU is applied per node, before the node outputs are
+ *    summed; in FFF-post (variant 1) the node outputs a_n * v_n are summed
+ *    first and GELU is applied once to each element of the tree's h-vector.
+ *    The thelatestinai.com page, Figure 3 and Table 6, names both variants.
+ *    Routing is the same in both: it depends on the logits only.
  *  - thelatestinai.com page of the same paper, Figure 1(c) caption: the tree
  *    outputs are concatenated and passed through one final linear projection.
  *  - Table 4 of that page (MLP-block sparsity 83% / 94% / 99% at depths
@@ -61,13 +65,14 @@ static double dot(const double *u, const double *v, int n)
 }
 
 /*
- * One token through one tree.  Walks root to leaf, adding GELU(a) * v_n for
- * every visited node into acc[0..h).  If forced_leaf >= 0 the branch at each
- * level is taken from that leaf's bits instead of the logit's sign.
- * Returns the leaf index.
+ * One token through one tree.  Walks root to leaf, adding GELU(a) * v_n
+ * (variant 0) or a * v_n (variant 1) for every visited node into acc[0..h);
+ * variant 1 then replaces each acc[j] by GELU(acc[j]).  If forced_leaf >= 0
+ * the branch at each level is taken from that leaf's bits instead of the
+ * logit's sign.  Returns the leaf index.
  */
 static int32_t walk_tree(const double *xt, double xnorm, const double *Wp, const double *bp,
-                         const double *Vp, int d, int D, int h, int32_t forced_leaf,
+                         const double *Vp, int d, int D, int h, int variant, int32_t forced_leaf,
                          double *acc, double *rec_a, double *rec_thr, int32_t *rec_node)
 {
     int64_t n = 0; /* heap index of the current node */
@@ -82,7 +87,7 @@ static int32_t walk_tree(const double *xt, double xnorm, const double *Wp, const
             rec_thr[level] = 1e-4 * xnorm * sqrt(dot(w, w, d));
         if (rec_node)
             rec_node[level] = (int32_t)n;
-        double g = gelu_tanh(a);
+        double g = variant == 1 ? a : gelu_tanh(a);
         const double *v = Vp + n * (int64_t)h;
         for (int j = 0; j < h; ++j)
             acc[j] += g * v[j];
@@ -95,6 +100,9 @@ static int32_t walk_tree(const double *xt, double xnorm, const double *Wp, const
             n = 2 * n + 1 + go_right;
         }
     }
+    if (variant == 1)
+        for (int j = 0; j < h; ++j)
+            acc[j] = gelu_tanh(acc[j]);
     return (int32_t)(n - (((int64_t)1 << D) - 1));
 }
 
@@ -107,17 +115,18 @@ static int32_t walk_tree(const double *xt, double xnorm, const double *Wp, const
  *   H       [T,P*h] out (the concatenated tree outputs), or NULL
  *   path    [T,P] out (leaf indices), or NULL
  *   rec_a, rec_thr, rec_node  [T,P,D+1] per-visit records, each may be NULL
+ *   variant   0 = FFF (GELU per node), 1 = FFF-post (GELU after the sum)
  *   nthreads  worker threads (<= 0: runtime default)
  *
- * Returns 0, or 1 for a bad shape.
+ * Returns 0, or 1 for a bad shape or variant.
  */
-int fffo_forward(int64_t T, int d, int P, int D, int h,
+int fffo_forward(int64_t T, int d, int P, int D, int h, int variant,
                  const double *x, const double *W, const double *b, const double *V,
                  const double *Wout, const int32_t *forced,
                  double *y, double *H, int32_t *path,
                  double *rec_a, double *rec_thr, int32_t *rec_node, int nthreads)
 {
-    if (T < 0 || d <= 0 || P <= 0 || D < 0 || D > 24 || h <= 0)
+    if (T < 0 || d <= 0 || P <= 0 || D < 0 || D > 24 || h <= 0 || variant < 0 || variant > 1)
         return FFFO_BAD_ARG;
     const int64_t N = ((int64_t)1 << (D + 1)) - 1;
     const int64_t K = (int64_t)P * h;
@@ -136,7 +145,7 @@ int fffo_forward(int64_t T, int d, int P, int D, int h,
             int64_t tp = t * P + p;
             int32_t fl = forced ? forced[tp] : -1;
             int32_t leaf = walk_tree(xt, xnorm, W + (int64_t)p * N * d, b + (int64_t)p * N,
-                                     V + (int64_t)p * N * h, d, D, h, fl, Ht + (int64_t)p * h,
+                                     V + (int64_t)p * N * h, d, D, h, variant, fl, Ht + (int64_t)p * h,
                                      rec_a ? rec_a + tp * L : NULL,
                                      rec_thr ? rec_thr + tp * L : NULL,
                                      rec_node ? rec_node + tp * L : NULL);

@@ -19,6 +19,12 @@ AssertionError when the oracle disagrees with:
 * invariances: positive rescaling of a node's (w, b), token and tree
   permutation, linearity in V and W_out, batch invariance.
 
+The FFF-post variant (explainer page, section 3.C: GELU after the sum of the
+node outputs a_n v_n instead of on each a_n) has its own pins: the masked
+brute force with GELU moved outside the masked sum, hand routing with an
+all-ones V column (where the two placements give different closed forms),
+the constant-bias and depth-0 closed forms, and routing identical to FFF's.
+
 GELU references come from ``torch.nn.functional.gelu(approximate="tanh")``
 in float64, a library implementation independent of the oracle's C code.
 """
@@ -60,8 +66,11 @@ def ancestors_of_leaf(leaf: int, D: int):
     return nodes[::-1]
 
 
-def brute_force(L, forced=None):
-    """Masked formulation: dense logits, enumerate all 2^D paths."""
+def brute_force(L, forced=None, variant=0):
+    """Masked formulation: dense logits, enumerate all 2^D paths.
+
+    variant 0 sums GELU(a_n) v_n over the path's nodes; variant 1 (FFF-post)
+    sums a_n v_n and applies GELU to the result."""
     x, W, b, V, Wo = L["x"], L["W_node"], L["b_node"], L["V_node"], L["W_out"]
     T, d = x.shape
     P, N, _ = W.shape
@@ -92,7 +101,10 @@ def brute_force(L, forced=None):
             mask = np.zeros(N)
             mask[ancestors_of_leaf(leaf, D)] = 1.0
             path[t, p] = leaf
-            H[t, p * h:(p + 1) * h] = (mask * G[t, p]) @ V[p]
+            if variant == 0:
+                H[t, p * h:(p + 1) * h] = (mask * G[t, p]) @ V[p]
+            else:
+                H[t, p * h:(p + 1) * h] = gelu_ref((mask * A[t, p]) @ V[p])
     return path, H, H @ Wo
 
 
@@ -301,6 +313,104 @@ def pin_tie_threshold(lib):
                 _close(r["rec_a"][t, p, lvl], L["x"][t] @ L["W_node"][p, n] + L["b_node"][p, n])
 
 
+def pin_post_brute_force(lib, n_cases=16):
+    rng = np.random.default_rng(4321)
+    shapes = [(7, 5, 3, 3, 4), (4, 8, 2, 5, 3), (9, 3, 1, 2, 6), (5, 4, 3, 1, 2)]
+    for i in range(n_cases):
+        T, d, P, D, h = shapes[i % len(shapes)]
+        L = rand_layer(rng, T, d, P, D, h)
+        r = oracle.forward(**L, want_H=True, variant=1, lib=lib, nthreads=2)
+        path, H, y = brute_force(L, variant=1)
+        np.testing.assert_array_equal(r["path"], path)
+        _close(r["H"], H)
+        _close(r["y"], y)
+    # Forced paths follow the same masked sum along the given leaves.
+    T, d, P, D, h = 6, 7, 2, 3, 4
+    L = rand_layer(rng, T, d, P, D, h)
+    forced = rng.integers(0, 1 << D, size=(T, P)).astype(np.int32)
+    r = oracle.forward(**L, forced=forced, want_H=True, variant=1, lib=lib, nthreads=1)
+    _, H, y = brute_force(L, forced=forced, variant=1)
+    _close(r["H"], H)
+    _close(r["y"], y)
+
+
+def pin_post_hand_routing(lib):
+    """Hand routing as in pin_hand_routing (every |a| = 1) with an all-ones
+    first V column: FFF-post gives H[t, p*h] = GELU(#right - #left) along the
+    path, where FFF would give #right GELU(1) + #left GELU(-1)."""
+    D, P, T = 4, 2, 32
+    N = (1 << (D + 1)) - 1
+    d, h = D + 3, 3
+    rng = np.random.default_rng(17)
+    s = np.array([1.0, -1.0])
+    x = np.zeros((T, d))
+    x[:, :D + 1] = rng.choice([-1.0, 1.0], size=(T, D + 1))
+    W = np.zeros((P, N, d))
+    for p in range(P):
+        for n in range(N):
+            W[p, n, int(np.floor(np.log2(n + 1)))] = s[p]
+    V = np.zeros((P, N, h))
+    V[:, :, 0] = 1.0
+    b = np.zeros((P, N))
+    Wo = rng.standard_normal((P * h, d))
+    post = oracle.forward(x, W, b, V, Wo, want_H=True, variant=1, lib=lib, nthreads=2)
+    pre = oracle.forward(x, W, b, V, Wo, want_H=True, variant=0, lib=lib, nthreads=2)
+    np.testing.assert_array_equal(post["path"], pre["path"])
+    g_pos, g_neg = gelu_ref(np.array([1.0, -1.0]))
+    for t in range(T):
+        for p in range(P):
+            n_right = sum(int(s[p] * x[t, lvl] > 0) for lvl in range(D + 1))
+            n_left = D + 1 - n_right
+            leaf = sum(int(s[p] * x[t, lvl] > 0) << (D - 1 - lvl) for lvl in range(D))
+            assert post["path"][t, p] == leaf
+            _close(post["H"][t, p * h], gelu_ref(np.array([float(n_right - n_left)]))[0])
+            _close(pre["H"][t, p * h], n_right * g_pos + n_left * g_neg)
+            assert (post["H"][t, p * h + 1:(p + 1) * h] == 0).all()
+    _close(post["y"], post["H"] @ Wo)
+
+
+def pin_post_closed_forms(lib):
+    """Constant bias -beta (W = 0): H_p = GELU(-beta * sum of the spine's v);
+    depth 0: H[t, p*h + j] = GELU((x_t . w_p + b_p) v_p[j]), checked against
+    torch's linear and GELU."""
+    T, d, P, D, h = 5, 4, 3, 4, 6
+    beta = 0.75
+    rng = np.random.default_rng(14)
+    L = rand_layer(rng, T, d, P, D, h)
+    L["W_node"][:] = 0.0
+    L["b_node"][:] = -beta
+    r = oracle.forward(**L, want_H=True, variant=1, lib=lib, nthreads=1)
+    assert (r["path"] == 0).all()
+    for p in range(P):
+        spine = sum(L["V_node"][p, (1 << lvl) - 1] for lvl in range(D + 1))
+        for t in range(T):
+            _close(r["H"][t, p * h:(p + 1) * h], gelu_ref(-beta * spine))
+    T, d, P, h = 11, 9, 5, 3
+    L = rand_layer(rng, T, d, P, 0, h)
+    r = oracle.forward(**L, want_H=True, variant=1, lib=lib, nthreads=1)
+    logits = torch.nn.functional.linear(torch.from_numpy(L["x"]),
+                                        torch.from_numpy(L["W_node"][:, 0, :]),
+                                        torch.from_numpy(L["b_node"][:, 0]))
+    H = torch.nn.functional.gelu(logits[:, :, None] * torch.from_numpy(L["V_node"][:, 0, :])[None],
+                                 approximate="tanh").reshape(T, P * h)
+    _close(r["H"], H.numpy(), rtol=1e-11, atol=1e-12)
+    _close(r["y"], (H @ torch.from_numpy(L["W_out"])).numpy(), rtol=1e-11, atol=1e-12)
+
+
+def pin_post_routing_unchanged(lib):
+    """Routing depends on the logits only, so both variants take the same
+    paths and record the same per-visit logits."""
+    rng = np.random.default_rng(15)
+    L = rand_layer(rng, 12, 6, 3, 5, 4)
+    a = oracle.forward(**L, want_records=True, variant=0, lib=lib, nthreads=2)
+    b = oracle.forward(**L, want_records=True, variant=1, lib=lib, nthreads=2)
+    np.testing.assert_array_equal(a["path"], b["path"])
+    np.testing.assert_array_equal(a["rec_node"], b["rec_node"])
+    np.testing.assert_array_equal(a["rec_a"], b["rec_a"])
+    assert not np.allclose(a["y"], b["y"])
+
+
 ALL_PINS = [pin_brute_force, pin_hand_routing, pin_zero_ties, pin_negative_bias,
             pin_visit_count_table4, pin_depth0_dense, pin_forced_paths, pin_invariants,
-            pin_tie_threshold]
+            pin_tie_threshold, pin_post_brute_force, pin_post_hand_routing,
+            pin_post_closed_forms, pin_post_routing_unchanged]

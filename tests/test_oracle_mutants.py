@@ -26,14 +26,18 @@ MUTANTS = [
     ("v_row_by_level", "const double *v = Vp + n * (int64_t)h;",
      "const double *v = Vp + level * (int64_t)h;"),
     ("outputs_not_summed", "acc[j] += g * v[j];", "acc[j] = g * v[j];"),
-    ("concat_order_reversed", "d, D, h, fl, Ht + (int64_t)p * h,",
-     "d, D, h, fl, Ht + (int64_t)(P - 1 - p) * h,"),
+    ("concat_order_reversed", "d, D, h, variant, fl, Ht + (int64_t)p * h,",
+     "d, D, h, variant, fl, Ht + (int64_t)(P - 1 - p) * h,"),
     ("projection_transposed", "yt[c] += hk * wk[c];", "yt[c] += hk * Wout[(int64_t)c * K + k];"),
     ("path_is_node_id", "return (int32_t)(n - (((int64_t)1 << D) - 1));", "return (int32_t)n;"),
     ("forced_bits_reversed", "go_right = (forced_leaf >> (D - 1 - level)) & 1;",
      "go_right = (forced_leaf >> level) & 1;"),
     ("threshold_without_x_norm", "rec_thr[level] = 1e-4 * xnorm * sqrt(dot(w, w, d));",
      "rec_thr[level] = 1e-4 * sqrt(dot(w, w, d));"),
+    ("post_gelu_on_each_node", "double g = variant == 1 ? a : gelu_tanh(a);",
+     "double g = gelu_tanh(a);"),
+    ("post_final_gelu_dropped", "acc[j] = gelu_tanh(acc[j]);", "acc[j] = acc[j];"),
+    ("post_variant_ignored", "if (variant == 1)\n", "if (0)\n"),
 ]
 
 

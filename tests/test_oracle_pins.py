@@ -48,3 +48,9 @@ def test_bad_shape_rejected(lib):
     L = rand_layer(np.random.default_rng(0), 2, 3, 1, 1, 2)
     with pytest.raises(ValueError):
         oracle.forward(L["x"], L["W_node"], L["b_node"], L["V_node"], L["W_out"][:-1], lib=lib)
+
+
+def test_bad_variant_rejected(lib):
+    L = rand_layer(np.random.default_rng(0), 2, 3, 1, 1, 2)
+    with pytest.raises(ValueError):
+        oracle.forward(**L, variant=2, lib=lib)
