@@ -38,6 +38,8 @@ def parse():
     ap.add_argument("--algo", default="auto")
     ap.add_argument("--split-level", type=int, default=-1)
     ap.add_argument("--chunk-tokens", type=int, default=0)
+    ap.add_argument("--variant", default="fff", choices=["fff", "post"],
+                    help="GELU per node (fff) or on the summed tree output (post)")
     ap.add_argument("--rotate", type=int, default=0, help="input sets (0 = by footprint)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="oracle sample budget")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -106,7 +108,7 @@ def calibrate_copy():
     print(json.dumps({"copy_bytes_each_way": n, "dispatches": 3}), flush=True)
 
 
-def cpu_baseline(inp, budget_s):
+def cpu_baseline(inp, budget_s, variant=0):
     import numpy as np
 
     import oracle
@@ -117,7 +119,8 @@ def cpu_baseline(inp, budget_s):
 
     def timed(n):
         t0 = time.perf_counter()
-        oracle.forward(f["x"][:n], f["W_node"], f["b_node"], f["V_node"], f["W_out"], nthreads=threads)
+        oracle.forward(f["x"][:n], f["W_node"], f["b_node"], f["V_node"], f["W_out"], nthreads=threads,
+                       variant=variant)
         return time.perf_counter() - t0
 
     pilot = min(T, max(threads, 16))
@@ -177,7 +180,8 @@ def main():
                              for s in range(1, rotate)]
     torch.cuda.synchronize()
 
-    fshape = fff.shape_of(sets[0][0], sets[0][1], sets[0][3])
+    variant = fff.VARIANTS[args.variant]
+    fshape = fff.shape_of(sets[0][0], sets[0][1], sets[0][3], variant)
     plan = fff.resolve_plan(fshape, fff.make_plan(args.algo, args.split_level, args.chunk_tokens))
     ws, nbytes = fff.alloc_workspace(fshape, plan, dev)
     y = torch.empty((shape.T, shape.d), dtype=sets[0][0].dtype, device=dev)
@@ -188,7 +192,7 @@ def main():
         x, W, b, V, Wo = sets[i % rotate]
         fff.forward(x, W, b, V, Wo, algo=plan.algo, split_level=plan.split_level,
                     chunk_tokens=plan.chunk_tokens, workspace=ws, y=y, path_out=path, stream=stream,
-                    events=ev)
+                    events=ev, variant=variant)
 
     for i in range(args.warmup):
         step(i)
@@ -265,7 +269,8 @@ def main():
         "dtype": "bf16" if shape.dtype == "bf16" else "f32",
         "data": "synthetic (seeded Gaussian inputs and random-init weights of the named shape)",
         "config": {"workload": args.workload, "T": shape.T, "d": shape.d, "P": shape.P,
-                   "D": shape.D, "h": shape.h, "algo": fff.algo_name(plan.algo),
+                   "D": shape.D, "h": shape.h, "variant": args.variant,
+                   "algo": fff.algo_name(plan.algo),
                    "split_level": plan.split_level, "chunk_tokens": plan.chunk_tokens,
                    "rotated_sets": rotate,
                    "parallelism": "none (1 GPU)"},
@@ -280,7 +285,7 @@ def main():
         "host": platform.node(),
     }
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(inp0, args.cpu_seconds)
+        out["cpu_baseline"] = cpu_baseline(inp0, args.cpu_seconds, variant)
     print(json.dumps(out), flush=True)
 
 

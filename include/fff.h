@@ -23,6 +23,12 @@
  *     H[t, p*h : (p+1)*h] = acc
  *     y[t,:] = H[t,:] . W_out                  (no bias)
  *
+ * Section 3.C of the explainer also describes FFF-post, in which the node
+ * outputs are summed before the nonlinearity (the paper's page, Figure 3 and
+ * Table 6, lists it beside FFF).  With shape->variant = FFF_VARIANT_POST the
+ * loop above accumulates a * V_node[p,n,:] instead, and H[t, p*h + j] =
+ * GELU(acc[j]) for each of the h elements; routing is unchanged.
+ *
  * Readings fixed here where the pages are silent: GELU is the tanh form
  * 0.5 a (1 + tanh(sqrt(2/pi) (a + 0.044715 a^3))); a logit of exactly 0 (or
  * -0, or NaN) goes right; nodes are numbered in heap order; tree p owns
@@ -75,15 +81,25 @@ typedef enum fff_status {
     FFF_ERROR_HIP = 4            /* a HIP launch or runtime call failed */
 } fff_status_t;
 
+/* Where the GELU sits: on each visited node's logit before the node outputs
+ * are summed (FFF), or on each element of the summed h-vector (FFF-post). */
+typedef enum fff_variant {
+    FFF_VARIANT_FFF = 0,
+    FFF_VARIANT_POST = 1
+} fff_variant_t;
+
 /* Layer shape.  N = 2^(D+1) - 1 is implied.  Limits: T >= 0, d, P, h >= 1,
- * 0 <= D <= FFF_MAX_DEPTH, T < 2^31, and every tensor below 2^40 elements. */
+ * 0 <= D <= FFF_MAX_DEPTH, T < 2^31, and every tensor below 2^40 elements.
+ * A variant other than those of fff_variant_t is FFF_ERROR_INVALID_VALUE;
+ * every algorithm takes both variants. */
 typedef struct fff_shape {
-    int64_t T;     /* tokens */
-    int32_t d;     /* model width */
-    int32_t P;     /* parallel trees */
-    int32_t D;     /* depth: D+1 nodes visited per path */
-    int32_t h;     /* output width of one node */
-    int32_t dtype; /* fff_dtype_t */
+    int64_t T;       /* tokens */
+    int32_t d;       /* model width */
+    int32_t P;       /* parallel trees */
+    int32_t D;       /* depth: D+1 nodes visited per path */
+    int32_t h;       /* output width of one node */
+    int32_t dtype;   /* fff_dtype_t */
+    int32_t variant; /* fff_variant_t */
 } fff_shape_t;
 
 /* Algorithms.  AUTO picks by shape; the others force one (for tests and

@@ -30,12 +30,17 @@ ALGO_GENERIC = 1
 ALGO_PREFILL = 2
 ALGO_DECODE = 3
 ALGOS = {"auto": ALGO_AUTO, "generic": ALGO_GENERIC, "prefill": ALGO_PREFILL, "decode": ALGO_DECODE}
+# fff_variant_t
+VARIANT_FFF = 0
+VARIANT_POST = 1
+VARIANTS = {"fff": VARIANT_FFF, "post": VARIANT_POST}
 MAX_DEPTH = 20
 
 
 class Shape(ctypes.Structure):
     _fields_ = [("T", ctypes.c_int64), ("d", ctypes.c_int32), ("P", ctypes.c_int32),
-                ("D", ctypes.c_int32), ("h", ctypes.c_int32), ("dtype", ctypes.c_int32)]
+                ("D", ctypes.c_int32), ("h", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("variant", ctypes.c_int32)]
 
 
 class Plan(ctypes.Structure):
@@ -98,8 +103,12 @@ def algo_name(algo: int) -> str:
     return load_library().fff_algo_name(int(algo)).decode()
 
 
-def make_shape(T: int, d: int, P: int, D: int, h: int, dtype: int) -> Shape:
-    return Shape(int(T), int(d), int(P), int(D), int(h), int(dtype))
+def _variant_code(variant) -> int:
+    return VARIANTS[variant] if isinstance(variant, str) else int(variant)
+
+
+def make_shape(T: int, d: int, P: int, D: int, h: int, dtype: int, variant=VARIANT_FFF) -> Shape:
+    return Shape(int(T), int(d), int(P), int(D), int(h), int(dtype), _variant_code(variant))
 
 
 def make_plan(algo=ALGO_AUTO, split_level: int = -1, chunk_tokens: int = 0) -> Plan:
@@ -151,14 +160,14 @@ def _dtype_code(t) -> int:
     raise TypeError(f"unsupported dtype {t.dtype}")
 
 
-def shape_of(x, W_node, V_node) -> Shape:
+def shape_of(x, W_node, V_node, variant=VARIANT_FFF) -> Shape:
     T, d = x.shape
     P, N, d2 = W_node.shape
     h = V_node.shape[2]
     D = N.bit_length() - 1
     if d2 != d or (1 << (D + 1)) - 1 != N:
         raise ValueError("W_node must be [P, 2^(D+1)-1, d]")
-    return make_shape(T, d, P, D, h, _dtype_code(x))
+    return make_shape(T, d, P, D, h, _dtype_code(x), variant)
 
 
 def _check(tensors, dtype, device):
@@ -182,10 +191,14 @@ def alloc_workspace(shape: Shape, plan: Optional[Plan], device):
 
 def forward(x, W_node, b_node, V_node, W_out, *, algo=ALGO_AUTO, split_level: int = -1,
             chunk_tokens: int = 0, want_path: bool = True, workspace=None, y=None, path_out=None,
-            stream=None, events: Optional[StageEvents] = None) -> Tuple[object, Optional[object]]:
-    """y = FFF(x); returns (y, path_out[T,P] int32 or None)."""
+            stream=None, events: Optional[StageEvents] = None,
+            variant=VARIANT_FFF) -> Tuple[object, Optional[object]]:
+    """y = FFF(x); returns (y, path_out[T,P] int32 or None).
+
+    ``variant`` "fff" (0) applies GELU to each visited node's logit; "post"
+    (1) applies it to each element of a tree's summed output instead."""
     torch = _torch()
-    shape = shape_of(x, W_node, V_node)
+    shape = shape_of(x, W_node, V_node, variant)
     _check([x, W_node, b_node, V_node, W_out], x.dtype, x.device)
     plan = make_plan(algo, split_level, chunk_tokens)
     if workspace is None:
@@ -208,10 +221,10 @@ def forward(x, W_node, b_node, V_node, W_out, *, algo=ALGO_AUTO, split_level: in
 
 
 def route(x, W_node, b_node, V_node, *, algo=ALGO_AUTO, split_level: int = -1,
-          chunk_tokens: int = 0, stream=None):
+          chunk_tokens: int = 0, stream=None, variant=VARIANT_FFF):
     """Routing only: returns (H[T, P*h], path_out[T,P])."""
     torch = _torch()
-    shape = shape_of(x, W_node, V_node)
+    shape = shape_of(x, W_node, V_node, variant)
     _check([x, W_node, b_node, V_node], x.dtype, x.device)
     plan = make_plan(algo, split_level, chunk_tokens)
     workspace, nbytes = alloc_workspace(shape, plan, x.device)

@@ -22,7 +22,8 @@ fff_status_t check_shape(const fff_shape_t* s, Dims* out) {
   if (!s) return FFF_ERROR_INVALID_VALUE;
   if (s->dtype != FFF_DTYPE_F32 && s->dtype != FFF_DTYPE_BF16) return FFF_ERROR_NOT_SUPPORTED;
   if (s->T < 0 || s->T > INT32_MAX || s->d <= 0 || s->P <= 0 || s->h <= 0 || s->D < 0 ||
-      s->D > FFF_MAX_DEPTH || s->d > (1 << 22))
+      s->D > FFF_MAX_DEPTH || s->d > (1 << 22) ||
+      (s->variant != FFF_VARIANT_FFF && s->variant != FFF_VARIANT_POST))
     return FFF_ERROR_INVALID_VALUE;
   Dims d;
   d.T = s->T;
@@ -31,6 +32,7 @@ fff_status_t check_shape(const fff_shape_t* s, Dims* out) {
   d.D = s->D;
   d.h = s->h;
   d.dtype = s->dtype;
+  d.variant = s->variant;
   d.N = (int64_t(1) << (s->D + 1)) - 1;
   d.K = int64_t(s->P) * s->h;
   d.esize = s->dtype == FFF_DTYPE_F32 ? 4 : 2;

@@ -86,6 +86,7 @@ struct DecodeArgs {
   int T, d, P, D, h, K;
   int64_t N;
   int n_route_wg, n_proj_wg;
+  int post;  // 1: GELU on the summed h-vector instead of on each node's logit
 };
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
@@ -156,11 +157,13 @@ struct RouteLds {
 };
 constexpr size_t kDecLds = ProjLds::total > RouteLds::total ? ProjLds::total : RouteLds::total;
 
-// Adds one round's GELU(a) * v_n terms to the thread's H pieces (token m,
-// eight columns c0..c0+7; piece i is thread + 256 i).  rsm holds the rows
-// token m visited this round, lgs the round's logits [row][token].
+// Adds one round's GELU(a) * v_n terms (a * v_n when `post`) to the thread's
+// H pieces (token m, eight columns c0..c0+7; piece i is thread + 256 i).  rsm
+// holds the rows token m visited this round, lgs the round's logits
+// [row][token].
 __device__ __forceinline__ void add_h_terms(const unsigned char* lds, const uint16_t* vcb, int rl,
-                                            int nt, int h, float (&hacc)[kHPieces][8]) {
+                                            int nt, int h, int post,
+                                            float (&hacc)[kHPieces][8]) {
   const float* lgs = reinterpret_cast<const float*>(lds + RouteLds::lgs);
   const int32_t* rsm = reinterpret_cast<const int32_t*>(lds + RouteLds::rsm);
   const int hc = h / 8;
@@ -172,7 +175,8 @@ __device__ __forceinline__ void add_h_terms(const unsigned char* lds, const uint
       const int c0 = (e - m * hc) * 8;
       for (int lv = 0; lv < rl; ++lv) {
         const int row = rsm[m * 4 + lv];
-        const float g = gelu_tanh(lgs[row * 16 + m]);
+        const float lg = lgs[row * 16 + m];
+        const float g = post ? lg : gelu_tanh(lg);
         const uint4 v = *reinterpret_cast<const uint4*>(vcb + row * h + c0);
         hacc[i][0] += g * bf16lo(v.x);
         hacc[i][1] += g * bf16hi(v.x);
@@ -266,7 +270,7 @@ __device__ void route_item(const DecodeArgs& a, unsigned char* lds, int item, in
       braw[r] = buffer_load2(bbuf, 4 * q + r < R ? uint32_t(lev == 0 ? row : rows[row]) * 2 : kOob);
     }
     // The previous round's H terms, while these loads are in flight.
-    if (prev_rl) add_h_terms(lds, vc + (buf ^ 1) * vc_stride, prev_rl, nt, a.h, hacc);
+    if (prev_rl) add_h_terms(lds, vc + (buf ^ 1) * vc_stride, prev_rl, nt, a.h, a.post, hacc);
 
     // k steps past the width have zero operands.
     f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -350,7 +354,7 @@ __device__ void route_item(const DecodeArgs& a, unsigned char* lds, int item, in
     R = meta[0];
     rl = meta[1];
   }
-  add_h_terms(lds, vc + (buf ^ 1) * vc_stride, prev_rl, nt, a.h, hacc);
+  add_h_terms(lds, vc + (buf ^ 1) * vc_stride, prev_rl, nt, a.h, a.post, hacc);
 
   const __amdgpu_buffer_rsrc_t hbuf = buffer_of(a.H, uint32_t(a.T) * a.K * 2);
 #pragma unroll
@@ -359,6 +363,10 @@ __device__ void route_item(const DecodeArgs& a, unsigned char* lds, int item, in
     const int m = e / hc;
     if (m < nt) {
       const int c0 = (e - m * hc) * 8;
+      if (a.post) {
+#pragma unroll
+        for (int u = 0; u < 8; ++u) hacc[i][u] = gelu_tanh(hacc[i][u]);
+      }
       coherent_store16(hbuf, uint32_t((t0 + m) * a.K + p * a.h + c0) * 2,
                        make_uint4(pack_bf16x2(hacc[i][0], hacc[i][1]),
                                   pack_bf16x2(hacc[i][2], hacc[i][3]),
@@ -580,6 +588,7 @@ hipError_t launch_decode(const Dims& s, const void* x, const void* W, const void
   a.P = s.P;
   a.D = s.D;
   a.h = s.h;
+  a.post = s.variant;
   a.K = static_cast<int>(s.K);
   a.N = s.N;
 

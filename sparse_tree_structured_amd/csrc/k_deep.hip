@@ -137,7 +137,7 @@ __global__ __launch_bounds__(WAVES * 64, 2) void deep_kernel(
     const uint16_t* __restrict__ V, const float* __restrict__ rec_logit,
     const int32_t* __restrict__ perm, const int32_t* __restrict__ offs, uint16_t* __restrict__ H,
     int32_t* __restrict__ path_out, int T, int d, int P, int D, int h, int64_t N, int k,
-    int chunk, int nchunks) {
+    int chunk, int nchunks, int post) {
   extern __shared__ __align__(16) unsigned char lds[];
   const int S = 1 << k;
   const int ipc = P * S;  // items per chunk
@@ -240,7 +240,7 @@ __global__ __launch_bounds__(WAVES * 64, 2) void deep_kernel(
       const float v3 = __shfl(acc[3], src);
       const int rr = j & 3;
       const float a = (rr == 0 ? v0 : rr == 1 ? v1 : rr == 2 ? v2 : v3) + bsub[j];
-      gv[lv] = gelu_tanh(a);
+      gv[lv] = post ? a : gelu_tanh(a);
       jv[lv] = j;
       if (lv + 1 < sub_levels) j = 2 * j + 1 + go_right(a);
     }
@@ -248,7 +248,7 @@ __global__ __launch_bounds__(WAVES * 64, 2) void deep_kernel(
     // H slice of this lane: columns [q*hq, (q+1)*hq) of tree p.
     const float* tl = rec_logit + (static_cast<int64_t>(p) * T + tok) * k;
     float gt[8];
-    for (int l = 0; l < k; ++l) gt[l] = gelu_tanh(tl[l]);
+    for (int l = 0; l < k; ++l) gt[l] = post ? tl[l] : gelu_tanh(tl[l]);
     uint16_t* out = H + static_cast<int64_t>(tok) * P * h + static_cast<int64_t>(p) * h + q * hq;
     for (int c8 = 0; c8 < hq; c8 += 8) {
       float a8[8] = {};
@@ -267,6 +267,10 @@ __global__ __launch_bounds__(WAVES * 64, 2) void deep_kernel(
         a8[2] += gg * bf16lo(v.y); a8[3] += gg * bf16hi(v.y);
         a8[4] += gg * bf16lo(v.z); a8[5] += gg * bf16hi(v.z);
         a8[6] += gg * bf16lo(v.w); a8[7] += gg * bf16hi(v.w);
+      }
+      if (post) {
+#pragma unroll
+        for (int u = 0; u < 8; ++u) a8[u] = gelu_tanh(a8[u]);
       }
       const u32x4_t packed = {pack_bf16x2(a8[0], a8[1]), pack_bf16x2(a8[2], a8[3]),
                               pack_bf16x2(a8[4], a8[5]), pack_bf16x2(a8[6], a8[7])};
@@ -349,7 +353,7 @@ hipError_t launch_deep(const Dims& s, int k, const void* x, const void* W, const
       static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(W),
       static_cast<const uint16_t*>(b), static_cast<const uint16_t*>(V), rec_logit, perm, offs,
       static_cast<uint16_t*>(H), path_out, static_cast<int>(s.T), s.d, s.P, s.D, s.h, s.N, k,
-      chunk, nchunks);
+      chunk, nchunks, s.variant);
   return hipGetLastError();
 }
 

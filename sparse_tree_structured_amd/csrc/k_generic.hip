@@ -47,7 +47,7 @@ __global__ __launch_bounds__(256) void route_generic_kernel(
 template <typename E>
 __global__ __launch_bounds__(256) void hbuild_generic_kernel(
     const float* __restrict__ logits, const int32_t* __restrict__ leaf_ws, const E* __restrict__ V,
-    E* __restrict__ H, int64_t T, int P, int D, int h, int64_t N) {
+    E* __restrict__ H, int64_t T, int P, int D, int h, int64_t N, int post) {
   const int64_t K = static_cast<int64_t>(P) * h;
   const int64_t total = T * K;
   for (int64_t e = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; e < total;
@@ -62,10 +62,11 @@ __global__ __launch_bounds__(256) void hbuild_generic_kernel(
     float acc = 0.0f;
     int64_t n = 0;
     for (int level = 0; level <= D; ++level) {
-      acc += gelu_tanh(logits[pair * (D + 1) + level]) * Elem<E>::ld(Vp, n * h + j);
+      const float a = logits[pair * (D + 1) + level];
+      acc += (post ? a : gelu_tanh(a)) * Elem<E>::ld(Vp, n * h + j);
       if (level < D) n = 2 * n + 1 + ((leaf >> (D - 1 - level)) & 1);
     }
-    Elem<E>::st(H, e, acc);
+    Elem<E>::st(H, e, post ? gelu_tanh(acc) : acc);
   }
 }
 
@@ -140,11 +141,11 @@ hipError_t launch_hbuild_generic(const Dims& s, const float* logits, const int32
   if (s.dtype == 0)
     hbuild_generic_kernel<float><<<static_cast<unsigned>(blocks), 256, 0, st>>>(
         logits, leaf_ws, static_cast<const float*>(V), static_cast<float*>(H), s.T, s.P, s.D,
-        s.h, s.N);
+        s.h, s.N, s.variant);
   else
     hbuild_generic_kernel<uint16_t><<<static_cast<unsigned>(blocks), 256, 0, st>>>(
         logits, leaf_ws, static_cast<const uint16_t*>(V), static_cast<uint16_t*>(H), s.T, s.P,
-        s.D, s.h, s.N);
+        s.D, s.h, s.N, s.variant);
   return hipGetLastError();
 }
 

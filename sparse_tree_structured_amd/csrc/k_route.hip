@@ -236,7 +236,7 @@ __global__ __launch_bounds__(256) void hbuild_kernel(const float* __restrict__ r
                                                      const uint16_t* __restrict__ V,
                                                      uint16_t* __restrict__ H,
                                                      int32_t* __restrict__ path_out, int T, int P,
-                                                     int64_t N) {
+                                                     int64_t N, int post) {
   constexpr int L = LEVELS;
   constexpr int D = LEVELS - 1;
   constexpr int h = 16 << HSHIFT;     // node output width
@@ -261,7 +261,9 @@ __global__ __launch_bounds__(256) void hbuild_kernel(const float* __restrict__ r
     }
   }
   const float* rl = rec_logit + (static_cast<int64_t>(p) * T + t0) * L;
-  for (int i = threadIdx.x; i < ntok * L; i += blockDim.x) gl[i] = gelu_tanh(rl[i]);
+  // Per-node weights of the V rows: GELU(a) per node, or a itself when GELU is
+  // applied to the summed vector instead.
+  for (int i = threadIdx.x; i < ntok * L; i += blockDim.x) gl[i] = post ? rl[i] : gelu_tanh(rl[i]);
   for (int i = threadIdx.x; i < ntok; i += blockDim.x) {
     const int32_t n = rec_next[static_cast<int64_t>(p) * T + t0 + i];
     leaf[i] = n;
@@ -285,6 +287,10 @@ __global__ __launch_bounds__(256) void hbuild_kernel(const float* __restrict__ r
       const float gg = g[l];
 #pragma unroll
       for (int q = 0; q < 16; ++q) acc[q] += gg * v[q];
+    }
+    if (post) {
+#pragma unroll
+      for (int q = 0; q < 16; ++q) acc[q] = gelu_tanh(acc[q]);
     }
     uint4* dst = reinterpret_cast<uint4*>(Hp + static_cast<int64_t>(t0 + i) * P * h + j0);
     dst[0] = make_uint4(pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]),
@@ -371,7 +377,7 @@ hipError_t launch_hbuild_l(const Dims& s, const float* rec_logit, const int32_t*
   const dim3 grid(static_cast<unsigned>((s.T + kHbTok - 1) / kHbTok), static_cast<unsigned>(s.P));
   kern<<<grid, dim3(256), lds, st>>>(rec_logit, rec_next, static_cast<const uint16_t*>(V),
                                      static_cast<uint16_t*>(H), path_out, static_cast<int>(s.T),
-                                     s.P, s.N);
+                                     s.P, s.N, s.variant);
   return hipGetLastError();
 }
 

@@ -12,9 +12,10 @@ namespace fff {
 struct Dims {
   int64_t T;
   int d, P, D, h;
-  int dtype;  // fff_dtype_t
-  int64_t N;  // 2^(D+1) - 1
-  int64_t K;  // P * h
+  int dtype;    // fff_dtype_t
+  int variant;  // fff_variant_t: 0 = GELU per node, 1 = GELU after the sum
+  int64_t N;    // 2^(D+1) - 1
+  int64_t K;    // P * h
   size_t esize;
 };
 
@@ -24,7 +25,8 @@ struct Dims {
 hipError_t launch_route_generic(const Dims& s, const void* x, const void* W, const void* b,
                                 float* logits, int32_t* path_out, int32_t* leaf_ws,
                                 hipStream_t st);
-// H[t, p*h + j] = sum over levels of GELU(a_l) * V[p, n_l, j].
+// H[t, p*h + j] = sum over levels of GELU(a_l) * V[p, n_l, j]  (variant 0), or
+// GELU(sum over levels of a_l * V[p, n_l, j])  (variant 1).
 hipError_t launch_hbuild_generic(const Dims& s, const float* logits, const int32_t* leaf_ws,
                                  const void* V, void* H, hipStream_t st);
 // y = H . W_out with fp32 accumulation.
@@ -63,7 +65,7 @@ hipError_t launch_deep(const Dims& s, int k, const void* x, const void* W, const
                        const int32_t* offs, void* H, int32_t* path_out, int chunk,
                        hipStream_t st);
 
-// ---- decode (bf16, 1 <= T <= 64): one cooperative kernel for the layer ----
+// ---- decode (bf16, 1 <= T <= 64): one kernel for the whole layer ----
 // Workspace: H [T,K] bf16, fp32 K-chunk partials of y, per-slice counters.
 bool decode_supported(const Dims& s);
 size_t decode_workspace(const Dims& s);

@@ -67,6 +67,26 @@ def test_bad_shapes(lib, kw):
         fff.ERROR_INVALID_VALUE
 
 
+@pytest.mark.parametrize("variant", [-1, 2, 1 << 20])
+def test_bad_variant(lib, variant):
+    assert _forward(lib, _shape(variant=variant)) == fff.ERROR_INVALID_VALUE
+    n = ctypes.c_size_t()
+    assert lib.fff_workspace_size(ctypes.byref(_shape(variant=variant)), None,
+                                  ctypes.byref(n)) == fff.ERROR_INVALID_VALUE
+
+
+def test_variant_does_not_change_plans(lib):
+    # FFF-post moves the GELU only: every shape gets the same plan and workspace.
+    for kw in (dict(), dict(dtype=fff.DTYPE_F32), dict(T=8, d=2048, P=32, D=6, h=128),
+               dict(T=16384, d=2048, P=32, D=6, h=128), dict(T=500, d=256, P=4, D=10, h=64)):
+        a, b = _shape(**kw), _shape(variant=fff.VARIANT_POST, **kw)
+        pa, pb = fff.plan_default(a), fff.plan_default(b)
+        assert (pa.algo, pa.split_level, pa.chunk_tokens) == (pb.algo, pb.split_level,
+                                                              pb.chunk_tokens)
+        assert fff.workspace_size(a) == fff.workspace_size(b)
+    assert fff.make_shape(1, 1, 1, 0, 1, fff.DTYPE_F32, "post").variant == fff.VARIANT_POST
+
+
 def test_unknown_dtype(lib):
     assert _forward(lib, _shape(dtype=7)) == fff.ERROR_NOT_SUPPORTED
 
