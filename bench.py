@@ -43,6 +43,10 @@ def parse():
     ap.add_argument("--rotate", type=int, default=0, help="input sets (0 = by footprint)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="oracle sample budget")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--depth-sweep", action="store_true",
+                    help="time the layer at depths 0..11 (the headline's T, d, P, h) beside a "
+                         "dense FF block of width 4d; one JSON line per depth")
+    ap.add_argument("--sweep-depths", default="0-11")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run only a plain device copy of 256 MiB (3 times), the reference "
                          "for scaling the HBM byte counters")
@@ -142,10 +146,130 @@ def cpu_baseline(inp, budget_s, variant=0):
             "seconds": dt}
 
 
+def _events_ms(torch, fn, steps, warmup):
+    """Median milliseconds of fn(i) over `steps` calls, each bracketed by
+    events on the current stream, after at least `warmup` calls and 0.3 s of
+    warm-up work (the clocks ramp up after the idle input generation)."""
+    t0, i = time.perf_counter(), 0
+    while i < warmup or time.perf_counter() - t0 < 0.3:
+        fn(i)
+        i += 1
+        if i % 8 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+    for i, (a, b) in enumerate(evs):
+        a.record()
+        fn(i)
+        b.record()
+    torch.cuda.synchronize()
+    import numpy as np
+    return float(np.median([a.elapsed_time(b) for a, b in evs]))
+
+
+def depth_sweep(args):
+    """Speed against tree depth, the MI355X counterpart of the paper page's
+    Figure 5 and Table 5: the headline workload's T, d, P and h at depths
+    D = 0..11 (AUTO plan), beside a dense FF block (x W1^T + b1, tanh GELU,
+    then W2) of width 4d, which the pages do not state.  Depth 0 is itself a
+    dense layer of P units.  Inputs: x and W_out from the headline generator
+    (seed 0), W_node, b_node, V_node drawn per depth (seed 100 + depth); between
+    timed calls the sets rotate through copies with tokens and trees
+    permuted, so the 256 MB Infinity Cache cannot serve a repeated call."""
+    import numpy as np
+    import torch
+
+    import sparse_tree_structured_amd as fff
+    import workloads
+
+    dev = torch.device("cuda:0")
+    base, opts = workloads.WORKLOADS["opt1p3b_d6"]
+    T, d, P, h = base.T, base.d, base.P, base.h
+    lo, _, hi = args.sweep_depths.partition("-")
+    depths = range(int(lo), int(hi or lo) + 1)
+
+    def bf16(a):
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+
+    gen0 = workloads.make_inputs(dataclasses_replace(base, D=0), seed=0, **opts)
+    x0, wo0 = bf16(gen0.x), bf16(gen0.W_out)
+    g = torch.Generator(device="cpu")
+    g.manual_seed(1234)
+    steps, warmup = args.steps, args.warmup
+
+    # Dense comparator: d_ff = 4d, bf16 weights N(0, 1/fan_in), torch's
+    # matrix products (hipBLASLt) and tanh GELU.
+    dff = 4 * d
+    w1 = (torch.randn(dff, d, generator=g) / d ** 0.5).to(torch.bfloat16).to(dev)
+    b1 = (0.1 * torch.randn(dff, generator=g)).to(torch.bfloat16).to(dev)
+    w2 = (torch.randn(d, dff, generator=g) / dff ** 0.5).to(torch.bfloat16).to(dev)
+    xs = [x0] + [x0[torch.randperm(T, generator=g).to(dev)].contiguous() for _ in range(3)]
+
+    def dense(i):
+        hid = torch.nn.functional.gelu(torch.nn.functional.linear(xs[i % len(xs)], w1, b1),
+                                       approximate="tanh")
+        return torch.nn.functional.linear(hid, w2)
+
+    t_dense = _events_ms(torch, dense, steps, warmup)
+    dense_flops = 4 * T * d * dff
+    print(json.dumps({"sweep": "dense_ff", "d_ff": dff, "T": T, "d": d, "ms": t_dense,
+                      "tokens_per_s": T / (t_dense * 1e-3),
+                      "tflops": dense_flops / (t_dense * 1e-3) / 1e12,
+                      "impl": "torch linear (hipBLASLt) + tanh GELU, bf16"}), flush=True)
+    del xs
+
+    for D in depths:
+        shape = dataclasses_replace(base, D=D)
+        gen = workloads.make_inputs(dataclasses_replace(shape, T=1), seed=100 + D, **opts)
+        W, b, V = bf16(gen.W_node), bf16(gen.b_node), bf16(gen.V_node)
+        footprint = (T * d + P * shape.N * (d + h + 1) + P * h * d) * 2
+        rotate = int(min(8, max(2, -(-600_000_000 // footprint))))
+        sets = [(x0, W, b, V, wo0)]
+        for _ in range(rotate - 1):
+            tp = torch.randperm(P, generator=g).to(dev)
+            rows = (tp[:, None] * h + torch.arange(h, device=dev)[None, :]).reshape(-1)
+            sets.append((x0[torch.randperm(T, generator=g).to(dev)].contiguous(),
+                         W[tp].contiguous(), b[tp].contiguous(), V[tp].contiguous(),
+                         wo0[rows].contiguous()))
+        fshape = fff.shape_of(x0, W, V)
+        plan = fff.resolve_plan(fshape, fff.make_plan("auto"))
+        ws, _ = fff.alloc_workspace(fshape, plan, dev)
+        y = torch.empty((T, d), dtype=torch.bfloat16, device=dev)
+
+        def step(i):
+            xx, WW, bb, VV, oo = sets[i % rotate]
+            fff.forward(xx, WW, bb, VV, oo, workspace=ws, y=y, want_path=False)
+
+        t = _events_ms(torch, step, steps, warmup)
+        f_route, f_proj, _ = algorithmic_work(shape, 0)
+        # Levels evaluated as one dense product: 2^L columns per tree.
+        L = min(plan.split_level, D + 1)
+        dense_route = 2 * T * P * (1 << L) * d
+        print(json.dumps({
+            "sweep": "fff", "D": D, "T": T, "d": d, "P": P, "h": h, "ms": t,
+            "tokens_per_s": T / (t * 1e-3), "algo": fff.algo_name(plan.algo),
+            "split_level": plan.split_level, "rotated_sets": rotate,
+            "alg_gflop": (f_route + f_proj) / 1e9,
+            "dense_levels": L, "dense_route_gflop": dense_route / 1e9,
+            "speedup_vs_dense": t_dense / t,
+            "alg_flops_vs_dense": (f_route + f_proj) / dense_flops}), flush=True)
+        del sets, ws, W, b, V
+        torch.cuda.empty_cache()
+
+
+def dataclasses_replace(obj, **kw):
+    import dataclasses
+    return dataclasses.replace(obj, **kw)
+
+
 def main():
     args = parse()
     if args.calibrate_copy:
         calibrate_copy()
+        return
+    if args.depth_sweep:
+        depth_sweep(args)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "

@@ -93,7 +93,8 @@ fff_status_t resolve_plan(const Dims& s, const fff_plan_t* in, fff_plan_t* out,
       if (!split_ok(s, p.split_level)) return FFF_ERROR_NOT_SUPPORTED;
       if (p.chunk_tokens < 0) return FFF_ERROR_INVALID_VALUE;
       if (p.split_level <= s.D) {
-        if (p.chunk_tokens == 0) p.chunk_tokens = static_cast<int32_t>(fff::deep_chunk(s));
+        if (p.chunk_tokens == 0)
+          p.chunk_tokens = static_cast<int32_t>(fff::deep_chunk(s, p.split_level));
         if (p.chunk_tokens > s.T) p.chunk_tokens = static_cast<int32_t>(s.T > 0 ? s.T : 1);
       } else {
         p.chunk_tokens = 0;

@@ -316,9 +316,17 @@ bool deep_supported(const Dims& s, int k) {
          s.h % 32 == 0 && deep_lds(s.d, s.h, k).total <= 80 * 1024;
 }
 
-size_t deep_chunk(const Dims& s) {
-  // Tokens per chunk: about 4 MB of x rows (one XCD's L2), at least 64.
-  int64_t c = (4 << 20) / (int64_t(s.d) * 2);
+size_t deep_chunk(const Dims& s, int k) {
+  // Tokens per chunk: about 8 MB of x rows, and at least 16 tokens per
+  // level-k bucket on average so that the staged subtree rows serve a full
+  // 16-token tile.  Each chunk restages every subtree's rows, so small chunks
+  // cost W_node traffic; large ones lose the x rows' cache reuse across trees.
+  // Measured at d = 2048, P = 32, h = 128, T = 16384 (ms, chunk of 1024 /
+  // 2048 / 4096 tokens): D = 9: 1.80 / 1.25 / 1.69; D = 10: - / 2.05 / 2.26;
+  // D = 11: - / - / 3.93 (16384: 6.40).
+  int64_t c = (8 << 20) / (int64_t(s.d) * 2);
+  const int64_t per_bucket = int64_t(16) << k;
+  c = c < per_bucket ? per_bucket : c;
   c = c < 64 ? 64 : c;
   return static_cast<size_t>(c < s.T ? c : s.T);
 }

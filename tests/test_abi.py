@@ -142,6 +142,19 @@ def test_plans(lib):
     assert _forward(lib, _shape(), plan=fff.make_plan(9)) == fff.ERROR_INVALID_VALUE
 
 
+def test_deep_chunk_rule():
+    # Bucketed deep levels: about 8 MB of x rows per chunk, at least 16 tokens
+    # per level-k bucket on average, at most T.
+    wide = dict(T=16384, d=2048, P=32, h=128)
+    for D, k, chunk in ((8, 5, 2048), (9, 6, 2048), (10, 7, 2048), (11, 8, 4096)):
+        r = fff.resolve_plan(_shape(D=D, **wide), fff.make_plan("prefill"))
+        assert (r.split_level, r.chunk_tokens) == (k, chunk), (D, r.split_level, r.chunk_tokens)
+    r = fff.resolve_plan(_shape(T=300, d=512, P=8, D=11, h=128), fff.make_plan("prefill"))
+    assert (r.split_level, r.chunk_tokens) == (8, 300)
+    r = fff.resolve_plan(_shape(T=100000, d=512, P=8, D=9, h=128), fff.make_plan("prefill"))
+    assert r.chunk_tokens == 8192  # 8 MB of 1 KB rows
+
+
 def test_project_validation(lib):
     s = _shape()
     assert lib.fff_project(ctypes.byref(s), 7, FAKE, FAKE, FAKE, None) == fff.ERROR_INVALID_VALUE

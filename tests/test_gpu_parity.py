@@ -268,3 +268,22 @@ def test_decode_workspace_reuse():
     np.testing.assert_array_equal(outs[0][0], outs[2][0])
     np.testing.assert_array_equal(outs[0][1][:7], outs[1][1])
     check(big, outs[0][0], outs[0][1])
+
+
+# Depth sweep (D = 0..11, the measurement beside a dense FF block): every
+# depth on the path AUTO takes at the sweep's widths, at a ragged token count.
+@needs_gpu
+@pytest.mark.parametrize("D", list(range(12)))
+def test_depth_sweep_depths(D):
+    inp = workloads.random_inputs(300, 512, 8, D, 128, "bf16", seed=40 + D, unit_rms_x=True)
+    y, path = run(inp)
+    check(inp, y, path)
+
+
+@needs_gpu
+@pytest.mark.parametrize("D", [0, 8, 9])
+def test_depth_sweep_full_width(D):
+    # The sweep's own d, P and h (those of the OPT-1.3B-shaped workload).
+    inp = workloads.random_inputs(200, 2048, 32, D, 128, "bf16", seed=60 + D, unit_rms_x=True)
+    y, path = run(inp)
+    check(inp, y, path)
