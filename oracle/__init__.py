@@ -62,10 +62,11 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     lib = ctypes.CDLL(path)
     dp = ctypes.POINTER(ctypes.c_double)
     ip = ctypes.POINTER(ctypes.c_int32)
+    up = ctypes.POINTER(ctypes.c_uint8)
     lib.fffo_forward.restype = ctypes.c_int
     lib.fffo_forward.argtypes = [ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_int,
-                                 ctypes.c_int, ctypes.c_int, dp, dp, dp, dp, dp, ip, dp, dp, ip, dp, dp,
-                                 ip, ctypes.c_int]
+                                 ctypes.c_int, ctypes.c_int, dp, dp, dp, dp, dp, ip, up, dp, dp, ip,
+                                 dp, dp, ip, ctypes.c_int]
     _LIBS[path] = lib
     return lib
 
@@ -94,6 +95,7 @@ def _iptr(a: Optional[np.ndarray]):
 def forward(x: np.ndarray, W_node: np.ndarray, b_node: np.ndarray, V_node: np.ndarray,
             W_out: np.ndarray, forced: Optional[np.ndarray] = None, want_y: bool = True,
             want_H: bool = False, want_records: bool = False, variant: int = 0,
+            leaf_alive: Optional[np.ndarray] = None,
             nthreads: Optional[int] = None, lib: Optional[ctypes.CDLL] = None) -> Dict[str, np.ndarray]:
     """Run the oracle.
 
@@ -102,6 +104,8 @@ def forward(x: np.ndarray, W_node: np.ndarray, b_node: np.ndarray, V_node: np.nd
     ``forced`` [T,P] int32 leaf indices walks those paths instead of routing.
     ``variant`` 0 is FFF (GELU on each node's logit before the sum), 1 is
     FFF-post (GELU applied once to each tree's summed h-vector).
+    ``leaf_alive`` [P, 2^D] (nonzero = alive) prunes paths statically: a
+    routed step into a subtree with no alive leaf goes to the sibling.
 
     Returns a dict with ``path`` [T,P] int32, and as requested ``y`` [T,d],
     ``H`` [T,P*h], and the per-visit records ``rec_a``, ``rec_thr`` (float64)
@@ -134,12 +138,18 @@ def forward(x: np.ndarray, W_node: np.ndarray, b_node: np.ndarray, V_node: np.nd
         forced = np.ascontiguousarray(forced, dtype=np.int32)
         if forced.shape != (T, P):
             raise ValueError("forced must be [T,P]")
+    alive_ptr = None
+    if leaf_alive is not None:
+        leaf_alive = np.ascontiguousarray(leaf_alive, dtype=np.uint8)
+        if leaf_alive.shape != (P, 1 << D):
+            raise ValueError("leaf_alive must be [P, 2^D]")
+        alive_ptr = leaf_alive.ctypes.data_as(ctypes.POINTER(ctypes.c_uint8))
     rc = lib.fffo_forward(T, d, P, D, h, int(variant), _dptr(x), _dptr(W_node), _dptr(b_node),
-                          _dptr(V_node), _dptr(W_out), _iptr(forced), _dptr(out.get("y")), _dptr(out.get("H")),
+                          _dptr(V_node), _dptr(W_out), _iptr(forced), alive_ptr, _dptr(out.get("y")), _dptr(out.get("H")),
                           _iptr(out["path"]), _dptr(out.get("rec_a")), _dptr(out.get("rec_thr")),
                           _iptr(out.get("rec_node")), int(nthreads or default_threads()))
     if rc != 0:
-        raise ValueError("oracle rejected the shape")
+        raise ValueError("oracle rejected the shape, variant or mask")
     return out
 
 

@@ -37,6 +37,14 @@
  * leaf index n - (2^D - 1), whose bit (D-1-l) is the level-l decision
  * (1 = right).
  *
+ * Static path pruning (thelatestinai.com page, Figure 4: paths removed
+ * permanently at fixed ratios; explainer page, section 3.B: paths that
+ * training leaves inactive): an optional mask marks each leaf of each tree
+ * alive or pruned.  A node is alive when some leaf below it is alive.  The
+ * pages do not say where a token goes when its logit points into a pruned
+ * subtree; here it takes the other child, which is alive whenever its parent
+ * is.  Every tree must keep at least one alive leaf.
+ *
  * Near-tie threshold: for each visited node the oracle also records
  * thr = 1e-4 * ||x_t||_2 * ||w_n||_2; a device path that takes the other
  * branch at a node whose |a| <= thr is excused (and counted) by the tests.
@@ -65,15 +73,30 @@ static double dot(const double *u, const double *v, int n)
 }
 
 /*
+ * alive[0..N) of one tree from its leaf mask (leaf i is heap node 2^D-1+i):
+ * leaves as given, every internal node alive iff one of its children is.
+ */
+static void alive_nodes(const uint8_t *leaf_alive, int D, uint8_t *alive)
+{
+    const int64_t first_leaf = ((int64_t)1 << D) - 1;
+    for (int64_t i = 0; i <= first_leaf; ++i)
+        alive[first_leaf + i] = leaf_alive[i] != 0;
+    for (int64_t n = first_leaf - 1; n >= 0; --n)
+        alive[n] = alive[2 * n + 1] | alive[2 * n + 2];
+}
+
+/*
  * One token through one tree.  Walks root to leaf, adding GELU(a) * v_n
  * (variant 0) or a * v_n (variant 1) for every visited node into acc[0..h);
  * variant 1 then replaces each acc[j] by GELU(acc[j]).  If forced_leaf >= 0
  * the branch at each level is taken from that leaf's bits instead of the
- * logit's sign.  Returns the leaf index.
+ * logit's sign.  With `alive` (this tree's node mask, or NULL for an
+ * unpruned tree) a routed step into a pruned child goes to its sibling.
+ * Returns the leaf index.
  */
 static int32_t walk_tree(const double *xt, double xnorm, const double *Wp, const double *bp,
                          const double *Vp, int d, int D, int h, int variant, int32_t forced_leaf,
-                         double *acc, double *rec_a, double *rec_thr, int32_t *rec_node)
+                         const uint8_t *alive, double *acc, double *rec_a, double *rec_thr, int32_t *rec_node)
 {
     int64_t n = 0; /* heap index of the current node */
     for (int j = 0; j < h; ++j)
@@ -95,8 +118,11 @@ static int32_t walk_tree(const double *xt, double xnorm, const double *Wp, const
             int go_right;
             if (forced_leaf >= 0)
                 go_right = (forced_leaf >> (D - 1 - level)) & 1;
-            else
+            else {
                 go_right = !(a < 0.0);
+                if (alive && !alive[2 * n + 1 + go_right])
+                    go_right = !go_right;
+            }
             n = 2 * n + 1 + go_right;
         }
     }
@@ -111,6 +137,8 @@ static int32_t walk_tree(const double *xt, double xnorm, const double *Wp, const
  *
  *   x [T,d], W [P,N,d], b [P,N], V [P,N,h], Wout [P*h,d]   (N = 2^(D+1)-1)
  *   forced  [T,P] leaf indices, or NULL to route by sign
+ *   leaf_alive  [P, 2^D] nonzero = alive, or NULL for unpruned trees; a tree
+ *               with no alive leaf is a bad argument
  *   y       [T,d] out, or NULL to skip the projection
  *   H       [T,P*h] out (the concatenated tree outputs), or NULL
  *   path    [T,P] out (leaf indices), or NULL
@@ -122,7 +150,7 @@ static int32_t walk_tree(const double *xt, double xnorm, const double *Wp, const
  */
 int fffo_forward(int64_t T, int d, int P, int D, int h, int variant,
                  const double *x, const double *W, const double *b, const double *V,
-                 const double *Wout, const int32_t *forced,
+                 const double *Wout, const int32_t *forced, const uint8_t *leaf_alive,
                  double *y, double *H, int32_t *path,
                  double *rec_a, double *rec_thr, int32_t *rec_node, int nthreads)
 {
@@ -133,6 +161,19 @@ int fffo_forward(int64_t T, int d, int P, int D, int h, int variant,
     const int L = D + 1;
     if (nthreads <= 0)
         nthreads = 1;
+    uint8_t *alive = NULL;
+    if (leaf_alive) {
+        alive = (uint8_t *)malloc((size_t)(P * N));
+        if (!alive)
+            abort();
+        for (int p = 0; p < P; ++p) {
+            alive_nodes(leaf_alive + ((int64_t)p << D), D, alive + p * N);
+            if (!alive[p * N]) {
+                free(alive);
+                return FFFO_BAD_ARG;
+            }
+        }
+    }
 
 #pragma omp parallel for schedule(dynamic, 1) num_threads(nthreads)
     for (int64_t t = 0; t < T; ++t) {
@@ -145,7 +186,8 @@ int fffo_forward(int64_t T, int d, int P, int D, int h, int variant,
             int64_t tp = t * P + p;
             int32_t fl = forced ? forced[tp] : -1;
             int32_t leaf = walk_tree(xt, xnorm, W + (int64_t)p * N * d, b + (int64_t)p * N,
-                                     V + (int64_t)p * N * h, d, D, h, variant, fl, Ht + (int64_t)p * h,
+                                     V + (int64_t)p * N * h, d, D, h, variant, fl,
+                                     alive ? alive + p * N : NULL, Ht + (int64_t)p * h,
                                      rec_a ? rec_a + tp * L : NULL,
                                      rec_thr ? rec_thr + tp * L : NULL,
                                      rec_node ? rec_node + tp * L : NULL);
@@ -170,5 +212,6 @@ int fffo_forward(int64_t T, int d, int P, int D, int h, int variant,
         }
         free(Ht);
     }
+    free(alive);
     return FFFO_OK;
 }

@@ -410,7 +410,95 @@ def pin_post_routing_unchanged(lib):
     assert not np.allclose(a["y"], b["y"])
 
 
+def subtree_alive(leaf_alive_p: np.ndarray, D: int, n: int) -> bool:
+    """Whether any leaf below heap node n is alive (leaf range by level)."""
+    level = int(np.floor(np.log2(n + 1)))
+    span = 1 << (D - level)
+    first = (n - ((1 << level) - 1)) * span
+    return bool(leaf_alive_p[first:first + span].any())
+
+
+def brute_force_pruned(L, leaf_alive):
+    """Enumerate the alive leaves; keep the one whose every step either
+    follows its logit's sign or is forced because the preferred child's
+    subtree has no alive leaf."""
+    x, W, b, V, Wo = L["x"], L["W_node"], L["b_node"], L["V_node"], L["W_out"]
+    T = x.shape[0]
+    P, N, _ = W.shape
+    h = V.shape[2]
+    D = int(np.log2(N + 1)) - 1
+    A = np.einsum("td,pnd->tpn", x, W) + b[None, :, :]
+    G = gelu_ref(A)
+    path = np.zeros((T, P), dtype=np.int32)
+    H = np.zeros((T, P * h))
+    for t in range(T):
+        for p in range(P):
+            ok = []
+            for leaf in np.flatnonzero(leaf_alive[p]):
+                nodes = ancestors_of_leaf(int(leaf), D)
+                good = True
+                for lvl in range(D):
+                    n = nodes[lvl]
+                    pref = 2 * n + 1 if A[t, p, n] < 0 else 2 * n + 2
+                    if nodes[lvl + 1] != pref and subtree_alive(leaf_alive[p], D, pref):
+                        good = False
+                        break
+                if good:
+                    ok.append(int(leaf))
+            assert len(ok) == 1, "exactly one alive leaf is consistent"
+            mask = np.zeros(N)
+            mask[ancestors_of_leaf(ok[0], D)] = 1.0
+            path[t, p] = ok[0]
+            H[t, p * h:(p + 1) * h] = (mask * G[t, p]) @ V[p]
+    return path, H, H @ Wo
+
+
+def pin_prune_brute_force(lib):
+    rng = np.random.default_rng(77)
+    for i, (T, d, P, D, h) in enumerate([(9, 5, 3, 3, 4), (6, 8, 2, 5, 3), (7, 4, 2, 1, 2),
+                                         (5, 6, 4, 4, 3)]):
+        L = rand_layer(rng, T, d, P, D, h)
+        for frac in (0.3, 0.7):
+            alive = (rng.random((P, 1 << D)) > frac).astype(np.uint8)
+            alive[np.arange(P), rng.integers(0, 1 << D, size=P)] = 1  # every tree keeps a leaf
+            r = oracle.forward(**L, leaf_alive=alive, want_H=True, lib=lib, nthreads=2)
+            path, H, y = brute_force_pruned(L, alive)
+            np.testing.assert_array_equal(r["path"], path)
+            assert alive[np.arange(P)[None, :], r["path"]].all()
+            _close(r["H"], H)
+            _close(r["y"], y)
+
+
+def pin_prune_reductions(lib):
+    """All leaves alive: the unpruned result bit for bit.  One alive leaf per
+    tree: every token takes it, exactly as the forced-path mode computes.
+    Pruning only leaves that no token reaches: nothing changes."""
+    rng = np.random.default_rng(78)
+    T, d, P, D, h = 40, 6, 3, 4, 5
+    L = rand_layer(rng, T, d, P, D, h)
+    base = oracle.forward(**L, want_H=True, lib=lib, nthreads=2)
+    full = oracle.forward(**L, want_H=True, leaf_alive=np.ones((P, 1 << D), np.uint8), lib=lib,
+                          nthreads=2)
+    for k in ("path", "H", "y"):
+        np.testing.assert_array_equal(full[k], base[k])
+    only = rng.integers(0, 1 << D, size=P)
+    alive = np.zeros((P, 1 << D), np.uint8)
+    alive[np.arange(P), only] = 1
+    one = oracle.forward(**L, want_H=True, leaf_alive=alive, lib=lib, nthreads=2)
+    assert (one["path"] == only[None, :]).all()
+    forced = oracle.forward(**L, want_H=True, forced=np.tile(only.astype(np.int32), (T, 1)),
+                            lib=lib, nthreads=2)
+    np.testing.assert_array_equal(one["y"], forced["y"])
+    np.testing.assert_array_equal(one["H"], forced["H"])
+    visited = np.zeros((P, 1 << D), np.uint8)
+    visited[np.arange(P)[None, :], base["path"]] = 1
+    same = oracle.forward(**L, want_H=True, leaf_alive=visited, lib=lib, nthreads=2)
+    for k in ("path", "H", "y"):
+        np.testing.assert_array_equal(same[k], base[k])
+
+
 ALL_PINS = [pin_brute_force, pin_hand_routing, pin_zero_ties, pin_negative_bias,
             pin_visit_count_table4, pin_depth0_dense, pin_forced_paths, pin_invariants,
             pin_tie_threshold, pin_post_brute_force, pin_post_hand_routing,
-            pin_post_closed_forms, pin_post_routing_unchanged]
+            pin_post_closed_forms, pin_post_routing_unchanged, pin_prune_brute_force,
+            pin_prune_reductions]

@@ -26,8 +26,8 @@ MUTANTS = [
     ("v_row_by_level", "const double *v = Vp + n * (int64_t)h;",
      "const double *v = Vp + level * (int64_t)h;"),
     ("outputs_not_summed", "acc[j] += g * v[j];", "acc[j] = g * v[j];"),
-    ("concat_order_reversed", "d, D, h, variant, fl, Ht + (int64_t)p * h,",
-     "d, D, h, variant, fl, Ht + (int64_t)(P - 1 - p) * h,"),
+    ("concat_order_reversed", "alive ? alive + p * N : NULL, Ht + (int64_t)p * h,",
+     "alive ? alive + p * N : NULL, Ht + (int64_t)(P - 1 - p) * h,"),
     ("projection_transposed", "yt[c] += hk * wk[c];", "yt[c] += hk * Wout[(int64_t)c * K + k];"),
     ("path_is_node_id", "return (int32_t)(n - (((int64_t)1 << D) - 1));", "return (int32_t)n;"),
     ("forced_bits_reversed", "go_right = (forced_leaf >> (D - 1 - level)) & 1;",
@@ -37,6 +37,14 @@ MUTANTS = [
     ("post_gelu_on_each_node", "double g = variant == 1 ? a : gelu_tanh(a);",
      "double g = gelu_tanh(a);"),
     ("post_final_gelu_dropped", "acc[j] = gelu_tanh(acc[j]);", "acc[j] = acc[j];"),
+    ("prune_mask_ignored", "if (alive && !alive[2 * n + 1 + go_right])",
+     "if (0 && alive && !alive[2 * n + 1 + go_right])"),
+    ("prune_alive_is_and", "alive[n] = alive[2 * n + 1] | alive[2 * n + 2];",
+     "alive[n] = alive[2 * n + 1] & alive[2 * n + 2];"),
+    ("prune_forced_step_always_right", "                    go_right = !go_right;",
+     "                    go_right = 1;"),
+    ("prune_leaves_reversed", "alive[first_leaf + i] = leaf_alive[i] != 0;",
+     "alive[first_leaf + i] = leaf_alive[first_leaf - i] != 0;"),
     ("post_variant_ignored", "if (variant == 1)\n", "if (0)\n"),
 ]
 
@@ -46,7 +54,7 @@ def _caught(lib):
     for pin in ALL_PINS:
         try:
             pin(lib)
-        except AssertionError:
+        except (AssertionError, ValueError):  # a wrong value, or a rejected valid input
             failures.append(pin.__name__)
     return failures
 

@@ -54,3 +54,13 @@ def test_bad_variant_rejected(lib):
     L = rand_layer(np.random.default_rng(0), 2, 3, 1, 1, 2)
     with pytest.raises(ValueError):
         oracle.forward(**L, variant=2, lib=lib)
+
+
+def test_pruned_tree_without_alive_leaf_rejected(lib):
+    L = rand_layer(np.random.default_rng(0), 3, 4, 2, 2, 3)
+    alive = np.ones((2, 4), np.uint8)
+    alive[1] = 0
+    with pytest.raises(ValueError):
+        oracle.forward(**L, leaf_alive=alive, lib=lib)
+    with pytest.raises(ValueError):
+        oracle.forward(**L, leaf_alive=np.ones((2, 3), np.uint8), lib=lib)
