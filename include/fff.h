@@ -190,6 +190,64 @@ fff_status_t fff_route(const fff_shape_t *shape, const fff_plan_t *plan,
 fff_status_t fff_project(const fff_shape_t *shape, int32_t algo, const void *H,
                          const void *W_out, void *y, hipStream_t stream);
 
+/*
+ * Static path pruning
+ * -------------------
+ * The paper's page (Figure 4) removes paths of trained trees permanently at
+ * fixed ratios, and the explainer page (section 3.B) describes paths that
+ * training itself leaves inactive.  Here a mask marks each leaf (path) of
+ * each tree alive or pruned; a node is alive when some leaf below it is.
+ * The pages do not say where a token goes when its logit points into a
+ * pruned subtree: it takes the other child, which is alive whenever its
+ * parent is.  Every tree must keep at least one alive leaf.  Routing,
+ * nonlinearity and projection are otherwise those of fff_forward.
+ *
+ * The mask is static, so it is prepared once into a device table owned by
+ * the caller: node alive flags, and for the PREFILL plan the alive node rows
+ * of the densely evaluated levels (< split_level) packed tree by tree into
+ * 256-column tiles, so that the dense product reads and multiplies only
+ * those.  The packed rows are a copy of W_node: prepare again after the
+ * weights change.
+ */
+typedef struct fff_pruning {
+    const void *table;   /* device table written by fff_prune_prepare */
+    int32_t P, D, d;     /* the shape it was prepared for */
+    int32_t split_level; /* PREFILL split level whose rows are packed; 0 = none */
+    int32_t col_tiles;   /* 256-column tiles of packed rows */
+} fff_pruning_t;
+
+/* Device bytes of the table for this shape and plan (plan NULL = the
+ * default plan; only the resolved algorithm and split level matter, T does
+ * not once the plan is fixed). */
+fff_status_t fff_prune_table_size(const fff_shape_t *shape, const fff_plan_t *plan, size_t *bytes);
+
+/*
+ * Builds the table.  leaf_alive: HOST array [P, 2^D] of bytes, nonzero =
+ * alive.  W_node: the layer's node weights (device).  table: device buffer of
+ * at least fff_prune_table_size() bytes, 256-byte aligned.  The call returns
+ * once the table is complete on the device (it synchronizes `stream`), and
+ * fills *out.  FFF_ERROR_INVALID_VALUE if a tree has no alive leaf or a
+ * pointer is missing; FFF_ERROR_WORKSPACE if the table is too small.
+ */
+fff_status_t fff_prune_prepare(const fff_shape_t *shape, const fff_plan_t *plan,
+                               const uint8_t *leaf_alive, const void *W_node, void *table,
+                               size_t table_bytes, hipStream_t stream, fff_pruning_t *out);
+
+/*
+ * fff_forward on pruned trees.  Same arguments and workspace as fff_forward
+ * plus the prepared table.  The plan resolves as for fff_forward; a PREFILL
+ * plan must have the split level the table was prepared with
+ * (FFF_ERROR_NOT_SUPPORTED otherwise); DECODE and GENERIC use the alive
+ * flags only.  A table prepared for another P, D or d is
+ * FFF_ERROR_INVALID_VALUE.
+ */
+fff_status_t fff_forward_pruned(const fff_shape_t *shape, const fff_plan_t *plan,
+                                const fff_pruning_t *pruning, const void *x, const void *W_node,
+                                const void *b_node, const void *V_node, const void *W_out,
+                                void *y, int32_t *path_out, void *workspace,
+                                size_t workspace_bytes, hipStream_t stream,
+                                const fff_stage_events_t *events);
+
 /* Static, human-readable text for a status code. */
 const char *fff_status_string(fff_status_t status);
 

@@ -52,6 +52,14 @@ class StageEvents(ctypes.Structure):
     _fields_ = [("start", ctypes.c_void_p), ("routed", ctypes.c_void_p), ("done", ctypes.c_void_p)]
 
 
+class Pruning(ctypes.Structure):
+    """fff_pruning_t: a prepared static-pruning table (device memory is the
+    caller's; keep the tensor that holds it alive while the table is used)."""
+    _fields_ = [("table", ctypes.c_void_p), ("P", ctypes.c_int32), ("D", ctypes.c_int32),
+                ("d", ctypes.c_int32), ("split_level", ctypes.c_int32),
+                ("col_tiles", ctypes.c_int32)]
+
+
 class FFFError(RuntimeError):
     def __init__(self, status: int, what: str):
         self.status = status
@@ -59,7 +67,8 @@ class FFFError(RuntimeError):
 
 
 EXPORTS = ("fff_plan_default", "fff_plan_resolve", "fff_workspace_size", "fff_forward",
-           "fff_route", "fff_project", "fff_status_string", "fff_algo_name")
+           "fff_route", "fff_project", "fff_status_string", "fff_algo_name",
+           "fff_prune_table_size", "fff_prune_prepare", "fff_forward_pruned")
 
 _lib: Optional[ctypes.CDLL] = None
 
@@ -83,12 +92,18 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
                                 ctypes.POINTER(StageEvents)]
     lib.fff_route.argtypes = [SP, PP, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.fff_project.argtypes = [SP, ctypes.c_int32, vp, vp, vp, vp]
+    PrP = ctypes.POINTER(Pruning)
+    lib.fff_prune_table_size.argtypes = [SP, PP, ctypes.POINTER(sz)]
+    lib.fff_prune_prepare.argtypes = [SP, PP, vp, vp, vp, sz, vp, PrP]
+    lib.fff_forward_pruned.argtypes = [SP, PP, PrP, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp,
+                                       ctypes.POINTER(StageEvents)]
     lib.fff_status_string.argtypes = [ctypes.c_int]
     lib.fff_status_string.restype = ctypes.c_char_p
     lib.fff_algo_name.argtypes = [ctypes.c_int32]
     lib.fff_algo_name.restype = ctypes.c_char_p
     for name in ("fff_plan_default", "fff_plan_resolve", "fff_workspace_size", "fff_forward",
-                 "fff_route", "fff_project"):
+                 "fff_route", "fff_project", "fff_prune_table_size", "fff_prune_prepare",
+                 "fff_forward_pruned"):
         getattr(lib, name).restype = ctypes.c_int
     if path is None:
         _lib = lib
@@ -258,3 +273,69 @@ def project(H, W_out, *, algo=ALGO_AUTO, stream=None, y=None):
     if st != SUCCESS:
         raise FFFError(st, "fff_project")
     return y
+
+
+def prune_table_size(shape: Shape, plan: Optional[Plan] = None) -> int:
+    n = ctypes.c_size_t()
+    st = load_library().fff_prune_table_size(ctypes.byref(shape),
+                                             ctypes.byref(plan) if plan is not None else None,
+                                             ctypes.byref(n))
+    if st != SUCCESS:
+        raise FFFError(st, "fff_prune_table_size")
+    return int(n.value)
+
+
+def prune_prepare(leaf_alive, W_node, V_node, *, algo=ALGO_AUTO, split_level: int = -1,
+                  chunk_tokens: int = 0, T: Optional[int] = None, stream=None,
+                  variant=VARIANT_FFF):
+    """Static path pruning table for trees W_node [P,N,d] (device) and a leaf
+    mask leaf_alive [P, 2^D] (host: numpy or CPU tensor, nonzero = alive).
+    The plan is resolved for T tokens (default 65536, a prefill batch) and
+    the given options; returns (Pruning, table tensor), the tensor owning the
+    device memory."""
+    import numpy as np
+    torch = _torch()
+    P, N, d = W_node.shape
+    D = N.bit_length() - 1
+    mask = np.ascontiguousarray(np.asarray(leaf_alive, dtype=np.uint8))
+    if mask.shape != (P, 1 << D):
+        raise ValueError("leaf_alive must be [P, 2^D]")
+    shape = make_shape(T if T is not None else 65536, d, P, D, V_node.shape[2],
+                       _dtype_code(W_node), variant)
+    plan = make_plan(algo, split_level, chunk_tokens)
+    n = prune_table_size(shape, plan)
+    table = torch.empty(max(n, 1), dtype=torch.uint8, device=W_node.device)
+    out = Pruning()
+    st = load_library().fff_prune_prepare(
+        ctypes.byref(shape), ctypes.byref(plan), mask.ctypes.data_as(ctypes.c_void_p),
+        W_node.data_ptr(), table.data_ptr(), n, _stream_handle(stream), ctypes.byref(out))
+    if st != SUCCESS:
+        raise FFFError(st, "fff_prune_prepare")
+    return out, table
+
+
+def forward_pruned(x, W_node, b_node, V_node, W_out, pruning: Pruning, *, algo=ALGO_AUTO,
+                   split_level: int = -1, chunk_tokens: int = 0, want_path: bool = True,
+                   workspace=None, y=None, path_out=None, stream=None,
+                   events: Optional[StageEvents] = None, variant=VARIANT_FFF):
+    """fff_forward_pruned: y and path_out of the pruned trees."""
+    torch = _torch()
+    shape = shape_of(x, W_node, V_node, variant)
+    _check([x, W_node, b_node, V_node, W_out], x.dtype, x.device)
+    plan = make_plan(algo, split_level, chunk_tokens)
+    if workspace is None:
+        workspace, nbytes = alloc_workspace(shape, plan, x.device)
+    else:
+        nbytes = workspace.numel() * workspace.element_size()
+    if y is None:
+        y = torch.empty((shape.T, shape.d), dtype=x.dtype, device=x.device)
+    if want_path and path_out is None:
+        path_out = torch.empty((shape.T, shape.P), dtype=torch.int32, device=x.device)
+    st = load_library().fff_forward_pruned(
+        ctypes.byref(shape), ctypes.byref(plan), ctypes.byref(pruning), x.data_ptr(),
+        W_node.data_ptr(), b_node.data_ptr(), V_node.data_ptr(), W_out.data_ptr(), y.data_ptr(),
+        path_out.data_ptr() if path_out is not None else None, workspace.data_ptr(), nbytes,
+        _stream_handle(stream), ctypes.byref(events) if events is not None else None)
+    if st != SUCCESS:
+        raise FFFError(st, "fff_forward_pruned")
+    return y, path_out

@@ -6,6 +6,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <vector>
+
 #include "../../include/fff.h"
 #include "launch.hpp"
 
@@ -33,6 +35,7 @@ fff_status_t check_shape(const fff_shape_t* s, Dims* out) {
   d.h = s->h;
   d.dtype = s->dtype;
   d.variant = s->variant;
+  d.prune = nullptr;
   d.N = (int64_t(1) << (s->D + 1)) - 1;
   d.K = int64_t(s->P) * s->h;
   d.esize = s->dtype == FFF_DTYPE_F32 ? 4 : 2;
@@ -162,6 +165,46 @@ Layout layout_for(const Dims& s, const fff_plan_t& p) {
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
+// Pruning table carve-up (offsets are multiples of kWsAlign), for L packed
+// dense levels (0: alive flags only).  At most P tiles: a tree has fewer
+// than 256 columns of levels < L <= 8.
+//   alive       [P][N] uint8
+//   colidx      [P][2^L - 1] int16   packed column of node n within its tree, -1 pruned
+//   tree_base   [P] int32            first column of tree p within its tile
+//   tile_first  [P] int32, tile_count [P] int32
+//   colmap      [P * 256] int32      source row p*N + n of each packed column, -1 = zero row
+//   packed      [P * 256][d] bf16
+struct PruneLayout {
+  size_t alive = 0, colidx = 0, tree_base = 0, tile_first = 0, tile_count = 0, colmap = 0,
+         packed = 0, total = 0;
+};
+
+PruneLayout prune_layout(const Dims& s, int L) {
+  PruneLayout PL;
+  size_t off = 0;
+  PL.alive = off;
+  off = align_up(off + size_t(s.P) * size_t(s.N));
+  if (L > 0) {
+    const size_t cols = (size_t(1) << L) - 1;
+    PL.colidx = off;
+    off = align_up(off + size_t(s.P) * cols * sizeof(int16_t));
+    PL.tree_base = off;
+    off = align_up(off + size_t(s.P) * sizeof(int32_t));
+    PL.tile_first = off;
+    off = align_up(off + size_t(s.P) * sizeof(int32_t));
+    PL.tile_count = off;
+    off = align_up(off + size_t(s.P) * sizeof(int32_t));
+    PL.colmap = off;
+    off = align_up(off + size_t(s.P) * 256 * sizeof(int32_t));
+    PL.packed = off;
+    off = align_up(off + size_t(s.P) * 256 * size_t(s.d) * 2);
+  }
+  PL.total = off;
+  return PL;
+}
+
+int packed_levels(const fff_plan_t& p) { return p.algo == FFF_ALGO_PREFILL ? p.split_level : 0; }
+
 fff_status_t hip_status(hipError_t e) { return e == hipSuccess ? FFF_SUCCESS : FFF_ERROR_HIP; }
 
 fff_status_t record(hipEvent_t ev, hipStream_t st) {
@@ -209,6 +252,50 @@ fff_status_t check_inputs(const Dims& s, const void* x, const void* W, const voi
   if (!x || !W || !b || !V) return FFF_ERROR_INVALID_VALUE;
   if (!aligned(x, 16) || !aligned(W, 16) || !aligned(V, 16) || !aligned(b, s.esize))
     return FFF_ERROR_INVALID_VALUE;
+  return FFF_SUCCESS;
+}
+
+// The whole layer for a validated shape and resolved plan (s.prune set for
+// pruned trees).
+fff_status_t forward_impl(const Dims& s, const fff_plan_t& p, const void* x, const void* W_node,
+                          const void* b_node, const void* V_node, const void* W_out, void* y,
+                          int32_t* path_out, void* workspace, size_t workspace_bytes,
+                          hipStream_t stream, const fff_stage_events_t* events) {
+  fff_status_t st;
+  if (s.T == 0) return FFF_SUCCESS;
+  st = check_inputs(s, x, W_node, b_node, V_node);
+  if (st != FFF_SUCCESS) return st;
+  if (!W_out || !y || !aligned(W_out, 16) || !aligned(y, 16) ||
+      (path_out && !aligned(path_out, 4)))
+    return FFF_ERROR_INVALID_VALUE;
+  const Layout L = layout_for(s, p);
+  if (L.total > 0 && (!workspace || workspace_bytes < L.total)) return FFF_ERROR_WORKSPACE;
+  if (workspace && !aligned(workspace, kWsAlign)) return FFF_ERROR_INVALID_VALUE;
+
+  char* ws = static_cast<char*>(workspace);
+  void* H = ws + L.H;
+  if (events && (st = record(events->start, stream)) != FFF_SUCCESS) return st;
+  if (p.algo == FFF_ALGO_DECODE) {
+    st = hip_status(fff::launch_decode(s, x, W_node, b_node, V_node, W_out, y, path_out, ws,
+                                       stream));
+    if (st != FFF_SUCCESS) return st;
+    if (events && (st = record(events->routed, stream)) != FFF_SUCCESS) return st;
+    if (events && (st = record(events->done, stream)) != FFF_SUCCESS) return st;
+    return FFF_SUCCESS;
+  }
+  // The projection's transposed W_out is prepared first, so that the
+  // projection stage is the matrix product alone.
+  if (L.use_wt && fff::launch_transpose(W_out, ws + L.WT, s.K, s.d, stream) != hipSuccess)
+    return FFF_ERROR_HIP;
+  st = run_route(s, p, L, x, W_node, b_node, V_node, H, path_out, ws, stream);
+  if (st != FFF_SUCCESS) return st;
+  if (events && (st = record(events->routed, stream)) != FFF_SUCCESS) return st;
+  if (L.use_wt)
+    st = hip_status(fff::launch_project_direct(s, H, ws + L.WT, y, stream));
+  else
+    st = run_project(s, p.algo, H, W_out, y, stream);
+  if (st != FFF_SUCCESS) return st;
+  if (events && (st = record(events->done, stream)) != FFF_SUCCESS) return st;
   return FFF_SUCCESS;
 }
 
@@ -262,41 +349,138 @@ fff_status_t fff_forward(const fff_shape_t* shape, const fff_plan_t* plan, const
   fff_plan_t p;
   st = resolve_plan(s, plan, &p);
   if (st != FFF_SUCCESS) return st;
-  if (s.T == 0) return FFF_SUCCESS;
-  st = check_inputs(s, x, W_node, b_node, V_node);
-  if (st != FFF_SUCCESS) return st;
-  if (!W_out || !y || !aligned(W_out, 16) || !aligned(y, 16) ||
-      (path_out && !aligned(path_out, 4)))
-    return FFF_ERROR_INVALID_VALUE;
-  const Layout L = layout_for(s, p);
-  if (L.total > 0 && (!workspace || workspace_bytes < L.total)) return FFF_ERROR_WORKSPACE;
-  if (workspace && !aligned(workspace, kWsAlign)) return FFF_ERROR_INVALID_VALUE;
+  return forward_impl(s, p, x, W_node, b_node, V_node, W_out, y, path_out, workspace,
+                      workspace_bytes, stream, events);
+}
 
-  char* ws = static_cast<char*>(workspace);
-  void* H = ws + L.H;
-  if (events && (st = record(events->start, stream)) != FFF_SUCCESS) return st;
-  if (p.algo == FFF_ALGO_DECODE) {
-    st = hip_status(fff::launch_decode(s, x, W_node, b_node, V_node, W_out, y, path_out, ws,
-                                       stream));
-    if (st != FFF_SUCCESS) return st;
-    if (events && (st = record(events->routed, stream)) != FFF_SUCCESS) return st;
-    if (events && (st = record(events->done, stream)) != FFF_SUCCESS) return st;
-    return FFF_SUCCESS;
-  }
-  // The projection's transposed W_out is prepared first, so that the
-  // projection stage is the matrix product alone.
-  if (L.use_wt && fff::launch_transpose(W_out, ws + L.WT, s.K, s.d, stream) != hipSuccess)
-    return FFF_ERROR_HIP;
-  st = run_route(s, p, L, x, W_node, b_node, V_node, H, path_out, ws, stream);
+fff_status_t fff_prune_table_size(const fff_shape_t* shape, const fff_plan_t* plan,
+                                  size_t* bytes) {
+  Dims s;
+  fff_status_t st = check_shape(shape, &s);
   if (st != FFF_SUCCESS) return st;
-  if (events && (st = record(events->routed, stream)) != FFF_SUCCESS) return st;
-  if (L.use_wt)
-    st = hip_status(fff::launch_project_direct(s, H, ws + L.WT, y, stream));
-  else
-    st = run_project(s, p.algo, H, W_out, y, stream);
+  if (!bytes) return FFF_ERROR_INVALID_VALUE;
+  fff_plan_t p;
+  st = resolve_plan(s, plan, &p);
   if (st != FFF_SUCCESS) return st;
-  if (events && (st = record(events->done, stream)) != FFF_SUCCESS) return st;
+  *bytes = prune_layout(s, packed_levels(p)).total;
   return FFF_SUCCESS;
+}
+
+fff_status_t fff_prune_prepare(const fff_shape_t* shape, const fff_plan_t* plan,
+                               const uint8_t* leaf_alive, const void* W_node, void* table,
+                               size_t table_bytes, hipStream_t stream, fff_pruning_t* out) {
+  Dims s;
+  fff_status_t st = check_shape(shape, &s);
+  if (st != FFF_SUCCESS) return st;
+  fff_plan_t p;
+  st = resolve_plan(s, plan, &p);
+  if (st != FFF_SUCCESS) return st;
+  if (!leaf_alive || !W_node || !table || !out || !aligned(table, kWsAlign) ||
+      !aligned(W_node, 16))
+    return FFF_ERROR_INVALID_VALUE;
+  if (int64_t(s.P) * s.N > INT32_MAX) return FFF_ERROR_NOT_SUPPORTED;
+  const int L = packed_levels(p);
+  const PruneLayout PL = prune_layout(s, L);
+  if (table_bytes < PL.total) return FFF_ERROR_WORKSPACE;
+
+  // Node flags: leaves as given, internal nodes alive iff a child is.
+  const int64_t N = s.N;
+  const int64_t first_leaf = (int64_t(1) << s.D) - 1;
+  std::vector<uint8_t> alive(size_t(s.P) * N);
+  for (int64_t t = 0; t < s.P; ++t) {
+    uint8_t* a = alive.data() + t * N;
+    for (int64_t i = 0; i <= first_leaf; ++i) a[first_leaf + i] = leaf_alive[t * (first_leaf + 1) + i] != 0;
+    for (int64_t n = first_leaf - 1; n >= 0; --n) a[n] = a[2 * n + 1] | a[2 * n + 2];
+    if (!a[0]) return FFF_ERROR_INVALID_VALUE;
+  }
+  // Packed columns of the dense levels: trees in order, a new tile when the
+  // next tree does not fit; within a tree, alive nodes in heap order.
+  const int64_t cols = L > 0 ? (int64_t(1) << L) - 1 : 0;
+  std::vector<int16_t> colidx(size_t(s.P) * cols, -1);
+  std::vector<int32_t> tree_base(s.P, 0), tile_first(s.P, 0), tile_count(s.P, 0);
+  std::vector<int32_t> colmap(size_t(s.P) * 256, -1);
+  int tiles = 0;
+  if (L > 0) {
+    int used = 256;
+    for (int t = 0; t < s.P; ++t) {
+      int cnt = 0;
+      for (int64_t n = 0; n < cols; ++n) cnt += alive[t * N + n];
+      if (used + cnt > 256) {
+        tile_first[tiles] = t;
+        ++tiles;
+        used = 0;
+      }
+      tree_base[t] = used;
+      ++tile_count[tiles - 1];
+      int i = 0;
+      for (int64_t n = 0; n < cols; ++n) {
+        if (!alive[t * N + n]) continue;
+        colidx[t * cols + n] = static_cast<int16_t>(i);
+        colmap[size_t(tiles - 1) * 256 + used + i] = static_cast<int32_t>(t * N + n);
+        ++i;
+      }
+      used += cnt;
+    }
+  }
+  char* tb = static_cast<char*>(table);
+  auto put = [&](size_t off, const void* src, size_t n) {
+    return n == 0 || hipMemcpyAsync(tb + off, src, n, hipMemcpyHostToDevice, stream) == hipSuccess;
+  };
+  bool ok = put(PL.alive, alive.data(), alive.size());
+  if (L > 0) {
+    ok = ok && put(PL.colidx, colidx.data(), colidx.size() * sizeof(int16_t)) &&
+         put(PL.tree_base, tree_base.data(), tree_base.size() * sizeof(int32_t)) &&
+         put(PL.tile_first, tile_first.data(), tile_first.size() * sizeof(int32_t)) &&
+         put(PL.tile_count, tile_count.data(), tile_count.size() * sizeof(int32_t)) &&
+         put(PL.colmap, colmap.data(), colmap.size() * sizeof(int32_t)) &&
+         fff::launch_prune_pack(W_node, reinterpret_cast<const int32_t*>(tb + PL.colmap),
+                                tb + PL.packed, tiles * 256, s.d, stream) == hipSuccess;
+  }
+  // The host vectors above are the copies' sources: wait before they go.
+  if (hipStreamSynchronize(stream) != hipSuccess || !ok) return FFF_ERROR_HIP;
+  out->table = table;
+  out->P = s.P;
+  out->D = s.D;
+  out->d = s.d;
+  out->split_level = L;
+  out->col_tiles = tiles;
+  return FFF_SUCCESS;
+}
+
+fff_status_t fff_forward_pruned(const fff_shape_t* shape, const fff_plan_t* plan,
+                                const fff_pruning_t* pruning, const void* x, const void* W_node,
+                                const void* b_node, const void* V_node, const void* W_out,
+                                void* y, int32_t* path_out, void* workspace,
+                                size_t workspace_bytes, hipStream_t stream,
+                                const fff_stage_events_t* events) {
+  Dims s;
+  fff_status_t st = check_shape(shape, &s);
+  if (st != FFF_SUCCESS) return st;
+  if (!pruning || !pruning->table || !aligned(pruning->table, kWsAlign) || pruning->P != s.P ||
+      pruning->D != s.D || pruning->d != s.d || pruning->split_level < 0 ||
+      pruning->split_level > 8 || pruning->col_tiles < 0 || pruning->col_tiles > s.P)
+    return FFF_ERROR_INVALID_VALUE;
+  fff_plan_t p;
+  st = resolve_plan(s, plan, &p);
+  if (st != FFF_SUCCESS) return st;
+  if (p.algo == FFF_ALGO_PREFILL && p.split_level != pruning->split_level)
+    return FFF_ERROR_NOT_SUPPORTED;
+  const PruneLayout PL = prune_layout(s, pruning->split_level);
+  const char* tb = static_cast<const char*>(pruning->table);
+  fff::PruneView pv{};
+  pv.alive = reinterpret_cast<const uint8_t*>(tb + PL.alive);
+  if (pruning->split_level > 0) {
+    pv.colidx = reinterpret_cast<const int16_t*>(tb + PL.colidx);
+    pv.tree_base = reinterpret_cast<const int32_t*>(tb + PL.tree_base);
+    pv.tile_first = reinterpret_cast<const int32_t*>(tb + PL.tile_first);
+    pv.tile_count = reinterpret_cast<const int32_t*>(tb + PL.tile_count);
+    pv.W_packed = reinterpret_cast<const uint16_t*>(tb + PL.packed);
+  }
+  pv.L = pruning->split_level;
+  pv.col_tiles = pruning->col_tiles;
+  s.prune = &pv;
+  return forward_impl(s, p, x, W_node, b_node, V_node, W_out, y, path_out, workspace,
+                      workspace_bytes, stream, events);
 }
 
 fff_status_t fff_route(const fff_shape_t* shape, const fff_plan_t* plan, const void* x,

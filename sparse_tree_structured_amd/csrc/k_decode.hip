@@ -86,7 +86,8 @@ struct DecodeArgs {
   int T, d, P, D, h, K;
   int64_t N;
   int n_route_wg, n_proj_wg;
-  int post;  // 1: GELU on the summed h-vector instead of on each node's logit
+  int post;              // 1: GELU on the summed h-vector instead of on each node's logit
+  const uint8_t* alive;  // static pruning: [P][N] 1 = node alive; null = every node
 };
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
@@ -120,6 +121,9 @@ __device__ __forceinline__ uint4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_
 }
 __device__ __forceinline__ uint16_t buffer_load2(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
+}
+__device__ __forceinline__ uint8_t buffer_load1(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b8(r, off, 0, 0);
 }
 __device__ __forceinline__ uint4 coherent_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kSc1));
@@ -216,6 +220,12 @@ __device__ void route_item(const DecodeArgs& a, unsigned char* lds, int item, in
   const __amdgpu_buffer_rsrc_t bbuf = buffer_of(a.b + static_cast<int64_t>(p) * a.N, uint32_t(a.N) * 2);
   const __amdgpu_buffer_rsrc_t vbuf =
       buffer_of(a.V + static_cast<int64_t>(p) * a.N * a.h, uint32_t(a.N) * a.h * 2);
+  // Node alive flags of this tree (an empty buffer when nothing is pruned:
+  // its loads return 0 and are then read as alive).
+  const __amdgpu_buffer_rsrc_t abuf =
+      buffer_of(a.alive ? static_cast<const void*>(a.alive + static_cast<int64_t>(p) * a.N)
+                        : static_cast<const void*>(a.x),
+                a.alive ? uint32_t(a.N) : 0);
 
   // This wave's slice of the token rows, kept for every round (rows past
   // nt repeat the last token; their results are not used; k steps past the
@@ -269,6 +279,17 @@ __device__ void route_item(const DecodeArgs& a, unsigned char* lds, int item, in
       const int row = 4 * q + r < R ? 4 * q + r : 0;
       braw[r] = buffer_load2(bbuf, 4 * q + r < R ? uint32_t(lev == 0 ? row : rows[row]) * 2 : kOob);
     }
+    // Alive flags of both children of row j (wave 0, lanes j < R; rows at
+    // the leaf level read past the buffer and get 0, never used).
+    uint8_t child_l, child_r;
+    {
+      const int row = j < R ? j : 0;
+      const uint32_t off = wave == 0 && q == 0 && j < R
+                               ? uint32_t(2 * (lev == 0 ? row : rows[row]) + 1)
+                               : kOob;
+      child_l = buffer_load1(abuf, off);
+      child_r = buffer_load1(abuf, off == kOob ? kOob : off + 1);
+    }
     // The previous round's H terms, while these loads are in flight.
     if (prev_rl) add_h_terms(lds, vc + (buf ^ 1) * vc_stride, prev_rl, nt, a.h, a.post, hacc);
 
@@ -304,6 +325,9 @@ __device__ void route_item(const DecodeArgs& a, unsigned char* lds, int item, in
         lgs[row * 16 + j] = lg;
         right[r] = __ballot(go_right(lg));
       }
+      // Bit r of alive_l / alive_r: the left / right child of row r is alive.
+      const uint64_t alive_l = __ballot(lane < 16 && (!a.alive || child_l != 0));
+      const uint64_t alive_r = __ballot(lane < 16 && (!a.alive || child_r != 0));
       // Walk of token j through its subtree (the four lanes of token j do
       // the same walk; lane q == 0 records the visited rows).
       const int base = troot * S;
@@ -313,6 +337,8 @@ __device__ void route_item(const DecodeArgs& a, unsigned char* lds, int item, in
         const int sel = row & 3;
         const uint64_t m = sel == 0 ? right[0] : sel == 1 ? right[1] : sel == 2 ? right[2] : right[3];
         bit = static_cast<int>((m >> ((row >> 2) * 16 + j)) & 1);
+        // Static pruning: a step into a pruned child goes to its sibling.
+        if (!(((bit ? alive_r : alive_l) >> row) & 1)) bit ^= 1;
         if (q == 0 && j < nt) rsm[j * 4 + lv] = row;
         jj = 2 * jj + 1 + bit;
       }
@@ -594,6 +620,7 @@ hipError_t launch_decode(const Dims& s, const void* x, const void* W, const void
   a.D = s.D;
   a.h = s.h;
   a.post = s.variant;
+  a.alive = s.prune ? s.prune->alive : nullptr;
   a.K = static_cast<int>(s.K);
   a.N = s.N;
 

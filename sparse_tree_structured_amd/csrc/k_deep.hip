@@ -118,8 +118,9 @@ __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_ca
 //   Vsub  kSubRows x h bf16         subtree v_n rows
 //   Vtop  k x h bf16                v_n rows of the top path shared by the bucket
 //   bsub  kSubRows fp32             subtree biases
+//   asub  kSubRows int32            1 = subtree node alive (static pruning)
 struct DeepLds {
-  size_t w, vsub, vtop, bsub, total;
+  size_t w, vsub, vtop, bsub, asub, total;
 };
 __host__ __device__ inline DeepLds deep_lds(int d, int h, int k) {
   DeepLds L;
@@ -127,7 +128,8 @@ __host__ __device__ inline DeepLds deep_lds(int d, int h, int k) {
   L.vsub = L.w + size_t(kSubRows) * (d + 8) * 2;
   L.vtop = L.vsub + size_t(kSubRows) * h * 2;
   L.bsub = L.vtop + size_t(k) * h * 2;
-  L.total = L.bsub + kSubRows * 4;
+  L.asub = L.bsub + kSubRows * 4;
+  L.total = L.asub + kSubRows * 4;
   return L;
 }
 
@@ -137,7 +139,7 @@ __global__ __launch_bounds__(WAVES * 64, 2) void deep_kernel(
     const uint16_t* __restrict__ V, const float* __restrict__ rec_logit,
     const int32_t* __restrict__ perm, const int32_t* __restrict__ offs, uint16_t* __restrict__ H,
     int32_t* __restrict__ path_out, int T, int d, int P, int D, int h, int64_t N, int k,
-    int chunk, int nchunks, int post) {
+    int chunk, int nchunks, int post, const uint8_t* __restrict__ alive) {
   extern __shared__ __align__(16) unsigned char lds[];
   const int S = 1 << k;
   const int ipc = P * S;  // items per chunk
@@ -161,6 +163,7 @@ __global__ __launch_bounds__(WAVES * 64, 2) void deep_kernel(
   uint16_t* Vsub = reinterpret_cast<uint16_t*>(lds + L.vsub);
   uint16_t* Vtop = reinterpret_cast<uint16_t*>(lds + L.vtop);
   float* bsub = reinterpret_cast<float*>(lds + L.bsub);
+  int32_t* asub = reinterpret_cast<int32_t*>(lds + L.asub);
   const int ld = d + 8;
   const uint16_t* Wp = W + static_cast<int64_t>(p) * N * d;
   const uint16_t* Vp = V + static_cast<int64_t>(p) * N * h;
@@ -188,8 +191,11 @@ __global__ __launch_bounds__(WAVES * 64, 2) void deep_kernel(
       *reinterpret_cast<uint4*>(Vtop + l * h + cc * 8) = ldg16(Vp + n * h + cc * 8);
     }
   }
-  for (int j = threadIdx.x; j < kSubRows; j += blockDim.x)
-    bsub[j] = j < used ? bf16_to_f32(b[static_cast<int64_t>(p) * N + subtree_global(r, j)]) : 0.0f;
+  for (int j = threadIdx.x; j < kSubRows; j += blockDim.x) {
+    const int64_t g = static_cast<int64_t>(p) * N + (j < used ? subtree_global(r, j) : 0);
+    bsub[j] = j < used ? bf16_to_f32(b[g]) : 0.0f;
+    asub[j] = j < used && (!alive || alive[g]);
+  }
   __syncthreads();
 
   const int lane = threadIdx.x & (kWave - 1);
@@ -242,7 +248,11 @@ __global__ __launch_bounds__(WAVES * 64, 2) void deep_kernel(
       const float a = (rr == 0 ? v0 : rr == 1 ? v1 : rr == 2 ? v2 : v3) + bsub[j];
       gv[lv] = post ? a : gelu_tanh(a);
       jv[lv] = j;
-      if (lv + 1 < sub_levels) j = 2 * j + 1 + go_right(a);
+      if (lv + 1 < sub_levels) {
+        int rr2 = go_right(a);
+        if (!asub[2 * j + 1 + rr2]) rr2 ^= 1;  // pruned child: its sibling
+        j = 2 * j + 1 + rr2;
+      }
     }
     if (!valid) return;
     // H slice of this lane: columns [q*hq, (q+1)*hq) of tree p.
@@ -361,7 +371,7 @@ hipError_t launch_deep(const Dims& s, int k, const void* x, const void* W, const
       static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(W),
       static_cast<const uint16_t*>(b), static_cast<const uint16_t*>(V), rec_logit, perm, offs,
       static_cast<uint16_t*>(H), path_out, static_cast<int>(s.T), s.d, s.P, s.D, s.h, s.N, k,
-      chunk, nchunks, s.variant);
+      chunk, nchunks, s.variant, s.prune ? s.prune->alive : nullptr);
   return hipGetLastError();
 }
 

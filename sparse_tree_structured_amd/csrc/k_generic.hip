@@ -20,7 +20,7 @@ template <typename E>
 __global__ __launch_bounds__(256) void route_generic_kernel(
     const E* __restrict__ x, const E* __restrict__ W, const E* __restrict__ b,
     float* __restrict__ logits, int32_t* __restrict__ path_out, int32_t* __restrict__ leaf_ws,
-    int64_t T, int d, int P, int D, int64_t N) {
+    int64_t T, int d, int P, int D, int64_t N, const uint8_t* __restrict__ alive) {
   const int lane = threadIdx.x & (kWave - 1);
   const int64_t pair = static_cast<int64_t>(blockIdx.x) * (blockDim.x / kWave) + (threadIdx.x / kWave);
   if (pair >= T * P) return;  // whole wavefront leaves together
@@ -35,7 +35,12 @@ __global__ __launch_bounds__(256) void route_generic_kernel(
     for (int i = lane; i < d; i += kWave) acc += Elem<E>::ld(xt, i) * Elem<E>::ld(w, i);
     const float a = wave_sum(acc) + Elem<E>::ld(b, static_cast<size_t>(p) * N + n);
     if (lane == 0) logits[pair * (D + 1) + level] = a;
-    if (level < D) n = 2 * n + 1 + go_right(a);
+    if (level < D) {
+      int r = go_right(a);
+      // Static pruning: a step into a pruned child goes to the sibling.
+      if (alive && !alive[static_cast<int64_t>(p) * N + 2 * n + 1 + r]) r ^= 1;
+      n = 2 * n + 1 + r;
+    }
   }
   if (lane == 0) {
     const int32_t leaf = static_cast<int32_t>(n - ((int64_t(1) << D) - 1));
@@ -125,11 +130,12 @@ hipError_t launch_route_generic(const Dims& s, const void* x, const void* W, con
   if (s.dtype == 0)
     route_generic_kernel<float><<<grid, 256, 0, st>>>(
         static_cast<const float*>(x), static_cast<const float*>(W), static_cast<const float*>(b),
-        logits, path_out, leaf_ws, s.T, s.d, s.P, s.D, s.N);
+        logits, path_out, leaf_ws, s.T, s.d, s.P, s.D, s.N, s.prune ? s.prune->alive : nullptr);
   else
     route_generic_kernel<uint16_t><<<grid, 256, 0, st>>>(
         static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(W),
-        static_cast<const uint16_t*>(b), logits, path_out, leaf_ws, s.T, s.d, s.P, s.D, s.N);
+        static_cast<const uint16_t*>(b), logits, path_out, leaf_ws, s.T, s.d, s.P, s.D, s.N,
+        s.prune ? s.prune->alive : nullptr);
   return hipGetLastError();
 }
 

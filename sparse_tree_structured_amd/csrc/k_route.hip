@@ -13,6 +13,11 @@
 //     rec_logit[p][t][l]   (fp32, l < L)
 //     rec_next[p][t]       (heap id at level L, or the leaf if L = D+1)
 //
+// With static path pruning (a leaf mask per tree, paper page Figure 4) the
+// B operand is the table's packed alive rows instead: whole trees per
+// 256-column tile, a per-tree column map, and a step into a pruned child
+// goes to its sibling.
+//
 // When L = D+1 the whole path is known and hbuild_kernel forms
 //     H[t, p*h + j] = sum over l of GELU(a_l) * V_node[p, n_l, j]
 // (GELU before the sum: explainer section 3.C) and path_out; otherwise the
@@ -48,10 +53,12 @@ template <class C>
 struct NodeRowLoader {
   RowLoader<C::BN, C::BK, C::kThreads> rl;
   const uint16_t* W;
+  const uint16_t* packed;  // pruned: the table's packed rows, else null
   int d, P, L, n0, tid;
   int64_t N;
   __device__ __forceinline__ void load(int k0) {
     rl.load([&](int i) {
+      if (packed) return packed + static_cast<int64_t>(n0 + i) * d;
       const int gc = n0 + i;
       const int p = gc >> L;
       const int n = gc & ((1 << L) - 1);
@@ -70,7 +77,8 @@ __device__ __forceinline__ void top_walk_epilogue(const f32x16_t (&acc)[C::kTm][
                                                   const uint16_t* __restrict__ b,
                                                   float* __restrict__ rec_logit,
                                                   int32_t* __restrict__ rec_next, int T, int P,
-                                                  int D, int L, int64_t N, int m0, int n0) {
+                                                  int D, int L, int64_t N, int m0, int n0,
+                                                  const PruneView& pv) {
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = tid / kWave;
@@ -81,8 +89,11 @@ __device__ __forceinline__ void top_walk_epilogue(const f32x16_t (&acc)[C::kTm][
   constexpr int kRows = C::WM;
   constexpr int kPitch = C::BN + 4;
   const int cpt = 1 << L;
-  const int tpt = C::BN >> L;  // trees per tile
-  const int p_base = n0 >> L;
+  // Trees of this column tile (consecutive ids).  Unpruned: BN >> L trees of
+  // cpt columns each; pruned: as the table packed them.
+  const int tn = n0 / C::BN;
+  const int tpt = pv.alive ? pv.tile_count[tn] : C::BN >> L;
+  const int p_base = pv.alive ? pv.tile_first[tn] : n0 >> L;
 #pragma unroll 1
   for (int half = 0; half < C::kWavesM; ++half) {
     if (wm == half) {
@@ -106,14 +117,41 @@ __device__ __forceinline__ void top_walk_epilogue(const f32x16_t (&acc)[C::kTm][
       const int t = m0 + half * kRows + tr;
       const int p = p_base + tp;
       if (t >= T || p >= P) continue;
-      const float* row = lg + tr * kPitch + tp * cpt;
       const uint16_t* bp = b + static_cast<int64_t>(p) * N;
       float* out = rec_logit + (static_cast<int64_t>(p) * T + t) * L;
       int n = 0;
-      for (int level = 0; level < L; ++level) {
-        const float a = row[n] + bf16_to_f32(bp[n]);
-        out[level] = a;
-        if (level < D) n = 2 * n + 1 + go_right(a);
+      if (!pv.alive) {
+        const float* row = lg + tr * kPitch + tp * cpt;
+        for (int level = 0; level < L; ++level) {
+          const float a = row[n] + bf16_to_f32(bp[n]);
+          out[level] = a;
+          if (level < D) n = 2 * n + 1 + go_right(a);
+        }
+      } else {
+        // Packed columns: node n sits at column colidx[n] of its tree (the
+        // root first).  The bias, both children's alive flags and their
+        // columns are read together, one round trip per level.
+        const float* row = lg + tr * kPitch + pv.tree_base[p];
+        const int16_t* ci = pv.colidx + static_cast<int64_t>(p) * (cpt - 1);
+        const uint8_t* al = pv.alive + static_cast<int64_t>(p) * N;
+        int col = 0;
+        for (int level = 0; level < L; ++level) {
+          const float bn = bf16_to_f32(bp[n]);
+          const bool deeper = level < D;
+          const bool in_tile = level + 1 < L;
+          const int alive_l = deeper ? al[2 * n + 1] : 0;
+          const int alive_r = deeper ? al[2 * n + 2] : 0;
+          const int col_l = in_tile ? ci[2 * n + 1] : 0;
+          const int col_r = in_tile ? ci[2 * n + 2] : 0;
+          const float a = row[col] + bn;
+          out[level] = a;
+          if (deeper) {
+            int r = go_right(a);
+            if (!(r ? alive_r : alive_l)) r ^= 1;  // pruned child: its sibling
+            n = 2 * n + 1 + r;
+            col = r ? col_r : col_l;
+          }
+        }
       }
       rec_next[static_cast<int64_t>(p) * T + t] = n;
     }
@@ -131,7 +169,7 @@ template <class C>
 __global__ __launch_bounds__(C::kThreads) void route_top_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ W, const uint16_t* __restrict__ b,
     float* __restrict__ rec_logit, int32_t* __restrict__ rec_next, int T, int d, int P, int D,
-    int L, int64_t N, int tiles_n) {
+    int L, int64_t N, int tiles_n, PruneView pv) {
   extern __shared__ __align__(16) uint16_t smem[];
   const int logical = xcd_logical_tile(blockIdx.x, gridDim.x);
   const int tn = logical % tiles_n;
@@ -146,6 +184,7 @@ __global__ __launch_bounds__(C::kThreads) void route_top_kernel(
   la.tid = threadIdx.x;
   NodeRowLoader<C> lb;
   lb.W = W;
+  lb.packed = pv.W_packed;
   lb.d = d;
   lb.P = P;
   lb.L = L;
@@ -155,7 +194,7 @@ __global__ __launch_bounds__(C::kThreads) void route_top_kernel(
   f32x16_t acc[C::kTm][C::kTn];
   gemm_mainloop<C>(acc, smem, d, la, lb);
   top_walk_epilogue<C>(acc, reinterpret_cast<float*>(smem), b, rec_logit, rec_next, T, P, D, L, N,
-                       m0, n0);
+                       m0, n0, pv);
 }
 
 // Same product through the direct-to-LDS multi-stage main loop.
@@ -163,7 +202,7 @@ template <class C>
 __global__ __launch_bounds__(C::kThreads) void route_top_direct_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ W, const uint16_t* __restrict__ b,
     float* __restrict__ rec_logit, int32_t* __restrict__ rec_next, int T, int d, int P, int D,
-    int L, int64_t N, int tiles_n) {
+    int L, int64_t N, int tiles_n, PruneView pv) {
   extern __shared__ __align__(16) unsigned char lds[];
   const int logical = xcd_logical_tile(blockIdx.x, gridDim.x);
   const int tn = logical % tiles_n;
@@ -176,6 +215,7 @@ __global__ __launch_bounds__(C::kThreads) void route_top_direct_kernel(
     return x + static_cast<size_t>(r) * d;
   };
   auto b_row = [&](int j) {
+    if (pv.W_packed) return pv.W_packed + static_cast<int64_t>(n0 + j) * d;
     const int gc = n0 + j;
     const int p = gc >> L;
     const int n = gc & cmask;
@@ -185,7 +225,7 @@ __global__ __launch_bounds__(C::kThreads) void route_top_direct_kernel(
   f32x16_t acc[C::kTm][C::kTn];
   gemm_mainloop_direct<C>(acc, lds, d, a_row, b_row);
   top_walk_epilogue<C>(acc, reinterpret_cast<float*>(lds), b, rec_logit, rec_next, T, P, D, L, N,
-                       m0, n0);
+                       m0, n0, pv);
 }
 
 // H for fully routed paths (L = D+1).  One workgroup per (tile of kHbTok
@@ -307,14 +347,21 @@ size_t hbuild_lds_bytes(const Dims& s) {
          kHbTok * 4;
 }
 
+// Column tiles of the dense product over levels < L: whole trees of 2^L
+// columns, or the pruning table's packed tiles.
+int top_col_tiles(const Dims& s, int L) {
+  if (s.prune) return s.prune->col_tiles;
+  return static_cast<int>(((static_cast<int64_t>(s.P) << L) + 255) / 256);
+}
+
 template <class C, bool kDirect>
 hipError_t launch_top_cfg(const Dims& s, int L, const void* x, const void* W, const void* b,
                           float* rec_logit, int32_t* rec_next, hipStream_t st) {
   const int tiles_m = static_cast<int>((s.T + C::BM - 1) / C::BM);
-  const int64_t cols = static_cast<int64_t>(s.P) << L;
-  const int tiles_n = static_cast<int>((cols + C::BN - 1) / C::BN);
+  const int tiles_n = top_col_tiles(s, L);
+  const PruneView pv = s.prune ? *s.prune : PruneView{};
   void (*kern)(const uint16_t*, const uint16_t*, const uint16_t*, float*, int32_t*, int, int, int,
-               int, int, int64_t, int);
+               int, int, int64_t, int, PruneView);
   if constexpr (kDirect)
     kern = route_top_direct_kernel<C>;
   else
@@ -331,7 +378,7 @@ hipError_t launch_top_cfg(const Dims& s, int L, const void* x, const void* W, co
   kern<<<dim3(tiles_m * tiles_n), dim3(C::kThreads), lds, st>>>(
       static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(W),
       static_cast<const uint16_t*>(b), rec_logit, rec_next, static_cast<int>(s.T), s.d, s.P, s.D,
-      L, s.N, tiles_n);
+      L, s.N, tiles_n, pv);
   return hipGetLastError();
 }
 
@@ -340,7 +387,28 @@ using SmallTile = TileCfg<64, 256, 64, 64, 64>;
 using TopDirect = DirectCfg<256, 256, 128, 64, 4>;
 
 
+// One workgroup per packed row: packed[i] = W row colmap[i] (zeros for -1).
+__global__ __launch_bounds__(256) void prune_pack_kernel(const uint16_t* __restrict__ W,
+                                                         const int32_t* __restrict__ colmap,
+                                                         uint16_t* __restrict__ packed, int d) {
+  const int i = blockIdx.x;
+  const int64_t src = colmap[i];
+  uint16_t* dst = packed + static_cast<int64_t>(i) * d;
+  for (int c = threadIdx.x * 8; c < d; c += 256 * 8) {
+    const uint4 v = src >= 0 ? ldg16(W + src * d + c) : make_uint4(0, 0, 0, 0);
+    *reinterpret_cast<uint4*>(dst + c) = v;
+  }
+}
+
 }  // namespace
+
+hipError_t launch_prune_pack(const void* W, const int32_t* colmap, void* packed, int rows, int d,
+                             hipStream_t st) {
+  if (rows <= 0) return hipSuccess;
+  prune_pack_kernel<<<dim3(rows), dim3(256), 0, st>>>(static_cast<const uint16_t*>(W), colmap,
+                                                      static_cast<uint16_t*>(packed), d);
+  return hipGetLastError();
+}
 
 bool hbuild_supported(const Dims& s);
 
@@ -351,9 +419,11 @@ bool route_top_supported(const Dims& s, int L) {
 
 hipError_t launch_route_top(const Dims& s, int L, const void* x, const void* W, const void* b,
                             float* rec_logit, int32_t* rec_next, hipStream_t st) {
+  // A pruning table packs the rows of one split level only.
+  if (s.prune && s.prune->L != L) return hipErrorInvalidValue;
   // Enough tiles to cover the 256 compute units: shrink the token tile when
   // the column count is small (few trees or few levels).
-  const int64_t tiles_n = ((static_cast<int64_t>(s.P) << L) + TopTile::BN - 1) / TopTile::BN;
+  const int64_t tiles_n = top_col_tiles(s, L);
   if ((1 << L) <= TopDirect::BN && ((s.T + 255) / 256) * tiles_n >= 256)
     return launch_top_cfg<TopDirect, true>(s, L, x, W, b, rec_logit, rec_next, st);
   if (((s.T + 127) / 128) * tiles_n >= 256)

@@ -9,6 +9,22 @@
 
 namespace fff {
 
+// Static path pruning: views into a device table built once per leaf mask.
+// A node is alive when some leaf below it is; a routed step into a pruned
+// child goes to its sibling.  For the dense top levels the table also holds
+// the alive node rows of levels < L packed tree by tree into 256-column
+// tiles (no tree straddles a tile), so the dense product streams only them.
+struct PruneView {
+  const uint8_t* alive;        // [P][N] 1 = alive
+  const int16_t* colidx;       // [P][2^L - 1] column of node n among its tree's packed ones, -1 pruned
+  const int32_t* tree_base;    // [P] first packed column of tree p within its tile
+  const int32_t* tile_first;   // [col_tiles] first tree of each tile
+  const int32_t* tile_count;   // [col_tiles] trees in each tile
+  const uint16_t* W_packed;    // [col_tiles * 256][d] packed rows (zero rows fill a tile)
+  int L;                       // dense levels packed (0: none)
+  int col_tiles;
+};
+
 struct Dims {
   int64_t T;
   int d, P, D, h;
@@ -17,6 +33,7 @@ struct Dims {
   int64_t N;    // 2^(D+1) - 1
   int64_t K;    // P * h
   size_t esize;
+  const PruneView* prune;  // null: every path alive
 };
 
 // ---- generic path: any shape, fp32 or bf16 ----
@@ -64,6 +81,11 @@ hipError_t launch_deep(const Dims& s, int k, const void* x, const void* W, const
                        const void* V, const float* rec_logit, const int32_t* perm,
                        const int32_t* offs, void* H, int32_t* path_out, int chunk,
                        hipStream_t st);
+
+// Copies the node rows that colmap[i] names (heap row p*N + n, or -1 for a
+// zero row) into packed[i], for i < rows.
+hipError_t launch_prune_pack(const void* W, const int32_t* colmap, void* packed, int rows, int d,
+                             hipStream_t st);
 
 // ---- decode (bf16, 1 <= T <= 64): one kernel for the whole layer ----
 // Workspace: H [T,K] bf16, fp32 K-chunk partials of y, per-slice counters.

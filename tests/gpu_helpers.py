@@ -37,20 +37,22 @@ def run(inp, algo="auto", split_level=-1, dev="cuda:0", variant=0, chunk_tokens=
     return to_f64(y), path.cpu().numpy()
 
 
-def check(inp, y_dev, path_dev, sample=None, nthreads=None, max_flip_frac=1e-3, variant=0):
+def check(inp, y_dev, path_dev, sample=None, nthreads=None, max_flip_frac=1e-3, variant=0,
+          leaf_alive=None):
     """Paths of all tokens against the oracle, y on `sample` token rows (all
     if None).  Returns a summary dict; raises AssertionError on failure."""
     s = inp.shape
     f = inp.as_f64()
     ref = oracle.forward(f["x"], f["W_node"], f["b_node"], f["V_node"], f["W_out"], want_y=False,
-                         want_records=True, nthreads=nthreads, variant=variant)
+                         want_records=True, nthreads=nthreads, variant=variant,
+                         leaf_alive=leaf_alive)
     cls = classify_paths(path_dev, ref, s.D)
     assert not cls["bad"], f"routing mismatches beyond near-ties: {cls['bad'][:5]}"
     assert cls["flips_near_tie"] <= max(2, max_flip_frac * s.T * s.P), cls["flips_near_tie"]
     rows = np.arange(s.T) if sample is None else np.asarray(sample)
     rows = rows[cls["tokens_ok"][rows]]
     ry = oracle.forward(f["x"][rows], f["W_node"], f["b_node"], f["V_node"], f["W_out"],
-                        nthreads=nthreads, variant=variant)
+                        nthreads=nthreads, variant=variant, leaf_alive=leaf_alive)
     np.testing.assert_array_equal(ry["path"], path_dev[rows])
     err = y_error(y_dev[rows], ry["y"])
     assert err["err"] <= TOL[s.dtype], f"y error {err} above {TOL[s.dtype]}"

@@ -5,6 +5,7 @@ import ctypes
 import os
 import re
 
+import numpy as np
 import pytest
 
 import sparse_tree_structured_amd as fff
@@ -196,3 +197,61 @@ def test_decode_workspace_covers_route(lib):
     st = lib.fff_route(ctypes.byref(s), ctypes.byref(fff.make_plan("decode")), FAKE, FAKE, FAKE,
                        FAKE, FAKE, FAKE, FAKE, 1 << 40, None)
     assert st == fff.ERROR_NOT_SUPPORTED
+
+
+def test_prune_table_size():
+    # Alive flags [P][N]; for PREFILL also the packed rows of the dense
+    # levels (at most P tiles of 256 columns) and their maps.
+    dec = _shape(T=8, d=2048, P=32, D=6, h=128)
+    assert fff.prune_table_size(dec) == 4096  # 32 * 127 bytes, rounded to 256
+    pre = _shape(T=16384, d=2048, P=32, D=6, h=128)
+    up = lambda v: (v + 255) // 256 * 256  # noqa: E731
+    expect = up(32 * 127) + up(32 * 127 * 2) + 3 * up(32 * 4) + up(32 * 256 * 4) + \
+        up(32 * 256 * 2048 * 2)
+    assert fff.prune_table_size(pre) == expect
+    split = fff.resolve_plan(pre, fff.make_plan("prefill", 4))
+    cols = (1 << 4) - 1
+    assert fff.prune_table_size(pre, split) == up(32 * 127) + up(32 * cols * 2) + \
+        3 * up(32 * 4) + up(32 * 256 * 4) + up(32 * 256 * 2048 * 2)
+
+
+def _prepare(lib, shape, mask, W=FAKE, table=FAKE, nbytes=1 << 40, out=True):
+    res = fff.Pruning()
+    m = np.ascontiguousarray(mask, dtype=np.uint8) if mask is not None else None
+    return lib.fff_prune_prepare(ctypes.byref(shape), None,
+                                 m.ctypes.data_as(ctypes.c_void_p) if m is not None else None, W,
+                                 table, nbytes, None, ctypes.byref(res) if out else None)
+
+
+def test_prune_prepare_validation(lib):
+    s = _shape(T=1000, d=128, P=3, D=4, h=64)
+    mask = np.ones((3, 16), np.uint8)
+    dead = mask.copy()
+    dead[1] = 0  # a tree with no alive leaf
+    assert _prepare(lib, s, dead) == fff.ERROR_INVALID_VALUE
+    assert _prepare(lib, s, None) == fff.ERROR_INVALID_VALUE
+    assert _prepare(lib, s, mask, W=None) == fff.ERROR_INVALID_VALUE
+    assert _prepare(lib, s, mask, table=None) == fff.ERROR_INVALID_VALUE
+    assert _prepare(lib, s, mask, table=FAKE + 16) == fff.ERROR_INVALID_VALUE
+    assert _prepare(lib, s, mask, out=False) == fff.ERROR_INVALID_VALUE
+    assert _prepare(lib, s, mask, nbytes=fff.prune_table_size(s) - 1) == fff.ERROR_WORKSPACE
+
+
+def test_forward_pruned_validation(lib):
+    s = _shape(T=1000, d=128, P=3, D=4, h=64)
+    plan = fff.resolve_plan(s, fff.make_plan("auto"))
+    assert plan.algo == fff.ALGO_PREFILL and plan.split_level == 5
+
+    def run(pr, pl=None):
+        return lib.fff_forward_pruned(ctypes.byref(s), ctypes.byref(pl) if pl else None,
+                                      ctypes.byref(pr) if pr is not None else None, FAKE, FAKE,
+                                      FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 40, None, None)
+
+    good = dict(table=FAKE, P=3, D=4, d=128, split_level=5, col_tiles=1)
+    assert run(None) == fff.ERROR_INVALID_VALUE
+    for bad in (dict(table=None), dict(table=FAKE + 8), dict(P=4), dict(D=3), dict(d=64),
+                dict(split_level=9), dict(col_tiles=4)):
+        assert run(fff.Pruning(**dict(good, **bad))) == fff.ERROR_INVALID_VALUE, bad
+    # A PREFILL plan must use the split level the table packed.
+    assert run(fff.Pruning(**dict(good, split_level=3))) == fff.ERROR_NOT_SUPPORTED
+    assert run(fff.Pruning(**good), fff.make_plan("prefill", 3)) == fff.ERROR_NOT_SUPPORTED
