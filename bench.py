@@ -41,6 +41,9 @@ def parse():
     ap.add_argument("--variant", default="fff", choices=["fff", "post"],
                     help="GELU per node (fff) or on the summed tree output (post)")
     ap.add_argument("--rotate", type=int, default=0, help="input sets (0 = by footprint)")
+    ap.add_argument("--prune", type=float, default=0.0,
+                    help="statically prune this fraction of each tree's paths (seeded random "
+                         "leaf mask) and run fff_forward_pruned")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="oracle sample budget")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--depth-sweep", action="store_true",
@@ -312,8 +315,26 @@ def main():
     path = torch.empty((shape.T, shape.P), dtype=torch.int32, device=dev)
     stream = torch.cuda.current_stream()
 
+    prunings = None
+    if args.prune > 0:
+        # Each tree keeps at least one path; one table per input set.
+        rng = np.random.default_rng(0)
+        mask = (rng.random((shape.P, 1 << shape.D)) >= args.prune).astype(np.uint8)
+        mask[np.arange(shape.P), rng.integers(0, 1 << shape.D, size=shape.P)] = 1
+        prunings = [fff.prune_prepare(mask, st[1], st[3], algo=plan.algo,
+                                      split_level=plan.split_level,
+                                      chunk_tokens=plan.chunk_tokens, T=shape.T)
+                    for st in sets]
+        torch.cuda.synchronize()
+
     def step(i, ev=None):
         x, W, b, V, Wo = sets[i % rotate]
+        if prunings is not None:
+            fff.forward_pruned(x, W, b, V, Wo, prunings[i % rotate][0], algo=plan.algo,
+                               split_level=plan.split_level, chunk_tokens=plan.chunk_tokens,
+                               workspace=ws, y=y, path_out=path, stream=stream, events=ev,
+                               variant=variant)
+            return
         fff.forward(x, W, b, V, Wo, algo=plan.algo, split_level=plan.split_level,
                     chunk_tokens=plan.chunk_tokens, workspace=ws, y=y, path_out=path, stream=stream,
                     events=ev, variant=variant)
@@ -397,7 +418,12 @@ def main():
                    "algo": fff.algo_name(plan.algo),
                    "split_level": plan.split_level, "chunk_tokens": plan.chunk_tokens,
                    "rotated_sets": rotate,
-                   "parallelism": "none (1 GPU)"},
+                   "parallelism": "none (1 GPU)",
+                   **({"pruning": {"ratio": args.prune, "alive_leaves": float(mask.mean()),
+                                   "col_tiles": int(prunings[0][0].col_tiles),
+                                   "unpruned_col_tiles": -(-(shape.P << plan.split_level) // 256)
+                                   if plan.algo == fff.ALGO_PREFILL else None}}
+                      if prunings is not None else {})},
         "roofline": roof,
         "layer": {"F_alg": f_route + f_proj, "B_alg": b_alg, "U": U,
                   "t_roof_us": t_roof * 1e6, "roof_frac": t_roof / (ms_step * 1e-3),

@@ -169,14 +169,14 @@ bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) %
 // dense levels (0: alive flags only).  At most P tiles: a tree has fewer
 // than 256 columns of levels < L <= 8.
 //   alive       [P][N] uint8
-//   colidx      [P][2^L - 1] int16   packed column of node n within its tree, -1 pruned
 //   tree_base   [P] int32            first column of tree p within its tile
 //   tile_first  [P] int32, tile_count [P] int32
 //   colmap      [P * 256] int32      source row p*N + n of each packed column, -1 = zero row
+//   colinfo     [P * 256] uint32     children of each packed column (tile columns, alive bits)
 //   packed      [P * 256][d] bf16
 struct PruneLayout {
-  size_t alive = 0, colidx = 0, tree_base = 0, tile_first = 0, tile_count = 0, colmap = 0,
-         packed = 0, total = 0;
+  size_t alive = 0, tree_base = 0, tile_first = 0, tile_count = 0, colmap = 0,
+         colinfo = 0, packed = 0, total = 0;
 };
 
 PruneLayout prune_layout(const Dims& s, int L) {
@@ -185,9 +185,6 @@ PruneLayout prune_layout(const Dims& s, int L) {
   PL.alive = off;
   off = align_up(off + size_t(s.P) * size_t(s.N));
   if (L > 0) {
-    const size_t cols = (size_t(1) << L) - 1;
-    PL.colidx = off;
-    off = align_up(off + size_t(s.P) * cols * sizeof(int16_t));
     PL.tree_base = off;
     off = align_up(off + size_t(s.P) * sizeof(int32_t));
     PL.tile_first = off;
@@ -196,6 +193,8 @@ PruneLayout prune_layout(const Dims& s, int L) {
     off = align_up(off + size_t(s.P) * sizeof(int32_t));
     PL.colmap = off;
     off = align_up(off + size_t(s.P) * 256 * sizeof(int32_t));
+    PL.colinfo = off;
+    off = align_up(off + size_t(s.P) * 256 * sizeof(uint32_t));
     PL.packed = off;
     off = align_up(off + size_t(s.P) * 256 * size_t(s.d) * 2);
   }
@@ -422,17 +421,34 @@ fff_status_t fff_prune_prepare(const fff_shape_t* shape, const fff_plan_t* plan,
       used += cnt;
     }
   }
+  // Children of every packed column: their columns in the tile (when they
+  // are dense too) and whether they are alive.
+  std::vector<uint32_t> colinfo(size_t(s.P) * 256, 0);
+  for (size_t c = 0; c < colmap.size(); ++c) {
+    if (colmap[c] < 0) continue;
+    const int64_t t = colmap[c] / N;
+    const int64_t n = colmap[c] - t * N;
+    if (n >= first_leaf) continue;  // a leaf: no children
+    uint32_t info = 0;
+    for (int r = 0; r < 2; ++r) {
+      const int64_t ch = 2 * n + 1 + r;
+      if (!alive[t * N + ch]) continue;
+      info |= 1u << (18 + r);
+      if (ch < cols) info |= uint32_t(tree_base[t] + colidx[t * cols + ch]) << (9 * r);
+    }
+    colinfo[c] = info;
+  }
   char* tb = static_cast<char*>(table);
   auto put = [&](size_t off, const void* src, size_t n) {
     return n == 0 || hipMemcpyAsync(tb + off, src, n, hipMemcpyHostToDevice, stream) == hipSuccess;
   };
   bool ok = put(PL.alive, alive.data(), alive.size());
   if (L > 0) {
-    ok = ok && put(PL.colidx, colidx.data(), colidx.size() * sizeof(int16_t)) &&
-         put(PL.tree_base, tree_base.data(), tree_base.size() * sizeof(int32_t)) &&
+    ok = ok && put(PL.tree_base, tree_base.data(), tree_base.size() * sizeof(int32_t)) &&
          put(PL.tile_first, tile_first.data(), tile_first.size() * sizeof(int32_t)) &&
          put(PL.tile_count, tile_count.data(), tile_count.size() * sizeof(int32_t)) &&
          put(PL.colmap, colmap.data(), colmap.size() * sizeof(int32_t)) &&
+         put(PL.colinfo, colinfo.data(), colinfo.size() * sizeof(uint32_t)) &&
          fff::launch_prune_pack(W_node, reinterpret_cast<const int32_t*>(tb + PL.colmap),
                                 tb + PL.packed, tiles * 256, s.d, stream) == hipSuccess;
   }
@@ -470,10 +486,11 @@ fff_status_t fff_forward_pruned(const fff_shape_t* shape, const fff_plan_t* plan
   fff::PruneView pv{};
   pv.alive = reinterpret_cast<const uint8_t*>(tb + PL.alive);
   if (pruning->split_level > 0) {
-    pv.colidx = reinterpret_cast<const int16_t*>(tb + PL.colidx);
     pv.tree_base = reinterpret_cast<const int32_t*>(tb + PL.tree_base);
     pv.tile_first = reinterpret_cast<const int32_t*>(tb + PL.tile_first);
     pv.tile_count = reinterpret_cast<const int32_t*>(tb + PL.tile_count);
+    pv.colmap = reinterpret_cast<const int32_t*>(tb + PL.colmap);
+    pv.colinfo = reinterpret_cast<const uint32_t*>(tb + PL.colinfo);
     pv.W_packed = reinterpret_cast<const uint16_t*>(tb + PL.packed);
   }
   pv.L = pruning->split_level;

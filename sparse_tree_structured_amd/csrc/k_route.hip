@@ -71,7 +71,7 @@ struct NodeRowLoader {
 
 // Walk epilogue shared by the top-level kernels.  acc holds the tile's
 // logits without bias (transposed-block layout of mfma_tile.hpp); `lg` is
-// LDS of at least WM * (BN + 4) floats, free for reuse.
+// LDS of at least WM * (BN + 4) + 2 * BN floats, free for reuse.
 template <class C>
 __device__ __forceinline__ void top_walk_epilogue(const f32x16_t (&acc)[C::kTm][C::kTn], float* lg,
                                                   const uint16_t* __restrict__ b,
@@ -94,6 +94,23 @@ __device__ __forceinline__ void top_walk_epilogue(const f32x16_t (&acc)[C::kTm][
   const int tn = n0 / C::BN;
   const int tpt = pv.alive ? pv.tile_count[tn] : C::BN >> L;
   const int p_base = pv.alive ? pv.tile_first[tn] : n0 >> L;
+  // Per column of the tile: its node's bias and, pruned, its children's
+  // columns and alive flags; staged once so that the walks below read no
+  // global memory per level (visible after the first pass's barrier).
+  float* bias_s = lg + kRows * kPitch;
+  uint32_t* info_s = reinterpret_cast<uint32_t*>(bias_s + C::BN);
+  for (int c = tid; c < C::BN; c += C::kThreads) {
+    int64_t g = -1;  // heap row p*N + n of column c
+    if (pv.alive) {
+      g = pv.colmap[n0 + c];
+      info_s[c] = pv.colinfo[n0 + c];
+    } else {
+      const int p = (n0 + c) >> L;
+      const int n = (n0 + c) & (cpt - 1);
+      if (p < P && n < cpt - 1) g = static_cast<int64_t>(p) * N + n;
+    }
+    bias_s[c] = g >= 0 ? bf16_to_f32(b[g]) : 0.0f;
+  }
 #pragma unroll 1
   for (int half = 0; half < C::kWavesM; ++half) {
     if (wm == half) {
@@ -117,39 +134,29 @@ __device__ __forceinline__ void top_walk_epilogue(const f32x16_t (&acc)[C::kTm][
       const int t = m0 + half * kRows + tr;
       const int p = p_base + tp;
       if (t >= T || p >= P) continue;
-      const uint16_t* bp = b + static_cast<int64_t>(p) * N;
       float* out = rec_logit + (static_cast<int64_t>(p) * T + t) * L;
+      const float* row = lg + tr * kPitch;
       int n = 0;
       if (!pv.alive) {
-        const float* row = lg + tr * kPitch + tp * cpt;
+        const int c0 = tp * cpt;  // node n at column c0 + n
         for (int level = 0; level < L; ++level) {
-          const float a = row[n] + bf16_to_f32(bp[n]);
+          const float a = row[c0 + n] + bias_s[c0 + n];
           out[level] = a;
           if (level < D) n = 2 * n + 1 + go_right(a);
         }
       } else {
-        // Packed columns: node n sits at column colidx[n] of its tree (the
-        // root first).  The bias, both children's alive flags and their
-        // columns are read together, one round trip per level.
-        const float* row = lg + tr * kPitch + pv.tree_base[p];
-        const int16_t* ci = pv.colidx + static_cast<int64_t>(p) * (cpt - 1);
-        const uint8_t* al = pv.alive + static_cast<int64_t>(p) * N;
-        int col = 0;
+        // Packed columns: the root at the tree's base column, each node's
+        // children where its column info points.
+        int c = pv.tree_base[p];
         for (int level = 0; level < L; ++level) {
-          const float bn = bf16_to_f32(bp[n]);
-          const bool deeper = level < D;
-          const bool in_tile = level + 1 < L;
-          const int alive_l = deeper ? al[2 * n + 1] : 0;
-          const int alive_r = deeper ? al[2 * n + 2] : 0;
-          const int col_l = in_tile ? ci[2 * n + 1] : 0;
-          const int col_r = in_tile ? ci[2 * n + 2] : 0;
-          const float a = row[col] + bn;
+          const float a = row[c] + bias_s[c];
           out[level] = a;
-          if (deeper) {
+          if (level < D) {
+            const uint32_t info = info_s[c];
             int r = go_right(a);
-            if (!(r ? alive_r : alive_l)) r ^= 1;  // pruned child: its sibling
+            if (!((info >> (18 + r)) & 1)) r ^= 1;  // pruned child: its sibling
             n = 2 * n + 1 + r;
-            col = r ? col_r : col_l;
+            c = (info >> (9 * r)) & 511;
           }
         }
       }
@@ -161,8 +168,9 @@ __device__ __forceinline__ void top_walk_epilogue(const f32x16_t (&acc)[C::kTm][
 
 template <class C>
 constexpr size_t top_lds_bytes() {
-  return C::kLdsBytes > size_t(C::WM) * (C::BN + 4) * 4 ? C::kLdsBytes
-                                                        : size_t(C::WM) * (C::BN + 4) * 4;
+  // Main-loop stages, or the epilogue's logits plus its per-column arrays.
+  constexpr size_t epi = size_t(C::WM) * (C::BN + 4) * 4 + size_t(C::BN) * 8;
+  return C::kLdsBytes > epi ? C::kLdsBytes : epi;
 }
 
 template <class C>

@@ -16,10 +16,12 @@ namespace fff {
 // tiles (no tree straddles a tile), so the dense product streams only them.
 struct PruneView {
   const uint8_t* alive;        // [P][N] 1 = alive
-  const int16_t* colidx;       // [P][2^L - 1] column of node n among its tree's packed ones, -1 pruned
   const int32_t* tree_base;    // [P] first packed column of tree p within its tile
   const int32_t* tile_first;   // [col_tiles] first tree of each tile
   const int32_t* tile_count;   // [col_tiles] trees in each tile
+  const int32_t* colmap;       // [col_tiles * 256] heap row p*N + n of each packed column, -1 none
+  const uint32_t* colinfo;     // [col_tiles * 256] children of each packed column: bits 0-8 and
+                               // 9-17 their tile columns (dense levels), bits 18 / 19 alive
   const uint16_t* W_packed;    // [col_tiles * 256][d] packed rows (zero rows fill a tile)
   int L;                       // dense levels packed (0: none)
   int col_tiles;

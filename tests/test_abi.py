@@ -206,13 +206,12 @@ def test_prune_table_size():
     assert fff.prune_table_size(dec) == 4096  # 32 * 127 bytes, rounded to 256
     pre = _shape(T=16384, d=2048, P=32, D=6, h=128)
     up = lambda v: (v + 255) // 256 * 256  # noqa: E731
-    expect = up(32 * 127) + up(32 * 127 * 2) + 3 * up(32 * 4) + up(32 * 256 * 4) + \
-        up(32 * 256 * 2048 * 2)
+    # alive flags, tree bases, tile first/count, column map and info, packed rows
+    expect = up(32 * 127) + 3 * up(32 * 4) + 2 * up(32 * 256 * 4) + up(32 * 256 * 2048 * 2)
     assert fff.prune_table_size(pre) == expect
     split = fff.resolve_plan(pre, fff.make_plan("prefill", 4))
-    cols = (1 << 4) - 1
-    assert fff.prune_table_size(pre, split) == up(32 * 127) + up(32 * cols * 2) + \
-        3 * up(32 * 4) + up(32 * 256 * 4) + up(32 * 256 * 2048 * 2)
+    assert split.split_level == 4
+    assert fff.prune_table_size(pre, split) == expect  # bounded by P tiles either way
 
 
 def _prepare(lib, shape, mask, W=FAKE, table=FAKE, nbytes=1 << 40, out=True):
