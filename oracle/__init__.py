@@ -67,6 +67,10 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     lib.fffo_forward.argtypes = [ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                  ctypes.c_int, ctypes.c_int, dp, dp, dp, dp, dp, ip, up, dp, dp, ip,
                                  dp, dp, ip, ctypes.c_int]
+    lib.fffo_backward.restype = ctypes.c_int
+    lib.fffo_backward.argtypes = [ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                  ctypes.c_int, ctypes.c_int, dp, dp, dp, dp, dp, up, dp, dp, dp,
+                                  dp, dp, dp, ctypes.c_int]
     _LIBS[path] = lib
     return lib
 
@@ -148,6 +152,45 @@ def forward(x: np.ndarray, W_node: np.ndarray, b_node: np.ndarray, V_node: np.nd
                           _dptr(V_node), _dptr(W_out), _iptr(forced), alive_ptr, _dptr(out.get("y")), _dptr(out.get("H")),
                           _iptr(out["path"]), _dptr(out.get("rec_a")), _dptr(out.get("rec_thr")),
                           _iptr(out.get("rec_node")), int(nthreads or default_threads()))
+    if rc != 0:
+        raise ValueError("oracle rejected the shape, variant or mask")
+    return out
+
+
+def backward(x: np.ndarray, W_node: np.ndarray, b_node: np.ndarray, V_node: np.ndarray,
+             W_out: np.ndarray, dy: np.ndarray, variant: int = 0,
+             leaf_alive: Optional[np.ndarray] = None, nthreads: Optional[int] = None,
+             lib: Optional[ctypes.CDLL] = None) -> Dict[str, np.ndarray]:
+    """Gradients of sum(y * dy) with the forward's paths held fixed.
+
+    Returns float64 ``dx`` [T,d], ``dW_node`` [P,N,d], ``db_node`` [P,N],
+    ``dV_node`` [P,N,h] and ``dW_out`` [P*h,d].
+    """
+    lib = lib or load()
+    x = np.ascontiguousarray(x, dtype=np.float64)
+    W_node = np.ascontiguousarray(W_node, dtype=np.float64)
+    b_node = np.ascontiguousarray(b_node, dtype=np.float64)
+    V_node = np.ascontiguousarray(V_node, dtype=np.float64)
+    W_out = np.ascontiguousarray(W_out, dtype=np.float64)
+    dy = np.ascontiguousarray(dy, dtype=np.float64)
+    T, d = x.shape
+    P, N, _ = W_node.shape
+    h = V_node.shape[2]
+    D = int(round(np.log2(N + 1))) - 1
+    if dy.shape != (T, d) or W_out.shape != (P * h, d):
+        raise ValueError("inconsistent shapes")
+    alive_ptr = None
+    if leaf_alive is not None:
+        leaf_alive = np.ascontiguousarray(leaf_alive, dtype=np.uint8)
+        if leaf_alive.shape != (P, 1 << D):
+            raise ValueError("leaf_alive must be [P, 2^D]")
+        alive_ptr = leaf_alive.ctypes.data_as(ctypes.POINTER(ctypes.c_uint8))
+    out = {"dx": np.empty((T, d)), "dW_node": np.empty((P, N, d)), "db_node": np.empty((P, N)),
+           "dV_node": np.empty((P, N, h)), "dW_out": np.empty((P * h, d))}
+    rc = lib.fffo_backward(T, d, P, D, h, int(variant), _dptr(x), _dptr(W_node), _dptr(b_node),
+                           _dptr(V_node), _dptr(W_out), alive_ptr, _dptr(dy), _dptr(out["dx"]),
+                           _dptr(out["dW_node"]), _dptr(out["db_node"]), _dptr(out["dV_node"]),
+                           _dptr(out["dW_out"]), int(nthreads or default_threads()))
     if rc != 0:
         raise ValueError("oracle rejected the shape, variant or mask")
     return out

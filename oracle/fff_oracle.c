@@ -1,6 +1,6 @@
 /*
  * fff_oracle.c -- plain CPU reference for the Fast FeedForward (FFF) layer
- * forward pass.  TEST INFRASTRUCTURE ONLY: the tests, the smoke check and the
+ * forward and backward passes.  TEST INFRASTRUCTURE ONLY: the tests, the smoke check and the
  * benchmark's CPU-baseline leg may load it; the HIP library never does, and
  * the two share no code.
  *
@@ -212,6 +212,175 @@ int fffo_forward(int64_t T, int d, int P, int D, int h, int variant,
         }
         free(Ht);
     }
+    free(alive);
+    return FFFO_OK;
+}
+
+/*
+ * Backward pass.  The paths are those of the forward pass (hard decisions,
+ * no gradient through them: explainer page, section 3.B, describes
+ * gradients that reach only the visited nodes); every visited node's output
+ * is differentiated with the routing held fixed.  With f the scalar
+ * sum over t, c of y[t,c] * dy[t,c]:
+ *
+ *   dH[t,k]        = sum_c dy[t,c] Wout[k,c]
+ *   dWout[k,c]     = sum_t H[t,k] dy[t,c]
+ *   FFF (variant 0), per visited node n at level l of tree p:
+ *     da           = GELU'(a) * sum_j dH[t, p*h+j] V[p,n,j]
+ *     dV[p,n,j]   += GELU(a) * dH[t, p*h+j]
+ *   FFF-post (variant 1), with s_j = sum over the path of a * V[p,n,j]:
+ *     ds_j         = GELU'(s_j) * dH[t, p*h+j]
+ *     da           = sum_j ds_j V[p,n,j]
+ *     dV[p,n,j]   += a * ds_j
+ *   then  db[p,n] += da;  dW[p,n,:] += da * x[t,:];  dx[t,:] += da * W[p,n,:].
+ *
+ * GELU'(a) of the tanh form, u = sqrt(2/pi)(a + 0.044715 a^3):
+ *   0.5 (1 + tanh u) + 0.5 a (1 - tanh^2 u) sqrt(2/pi) (1 + 3 * 0.044715 a^2).
+ *
+ * Outputs (all float64, fully overwritten): dx [T,d], dW [P,N,d], db [P,N],
+ * dV [P,N,h], dWout [P*h,d].  Sums over tokens run in ascending t.
+ * Returns 0, or 1 for a bad argument (as fffo_forward).
+ */
+static double gelu_tanh_grad(double a)
+{
+    const double k0 = 0.7978845608028654;
+    const double k1 = 0.044715;
+    const double th = tanh(k0 * a * (1.0 + k1 * a * a));
+    return 0.5 * (1.0 + th) + 0.5 * a * (1.0 - th * th) * k0 * (1.0 + 3.0 * k1 * a * a);
+}
+
+int fffo_backward(int64_t T, int d, int P, int D, int h, int variant,
+                  const double *x, const double *W, const double *b, const double *V,
+                  const double *Wout, const uint8_t *leaf_alive, const double *dy,
+                  double *dx, double *dW, double *db, double *dV, double *dWout, int nthreads)
+{
+    if (T < 0 || d <= 0 || P <= 0 || D < 0 || D > 24 || h <= 0 || variant < 0 || variant > 1)
+        return FFFO_BAD_ARG;
+    const int64_t N = ((int64_t)1 << (D + 1)) - 1;
+    const int64_t K = (int64_t)P * h;
+    const int L = D + 1;
+    if (nthreads <= 0)
+        nthreads = 1;
+    uint8_t *alive = NULL;
+    if (leaf_alive) {
+        alive = (uint8_t *)malloc((size_t)(P * N));
+        if (!alive)
+            abort();
+        for (int p = 0; p < P; ++p) {
+            alive_nodes(leaf_alive + ((int64_t)p << D), D, alive + p * N);
+            if (!alive[p * N]) {
+                free(alive);
+                return FFFO_BAD_ARG;
+            }
+        }
+    }
+    /* Forward records (the forward walk itself): visited nodes and logits
+     * [T,P,L], H [T,K], and for FFF-post the summed pre-activation S [T,K]. */
+    int32_t *node = (int32_t *)calloc((size_t)(T * P * L + 1), sizeof(int32_t));
+    double *la = (double *)calloc((size_t)(T * P * L + 1), sizeof(double));
+    double *H = (double *)malloc(sizeof(double) * (size_t)(T * K + 1));
+    double *S = (double *)malloc(sizeof(double) * (size_t)(T * K + 1));
+    double *dH = (double *)malloc(sizeof(double) * (size_t)(T * K + 1));
+    double *da = (double *)malloc(sizeof(double) * (size_t)(T * P * L + 1));
+    if (!node || !la || !H || !S || !dH || !da)
+        abort();
+
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nthreads)
+    for (int64_t t = 0; t < T; ++t) {
+        const double *xt = x + t * d;
+        for (int p = 0; p < P; ++p) {
+            const double *Vp = V + (int64_t)p * N * h;
+            const int64_t tp = t * P + p;
+            walk_tree(xt, 0.0, W + (int64_t)p * N * d, b + (int64_t)p * N, Vp, d, D, h, variant,
+                      -1, alive ? alive + p * N : NULL, H + t * K + (int64_t)p * h,
+                      la + tp * L, NULL, node + tp * L);
+            double *St = S + t * K + (int64_t)p * h;
+            for (int j = 0; j < h; ++j) {
+                St[j] = 0.0;
+                for (int level = 0; level <= D; ++level)
+                    St[j] += la[tp * L + level] * Vp[(int64_t)node[tp * L + level] * h + j];
+            }
+        }
+        /* dH, then da and dx for this token. */
+        const double *dyt = dy + t * d;
+        for (int64_t k = 0; k < K; ++k)
+            dH[t * K + k] = dot(dyt, Wout + k * d, d);
+        double *dxt = dx + t * d;
+        for (int c = 0; c < d; ++c)
+            dxt[c] = 0.0;
+        for (int p = 0; p < P; ++p) {
+            const double *Vp = V + (int64_t)p * N * h;
+            const double *dHp = dH + t * K + (int64_t)p * h;
+            const double *Sp = S + t * K + (int64_t)p * h;
+            const int64_t tp = t * P + p;
+            for (int level = 0; level <= D; ++level) {
+                const int64_t n = node[tp * L + level];
+                double g = 0.0;
+                for (int j = 0; j < h; ++j) {
+                    const double dj = variant == 1 ? gelu_tanh_grad(Sp[j]) * dHp[j] : dHp[j];
+                    g += dj * Vp[n * h + j];
+                }
+                const double dal = variant == 1 ? g : g * gelu_tanh_grad(la[tp * L + level]);
+                da[tp * L + level] = dal;
+                const double *w = W + ((int64_t)p * N + n) * d;
+                for (int c = 0; c < d; ++c)
+                    dxt[c] += dal * w[c];
+            }
+        }
+    }
+
+    /* Node gradients, one tree per worker, tokens in ascending order. */
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nthreads)
+    for (int p = 0; p < P; ++p) {
+        double *dWp = dW + (int64_t)p * N * d;
+        double *dbp = db + (int64_t)p * N;
+        double *dVp = dV + (int64_t)p * N * h;
+        for (int64_t i = 0; i < N * d; ++i)
+            dWp[i] = 0.0;
+        for (int64_t i = 0; i < N; ++i)
+            dbp[i] = 0.0;
+        for (int64_t i = 0; i < N * h; ++i)
+            dVp[i] = 0.0;
+        for (int64_t t = 0; t < T; ++t) {
+            const int64_t tp = t * P + p;
+            const double *xt = x + t * d;
+            const double *dHp = dH + t * K + (int64_t)p * h;
+            const double *Sp = S + t * K + (int64_t)p * h;
+            for (int level = 0; level <= D; ++level) {
+                const int64_t n = node[tp * L + level];
+                const double dal = da[tp * L + level];
+                const double a = la[tp * L + level];
+                dbp[n] += dal;
+                for (int c = 0; c < d; ++c)
+                    dWp[n * d + c] += dal * xt[c];
+                for (int j = 0; j < h; ++j) {
+                    const double cj = variant == 1 ? a * gelu_tanh_grad(Sp[j]) * dHp[j]
+                                                   : gelu_tanh(a) * dHp[j];
+                    dVp[n * h + j] += cj;
+                }
+            }
+        }
+    }
+
+    /* dWout[k,c] = sum_t H[t,k] dy[t,c]. */
+#pragma omp parallel for schedule(static) num_threads(nthreads)
+    for (int64_t k = 0; k < K; ++k) {
+        double *row = dWout + k * d;
+        for (int c = 0; c < d; ++c)
+            row[c] = 0.0;
+        for (int64_t t = 0; t < T; ++t) {
+            const double hk = H[t * K + k];
+            const double *dyt = dy + t * d;
+            for (int c = 0; c < d; ++c)
+                row[c] += hk * dyt[c];
+        }
+    }
+    free(node);
+    free(la);
+    free(H);
+    free(S);
+    free(dH);
+    free(da);
     free(alive);
     return FFFO_OK;
 }

@@ -497,8 +497,97 @@ def pin_prune_reductions(lib):
         np.testing.assert_array_equal(same[k], base[k])
 
 
+def _fd_layer(rng, T, d, P, D, h, margin=0.05):
+    """A random tiny layer whose logits are all at least `margin` from 0."""
+    for _ in range(1000):
+        L = rand_layer(rng, T, d, P, D, h)
+        A = np.einsum("td,pnd->tpn", L["x"], L["W_node"]) + L["b_node"][None]
+        if np.abs(A).min() > margin:
+            return L
+    raise AssertionError("no layer with logits away from zero")
+
+
+def _check_fd(lib, L, dy, variant=0, leaf_alive=None, eps=1e-6):
+    g = oracle.backward(**L, dy=dy, variant=variant, leaf_alive=leaf_alive, lib=lib, nthreads=1)
+    base_path = oracle.forward(**L, variant=variant, leaf_alive=leaf_alive, lib=lib,
+                               nthreads=1)["path"]
+    names = {"x": "dx", "W_node": "dW_node", "b_node": "db_node", "V_node": "dV_node",
+             "W_out": "dW_out"}
+    for key, gname in names.items():
+        arr = L[key]
+        fd = np.zeros_like(arr)
+        for idx in np.ndindex(arr.shape):
+            vals = []
+            for sgn in (1.0, -1.0):
+                L2 = dict(L)
+                L2[key] = arr.copy()
+                L2[key][idx] += sgn * eps
+                r = oracle.forward(**L2, variant=variant, leaf_alive=leaf_alive, lib=lib,
+                                   nthreads=1)
+                np.testing.assert_array_equal(r["path"], base_path)
+                vals.append(float((r["y"] * dy).sum()))
+            fd[idx] = (vals[0] - vals[1]) / (2 * eps)
+        np.testing.assert_allclose(g[gname], fd, rtol=1e-5, atol=1e-7, err_msg=gname)
+
+
+def pin_backward_finite_differences(lib):
+    rng = np.random.default_rng(90)
+    for variant in (0, 1):
+        L = _fd_layer(rng, 3, 4, 2, 2, 3)
+        dy = rng.standard_normal((3, 4))
+        _check_fd(lib, L, dy, variant=variant)
+    # Pruned trees: the forced steps are part of the fixed paths.
+    L = _fd_layer(rng, 4, 3, 2, 3, 2)
+    alive = np.array([[1, 0, 0, 1, 1, 0, 0, 0], [0, 0, 0, 0, 1, 1, 0, 1]], np.uint8)
+    _check_fd(lib, L, rng.standard_normal((4, 3)), variant=0, leaf_alive=alive)
+    _check_fd(lib, L, rng.standard_normal((4, 3)), variant=1, leaf_alive=alive)
+
+
+def pin_backward_dense_autograd(lib):
+    """Depth 0 is a dense layer: torch autograd in float64 gives every
+    gradient (both variants)."""
+    rng = np.random.default_rng(91)
+    T, d, P, h = 7, 5, 4, 3
+    L = rand_layer(rng, T, d, P, 0, h)
+    dy = rng.standard_normal((T, d))
+    for variant in (0, 1):
+        t = {k: torch.from_numpy(L[k].copy()).requires_grad_(True) for k in L}
+        logits = torch.nn.functional.linear(t["x"], t["W_node"][:, 0, :], t["b_node"][:, 0])
+        if variant == 0:
+            hid = torch.nn.functional.gelu(logits, approximate="tanh")[:, :, None] * \
+                t["V_node"][:, 0, :][None]
+        else:
+            hid = torch.nn.functional.gelu(logits[:, :, None] * t["V_node"][:, 0, :][None],
+                                           approximate="tanh")
+        y = hid.reshape(T, P * h) @ t["W_out"]
+        (y * torch.from_numpy(dy)).sum().backward()
+        g = oracle.backward(**L, dy=dy, variant=variant, lib=lib, nthreads=2)
+        for key, gname in (("x", "dx"), ("W_node", "dW_node"), ("b_node", "db_node"),
+                           ("V_node", "dV_node"), ("W_out", "dW_out")):
+            _close(g[gname], t[key].grad.numpy(), rtol=1e-11, atol=1e-12)
+
+
+def pin_backward_linear_in_dy(lib):
+    rng = np.random.default_rng(92)
+    L = rand_layer(rng, 9, 6, 3, 4, 5)
+    dy1, dy2 = rng.standard_normal((2, 9, 6))
+    g1 = oracle.backward(**L, dy=dy1, lib=lib)
+    g2 = oracle.backward(**L, dy=dy2, lib=lib)
+    g3 = oracle.backward(**L, dy=dy1 - 2.0 * dy2, lib=lib)
+    for k in g1:
+        _close(g3[k], g1[k] - 2.0 * g2[k], rtol=1e-10, atol=1e-11)
+    # Nodes off every path get no gradient.
+    paths = oracle.forward(**L, lib=lib)["path"]
+    visited = np.zeros(L["b_node"].shape, bool)
+    for t in range(9):
+        for p in range(3):
+            visited[p, ancestors_of_leaf(int(paths[t, p]), 4)] = True
+    assert (g1["db_node"][~visited] == 0).all() and (g1["dW_node"][~visited] == 0).all()
+
+
 ALL_PINS = [pin_brute_force, pin_hand_routing, pin_zero_ties, pin_negative_bias,
             pin_visit_count_table4, pin_depth0_dense, pin_forced_paths, pin_invariants,
             pin_tie_threshold, pin_post_brute_force, pin_post_hand_routing,
             pin_post_closed_forms, pin_post_routing_unchanged, pin_prune_brute_force,
-            pin_prune_reductions]
+            pin_prune_reductions, pin_backward_finite_differences, pin_backward_dense_autograd,
+            pin_backward_linear_in_dy]
