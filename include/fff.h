@@ -248,6 +248,39 @@ fff_status_t fff_forward_pruned(const fff_shape_t *shape, const fff_plan_t *plan
                                 size_t workspace_bytes, hipStream_t stream,
                                 const fff_stage_events_t *events);
 
+/*
+ * Backward pass
+ * -------------
+ * Gradients of f = sum over t, c of y[t,c] * dy[t,c] with every token's
+ * paths held as the forward pass takes them: the sign decision has no
+ * gradient (the pages name no estimator) and only visited nodes receive one
+ * (explainer page, section 3.B).  Per token t, tree p and visited node n
+ * with logit a, dH = dy . W_out^T:
+ *   FFF       da = GELU'(a) (dH_p . v_n),           dV_n += GELU(a) dH_p
+ *   FFF-post  s = sum over the path of a v_n,      ds = GELU'(s) * dH_p,
+ *             da = ds . v_n,                        dV_n += a ds
+ *   db_n += da,  dW_n += da x_t,  dx_t += da w_n,   dW_out = H^T dy
+ * (GELU' of the tanh form).  Not for pruned trees.
+ *
+ *   dy        [T,d] dtype (device)
+ *   dx        [T,d] dtype out
+ *   dW_node   [P,N,d] float32 out    db_node [P,N] float32 out
+ *   dV_node   [P,N,h] float32 out    dW_out  [P*h,d] float32 out
+ * Every output is overwritten (nodes off every path get 0).  Plans: GENERIC
+ * (any shape and dtype) or PREFILL (bf16, every level dense: D+1 <= 8,
+ * d % 64 == 0, h % 64 == 0, P*2^(D+1) % 64 == 0); AUTO picks PREFILL when the
+ * shape allows; DECODE and split PREFILL plans are FFF_ERROR_NOT_SUPPORTED.
+ * Sums over tokens use float32 atomics in some kernels, so results may
+ * differ in the last bits between calls.  Workspace: fff_backward_workspace_size.
+ */
+fff_status_t fff_backward_workspace_size(const fff_shape_t *shape, const fff_plan_t *plan,
+                                         size_t *bytes);
+fff_status_t fff_backward(const fff_shape_t *shape, const fff_plan_t *plan, const void *x,
+                          const void *W_node, const void *b_node, const void *V_node,
+                          const void *W_out, const void *dy, void *dx, float *dW_node,
+                          float *db_node, float *dV_node, float *dW_out, void *workspace,
+                          size_t workspace_bytes, hipStream_t stream);
+
 /* Static, human-readable text for a status code. */
 const char *fff_status_string(fff_status_t status);
 

@@ -68,7 +68,8 @@ class FFFError(RuntimeError):
 
 EXPORTS = ("fff_plan_default", "fff_plan_resolve", "fff_workspace_size", "fff_forward",
            "fff_route", "fff_project", "fff_status_string", "fff_algo_name",
-           "fff_prune_table_size", "fff_prune_prepare", "fff_forward_pruned")
+           "fff_prune_table_size", "fff_prune_prepare", "fff_forward_pruned",
+           "fff_backward_workspace_size", "fff_backward")
 
 _lib: Optional[ctypes.CDLL] = None
 
@@ -97,13 +98,15 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.fff_prune_prepare.argtypes = [SP, PP, vp, vp, vp, sz, vp, PrP]
     lib.fff_forward_pruned.argtypes = [SP, PP, PrP, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp,
                                        ctypes.POINTER(StageEvents)]
+    lib.fff_backward_workspace_size.argtypes = [SP, PP, ctypes.POINTER(sz)]
+    lib.fff_backward.argtypes = [SP, PP, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.fff_status_string.argtypes = [ctypes.c_int]
     lib.fff_status_string.restype = ctypes.c_char_p
     lib.fff_algo_name.argtypes = [ctypes.c_int32]
     lib.fff_algo_name.restype = ctypes.c_char_p
     for name in ("fff_plan_default", "fff_plan_resolve", "fff_workspace_size", "fff_forward",
                  "fff_route", "fff_project", "fff_prune_table_size", "fff_prune_prepare",
-                 "fff_forward_pruned"):
+                 "fff_forward_pruned", "fff_backward_workspace_size", "fff_backward"):
         getattr(lib, name).restype = ctypes.c_int
     if path is None:
         _lib = lib
@@ -339,3 +342,39 @@ def forward_pruned(x, W_node, b_node, V_node, W_out, pruning: Pruning, *, algo=A
     if st != SUCCESS:
         raise FFFError(st, "fff_forward_pruned")
     return y, path_out
+
+
+def backward_workspace_size(shape: Shape, plan: Optional[Plan] = None) -> int:
+    n = ctypes.c_size_t()
+    st = load_library().fff_backward_workspace_size(
+        ctypes.byref(shape), ctypes.byref(plan) if plan is not None else None, ctypes.byref(n))
+    if st != SUCCESS:
+        raise FFFError(st, "fff_backward_workspace_size")
+    return int(n.value)
+
+
+def backward(x, W_node, b_node, V_node, W_out, dy, *, algo=ALGO_AUTO, split_level: int = -1,
+             workspace=None, out=None, stream=None, variant=VARIANT_FFF):
+    """Gradients of sum(y * dy) with the forward's paths held fixed.  Returns
+    a dict: dx (dtype of x), dW_node, db_node, dV_node, dW_out (float32)."""
+    torch = _torch()
+    shape = shape_of(x, W_node, V_node, variant)
+    _check([x, W_node, b_node, V_node, W_out, dy], x.dtype, x.device)
+    plan = make_plan(algo, split_level, 0)
+    if workspace is None:
+        n = backward_workspace_size(shape, plan)
+        workspace = torch.empty(max(n, 1), dtype=torch.uint8, device=x.device)
+    nbytes = workspace.numel() * workspace.element_size()
+    f32 = dict(dtype=torch.float32, device=x.device)
+    g = out or {"dx": torch.empty_like(x), "dW_node": torch.empty(W_node.shape, **f32),
+                "db_node": torch.empty(b_node.shape, **f32),
+                "dV_node": torch.empty(V_node.shape, **f32),
+                "dW_out": torch.empty(W_out.shape, **f32)}
+    st = load_library().fff_backward(
+        ctypes.byref(shape), ctypes.byref(plan), x.data_ptr(), W_node.data_ptr(), b_node.data_ptr(),
+        V_node.data_ptr(), W_out.data_ptr(), dy.data_ptr(), g["dx"].data_ptr(),
+        g["dW_node"].data_ptr(), g["db_node"].data_ptr(), g["dV_node"].data_ptr(),
+        g["dW_out"].data_ptr(), workspace.data_ptr(), nbytes, _stream_handle(stream))
+    if st != SUCCESS:
+        raise FFFError(st, "fff_backward")
+    return g

@@ -298,7 +298,122 @@ fff_status_t forward_impl(const Dims& s, const fff_plan_t& p, const void* x, con
   return FFF_SUCCESS;
 }
 
+// ---- backward ----
+
+bool bwd_mfma_fits(const Dims& s) {
+  (void)s;
+  return false;
+}
+
+fff_status_t resolve_bwd_plan(const Dims& s, const fff_plan_t* in, fff_plan_t* out) {
+  fff_plan_t p;
+  p.algo = in ? in->algo : FFF_ALGO_AUTO;
+  p.split_level = in ? in->split_level : -1;
+  p.chunk_tokens = 0;
+  if (p.algo == FFF_ALGO_AUTO) p.algo = bwd_mfma_fits(s) ? FFF_ALGO_PREFILL : FFF_ALGO_GENERIC;
+  switch (p.algo) {
+    case FFF_ALGO_GENERIC:
+      p.split_level = 0;
+      break;
+    case FFF_ALGO_PREFILL:
+      if (!bwd_mfma_fits(s) || (p.split_level >= 0 && p.split_level != s.D + 1))
+        return FFF_ERROR_NOT_SUPPORTED;
+      p.split_level = s.D + 1;
+      break;
+    case FFF_ALGO_DECODE:
+      return FFF_ERROR_NOT_SUPPORTED;
+    default:
+      return FFF_ERROR_INVALID_VALUE;
+  }
+  *out = p;
+  return FFF_SUCCESS;
+}
+
+// Backward workspace (generic plan):
+//   logits [T][P][D+1] f32, leaf [T][P] i32, dH [T][K] f32, H [T][K] f32,
+//   dx accumulator [T][d] f32.
+struct BwdLayout {
+  size_t logits = 0, leaf = 0, dH = 0, H = 0, dxacc = 0, total = 0;
+};
+
+BwdLayout bwd_layout(const Dims& s, const fff_plan_t& p) {
+  (void)p;
+  BwdLayout B;
+  size_t off = 0;
+  B.logits = off;
+  off = align_up(off + size_t(s.T) * s.P * (s.D + 1) * 4);
+  B.leaf = off;
+  off = align_up(off + size_t(s.T) * s.P * 4);
+  B.dH = off;
+  off = align_up(off + size_t(s.T) * size_t(s.K) * 4);
+  B.H = off;
+  off = align_up(off + size_t(s.T) * size_t(s.K) * 4);
+  B.dxacc = off;
+  off = align_up(off + size_t(s.T) * s.d * 4);
+  B.total = s.T == 0 ? 0 : off;
+  return B;
+}
+
 }  // namespace
+
+extern "C" {
+
+fff_status_t fff_backward_workspace_size(const fff_shape_t* shape, const fff_plan_t* plan,
+                                         size_t* bytes) {
+  Dims s;
+  fff_status_t st = check_shape(shape, &s);
+  if (st != FFF_SUCCESS) return st;
+  if (!bytes) return FFF_ERROR_INVALID_VALUE;
+  fff_plan_t p;
+  st = resolve_bwd_plan(s, plan, &p);
+  if (st != FFF_SUCCESS) return st;
+  *bytes = bwd_layout(s, p).total;
+  return FFF_SUCCESS;
+}
+
+fff_status_t fff_backward(const fff_shape_t* shape, const fff_plan_t* plan, const void* x,
+                          const void* W_node, const void* b_node, const void* V_node,
+                          const void* W_out, const void* dy, void* dx, float* dW_node,
+                          float* db_node, float* dV_node, float* dW_out, void* workspace,
+                          size_t workspace_bytes, hipStream_t stream) {
+  Dims s;
+  fff_status_t st = check_shape(shape, &s);
+  if (st != FFF_SUCCESS) return st;
+  fff_plan_t p;
+  st = resolve_bwd_plan(s, plan, &p);
+  if (st != FFF_SUCCESS) return st;
+  if (!dW_node || !db_node || !dV_node || !dW_out || !aligned(dW_node, 16) ||
+      !aligned(db_node, 4) || !aligned(dV_node, 16) || !aligned(dW_out, 16))
+    return FFF_ERROR_INVALID_VALUE;
+  const int64_t nW = int64_t(s.P) * s.N * s.d, nb = int64_t(s.P) * s.N;
+  const int64_t nV = int64_t(s.P) * s.N * s.h, nO = s.K * s.d;
+  if (s.T == 0) {  // no token: every gradient is zero
+    if (fff::launch_fill_f32(dW_node, nW, stream) != hipSuccess ||
+        fff::launch_fill_f32(db_node, nb, stream) != hipSuccess ||
+        fff::launch_fill_f32(dV_node, nV, stream) != hipSuccess ||
+        fff::launch_fill_f32(dW_out, nO, stream) != hipSuccess)
+      return FFF_ERROR_HIP;
+    return FFF_SUCCESS;
+  }
+  st = check_inputs(s, x, W_node, b_node, V_node);
+  if (st != FFF_SUCCESS) return st;
+  if (!W_out || !dy || !dx || !aligned(W_out, 16) || !aligned(dy, 16) || !aligned(dx, 16))
+    return FFF_ERROR_INVALID_VALUE;
+  const BwdLayout B = bwd_layout(s, p);
+  if (!workspace || workspace_bytes < B.total) return FFF_ERROR_WORKSPACE;
+  if (!aligned(workspace, kWsAlign)) return FFF_ERROR_INVALID_VALUE;
+  char* ws = static_cast<char*>(workspace);
+  float* logits = reinterpret_cast<float*>(ws + B.logits);
+  int32_t* leaf = reinterpret_cast<int32_t*>(ws + B.leaf);
+  if (fff::launch_route_generic(s, x, W_node, b_node, logits, nullptr, leaf, stream) != hipSuccess)
+    return FFF_ERROR_HIP;
+  return hip_status(fff::launch_backward_generic(
+      s, x, W_node, V_node, W_out, dy, dx, dW_node, db_node, dV_node, dW_out, logits, leaf,
+      reinterpret_cast<float*>(ws + B.dH), reinterpret_cast<float*>(ws + B.H),
+      reinterpret_cast<float*>(ws + B.dxacc), stream));
+}
+
+}  // extern "C"
 
 extern "C" {
 

@@ -97,4 +97,15 @@ hipError_t launch_decode(const Dims& s, const void* x, const void* W, const void
                          const void* V, const void* Wout, void* y, int32_t* path_out, void* ws,
                          hipStream_t st);
 
+// ---- backward pass (gradients of sum(y * dy), paths held fixed) ----
+hipError_t launch_fill_f32(float* p, int64_t n, hipStream_t st);
+// Generic: any shape and dtype.  Uses the routing records of
+// launch_route_generic; dW, db, dV, dWout are fp32 outputs; dH, Hf ([T,K])
+// and dxacc ([T,d]) fp32 scratch.
+hipError_t launch_backward_generic(const Dims& s, const void* x, const void* W, const void* V,
+                                   const void* Wout, const void* dy, void* dx, float* dW, float* db,
+                                   float* dV, float* dWout, const float* logits,
+                                   const int32_t* leaf, float* dH, float* Hf, float* dxacc,
+                                   hipStream_t st);
+
 }  // namespace fff
