@@ -267,8 +267,9 @@ fff_status_t fff_forward_pruned(const fff_shape_t *shape, const fff_plan_t *plan
  *   dW_node   [P,N,d] float32 out    db_node [P,N] float32 out
  *   dV_node   [P,N,h] float32 out    dW_out  [P*h,d] float32 out
  * Every output is overwritten (nodes off every path get 0).  Plans: GENERIC
- * (any shape and dtype) or PREFILL (bf16, every level dense: D+1 <= 8,
- * d % 64 == 0, h % 64 == 0, P*2^(D+1) % 64 == 0); AUTO picks PREFILL when the
+ * (any shape and dtype) or PREFILL (bf16, every level dense: 3 <= D+1 <= 8,
+ * d % 64 == 0, h % 64 == 0, P*2^(D+1) % 64 == 0, and one tree's v rows plus
+ * 2^(D+1) floats within 64 KB); AUTO picks PREFILL when the
  * shape allows; DECODE and split PREFILL plans are FFF_ERROR_NOT_SUPPORTED.
  * Sums over tokens use float32 atomics in some kernels, so results may
  * differ in the last bits between calls.  Workspace: fff_backward_workspace_size.

@@ -300,10 +300,7 @@ fff_status_t forward_impl(const Dims& s, const fff_plan_t& p, const void* x, con
 
 // ---- backward ----
 
-bool bwd_mfma_fits(const Dims& s) {
-  (void)s;
-  return false;
-}
+bool bwd_mfma_fits(const Dims& s) { return fff::backward_mfma_supported(s); }
 
 fff_status_t resolve_bwd_plan(const Dims& s, const fff_plan_t* in, fff_plan_t* out) {
   fff_plan_t p;
@@ -337,8 +334,11 @@ struct BwdLayout {
 };
 
 BwdLayout bwd_layout(const Dims& s, const fff_plan_t& p) {
-  (void)p;
   BwdLayout B;
+  if (p.algo == FFF_ALGO_PREFILL) {
+    B.total = s.T == 0 ? 0 : fff::backward_mfma_layout(s).total;
+    return B;
+  }
   size_t off = 0;
   B.logits = off;
   off = align_up(off + size_t(s.T) * s.P * (s.D + 1) * 4);
@@ -402,6 +402,10 @@ fff_status_t fff_backward(const fff_shape_t* shape, const fff_plan_t* plan, cons
   const BwdLayout B = bwd_layout(s, p);
   if (!workspace || workspace_bytes < B.total) return FFF_ERROR_WORKSPACE;
   if (!aligned(workspace, kWsAlign)) return FFF_ERROR_INVALID_VALUE;
+  if (p.algo == FFF_ALGO_PREFILL)
+    return hip_status(fff::launch_backward_mfma(s, x, W_node, b_node, V_node, W_out, dy, dx,
+                                                dW_node, db_node, dV_node, dW_out, workspace,
+                                                stream));
   char* ws = static_cast<char*>(workspace);
   float* logits = reinterpret_cast<float*>(ws + B.logits);
   int32_t* leaf = reinterpret_cast<int32_t*>(ws + B.leaf);

@@ -13,10 +13,23 @@
 //
 // Generic kernels (any shape, fp32 or bf16): one wavefront per (token,
 // tree) and fp32 atomics for the sums over tokens.
+//
+// Matrix-core path (bf16, every level dense, as the forward's default
+// plan): the sums over tokens and nodes are products with the masked
+// matrix DA[t, (p, n)] (da at the token's visited nodes, 0 elsewhere, one
+// column per node of the dense levels), the same masked form the forward
+// uses for the logits (explainer page, section 2, Implementation):
+//   dH   = dy . W_out^T             dx     = DA . W_top
+//   dW   = DA^T . x                 dW_out = H^T . dy
+//   dV_p = G_p^T . dS_p  (G: GELU(a), or a for FFF-post, at visited nodes;
+//                         dS_p: dH_p, or GELU'(s) * dH_p)
+// all as one bf16 "A . B^T" kernel over K-contiguous rows (the forward's
+// direct-to-LDS main loop), with the token-major operands transposed once.
 #include "fff.h"
 
 #include "common.hpp"
 #include "launch.hpp"
+#include "mfma_tile.hpp"
 
 namespace fff {
 namespace {
@@ -188,6 +201,256 @@ hipError_t backward_generic_t(const Dims& s, const void* x, const void* W, const
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// Matrix-core path.
+
+using BwdTile = DirectCfg<256, 256, 128, 64, 4>;
+
+// C (+)= A . B^T over K-contiguous bf16 rows.  Grid: batches x ksplit x
+// tiles, XCD-aware.  Output modes: kBf16 stores; kF32 stores; kF32Add
+// float32 atomic adds (outputs pre-zeroed; split-K and batches allowed),
+// with rows remapped from the dense node layout (row r = p * 2^L + n ->
+// p * Nn + n, the spare column n = 2^L - 1 dropped) when L > 0.
+struct GemmArgs {
+  const uint16_t* A;
+  const uint16_t* B;
+  void* C;
+  int64_t lda, ldb, ldc;
+  int64_t a_bstride, b_bstride, c_bstride;  // rows per batch
+  int M, N, Kk;                             // Kk: k extent of one split
+  int tiles_m, tiles_n, ksplit;
+  int L;
+  int64_t Nn;
+};
+
+enum GemmOut { kBf16 = 0, kF32 = 1, kF32Add = 2 };
+
+template <int kOut>
+__global__ __launch_bounds__(BwdTile::kThreads) void gemm_nt_kernel(GemmArgs g) {
+  using C = BwdTile;
+  extern __shared__ __align__(16) unsigned char lds[];
+  const int logical = xcd_logical_tile(blockIdx.x, gridDim.x);
+  const int per = g.tiles_m * g.tiles_n;
+  const int tile = logical % per;
+  const int rest = logical / per;
+  const int ks = rest % g.ksplit;
+  const int batch = rest / g.ksplit;
+  const int m0 = (tile / g.tiles_n) * C::BM;
+  const int n0 = (tile % g.tiles_n) * C::BN;
+  const int64_t koff = static_cast<int64_t>(ks) * g.Kk;
+  auto a_row = [&](int i) {
+    const int r = m0 + i < g.M ? m0 + i : g.M - 1;
+    return g.A + (batch * g.a_bstride + r) * g.lda + koff;
+  };
+  auto b_row = [&](int j) {
+    const int c = n0 + j < g.N ? n0 + j : g.N - 1;
+    return g.B + (batch * g.b_bstride + c) * g.ldb + koff;
+  };
+  f32x16_t acc[C::kTm][C::kTn];
+  gemm_mainloop_direct<C>(acc, lds, g.Kk, a_row, b_row);
+
+  // Lane holds row (m-block i, lane % 32) and, for q = 0..3, the four
+  // consecutive columns 8q + 4 (lane / 32) + 0..3 of n-block j.
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x / kWave;
+  const int wm = wave / C::kWavesN;
+  const int wn = wave % C::kWavesN;
+  const int mask = (1 << g.L) - 1;
+#pragma unroll
+  for (int i = 0; i < C::kTm; ++i) {
+    const int row = m0 + wm * C::WM + i * 32 + (lane & 31);
+    if (row >= g.M) continue;
+    int64_t out_row = batch * g.c_bstride + row;
+    if (kOut == kF32Add && g.L > 0) {
+      const int n = row & mask;
+      if (n == mask) continue;  // the spare column of each tree
+      out_row = batch * g.c_bstride + static_cast<int64_t>(row >> g.L) * g.Nn + n;
+    }
+#pragma unroll
+    for (int j = 0; j < C::kTn; ++j) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int col = n0 + wn * C::WN + j * 32 + q * 8 + (lane >> 5) * 4;
+        if (col >= g.N) continue;
+        if constexpr (kOut == kF32Add) {
+          float* dst = static_cast<float*>(g.C) + out_row * g.ldc + col;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) atomicAdd(dst + e, acc[i][j][4 * q + e]);
+        } else if constexpr (kOut == kF32) {
+          *reinterpret_cast<float4*>(static_cast<float*>(g.C) + out_row * g.ldc + col) =
+              make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
+                          acc[i][j][4 * q + 3]);
+        } else {
+          uint16_t* dst = static_cast<uint16_t*>(g.C) + out_row * g.ldc + col;
+          *reinterpret_cast<uint2*>(dst) =
+              make_uint2(pack_bf16x2(acc[i][j][4 * q], acc[i][j][4 * q + 1]),
+                         pack_bf16x2(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]));
+        }
+      }
+    }
+  }
+}
+
+// dst[c][r] = src row r's element c (zero for rows without a source), for
+// r < Rp, c < Cn; 64 x 64 tiles through LDS.  Source row of r: r itself if
+// r < R (L = 0), else for the node layout (L > 0) p * Nn + n with
+// p = r >> L, n = r & (2^L - 1) when n < 2^L - 1 and p < P.
+__global__ __launch_bounds__(256) void transpose_rows_kernel(
+    const uint16_t* __restrict__ src, int64_t ld_src, uint16_t* __restrict__ dst, int64_t ld_dst,
+    int64_t R, int Cn, int L, int64_t Nn, int P) {
+  __shared__ uint16_t tile[64][72];
+  const int c0 = blockIdx.x * 64;
+  const int64_t r0 = static_cast<int64_t>(blockIdx.y) * 64;
+  const int tr = threadIdx.x >> 2;        // tile row (source row r0 + tr)
+  const int tc = (threadIdx.x & 3) * 16;  // 16 columns
+  const int64_t r = r0 + tr;
+  int64_t srow = -1;
+  if (L == 0) {
+    srow = r < R ? r : -1;
+  } else {
+    const int64_t p = r >> L;
+    const int64_t n = r & ((int64_t(1) << L) - 1);
+    srow = (p < P && n < (int64_t(1) << L) - 1) ? p * Nn + n : -1;
+  }
+  uint4 v0 = make_uint4(0, 0, 0, 0), v1 = v0;
+  if (srow >= 0 && c0 + tc < Cn) {
+    v0 = ldg16(src + srow * ld_src + c0 + tc);
+    v1 = ldg16(src + srow * ld_src + c0 + tc + 8);
+  }
+  *reinterpret_cast<uint4*>(&tile[tr][tc]) = v0;
+  *reinterpret_cast<uint4*>(&tile[tr][tc + 8]) = v1;
+  __syncthreads();
+  const int oc = threadIdx.x >> 2;        // output row c0 + oc
+  const int orr = (threadIdx.x & 3) * 16;  // 16 consecutive r
+  if (c0 + oc >= Cn) return;
+  uint16_t w[16];
+#pragma unroll
+  for (int e = 0; e < 16; ++e) w[e] = tile[orr + e][oc];
+  uint16_t* o = dst + static_cast<int64_t>(c0 + oc) * ld_dst + r0 + orr;
+  *reinterpret_cast<uint4*>(o) = make_uint4(w[0] | (uint32_t(w[1]) << 16), w[2] | (uint32_t(w[3]) << 16),
+                                            w[4] | (uint32_t(w[5]) << 16), w[6] | (uint32_t(w[7]) << 16));
+  *reinterpret_cast<uint4*>(o + 8) = make_uint4(w[8] | (uint32_t(w[9]) << 16), w[10] | (uint32_t(w[11]) << 16),
+                                                w[12] | (uint32_t(w[13]) << 16), w[14] | (uint32_t(w[15]) << 16));
+}
+
+// One thread per (tree p, token t < Tp): from the routing records, dH (fp32) and
+// the tree's v rows (staged in LDS), the path's da and GELU terms; writes
+// the masked rows DA[t][p*2^L ..], the transposed columns DA^T, G^T, H^T
+// and dS^T at token t (zeros for padding tokens t >= T), and db through an
+// LDS reduction per node.
+__global__ __launch_bounds__(256) void bwd_paths_kernel(
+    const float* __restrict__ rec_logit, const int32_t* __restrict__ rec_next,
+    const uint16_t* __restrict__ V, const float* __restrict__ dH, uint16_t* __restrict__ DA,
+    uint16_t* __restrict__ DAt, uint16_t* __restrict__ Gt, uint16_t* __restrict__ Ht,
+    uint16_t* __restrict__ dSt, float* __restrict__ db, int T, int Tp, int P, int D, int h,
+    int64_t N, int post) {
+  extern __shared__ __align__(16) unsigned char bp_lds[];
+  const int L = D + 1;
+  const int cpt = 1 << L;
+  uint16_t* Vs = reinterpret_cast<uint16_t*>(bp_lds);
+  float* dbs = reinterpret_cast<float*>(bp_lds + ((size_t(N) * h * 2 + 15) / 16) * 16);
+  const int p = blockIdx.y;
+  const int t = blockIdx.x * 256 + threadIdx.x;
+  const uint16_t* Vp = V + static_cast<int64_t>(p) * N * h;
+  for (int e = threadIdx.x; e < static_cast<int>(N) * (h / 8); e += 256)
+    *reinterpret_cast<uint4*>(Vs + static_cast<size_t>(e) * 8) = ldg16(Vp + static_cast<size_t>(e) * 8);
+  for (int c = threadIdx.x; c < cpt; c += 256) dbs[c] = 0.0f;
+  __syncthreads();
+
+  const bool live = t < T;
+  const int64_t K = static_cast<int64_t>(P) * h;
+  int node[8];
+  float a[8], g[8];
+  const int leaf = live ? rec_next[static_cast<int64_t>(p) * T + t] : 0;
+#pragma unroll
+  for (int l = 0; l < 8; ++l) {
+    node[l] = live && l < L ? ((leaf + 1) >> (D - l)) - 1 : 0;
+    a[l] = (live && l < L) ? rec_logit[(static_cast<int64_t>(p) * T + t) * L + l] : 0.0f;
+    g[l] = 0.0f;
+  }
+  const float* dHt = dH + static_cast<int64_t>(t) * K + static_cast<int64_t>(p) * h;
+  for (int j0 = 0; j0 < h; j0 += 8) {
+    float dj[8], hj[8];
+    if (live) {
+      const float4 u0 = *reinterpret_cast<const float4*>(dHt + j0);
+      const float4 u1 = *reinterpret_cast<const float4*>(dHt + j0 + 4);
+      dj[0] = u0.x; dj[1] = u0.y; dj[2] = u0.z; dj[3] = u0.w;
+      dj[4] = u1.x; dj[5] = u1.y; dj[6] = u1.z; dj[7] = u1.w;
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) dj[e] = 0.0f;
+    }
+    float sj[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) sj[e] = 0.0f;
+#pragma unroll
+    for (int l = 0; l < 8; ++l) {
+      if (l >= L) break;
+      const uint4 u = *reinterpret_cast<const uint4*>(Vs + static_cast<size_t>(node[l]) * h + j0);
+      const float v[8] = {bf16lo(u.x), bf16hi(u.x), bf16lo(u.y), bf16hi(u.y),
+                          bf16lo(u.z), bf16hi(u.z), bf16lo(u.w), bf16hi(u.w)};
+      const float w = post ? a[l] : gelu_tanh(a[l]);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) sj[e] += w * v[e];
+    }
+    // FFF: sj is H; FFF-post: sj is s, H = GELU(s), dS = GELU'(s) dH.
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      hj[e] = post ? gelu_tanh(sj[e]) : sj[e];
+      if (post) dj[e] *= gelu_tanh_grad(sj[e]);
+    }
+#pragma unroll
+    for (int l = 0; l < 8; ++l) {
+      if (l >= L) break;
+      const uint4 u = *reinterpret_cast<const uint4*>(Vs + static_cast<size_t>(node[l]) * h + j0);
+      g[l] += dj[0] * bf16lo(u.x) + dj[1] * bf16hi(u.x) + dj[2] * bf16lo(u.y) +
+              dj[3] * bf16hi(u.y) + dj[4] * bf16lo(u.z) + dj[5] * bf16hi(u.z) +
+              dj[6] * bf16lo(u.w) + dj[7] * bf16hi(u.w);
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int64_t row = static_cast<int64_t>(p) * h + j0 + e;
+      Ht[row * Tp + t] = live ? f32_to_bf16(hj[e]) : 0;
+      dSt[row * Tp + t] = live ? f32_to_bf16(dj[e]) : 0;
+    }
+  }
+  float da[8];
+#pragma unroll
+  for (int l = 0; l < 8; ++l) {
+    da[l] = (live && l < L) ? (post ? g[l] : g[l] * gelu_tanh_grad(a[l])) : 0.0f;
+    if (live && l < L) atomicAdd(dbs + node[l], da[l]);
+  }
+  // Masked rows and columns: node c (heap order) holds the value of the
+  // level it sits on if the path passes through it.
+  for (int c0 = 0; c0 < cpt; c0 += 8) {
+    uint16_t dv[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int c = c0 + e;
+      const int lvl = 31 - __clz(c + 1);
+      float vd = 0.0f, vg = 0.0f;
+#pragma unroll
+      for (int l = 0; l < 8; ++l)
+        if (l == lvl && l < L && node[l] == c) {
+          vd = da[l];
+          vg = post ? a[l] : gelu_tanh(a[l]);
+        }
+      if (!live) vd = vg = 0.0f;
+      dv[e] = f32_to_bf16(vd);
+      const int64_t col = static_cast<int64_t>(p) * cpt + c;
+      DAt[col * Tp + t] = dv[e];
+      Gt[col * Tp + t] = f32_to_bf16(vg);
+    }
+    if (live)
+      *reinterpret_cast<uint4*>(DA + static_cast<int64_t>(t) * P * cpt + static_cast<int64_t>(p) * cpt + c0) =
+          make_uint4(dv[0] | (uint32_t(dv[1]) << 16), dv[2] | (uint32_t(dv[3]) << 16),
+                     dv[4] | (uint32_t(dv[5]) << 16), dv[6] | (uint32_t(dv[7]) << 16));
+  }
+  __syncthreads();
+  for (int c = threadIdx.x; c < cpt - 1; c += 256)
+    if (dbs[c] != 0.0f) atomicAdd(db + static_cast<int64_t>(p) * N + c, dbs[c]);
+}
+
 }  // namespace
 
 hipError_t launch_fill_f32(float* p, int64_t n, hipStream_t st) {
@@ -206,6 +469,153 @@ hipError_t launch_backward_generic(const Dims& s, const void* x, const void* W, 
                                      Hf, dxacc, st);
   return backward_generic_t<uint16_t>(s, x, W, V, Wout, dy, dx, dW, db, dV, dWout, logits, leaf,
                                       dH, Hf, dxacc, st);
+}
+
+namespace {
+
+template <int kOut>
+hipError_t launch_gemm_nt(GemmArgs g, int batches, hipStream_t st) {
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_nt_kernel<kOut>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       static_cast<int>(BwdTile::kLdsBytes));
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  g.tiles_m = (g.M + BwdTile::BM - 1) / BwdTile::BM;
+  g.tiles_n = (g.N + BwdTile::BN - 1) / BwdTile::BN;
+  const int blocks = g.tiles_m * g.tiles_n * g.ksplit * batches;
+  gemm_nt_kernel<kOut><<<dim3(blocks), dim3(BwdTile::kThreads), BwdTile::kLdsBytes, st>>>(g);
+  return hipGetLastError();
+}
+
+// Splits of the token dimension so that a float32 product covers the 256
+// compute units (each split a multiple of the 32-wide k step).
+int token_splits(int tiles, int64_t Tp) {
+  int ks = 1;
+  while (tiles * ks < 256 && ks < 8 && (Tp / 32) % (2 * ks) == 0) ks *= 2;
+  return ks;
+}
+
+hipError_t transpose_rows(const uint16_t* src, int64_t ld_src, uint16_t* dst, int64_t ld_dst,
+                          int64_t R, int64_t Rp, int Cn, int L, int64_t Nn, int P,
+                          hipStream_t st) {
+  transpose_rows_kernel<<<dim3((Cn + 63) / 64, static_cast<unsigned>(Rp / 64)), 256, 0, st>>>(
+      src, ld_src, dst, ld_dst, R, Cn, L, Nn, P);
+  return hipGetLastError();
+}
+
+size_t paths_lds(const Dims& s) {
+  return (size_t(s.N) * s.h * 2 + 15) / 16 * 16 + (size_t(1) << (s.D + 1)) * 4;
+}
+
+}  // namespace
+
+bool backward_mfma_supported(const Dims& s) {
+  const int L = s.D + 1;
+  return s.dtype == 1 && L >= 3 && L <= 8 && route_top_supported(s, L) && s.d % 64 == 0 &&
+         s.h % 64 == 0 && (int64_t(s.P) << L) % 64 == 0 && paths_lds(s) <= 64 * 1024 &&
+         s.T >= 1;
+}
+
+BwdMfmaLayout backward_mfma_layout(const Dims& s) {
+  auto up = [](size_t v) { return (v + 255) / 256 * 256; };
+  const int L = s.D + 1;
+  const size_t cols = size_t(s.P) << L;
+  const size_t Tp = (size_t(s.T) + 255) / 256 * 256;
+  BwdMfmaLayout B;
+  size_t off = 0;
+  B.Tp = static_cast<int64_t>(Tp);
+  B.logits = off; off = up(off + size_t(s.T) * s.P * L * 4);
+  B.next = off;   off = up(off + size_t(s.T) * s.P * 4);
+  B.xT = off;     off = up(off + size_t(s.d) * Tp * 2);
+  B.dyT = off;    off = up(off + size_t(s.d) * Tp * 2);
+  B.dH = off;     off = up(off + size_t(s.T) * size_t(s.K) * 4);
+  B.DA = off;     off = up(off + size_t(s.T) * cols * 2);
+  B.DAt = off;    off = up(off + cols * Tp * 2);
+  B.Gt = off;     off = up(off + cols * Tp * 2);
+  B.Ht = off;     off = up(off + size_t(s.K) * Tp * 2);
+  B.dSt = off;    off = up(off + size_t(s.K) * Tp * 2);
+  B.WTn = off;    off = up(off + size_t(s.d) * cols * 2);
+  B.total = off;
+  return B;
+}
+
+hipError_t launch_backward_mfma(const Dims& s, const void* x, const void* W, const void* b,
+                                const void* V, const void* Wout, const void* dy, void* dx,
+                                float* dW, float* db, float* dV, float* dWout, void* ws,
+                                hipStream_t st) {
+  const int L = s.D + 1;
+  const int cols = s.P << L;
+  const BwdMfmaLayout B = backward_mfma_layout(s);
+  const int64_t Tp = B.Tp;
+  char* w = static_cast<char*>(ws);
+  float* logits = reinterpret_cast<float*>(w + B.logits);
+  int32_t* next = reinterpret_cast<int32_t*>(w + B.next);
+  uint16_t* xT = reinterpret_cast<uint16_t*>(w + B.xT);
+  uint16_t* dyT = reinterpret_cast<uint16_t*>(w + B.dyT);
+  float* dH = reinterpret_cast<float*>(w + B.dH);
+  uint16_t* DA = reinterpret_cast<uint16_t*>(w + B.DA);
+  uint16_t* DAt = reinterpret_cast<uint16_t*>(w + B.DAt);
+  uint16_t* Gt = reinterpret_cast<uint16_t*>(w + B.Gt);
+  uint16_t* Ht = reinterpret_cast<uint16_t*>(w + B.Ht);
+  uint16_t* dSt = reinterpret_cast<uint16_t*>(w + B.dSt);
+  uint16_t* WTn = reinterpret_cast<uint16_t*>(w + B.WTn);
+  const uint16_t* x16 = static_cast<const uint16_t*>(x);
+  const uint16_t* dy16 = static_cast<const uint16_t*>(dy);
+  hipError_t e;
+#define FFF_TRY(call) \
+  if ((e = (call)) != hipSuccess) return e
+  FFF_TRY(launch_fill_f32(dW, int64_t(s.P) * s.N * s.d, st));
+  FFF_TRY(launch_fill_f32(db, int64_t(s.P) * s.N, st));
+  FFF_TRY(launch_fill_f32(dV, int64_t(s.P) * s.N * s.h, st));
+  FFF_TRY(launch_fill_f32(dWout, s.K * s.d, st));
+  FFF_TRY(launch_route_top(s, L, x, W, b, logits, next, st));
+  FFF_TRY(transpose_rows(x16, s.d, xT, Tp, s.T, Tp, s.d, 0, 0, 0, st));
+  FFF_TRY(transpose_rows(dy16, s.d, dyT, Tp, s.T, Tp, s.d, 0, 0, 0, st));
+  FFF_TRY(transpose_rows(static_cast<const uint16_t*>(W), s.d, WTn, cols, cols, cols, s.d, L, s.N,
+                         s.P, st));
+  GemmArgs g{};
+  // dH = dy . W_out^T  [T, K]
+  g.A = dy16; g.lda = s.d; g.B = static_cast<const uint16_t*>(Wout); g.ldb = s.d;
+  g.C = dH; g.ldc = s.K; g.M = static_cast<int>(s.T); g.N = static_cast<int>(s.K); g.Kk = s.d;
+  g.ksplit = 1;
+  FFF_TRY(launch_gemm_nt<kF32>(g, 1, st));
+  bwd_paths_kernel<<<dim3(static_cast<unsigned>(Tp / 256), static_cast<unsigned>(s.P)), 256,
+                     paths_lds(s), st>>>(logits, next, static_cast<const uint16_t*>(V), dH, DA,
+                                         DAt, Gt, Ht, dSt, db, static_cast<int>(s.T),
+                                         static_cast<int>(Tp), s.P, s.D, s.h, s.N, s.variant);
+  FFF_TRY(hipGetLastError());
+  // dx = DA . W_top  [T, d]
+  g = GemmArgs{};
+  g.A = DA; g.lda = cols; g.B = WTn; g.ldb = cols; g.C = dx; g.ldc = s.d;
+  g.M = static_cast<int>(s.T); g.N = s.d; g.Kk = cols; g.ksplit = 1;
+  FFF_TRY(launch_gemm_nt<kBf16>(g, 1, st));
+  // dW = DA^T . x  [P*2^L -> P*N, d]
+  g = GemmArgs{};
+  g.A = DAt; g.lda = Tp; g.B = xT; g.ldb = Tp; g.C = dW; g.ldc = s.d;
+  g.M = cols; g.N = s.d; g.L = L; g.Nn = s.N;
+  g.ksplit = token_splits(((cols + 255) / 256) * ((s.d + 255) / 256), Tp);
+  g.Kk = static_cast<int>(Tp / g.ksplit);
+  FFF_TRY(launch_gemm_nt<kF32Add>(g, 1, st));
+  // dW_out = H^T . dy  [K, d]
+  g = GemmArgs{};
+  g.A = Ht; g.lda = Tp; g.B = dyT; g.ldb = Tp; g.C = dWout; g.ldc = s.d;
+  g.M = static_cast<int>(s.K); g.N = s.d;
+  g.ksplit = token_splits(static_cast<int>(((s.K + 255) / 256) * ((s.d + 255) / 256)), Tp);
+  g.Kk = static_cast<int>(Tp / g.ksplit);
+  FFF_TRY(launch_gemm_nt<kF32Add>(g, 1, st));
+  // dV_p = G_p^T . dS_p  [2^L -> N, h], one batch per tree
+  g = GemmArgs{};
+  g.A = Gt; g.lda = Tp; g.a_bstride = int64_t(1) << L;
+  g.B = dSt; g.ldb = Tp; g.b_bstride = s.h;
+  g.C = dV; g.ldc = s.h; g.c_bstride = s.N; g.M = 1 << L; g.N = s.h; g.L = L; g.Nn = s.N;
+  g.ksplit = token_splits(s.P * ((s.h + 255) / 256), Tp);
+  g.Kk = static_cast<int>(Tp / g.ksplit);
+  FFF_TRY(launch_gemm_nt<kF32Add>(g, s.P, st));
+#undef FFF_TRY
+  return hipSuccess;
 }
 
 }  // namespace fff

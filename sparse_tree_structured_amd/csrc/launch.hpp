@@ -108,4 +108,18 @@ hipError_t launch_backward_generic(const Dims& s, const void* x, const void* W, 
                                    const int32_t* leaf, float* dH, float* Hf, float* dxacc,
                                    hipStream_t st);
 
+// Matrix-core path: bf16, every level dense (3 <= D+1 <= 8), d and h
+// multiples of 64.  Workspace: routing records, transposed x and dy, dH, the
+// masked DA (and its transpose), G^T, H^T, dS^T and the node rows transposed.
+struct BwdMfmaLayout {
+  size_t logits, next, xT, dyT, dH, DA, DAt, Gt, Ht, dSt, WTn, total;
+  int64_t Tp;  // tokens padded to a multiple of 256
+};
+bool backward_mfma_supported(const Dims& s);
+BwdMfmaLayout backward_mfma_layout(const Dims& s);
+hipError_t launch_backward_mfma(const Dims& s, const void* x, const void* W, const void* b,
+                                const void* V, const void* Wout, const void* dy, void* dx,
+                                float* dW, float* db, float* dV, float* dWout, void* ws,
+                                hipStream_t st);
+
 }  // namespace fff

@@ -254,3 +254,25 @@ def test_forward_pruned_validation(lib):
     # A PREFILL plan must use the split level the table packed.
     assert run(fff.Pruning(**dict(good, split_level=3))) == fff.ERROR_NOT_SUPPORTED
     assert run(fff.Pruning(**good), fff.make_plan("prefill", 3)) == fff.ERROR_NOT_SUPPORTED
+
+
+def test_backward_plans_and_workspace():
+    up = lambda v: (v + 255) // 256 * 256  # noqa: E731
+    # AUTO takes the matrix-core path where every level is dense.
+    s = _shape(T=16384, d=2048, P=32, D=6, h=128)
+    assert fff.backward_workspace_size(s) == fff.backward_workspace_size(s, fff.make_plan("prefill"))
+    T, Tp, cols, K, d = 16384, 16384, 32 * 128, 32 * 128, 2048
+    expect = (up(T * 32 * 7 * 4) + up(T * 32 * 4) + 2 * up(d * Tp * 2) + up(T * K * 4) +
+              up(T * cols * 2) + 2 * up(cols * Tp * 2) + 2 * up(K * Tp * 2) + up(d * cols * 2))
+    assert fff.backward_workspace_size(s) == expect
+    # Generic for fp32, deep (split) trees and shallow trees.
+    g = _shape(T=100, d=64, P=2, D=3, h=32, dtype=fff.DTYPE_F32)
+    assert fff.backward_workspace_size(g) == up(100 * 2 * 4 * 4) + up(100 * 2 * 4) + \
+        2 * up(100 * 64 * 4) + up(100 * 64 * 4)
+    for shp in (_shape(T=100, d=2048, P=32, D=8, h=128), _shape(T=100, d=64, P=2, D=1, h=64)):
+        with pytest.raises(fff.FFFError):
+            fff.backward_workspace_size(shp, fff.make_plan("prefill"))
+    with pytest.raises(fff.FFFError):
+        fff.backward_workspace_size(s, fff.make_plan("decode"))
+    with pytest.raises(fff.FFFError):
+        fff.backward_workspace_size(s, fff.make_plan("prefill", 4))

@@ -2,11 +2,16 @@
 with the forward's paths held fixed), through fff_backward.
 
 Every gradient is compared element by element: error = max |g - g_ref| /
-max(|g_ref|, RMS of g_ref over the tensor), at most 1e-4 for float32
-layers and 2e-2 for bf16 ones (dx is rounded to the layer dtype; parameter
-gradients are float32).  Inputs are checked to route identically on both
-sides (no near-tie flips), since a flipped path changes which nodes get
-gradient.
+max(|g_ref|, RMS of g_ref over the tensor).  Float32 layers: at most 1e-4.
+bf16 layers: the matrix-core path rounds da, GELU(a) (or a), H and dS to
+bf16 once each before the products that sum them over tokens (unit roundoff
+u = 2^-8), so each gradient element carries a few independent roundings of
+relative size up to u; the bar is a normwise error (Frobenius) of at most
+1e-2 (about 2.5u) and an elementwise one of at most 8e-2 (about 20u, a
+tail bound over up to 10^7 elements).  dx is rounded to the layer dtype;
+parameter gradients are float32.  Inputs are checked to route identically
+on both sides (no near-tie flips), since a flipped path changes which
+nodes get gradient.
 """
 import numpy as np
 import pytest
@@ -20,7 +25,8 @@ from gpu_helpers import to_device, to_f64
 pytestmark = pytest.mark.gpu
 
 needs_gpu = pytest.mark.skipif(not torch.cuda.is_available(), reason="no GPU")
-TOL = {"f32": 1e-4, "bf16": 2e-2}
+TOL = {"f32": 1e-4, "bf16": 8e-2}          # elementwise, floored at the RMS
+TOL_NORM = {"f32": 1e-4, "bf16": 1e-2}     # ||g - g_ref|| / ||g_ref||
 GRADS = ("dx", "dW_node", "db_node", "dV_node", "dW_out")
 
 
@@ -30,6 +36,12 @@ def grad_error(g, ref):
     den = np.maximum(np.abs(ref), rms)
     den = np.where(den > 0, den, 1.0)
     return float(np.max(np.abs(g - ref) / den)) if ref.size else 0.0
+
+
+def norm_error(g, ref):
+    g = np.asarray(g, dtype=np.float64)
+    nr = np.linalg.norm(ref)
+    return float(np.linalg.norm(g - ref) / nr) if nr > 0 else float(np.linalg.norm(g))
 
 
 def make_dy(inp, seed):
@@ -63,9 +75,10 @@ def check_grads(inp, g, path, dy64, variant=0):
     np.testing.assert_array_equal(path, ref_path)
     ref = oracle.backward(f["x"], f["W_node"], f["b_node"], f["V_node"], f["W_out"], dy64,
                           variant=variant)
-    errs = {k: grad_error(g[k], ref[k]) for k in GRADS}
-    print("grad errors", errs, flush=True)
-    bad = {k: e for k, e in errs.items() if e > TOL[inp.shape.dtype]}
+    dt = inp.shape.dtype
+    errs = {k: (grad_error(g[k], ref[k]), norm_error(g[k], ref[k])) for k in GRADS}
+    print("grad errors (elementwise, normwise)", errs, flush=True)
+    bad = {k: e for k, e in errs.items() if e[0] > TOL[dt] or e[1] > TOL_NORM[dt]}
     assert not bad, bad
     return errs
 
@@ -106,3 +119,66 @@ def test_backward_zero_tokens_zeroes_gradients():
     torch.cuda.synchronize()
     for k in ("dW_node", "db_node", "dV_node", "dW_out"):
         assert (g[k] == 0).all()
+
+
+MFMA = [
+    # T, d, P, D, h  (bf16, every level dense)
+    (300, 256, 4, 6, 64),      # tokens not a multiple of the 256-token padding
+    (1000, 128, 8, 2, 64),     # the shallowest dense plan (3 levels)
+    (500, 512, 2, 7, 64),      # 256 columns per tree
+    (257, 256, 16, 5, 128),
+    (64, 192, 8, 3, 64),
+]
+
+
+@needs_gpu
+@pytest.mark.parametrize("variant", [0, 1])
+@pytest.mark.parametrize("shape", MFMA, ids=[str(s) for s in MFMA])
+def test_backward_mfma(shape, variant):
+    T, d, P, D, h = shape
+    inp = workloads.random_inputs(T, d, P, D, h, "bf16", seed=70 + D, unit_rms_x=True)
+    g, path, dy = run_backward(inp, algo="prefill", variant=variant)
+    check_grads(inp, g, path, dy, variant=variant)
+
+
+@needs_gpu
+@pytest.mark.parametrize("variant", [0, 1])
+def test_backward_full_size_sampled(variant):
+    # The OPT-1.3B-shaped depth-6 layer in the launch configuration the
+    # benchmark times, with dy nonzero on a sample of tokens only: every
+    # gradient then depends on those tokens alone, so the oracle's backward
+    # over the sample is the exact reference.
+    inp = workloads.workload("opt1p3b_d6")
+    s = inp.shape
+    T = to_device(inp)
+    print(f"[gpu] backward full size variant={variant}", flush=True)
+    _, path = fff.forward(T["x"], T["W_node"], T["b_node"], T["V_node"], T["W_out"],
+                          variant=variant)
+    torch.cuda.synchronize()
+    path = path.cpu().numpy()
+    # Sampled tokens whose paths match the oracle's (a near-tie flip would
+    # move gradient to other nodes).
+    cand = np.sort(np.random.default_rng(3).choice(s.T, size=48, replace=False))
+    fc = inp.subset_tokens(cand).as_f64()
+    ok = (oracle.forward(fc["x"], fc["W_node"], fc["b_node"], fc["V_node"], fc["W_out"],
+                         want_y=False, variant=variant)["path"] == path[cand]).all(axis=1)
+    rows = cand[ok][:24]
+    assert len(rows) == 24
+    dy = np.zeros((s.T, s.d))
+    dy[rows] = np.random.default_rng(4).standard_normal((len(rows), s.d))
+    dy_t = torch.from_numpy(dy).to(torch.bfloat16)
+    dy64 = dy_t.double().numpy()
+    g = fff.backward(T["x"], T["W_node"], T["b_node"], T["V_node"], T["W_out"],
+                     dy_t.to(T["x"].device), variant=variant)
+    torch.cuda.synchronize()
+    g = {k: to_f64(v) for k, v in g.items()}
+    f = inp.subset_tokens(rows).as_f64()
+    ref = oracle.backward(f["x"], f["W_node"], f["b_node"], f["V_node"], f["W_out"], dy64[rows],
+                          variant=variant)
+    assert (g["dx"][np.setdiff1d(np.arange(s.T), rows)] == 0).all()
+    errs = {"dx": (grad_error(g["dx"][rows], ref["dx"]), norm_error(g["dx"][rows], ref["dx"]))}
+    for k in ("dW_node", "db_node", "dV_node", "dW_out"):
+        errs[k] = (grad_error(g[k], ref[k]), norm_error(g[k], ref[k]))
+    print("grad errors (elementwise, normwise)", errs, flush=True)
+    bad = {k: e for k, e in errs.items() if e[0] > TOL["bf16"] or e[1] > TOL_NORM["bf16"]}
+    assert not bad, bad
