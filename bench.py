@@ -46,6 +46,8 @@ def parse():
                          "leaf mask) and run fff_forward_pruned")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="oracle sample budget")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--backward", action="store_true",
+                    help="time fff_backward (gradients of sum(y * dy)) on the workload instead")
     ap.add_argument("--depth-sweep", action="store_true",
                     help="time the layer at depths 0..11 (the headline's T, d, P, h) beside a "
                          "dense FF block of width 4d; one JSON line per depth")
@@ -262,6 +264,66 @@ def depth_sweep(args):
         torch.cuda.empty_cache()
 
 
+def backward_bench(args):
+    """fff_backward on the workload: one step is the whole backward pass
+    (routing again, dH, the masked products for dx, dW, dW_out, dV) for one
+    batch, inputs and dy resident in HBM, input sets rotated."""
+    import numpy as np
+    import torch
+
+    import sparse_tree_structured_amd as fff
+    import workloads
+
+    dev = torch.device("cuda:0")
+    shape, opts = workloads.WORKLOADS[args.workload]
+    footprint = (shape.T * shape.d * 2 + shape.P * shape.N * (shape.d + shape.h + 1)
+                 + shape.P * shape.h * shape.d) * 2
+    rotate = args.rotate or int(min(8, max(2, -(-600_000_000 // footprint))))
+
+    def upload(inp, seed):
+        out = [torch.from_numpy(getattr(inp, k).view(np.int16)).view(torch.bfloat16).to(dev)
+               for k in ("x", "W_node", "b_node", "V_node", "W_out")]
+        g = torch.Generator(device="cpu")
+        g.manual_seed(seed)
+        out.append((torch.randn(shape.T, shape.d, generator=g) / shape.d ** 0.5)
+                   .to(torch.bfloat16).to(dev))
+        return out
+
+    sets = [upload(workloads.make_inputs(shape, seed=s, **opts), s) for s in range(rotate)]
+    variant = fff.VARIANTS[args.variant]
+    fshape = fff.shape_of(sets[0][0], sets[0][1], sets[0][3], variant)
+    plan = fff.make_plan(args.algo)
+    nbytes = fff.backward_workspace_size(fshape, plan)
+    ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+    f32 = dict(dtype=torch.float32, device=dev)
+    out = {"dx": torch.empty_like(sets[0][0]), "dW_node": torch.empty(sets[0][1].shape, **f32),
+           "db_node": torch.empty(sets[0][2].shape, **f32),
+           "dV_node": torch.empty(sets[0][3].shape, **f32),
+           "dW_out": torch.empty(sets[0][4].shape, **f32)}
+
+    def step(i):
+        x, W, b, V, Wo, dy = sets[i % rotate]
+        fff.backward(x, W, b, V, Wo, dy, algo=args.algo, workspace=ws, out=out, variant=variant)
+
+    t_ms = _events_ms(torch, step, args.steps, args.warmup)
+    s = shape
+    L = s.D + 1
+    # The backward's matrix products as the method needs them (visited nodes
+    # only) and as the masked form executes them (every node of the levels).
+    alg = 2 * 2 * s.T * s.P * s.h * s.d + 2 * 2 * s.T * s.P * L * s.d + 2 * s.T * s.P * L * s.h
+    executed = 2 * 2 * s.T * s.P * s.h * s.d + 2 * 2 * s.T * (s.P << L) * s.d + \
+        2 * s.T * (s.P << L) * s.h
+    print(json.dumps({
+        "metric": "FFF layer backward tokens/sec (bf16)", "value": s.T / (t_ms * 1e-3),
+        "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": t_ms, "higher_is_better": True, "dtype": "bf16" if s.dtype == "bf16" else "f32",
+        "data": "synthetic", "config": {"workload": args.workload, "T": s.T, "d": s.d, "P": s.P,
+                                        "D": s.D, "h": s.h, "variant": args.variant,
+                                        "algo": args.algo, "rotated_sets": rotate},
+        "flops": {"algorithmic": alg, "executed": executed,
+                  "executed_tflops": executed / (t_ms * 1e-3) / 1e12}}), flush=True)
+
+
 def dataclasses_replace(obj, **kw):
     import dataclasses
     return dataclasses.replace(obj, **kw)
@@ -274,6 +336,9 @@ def main():
         return
     if args.depth_sweep:
         depth_sweep(args)
+        return
+    if args.backward:
+        backward_bench(args)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
