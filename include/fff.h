@@ -108,7 +108,11 @@ typedef struct fff_shape {
  * a split level k with 2^k <= 256 and D-k <= 3.  DECODE (one kernel for
  * the whole layer, routing overlapped with the stream of W_out) needs bf16,
  * 1 <= T <= 64, d % 128 == 0, d <= 2048, h % 8 == 0, h <= 256,
- * P*h % 512 == 0 and D <= 15; AUTO takes it whenever the shape allows. */
+ * P*h % 512 == 0 and D <= 15; AUTO takes it whenever the shape allows.
+ * DECODE tags its cross-workgroup slots with a fresh per-call value passed
+ * from the host, so a DECODE call must not be captured into a HIP graph and
+ * replayed (a replay would reuse the value); capture PREFILL or GENERIC
+ * plans instead, which launch only ordinary kernels (no memset nodes). */
 typedef enum fff_algo {
     FFF_ALGO_AUTO = 0,
     FFF_ALGO_GENERIC = 1,

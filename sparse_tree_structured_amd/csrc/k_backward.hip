@@ -475,13 +475,10 @@ namespace {
 
 template <int kOut>
 hipError_t launch_gemm_nt(GemmArgs g, int batches, hipStream_t st) {
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_nt_kernel<kOut>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       static_cast<int>(BwdTile::kLdsBytes));
+  {
+    const hipError_t e = ensure_lds_limit(reinterpret_cast<const void*>(gemm_nt_kernel<kOut>),
+                                          static_cast<int>(BwdTile::kLdsBytes));
     if (e != hipSuccess) return e;
-    attr_set = true;
   }
   g.tiles_m = (g.M + BwdTile::BM - 1) / BwdTile::BM;
   g.tiles_n = (g.N + BwdTile::BN - 1) / BwdTile::BN;

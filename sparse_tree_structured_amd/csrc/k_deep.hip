@@ -359,13 +359,10 @@ hipError_t launch_deep(const Dims& s, int k, const void* x, const void* W, const
   const int rounds = (nchunks + 7) / 8;
   const DeepLds L = deep_lds(s.d, s.h, k);
   auto kern = deep_kernel<8>;
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       static_cast<int>(80 * 1024));
+  {
+    const hipError_t e =
+        ensure_lds_limit(reinterpret_cast<const void*>(kern), 80 * 1024);
     if (e != hipSuccess) return e;
-    attr_set = true;
   }
   kern<<<dim3(rounds * 8 * ipc), dim3(8 * 64), L.total, st>>>(
       static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(W),

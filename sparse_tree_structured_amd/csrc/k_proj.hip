@@ -233,13 +233,10 @@ hipError_t launch_cfg(const Dims& s, const void* H, const void* Wout, void* y, h
   const int tiles_m = static_cast<int>((s.T + C::BM - 1) / C::BM);
   const int tiles_n = (s.d + C::BN - 1) / C::BN;
   auto kern = proj_mfma_kernel<C>;
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       static_cast<int>(C::kLdsBytes));
+  {
+    const hipError_t e =
+        ensure_lds_limit(reinterpret_cast<const void*>(kern), static_cast<int>(C::kLdsBytes));
     if (e != hipSuccess) return e;
-    attr_set = true;
   }
   kern<<<dim3(tiles_m * tiles_n), dim3(C::kThreads), C::kLdsBytes, st>>>(
       static_cast<const uint16_t*>(H), static_cast<const uint16_t*>(Wout),
@@ -284,13 +281,10 @@ hipError_t launch_project_direct(const Dims& s, const void* H, const void* WT, v
   const int tiles_m = static_cast<int>((s.T + C::BM - 1) / C::BM);
   const int tiles_n = (s.d + C::BN - 1) / C::BN;
   auto kern = proj_direct_kernel<C>;
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       static_cast<int>(C::kLdsBytes));
+  {
+    const hipError_t e =
+        ensure_lds_limit(reinterpret_cast<const void*>(kern), static_cast<int>(C::kLdsBytes));
     if (e != hipSuccess) return e;
-    attr_set = true;
   }
   kern<<<dim3(tiles_m * tiles_n), dim3(C::kThreads), C::kLdsBytes, st>>>(
       static_cast<const uint16_t*>(H), static_cast<const uint16_t*>(WT), static_cast<uint16_t*>(y),

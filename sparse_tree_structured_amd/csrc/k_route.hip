@@ -375,13 +375,10 @@ hipError_t launch_top_cfg(const Dims& s, int L, const void* x, const void* W, co
   else
     kern = route_top_kernel<C>;
   const size_t lds = top_lds_bytes<C>();
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       static_cast<int>(lds));
+  {
+    const hipError_t e =
+        ensure_lds_limit(reinterpret_cast<const void*>(kern), static_cast<int>(lds));
     if (e != hipSuccess) return e;
-    attr_set = true;
   }
   kern<<<dim3(tiles_m * tiles_n), dim3(C::kThreads), lds, st>>>(
       static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(W),
@@ -445,12 +442,10 @@ hipError_t launch_hbuild_l(const Dims& s, const float* rec_logit, const int32_t*
                            const void* V, void* H, int32_t* path_out, hipStream_t st) {
   const size_t lds = hbuild_lds_bytes(s);
   auto kern = hbuild_kernel<LEVELS, HSHIFT, F32>;
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+  {
+    const hipError_t e =
+        ensure_lds_limit(reinterpret_cast<const void*>(kern), 160 * 1024);
     if (e != hipSuccess) return e;
-    attr_set = true;
   }
   const dim3 grid(static_cast<unsigned>((s.T + kHbTok - 1) / kHbTok), static_cast<unsigned>(s.P));
   kern<<<grid, dim3(256), lds, st>>>(rec_logit, rec_next, static_cast<const uint16_t*>(V),

@@ -7,7 +7,27 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <mutex>
+#include <utility>
+#include <vector>
+
 namespace fff {
+
+// Raises a kernel's dynamic-LDS limit to `bytes`, once per (kernel, device):
+// the attribute belongs to the device current at the call.
+inline hipError_t ensure_lds_limit(const void* kernel, int bytes) {
+  static std::mutex mu;
+  static std::vector<std::pair<const void*, int>> done;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> lock(mu);
+  for (const auto& kd : done)
+    if (kd.first == kernel && kd.second == dev) return hipSuccess;
+  e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  if (e == hipSuccess) done.emplace_back(kernel, dev);
+  return e;
+}
 
 // Static path pruning: views into a device table built once per leaf mask.
 // A node is alive when some leaf below it is; a routed step into a pruned
