@@ -223,7 +223,25 @@ def depth_sweep(args):
                       "tokens_per_s": T / (t_dense * 1e-3),
                       "tflops": dense_flops / (t_dense * 1e-3) / 1e12,
                       "impl": "torch linear (hipBLASLt) + tanh GELU, bf16"}), flush=True)
-    del xs
+    # The same block with this library's matrix-core product (fff_project,
+    # y = H . W with W row-major [K, N]) for both products; bias and GELU in
+    # torch between them.
+    w1t, w2t = w1.t().contiguous(), w2.t().contiguous()
+    hid = torch.empty((T, dff), dtype=torch.bfloat16, device=dev)
+    yd = torch.empty((T, d), dtype=torch.bfloat16, device=dev)
+
+    def dense_ours(i):
+        fff.project(xs[i % len(xs)], w1t, y=hid)
+        h2 = torch.nn.functional.gelu(hid + b1, approximate="tanh")
+        fff.project(h2, w2t, y=yd)
+
+    t_ours = _events_ms(torch, dense_ours, steps, warmup)
+    print(json.dumps({"sweep": "dense_ff_ours", "d_ff": dff, "T": T, "d": d, "ms": t_ours,
+                      "tokens_per_s": T / (t_ours * 1e-3),
+                      "tflops": dense_flops / (t_ours * 1e-3) / 1e12,
+                      "impl": "fff_project (matrix-core) x2 + torch bias and tanh GELU, bf16"}),
+          flush=True)
+    del xs, hid, yd, w1t, w2t
 
     for D in depths:
         shape = dataclasses_replace(base, D=D)
