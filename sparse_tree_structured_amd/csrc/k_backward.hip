@@ -25,6 +25,8 @@
 //                         dS_p: dH_p, or GELU'(s) * dH_p)
 // all as one bf16 "A . B^T" kernel over K-contiguous rows (the forward's
 // direct-to-LDS main loop), with the token-major operands transposed once.
+#include <algorithm>
+
 #include "fff.h"
 
 #include "common.hpp"
@@ -206,11 +208,13 @@ hipError_t backward_generic_t(const Dims& s, const void* x, const void* W, const
 
 using BwdTile = DirectCfg<256, 256, 128, 64, 4>;
 
-// C (+)= A . B^T over K-contiguous bf16 rows.  Grid: batches x ksplit x
-// tiles, XCD-aware.  Output modes: kBf16 stores; kF32 stores; kF32Add
-// float32 atomic adds (outputs pre-zeroed; split-K and batches allowed),
-// with rows remapped from the dense node layout (row r = p * 2^L + n ->
-// p * Nn + n, the spare column n = 2^L - 1 dropped) when L > 0.
+// C = A . B^T over K-contiguous bf16 rows.  Grid: batches x ksplit x
+// tiles, XCD-aware.  Output modes: kBf16 stores; kF32 stores, split ks of
+// the k dimension writing its partial product at C + ks * split_stride (a
+// separate pass sums the splits: float32 atomics here measured 0.85 ms
+// slower per backward call at the OPT-1.3B shape), with rows remapped from
+// the dense node layout (row r = p * 2^L + n -> p * Nn + n, the spare column
+// n = 2^L - 1 dropped) when L > 0.
 struct GemmArgs {
   const uint16_t* A;
   const uint16_t* B;
@@ -221,9 +225,10 @@ struct GemmArgs {
   int tiles_m, tiles_n, ksplit;
   int L;
   int64_t Nn;
+  int64_t split_stride;  // elements of C between the splits' partial products
 };
 
-enum GemmOut { kBf16 = 0, kF32 = 1, kF32Add = 2 };
+enum GemmOut { kBf16 = 0, kF32 = 1 };
 
 template <int kOut>
 __global__ __launch_bounds__(BwdTile::kThreads) void gemm_nt_kernel(GemmArgs g) {
@@ -261,7 +266,7 @@ __global__ __launch_bounds__(BwdTile::kThreads) void gemm_nt_kernel(GemmArgs g) 
     const int row = m0 + wm * C::WM + i * 32 + (lane & 31);
     if (row >= g.M) continue;
     int64_t out_row = batch * g.c_bstride + row;
-    if (kOut == kF32Add && g.L > 0) {
+    if (kOut == kF32 && g.L > 0) {
       const int n = row & mask;
       if (n == mask) continue;  // the spare column of each tree
       out_row = batch * g.c_bstride + static_cast<int64_t>(row >> g.L) * g.Nn + n;
@@ -272,14 +277,10 @@ __global__ __launch_bounds__(BwdTile::kThreads) void gemm_nt_kernel(GemmArgs g) 
       for (int q = 0; q < 4; ++q) {
         const int col = n0 + wn * C::WN + j * 32 + q * 8 + (lane >> 5) * 4;
         if (col >= g.N) continue;
-        if constexpr (kOut == kF32Add) {
-          float* dst = static_cast<float*>(g.C) + out_row * g.ldc + col;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) atomicAdd(dst + e, acc[i][j][4 * q + e]);
-        } else if constexpr (kOut == kF32) {
-          *reinterpret_cast<float4*>(static_cast<float*>(g.C) + out_row * g.ldc + col) =
-              make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
-                          acc[i][j][4 * q + 3]);
+        if constexpr (kOut == kF32) {
+          float* dst = static_cast<float*>(g.C) + ks * g.split_stride + out_row * g.ldc + col;
+          *reinterpret_cast<float4*>(dst) = make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1],
+                                                        acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
         } else {
           uint16_t* dst = static_cast<uint16_t*>(g.C) + out_row * g.ldc + col;
           *reinterpret_cast<uint2*>(dst) =
@@ -288,6 +289,21 @@ __global__ __launch_bounds__(BwdTile::kThreads) void gemm_nt_kernel(GemmArgs g) 
         }
       }
     }
+  }
+}
+
+// out[i] = sum over s < ks of part[s * n + i], in split order (n % 4 == 0).
+__global__ __launch_bounds__(256) void sum_splits_kernel(const float* __restrict__ part,
+                                                         float* __restrict__ out, int64_t n,
+                                                         int ks) {
+  for (int64_t i = (static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x) * 4; i < n;
+       i += static_cast<int64_t>(gridDim.x) * blockDim.x * 4) {
+    float4 a = *reinterpret_cast<const float4*>(part + i);
+    for (int s = 1; s < ks; ++s) {
+      const float4 b = *reinterpret_cast<const float4*>(part + s * n + i);
+      a.x += b.x; a.y += b.y; a.z += b.z; a.w += b.w;
+    }
+    *reinterpret_cast<float4*>(out + i) = a;
   }
 }
 
@@ -503,6 +519,29 @@ hipError_t transpose_rows(const uint16_t* src, int64_t ld_src, uint16_t* dst, in
   return hipGetLastError();
 }
 
+// Splits of the token dimension of the dW, dW_out and dV products.
+struct BwdSplits {
+  int w, o, v;
+};
+BwdSplits bwd_splits(const Dims& s) {
+  const int L = s.D + 1;
+  const int64_t Tp = (s.T + 255) / 256 * 256;
+  const int cols = s.P << L;
+  BwdSplits k;
+  k.w = token_splits(((cols + 255) / 256) * ((s.d + 255) / 256), Tp);
+  k.o = token_splits(static_cast<int>(((s.K + 255) / 256) * ((s.d + 255) / 256)), Tp);
+  k.v = token_splits(s.P * ((s.h + 255) / 256), Tp);
+  return k;
+}
+
+hipError_t sum_splits(const float* part, float* out, int64_t n, int ks, hipStream_t st) {
+  int64_t blocks = (n / 4 + 255) / 256;
+  if (blocks > 8192) blocks = 8192;
+  sum_splits_kernel<<<dim3(static_cast<unsigned>(blocks < 1 ? 1 : blocks)), 256, 0, st>>>(part, out,
+                                                                                            n, ks);
+  return hipGetLastError();
+}
+
 size_t paths_lds(const Dims& s) {
   return (size_t(s.N) * s.h * 2 + 15) / 16 * 16 + (size_t(1) << (s.D + 1)) * 4;
 }
@@ -535,6 +574,14 @@ BwdMfmaLayout backward_mfma_layout(const Dims& s) {
   B.Ht = off;     off = up(off + size_t(s.K) * Tp * 2);
   B.dSt = off;    off = up(off + size_t(s.K) * Tp * 2);
   B.WTn = off;    off = up(off + size_t(s.d) * cols * 2);
+  // Partial products of the split token dimension (the largest of the three).
+  const BwdSplits k = bwd_splits(s);
+  size_t part = 0;
+  const size_t nW = size_t(s.P) * s.N * s.d, nO = size_t(s.K) * s.d, nV = size_t(s.P) * s.N * s.h;
+  if (k.w > 1) part = std::max(part, k.w * nW);
+  if (k.o > 1) part = std::max(part, k.o * nO);
+  if (k.v > 1) part = std::max(part, k.v * nV);
+  B.part = off;   off = up(off + part * 4);
   B.total = off;
   return B;
 }
@@ -564,10 +611,11 @@ hipError_t launch_backward_mfma(const Dims& s, const void* x, const void* W, con
   hipError_t e;
 #define FFF_TRY(call) \
   if ((e = (call)) != hipSuccess) return e
-  FFF_TRY(launch_fill_f32(dW, int64_t(s.P) * s.N * s.d, st));
+  float* part = reinterpret_cast<float*>(w + B.part);
+  const BwdSplits k = bwd_splits(s);
+  const int64_t nW = int64_t(s.P) * s.N * s.d, nO = s.K * s.d, nV = int64_t(s.P) * s.N * s.h;
+  // db gathers atomically; dW, dW_out and dV are written in full below.
   FFF_TRY(launch_fill_f32(db, int64_t(s.P) * s.N, st));
-  FFF_TRY(launch_fill_f32(dV, int64_t(s.P) * s.N * s.h, st));
-  FFF_TRY(launch_fill_f32(dWout, s.K * s.d, st));
   FFF_TRY(launch_route_top(s, L, x, W, b, logits, next, st));
   FFF_TRY(transpose_rows(x16, s.d, xT, Tp, s.T, Tp, s.d, 0, 0, 0, st));
   FFF_TRY(transpose_rows(dy16, s.d, dyT, Tp, s.T, Tp, s.d, 0, 0, 0, st));
@@ -593,24 +641,30 @@ hipError_t launch_backward_mfma(const Dims& s, const void* x, const void* W, con
   g = GemmArgs{};
   g.A = DAt; g.lda = Tp; g.B = xT; g.ldb = Tp; g.C = dW; g.ldc = s.d;
   g.M = cols; g.N = s.d; g.L = L; g.Nn = s.N;
-  g.ksplit = token_splits(((cols + 255) / 256) * ((s.d + 255) / 256), Tp);
+  g.ksplit = k.w;
   g.Kk = static_cast<int>(Tp / g.ksplit);
-  FFF_TRY(launch_gemm_nt<kF32Add>(g, 1, st));
+  if (k.w > 1) g.C = part, g.split_stride = nW;
+  FFF_TRY(launch_gemm_nt<kF32>(g, 1, st));
+  if (k.w > 1) FFF_TRY(sum_splits(part, dW, nW, k.w, st));
   // dW_out = H^T . dy  [K, d]
   g = GemmArgs{};
   g.A = Ht; g.lda = Tp; g.B = dyT; g.ldb = Tp; g.C = dWout; g.ldc = s.d;
   g.M = static_cast<int>(s.K); g.N = s.d;
-  g.ksplit = token_splits(static_cast<int>(((s.K + 255) / 256) * ((s.d + 255) / 256)), Tp);
+  g.ksplit = k.o;
   g.Kk = static_cast<int>(Tp / g.ksplit);
-  FFF_TRY(launch_gemm_nt<kF32Add>(g, 1, st));
+  if (k.o > 1) g.C = part, g.split_stride = nO;
+  FFF_TRY(launch_gemm_nt<kF32>(g, 1, st));
+  if (k.o > 1) FFF_TRY(sum_splits(part, dWout, nO, k.o, st));
   // dV_p = G_p^T . dS_p  [2^L -> N, h], one batch per tree
   g = GemmArgs{};
   g.A = Gt; g.lda = Tp; g.a_bstride = int64_t(1) << L;
   g.B = dSt; g.ldb = Tp; g.b_bstride = s.h;
   g.C = dV; g.ldc = s.h; g.c_bstride = s.N; g.M = 1 << L; g.N = s.h; g.L = L; g.Nn = s.N;
-  g.ksplit = token_splits(s.P * ((s.h + 255) / 256), Tp);
+  g.ksplit = k.v;
   g.Kk = static_cast<int>(Tp / g.ksplit);
-  FFF_TRY(launch_gemm_nt<kF32Add>(g, s.P, st));
+  if (k.v > 1) g.C = part, g.split_stride = nV;
+  FFF_TRY(launch_gemm_nt<kF32>(g, s.P, st));
+  if (k.v > 1) FFF_TRY(sum_splits(part, dV, nV, k.v, st));
 #undef FFF_TRY
   return hipSuccess;
 }

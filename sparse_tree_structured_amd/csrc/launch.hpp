@@ -130,9 +130,10 @@ hipError_t launch_backward_generic(const Dims& s, const void* x, const void* W, 
 
 // Matrix-core path: bf16, every level dense (3 <= D+1 <= 8), d and h
 // multiples of 64.  Workspace: routing records, transposed x and dy, dH, the
-// masked DA (and its transpose), G^T, H^T, dS^T and the node rows transposed.
+// masked DA (and its transpose), G^T, H^T, dS^T, the node rows transposed
+// and the float32 partial products of the split token dimension.
 struct BwdMfmaLayout {
-  size_t logits, next, xT, dyT, dH, DA, DAt, Gt, Ht, dSt, WTn, total;
+  size_t logits, next, xT, dyT, dH, DA, DAt, Gt, Ht, dSt, WTn, part, total;
   int64_t Tp;  // tokens padded to a multiple of 256
 };
 bool backward_mfma_supported(const Dims& s);

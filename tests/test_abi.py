@@ -263,7 +263,8 @@ def test_backward_plans_and_workspace():
     assert fff.backward_workspace_size(s) == fff.backward_workspace_size(s, fff.make_plan("prefill"))
     T, Tp, cols, K, d = 16384, 16384, 32 * 128, 32 * 128, 2048
     expect = (up(T * 32 * 7 * 4) + up(T * 32 * 4) + 2 * up(d * Tp * 2) + up(T * K * 4) +
-              up(T * cols * 2) + 2 * up(cols * Tp * 2) + 2 * up(K * Tp * 2) + up(d * cols * 2))
+              up(T * cols * 2) + 2 * up(cols * Tp * 2) + 2 * up(K * Tp * 2) + up(d * cols * 2) +
+              up(max(2 * 32 * 127 * d, 2 * K * d, 8 * 32 * 127 * 128) * 4))  # split partials
     assert fff.backward_workspace_size(s) == expect
     # Generic for fp32, deep (split) trees and shallow trees.
     g = _shape(T=100, d=64, P=2, D=3, h=32, dtype=fff.DTYPE_F32)
