@@ -57,7 +57,7 @@ typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kDecThreads = 256;
 constexpr int kDecWaves = kDecThreads / kWave;
-constexpr int kDecTok = 16;       // tokens per routing item (one MFMA column block)
+constexpr int kDecTok = 16;       // most tokens per routing item (one MFMA column block)
 constexpr int kKc = 512;          // projection: K rows per item
 constexpr int kColSlice = 64;     // projection: output columns per item
 constexpr int kMaxRows = 16;      // node rows per routing round (one MFMA row block)
@@ -86,6 +86,7 @@ struct DecodeArgs {
   int T, d, P, D, h, K;
   int64_t N;
   int n_route_wg, n_proj_wg;
+  int tok;               // tokens per routing item (<= kDecTok)
   int post;              // 1: GELU on the summed h-vector instead of on each node's logit
   const uint8_t* alive;  // static pruning: [P][N] 1 = node alive; null = every node
 };
@@ -507,14 +508,14 @@ __device__ void reduce_slice(const DecodeArgs& a, int cs) {
 __global__ __launch_bounds__(kDecThreads, 2) void decode_kernel(DecodeArgs a) {
   extern __shared__ __align__(16) unsigned char lds[];
   __shared__ int last;
-  const int per_tree = (a.T + kDecTok - 1) / kDecTok;
+  const int per_tree = (a.T + a.tok - 1) / a.tok;
   const int nroute = a.P * per_tree;
   const int g = blockIdx.x;
   if (g < a.n_route_wg) {
     for (int it = g; it < nroute; it += a.n_route_wg) {
       const int p = it / per_tree;
-      const int t0 = (it - p * per_tree) * kDecTok;
-      route_item(a, lds, it, p, t0, min(kDecTok, a.T - t0));
+      const int t0 = (it - p * per_tree) * a.tok;
+      route_item(a, lds, it, p, t0, min(a.tok, a.T - t0));
     }
     return;
   }
@@ -588,8 +589,18 @@ bool decode_supported(const Dims& s) {
          s.K * s.d < (int64_t(1) << 30);
 }
 
+// Tokens per routing item.  A round evaluates at most kMaxRows node rows:
+// below n distinct current nodes it takes the deepest subtree with
+// n (2^levels - 1) rows that fit, so with at most 2 tokens per item every
+// round after the first covers 3 levels (a depth-6 walk takes 2 rounds, not
+// the 4 of a 16-token item whose tokens spread over 16 nodes).  Small
+// batches use 2 while the items fit half of a 256-CU grid; larger ones 16.
+static int tokens_per_item(const Dims& s) {
+  return s.T <= 16 && int64_t(s.P) * ((s.T + 1) / 2) <= 256 ? 2 : kDecTok;
+}
+
 size_t decode_workspace(const Dims& s) {
-  const size_t items = size_t(s.P) * ((s.T + kDecTok - 1) / kDecTok);
+  const size_t items = size_t(s.P) * ((s.T + tokens_per_item(s) - 1) / tokens_per_item(s));
   return up256(items * 8) + up256(size_t(s.T) * s.K * 2) +
          up256(size_t(s.d / kColSlice) * (s.K / kKc) * 8) + up256(size_t(s.K / kKc) * s.T * s.d * 4);
 }
@@ -605,7 +616,8 @@ hipError_t launch_decode(const Dims& s, const void* x, const void* W, const void
   a.Wout = static_cast<const uint16_t*>(Wout);
   a.y = static_cast<uint16_t*>(y);
   a.path_out = path_out;
-  const int nroute = s.P * static_cast<int>((s.T + kDecTok - 1) / kDecTok);
+  a.tok = tokens_per_item(s);
+  const int nroute = s.P * static_cast<int>((s.T + a.tok - 1) / a.tok);
   char* w = static_cast<char*>(ws);
   a.done = reinterpret_cast<uint64_t*>(w);
   w += up256(size_t(nroute) * 8);

@@ -191,9 +191,14 @@ def test_decode_workspace_covers_route(lib):
     dec = fff.workspace_size(s, fff.make_plan("decode"))
     pre = fff.workspace_size(s, fff.make_plan("prefill"))
     assert auto >= dec > 0 and auto >= pre > 0
-    # 32 routing-item slots (64-bit, rounded up to 256 bytes), H [8, 4096]
-    # bf16, 32 x 8 arrival slots and 8 K-chunk partials of y [8, 2048] fp32.
-    assert dec == 256 + 8 * 4096 * 2 + 32 * 8 * 8 + 8 * 8 * 2048 * 4
+    # 128 routing-item slots (2 tokens per item at 8 tokens; 64-bit each),
+    # H [8, 4096] bf16, 32 x 8 arrival slots and 8 K-chunk partials of y
+    # [8, 2048] fp32.
+    assert dec == 32 * 4 * 8 + 8 * 4096 * 2 + 32 * 8 * 8 + 8 * 8 * 2048 * 4
+    # 64 tokens: 16 per item, 4 items per tree.
+    s64 = _shape(T=64, d=2048, P=32, D=6, h=128)
+    assert fff.workspace_size(s64, fff.make_plan("decode")) == \
+        32 * 4 * 8 + 64 * 4096 * 2 + 32 * 8 * 8 + 8 * 64 * 2048 * 4
     st = lib.fff_route(ctypes.byref(s), ctypes.byref(fff.make_plan("decode")), FAKE, FAKE, FAKE,
                        FAKE, FAKE, FAKE, FAKE, 1 << 40, None)
     assert st == fff.ERROR_NOT_SUPPORTED
