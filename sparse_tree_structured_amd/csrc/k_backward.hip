@@ -207,6 +207,9 @@ hipError_t backward_generic_t(const Dims& s, const void* x, const void* W, const
 // Matrix-core path.
 
 using BwdTile = DirectCfg<256, 256, 128, 64, 4>;
+// One tree's dV product is 2^L x h (128 x 128 at the headline): a quarter of
+// a 256 x 256 tile, so it takes 128 x 128 tiles on 4 waves.
+using BwdSmallTile = DirectCfg<128, 128, 64, 64, 4>;
 
 // C = A . B^T over K-contiguous bf16 rows.  Grid: batches x ksplit x
 // tiles, XCD-aware.  Output modes: kBf16 stores; kF32 stores, split ks of
@@ -230,9 +233,8 @@ struct GemmArgs {
 
 enum GemmOut { kBf16 = 0, kF32 = 1 };
 
-template <int kOut>
-__global__ __launch_bounds__(BwdTile::kThreads) void gemm_nt_kernel(GemmArgs g) {
-  using C = BwdTile;
+template <class C, int kOut>
+__global__ __launch_bounds__(C::kThreads) void gemm_nt_kernel(GemmArgs g) {
   extern __shared__ __align__(16) unsigned char lds[];
   const int logical = xcd_logical_tile(blockIdx.x, gridDim.x);
   const int per = g.tiles_m * g.tiles_n;
@@ -489,17 +491,17 @@ hipError_t launch_backward_generic(const Dims& s, const void* x, const void* W, 
 
 namespace {
 
-template <int kOut>
+template <class C, int kOut>
 hipError_t launch_gemm_nt(GemmArgs g, int batches, hipStream_t st) {
   {
-    const hipError_t e = ensure_lds_limit(reinterpret_cast<const void*>(gemm_nt_kernel<kOut>),
-                                          static_cast<int>(BwdTile::kLdsBytes));
+    const hipError_t e = ensure_lds_limit(reinterpret_cast<const void*>(gemm_nt_kernel<C, kOut>),
+                                          static_cast<int>(C::kLdsBytes));
     if (e != hipSuccess) return e;
   }
-  g.tiles_m = (g.M + BwdTile::BM - 1) / BwdTile::BM;
-  g.tiles_n = (g.N + BwdTile::BN - 1) / BwdTile::BN;
+  g.tiles_m = (g.M + C::BM - 1) / C::BM;
+  g.tiles_n = (g.N + C::BN - 1) / C::BN;
   const int blocks = g.tiles_m * g.tiles_n * g.ksplit * batches;
-  gemm_nt_kernel<kOut><<<dim3(blocks), dim3(BwdTile::kThreads), BwdTile::kLdsBytes, st>>>(g);
+  gemm_nt_kernel<C, kOut><<<dim3(blocks), dim3(C::kThreads), C::kLdsBytes, st>>>(g);
   return hipGetLastError();
 }
 
@@ -530,7 +532,7 @@ BwdSplits bwd_splits(const Dims& s) {
   BwdSplits k;
   k.w = token_splits(((cols + 255) / 256) * ((s.d + 255) / 256), Tp);
   k.o = token_splits(static_cast<int>(((s.K + 255) / 256) * ((s.d + 255) / 256)), Tp);
-  k.v = token_splits(s.P * ((s.h + 255) / 256), Tp);
+  k.v = token_splits(s.P * (((1 << L) + 127) / 128) * ((s.h + 127) / 128), Tp);
   return k;
 }
 
@@ -609,8 +611,8 @@ hipError_t launch_backward_mfma(const Dims& s, const void* x, const void* W, con
   const uint16_t* x16 = static_cast<const uint16_t*>(x);
   const uint16_t* dy16 = static_cast<const uint16_t*>(dy);
   hipError_t e;
-#define FFF_TRY(call) \
-  if ((e = (call)) != hipSuccess) return e
+#define FFF_TRY(...) \
+  if ((e = (__VA_ARGS__)) != hipSuccess) return e
   float* part = reinterpret_cast<float*>(w + B.part);
   const BwdSplits k = bwd_splits(s);
   const int64_t nW = int64_t(s.P) * s.N * s.d, nO = s.K * s.d, nV = int64_t(s.P) * s.N * s.h;
@@ -626,7 +628,7 @@ hipError_t launch_backward_mfma(const Dims& s, const void* x, const void* W, con
   g.A = dy16; g.lda = s.d; g.B = static_cast<const uint16_t*>(Wout); g.ldb = s.d;
   g.C = dH; g.ldc = s.K; g.M = static_cast<int>(s.T); g.N = static_cast<int>(s.K); g.Kk = s.d;
   g.ksplit = 1;
-  FFF_TRY(launch_gemm_nt<kF32>(g, 1, st));
+  FFF_TRY(launch_gemm_nt<BwdTile, kF32>(g, 1, st));
   bwd_paths_kernel<<<dim3(static_cast<unsigned>(Tp / 256), static_cast<unsigned>(s.P)), 256,
                      paths_lds(s), st>>>(logits, next, static_cast<const uint16_t*>(V), dH, DA,
                                          DAt, Gt, Ht, dSt, db, static_cast<int>(s.T),
@@ -636,7 +638,7 @@ hipError_t launch_backward_mfma(const Dims& s, const void* x, const void* W, con
   g = GemmArgs{};
   g.A = DA; g.lda = cols; g.B = WTn; g.ldb = cols; g.C = dx; g.ldc = s.d;
   g.M = static_cast<int>(s.T); g.N = s.d; g.Kk = cols; g.ksplit = 1;
-  FFF_TRY(launch_gemm_nt<kBf16>(g, 1, st));
+  FFF_TRY(launch_gemm_nt<BwdTile, kBf16>(g, 1, st));
   // dW = DA^T . x  [P*2^L -> P*N, d]
   g = GemmArgs{};
   g.A = DAt; g.lda = Tp; g.B = xT; g.ldb = Tp; g.C = dW; g.ldc = s.d;
@@ -644,7 +646,7 @@ hipError_t launch_backward_mfma(const Dims& s, const void* x, const void* W, con
   g.ksplit = k.w;
   g.Kk = static_cast<int>(Tp / g.ksplit);
   if (k.w > 1) g.C = part, g.split_stride = nW;
-  FFF_TRY(launch_gemm_nt<kF32>(g, 1, st));
+  FFF_TRY(launch_gemm_nt<BwdTile, kF32>(g, 1, st));
   if (k.w > 1) FFF_TRY(sum_splits(part, dW, nW, k.w, st));
   // dW_out = H^T . dy  [K, d]
   g = GemmArgs{};
@@ -653,7 +655,7 @@ hipError_t launch_backward_mfma(const Dims& s, const void* x, const void* W, con
   g.ksplit = k.o;
   g.Kk = static_cast<int>(Tp / g.ksplit);
   if (k.o > 1) g.C = part, g.split_stride = nO;
-  FFF_TRY(launch_gemm_nt<kF32>(g, 1, st));
+  FFF_TRY(launch_gemm_nt<BwdTile, kF32>(g, 1, st));
   if (k.o > 1) FFF_TRY(sum_splits(part, dWout, nO, k.o, st));
   // dV_p = G_p^T . dS_p  [2^L -> N, h], one batch per tree
   g = GemmArgs{};
@@ -663,7 +665,7 @@ hipError_t launch_backward_mfma(const Dims& s, const void* x, const void* W, con
   g.ksplit = k.v;
   g.Kk = static_cast<int>(Tp / g.ksplit);
   if (k.v > 1) g.C = part, g.split_stride = nV;
-  FFF_TRY(launch_gemm_nt<kF32>(g, s.P, st));
+  FFF_TRY(launch_gemm_nt<BwdSmallTile, kF32>(g, s.P, st));
   if (k.v > 1) FFF_TRY(sum_splits(part, dV, nV, k.v, st));
 #undef FFF_TRY
   return hipSuccess;
