@@ -175,6 +175,19 @@ def pin_zero_ties(lib):
     assert (r["H"] == 0).all() and (r["y"] == 0).all()
 
 
+def pin_nan_goes_right(lib):
+    """A NaN logit is not below zero: every decision goes right (the
+    rightmost leaf), and the outputs are NaN."""
+    T, d, P, D, h = 4, 5, 2, 3, 3
+    rng = np.random.default_rng(12)
+    L = rand_layer(rng, T, d, P, D, h)
+    L["W_node"][:] = 0.0
+    L["b_node"][:] = np.nan
+    r = oracle.forward(**L, want_H=True, lib=lib, nthreads=1)
+    assert (r["path"] == (1 << D) - 1).all()
+    assert np.isnan(r["y"]).all()
+
+
 def pin_negative_bias(lib):
     """W = 0, b = -beta: every path is leaf 0 (the leftmost spine) and
     H_p = GELU(-beta) * sum over levels of V[p, 2^l - 1]."""
@@ -585,8 +598,8 @@ def pin_backward_linear_in_dy(lib):
     assert (g1["db_node"][~visited] == 0).all() and (g1["dW_node"][~visited] == 0).all()
 
 
-ALL_PINS = [pin_brute_force, pin_hand_routing, pin_zero_ties, pin_negative_bias,
-            pin_visit_count_table4, pin_depth0_dense, pin_forced_paths, pin_invariants,
+ALL_PINS = [pin_brute_force, pin_hand_routing, pin_zero_ties, pin_nan_goes_right,
+            pin_negative_bias, pin_visit_count_table4, pin_depth0_dense, pin_forced_paths, pin_invariants,
             pin_tie_threshold, pin_post_brute_force, pin_post_hand_routing,
             pin_post_closed_forms, pin_post_routing_unchanged, pin_prune_brute_force,
             pin_prune_reductions, pin_backward_finite_differences, pin_backward_dense_autograd,

@@ -11,6 +11,7 @@ import numpy as np
 import pytest
 import torch
 
+import oracle
 import workloads
 from gpu_helpers import check, run, sample_rows, to_device, to_f64
 
@@ -285,5 +286,30 @@ def test_depth_sweep_depths(D):
 def test_depth_sweep_full_width(D):
     # The sweep's own d, P and h (those of the OPT-1.3B-shaped workload).
     inp = workloads.random_inputs(200, 2048, 32, D, 128, "bf16", seed=60 + D, unit_rms_x=True)
+    y, path = run(inp)
+    check(inp, y, path)
+
+
+@needs_gpu
+@pytest.mark.parametrize("algo", ["generic", "prefill", "decode"])
+def test_nan_logits_go_right(algo):
+    # A NaN logit is not below zero, so it routes right on every path; the
+    # affected trees' outputs (and y) are NaN on both sides.
+    T = 8 if algo == "decode" else 300
+    inp = workloads.random_inputs(T, 256, 8, 5, 64, "bf16", seed=13, unit_rms_x=True)
+    nan_bf16 = np.uint16(0x7FC0)
+    inp.b_node[:, [0, 2, 5]] = nan_bf16  # the root and two deeper nodes of every tree
+    y, path = run(inp, algo=algo)
+    f = inp.as_f64()
+    ref = oracle.forward(f["x"], f["W_node"], f["b_node"], f["V_node"], f["W_out"])
+    np.testing.assert_array_equal(path, ref["path"])
+    assert (path >= (1 << 4)).all()  # the root's decision was right for every token
+    np.testing.assert_array_equal(np.isnan(y), np.isnan(ref["y"]))
+
+
+@needs_gpu
+def test_maximum_depth_generic():
+    # D = 20 (the largest the boundary takes): 2^21 - 1 nodes per tree.
+    inp = workloads.random_inputs(50, 8, 1, 20, 2, "f32", seed=14, unit_rms_x=True)
     y, path = run(inp)
     check(inp, y, path)
