@@ -228,15 +228,13 @@ __device__ void route_item(const DecodeArgs& a, unsigned char* lds, int item, in
                         : static_cast<const void*>(a.x),
                 a.alive ? uint32_t(a.N) : 0);
 
-  // This wave's slice of the token rows, kept for every round (rows past
-  // nt repeat the last token; their results are not used; k steps past the
-  // width load zeros).
+  // Byte offset of this lane's slice of its token row (rows past nt repeat
+  // the last token; their results are not used; k steps past the width load
+  // zeros).
+  const uint32_t xoff = uint32_t((t0 + (j < nt ? j : nt - 1)) * a.d + wave * klen + q * 8) * 2;
   uint4 xf[16];
-  {
-    const uint32_t xoff = uint32_t((t0 + (j < nt ? j : nt - 1)) * a.d + wave * klen + q * 8) * 2;
 #pragma unroll
-    for (int u = 0; u < 16; ++u) xf[u] = buffer_load16(xbuf, u < nsteps ? xoff + u * 64 : kOob);
-  }
+  for (int u = 0; u < 16; ++u) xf[u] = buffer_load16(xbuf, u < nsteps ? xoff + u * 64 : kOob);
   float hacc[kHPieces][8];
 #pragma unroll
   for (int i = 0; i < kHPieces; ++i)
@@ -250,17 +248,31 @@ __device__ void route_item(const DecodeArgs& a, unsigned char* lds, int item, in
   int R = (1 << rl) - 1;
   int cur = 0, troot = 0, last_node = 0;
   int prev_rl = 0, buf = 0;
+  // The first round's rows are heap ids 0 .. S-1 (every earlier reader of
+  // rows[] passed the previous item's last barrier).
+  if (tid < kMaxRows) rows[tid] = tid;
   __syncthreads();  // LDS of a previous item is no longer read
 
   for (int lev = 0;;) {
     const int S = (1 << rl) - 1;
-    // Node rows (row j of the block; rows past R repeat row 0, unused), the
-    // round's V rows, and the biases of rows 4q .. 4q+3 (wave 0).
+    // Node ids of the rows this lane reads (LDS reads issued together, then
+    // one wait): its W row and alive flags (row j; rows past R repeat row
+    // 0, unused), its V pieces, and the biases of rows 4q .. 4q+3 (wave 0).
+    const int rw = j < R ? j : 0;
+    const int node_w = rows[rw];
+    int rv[kHPieces], node_v[kHPieces];
+#pragma unroll
+    for (int i = 0; i < kHPieces; ++i) {
+      const int e = tid + i * kDecThreads;
+      rv[i] = e / hc < R ? e / hc : R - 1;
+      node_v[i] = rows[rv[i]];
+    }
+    int node_b[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) node_b[r] = rows[4 * q + r < R ? 4 * q + r : 0];
     uint4 wf[16];
     {
-      const int r = j < R ? j : 0;
-      const int node = lev == 0 ? r : rows[r];
-      const uint32_t woff = uint32_t(node * a.d + wave * klen + q * 8) * 2;
+      const uint32_t woff = uint32_t(node_w * a.d + wave * klen + q * 8) * 2;
 #pragma unroll
       for (int u = 0; u < 16; ++u) wf[u] = buffer_load16(wbuf, u < nsteps ? woff + u * 64 : kOob);
     }
@@ -268,26 +280,21 @@ __device__ void route_item(const DecodeArgs& a, unsigned char* lds, int item, in
 #pragma unroll
     for (int i = 0; i < kHPieces; ++i) {
       const int e = tid + i * kDecThreads;
-      const int r = e / hc < R ? e / hc : R - 1;
-      const int node = lev == 0 ? r : rows[r];
-      vr[i] = buffer_load16(vbuf, e < R * hc ? uint32_t(node * a.h + (e - r * hc) * 8) * 2 : kOob);
+      vr[i] = buffer_load16(
+          vbuf, e < R * hc ? uint32_t(node_v[i] * a.h + (e - rv[i] * hc) * 8) * 2 : kOob);
     }
     // Raw bias bits of rows 4q .. 4q+3 (used by wave 0), converted only
     // after the MFMA so that nothing waits on these loads before then.
     uint16_t braw[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int row = 4 * q + r < R ? 4 * q + r : 0;
-      braw[r] = buffer_load2(bbuf, 4 * q + r < R ? uint32_t(lev == 0 ? row : rows[row]) * 2 : kOob);
-    }
+    for (int r = 0; r < 4; ++r)
+      braw[r] = buffer_load2(bbuf, 4 * q + r < R ? uint32_t(node_b[r]) * 2 : kOob);
     // Alive flags of both children of row j (wave 0, lanes j < R; rows at
     // the leaf level read past the buffer and get 0, never used).
     uint8_t child_l, child_r;
     {
-      const int row = j < R ? j : 0;
-      const uint32_t off = wave == 0 && q == 0 && j < R
-                               ? uint32_t(2 * (lev == 0 ? row : rows[row]) + 1)
-                               : kOob;
+      const uint32_t off =
+          wave == 0 && q == 0 && j < R ? uint32_t(2 * node_w + 1) : kOob;
       child_l = buffer_load1(abuf, off);
       child_r = buffer_load1(abuf, off == kOob ? kOob : off + 1);
     }
@@ -343,7 +350,7 @@ __device__ void route_item(const DecodeArgs& a, unsigned char* lds, int item, in
         if (q == 0 && j < nt) rsm[j * 4 + lv] = row;
         jj = 2 * jj + 1 + bit;
       }
-      last_node = lev == 0 ? row : rows[row];
+      last_node = rows[row];
       cur = 2 * last_node + 1 + bit;
       if (lev + rl <= a.D) {
         // Plan of the next round: distinct current nodes of the tokens
