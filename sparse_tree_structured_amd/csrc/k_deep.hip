@@ -143,10 +143,23 @@ __global__ __launch_bounds__(WAVES * 64, 2) void deep_kernel(
   extern __shared__ __align__(16) unsigned char lds[];
   const int S = 1 << k;
   const int ipc = P * S;  // items per chunk
+  // Hardware sends workgroup b to XCD b % 8.  With at least 8 chunks each
+  // XCD works through its own chunks (c % 8 == XCD) one at a time; with
+  // fewer, chunk c is shared by the XCDs x with x % nchunks == c, which take
+  // its items in turn, so that no XCD idles.
   const int bid = blockIdx.x;
-  const int c = (bid / (8 * ipc)) * 8 + (bid % 8);
-  const int item = (bid / 8) % ipc;
-  if (c >= nchunks) return;
+  const int xcd = bid % 8;
+  const int local = bid / 8;
+  int c, item;
+  if (nchunks >= 8) {
+    c = (local / ipc) * 8 + xcd;
+    item = local % ipc;
+  } else {
+    c = xcd % nchunks;
+    const int share = (8 - 1 - c) / nchunks + 1;  // XCDs on chunk c
+    item = local * share + xcd / nchunks;
+  }
+  if (c >= nchunks || item >= ipc) return;
   const int p = item / S;
   const int s = item - p * S;
   const int32_t* o = offs + (static_cast<int64_t>(c) * P + p) * (S + 1);
@@ -327,15 +340,17 @@ bool deep_supported(const Dims& s, int k) {
 }
 
 size_t deep_chunk(const Dims& s, int k) {
-  // Tokens per chunk: about 8 MB of x rows, and at least 16 tokens per
-  // level-k bucket on average so that the staged subtree rows serve a full
-  // 16-token tile.  Each chunk restages every subtree's rows, so small chunks
-  // cost W_node traffic; large ones lose the x rows' cache reuse across trees.
-  // Measured at d = 2048, P = 32, h = 128, T = 16384 (ms, chunk of 1024 /
-  // 2048 / 4096 tokens): D = 9: 1.80 / 1.25 / 1.69; D = 10: - / 2.05 / 2.26;
-  // D = 11: - / - / 3.93 (16384: 6.40).
-  int64_t c = (8 << 20) / (int64_t(s.d) * 2);
-  const int64_t per_bucket = int64_t(16) << k;
+  // Tokens per chunk: about 16 MB of x rows, and at least 32 tokens per
+  // level-k bucket on average so that the staged subtree rows serve whole
+  // 16-token groups.  Each chunk restages every subtree's rows, so small
+  // chunks cost W_node traffic; large ones lose the x rows' cache reuse
+  // across trees.  Measured at d = 2048, P = 32, h = 128, T = 16384 (ms per
+  // forward, chunks of 1024 / 2048 / 4096 / 8192 / 16384 tokens): D = 8:
+  // 1.09 / 0.98 / 1.00 / 1.05 / 1.28; D = 9: 1.79 / 1.25 / 1.16 / 1.27 / 1.54;
+  // D = 10: 3.17 / 2.04 / 1.55 / 1.54 / 1.89; D = 11: 5.99 / 3.62 / 2.51 /
+  // 2.09 / 2.35.
+  int64_t c = (16 << 20) / (int64_t(s.d) * 2);
+  const int64_t per_bucket = int64_t(32) << k;
   c = c < per_bucket ? per_bucket : c;
   c = c < 64 ? 64 : c;
   return static_cast<size_t>(c < s.T ? c : s.T);
@@ -356,7 +371,10 @@ hipError_t launch_deep(const Dims& s, int k, const void* x, const void* W, const
                        hipStream_t st) {
   const int nchunks = static_cast<int>((s.T + chunk - 1) / chunk);
   const int ipc = s.P << k;
-  const int rounds = (nchunks + 7) / 8;
+  // Workgroups per XCD: every chunk's items (at least 8 chunks), or the
+  // items of a chunk split over the fewest XCDs that share one.
+  const int per_xcd = nchunks >= 8 ? ((nchunks + 7) / 8) * ipc
+                                   : (ipc + 8 / nchunks - 1) / (8 / nchunks);
   const DeepLds L = deep_lds(s.d, s.h, k);
   auto kern = deep_kernel<8>;
   {
@@ -364,7 +382,7 @@ hipError_t launch_deep(const Dims& s, int k, const void* x, const void* W, const
         ensure_lds_limit(reinterpret_cast<const void*>(kern), 80 * 1024);
     if (e != hipSuccess) return e;
   }
-  kern<<<dim3(rounds * 8 * ipc), dim3(8 * 64), L.total, st>>>(
+  kern<<<dim3(8 * per_xcd), dim3(8 * 64), L.total, st>>>(
       static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(W),
       static_cast<const uint16_t*>(b), static_cast<const uint16_t*>(V), rec_logit, perm, offs,
       static_cast<uint16_t*>(H), path_out, static_cast<int>(s.T), s.d, s.P, s.D, s.h, s.N, k,
