@@ -7,26 +7,30 @@
 // subtree share its weights, so:
 //
 //  bucket_kernel  groups, per (token chunk, tree), the chunk's tokens by
-//                 their level-k node: a wavefront matches equal buckets with
-//                 ballots, ranks lanes with a masked popcount, and makes one
-//                 LDS atomic per (wavefront, bucket); counts are scanned into
-//                 offsets and token ids scattered into a permutation.
+//                 their level-k node: counts with LDS atomics, an exclusive
+//                 scan into bucket offsets, token ids scattered into a
+//                 permutation.
 //
-//  deep_kernel    one workgroup per (chunk, tree, subtree): stages the
-//                 subtree's w_n rows, biases and v_n rows (plus the v_n rows
-//                 of the shared top path) in LDS once, then for groups of 16
-//                 tokens computes all subtree logits with
-//                 v_mfma_f32_16x16x32_bf16 over x rows gathered straight from
-//                 global memory, walks the subtree in registers (cross-lane
-//                 shuffles), and writes the token's finished slice
+//  deep_kernel    one workgroup per (chunk, tree, subtree): copies the
+//                 subtree's w_n and v_n rows (plus the v_n rows of the shared
+//                 top path) straight into LDS once, then takes the bucket's
+//                 tokens in groups of 16.  The eight waves split the model
+//                 width of a group: each forms the partial logits of all
+//                 subtree rows for the 16 tokens over its slice with
+//                 v_mfma_f32_16x16x32_bf16, from x rows gathered straight
+//                 from global memory (issued a group ahead); the partials are
+//                 summed through LDS; every token is walked through the
+//                 subtree and its finished slice
 //                 H[t, p*h : (p+1)*h] = sum over all D+1 visited nodes of
-//                 GELU(a) * v_n (GELU before the sum: section 3.C), together
+//                 GELU(a) * v_n (GELU before the sum: section 3.C) is written
 //                 with path_out.  The top-level terms use the logits recorded
 //                 by the top-level kernel, so H is written exactly once.
 //
-// Chunks are sized to fit an XCD's L2 and the grid is ordered so each XCD
-// works through its own chunks one at a time: the x rows a chunk gathers for
-// all P trees stay in that XCD's L2.
+// Tokens are bucketed per chunk, and the grid is ordered so that an XCD works
+// through its chunks one at a time: the x rows a chunk gathers for all P
+// trees are then reread from cache rather than HBM.  The chunk size trades
+// that reuse against restaging every subtree's rows once per chunk
+// (deep_chunk).
 #include "common.hpp"
 #include "launch.hpp"
 #include "mfma_tile.hpp"
@@ -37,17 +41,7 @@ namespace {
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 
-// Streaming 16-byte load that should not displace reused data in L2.
-__device__ __forceinline__ uint4 ldg16_stream(const uint16_t* p) {
-  const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
-  return make_uint4(v[0], v[1], v[2], v[3]);
-}
-
 constexpr int kSubRows = 16;  // subtree nodes per MFMA column block (15 used)
-
-__device__ __forceinline__ uint64_t lanemask_lt(int lane) {
-  return (uint64_t(1) << lane) - 1;
-}
 
 // Heap id of local node j of the subtree rooted at global node r.
 __device__ __forceinline__ int64_t subtree_global(int64_t r, int j) {
@@ -55,86 +49,129 @@ __device__ __forceinline__ int64_t subtree_global(int64_t r, int j) {
   return ((r + 1) << lvl) - 1 + (j - ((1 << lvl) - 1));
 }
 
-__global__ __launch_bounds__(256) void bucket_kernel(const int32_t* __restrict__ rec_next,
-                                                     int32_t* __restrict__ perm,
-                                                     int32_t* __restrict__ offs, int T, int P,
-                                                     int k, int chunk) {
-  extern __shared__ int32_t sh[];  // cnt[S], cur[S]
-  const int S = 1 << k;
-  int32_t* cnt = sh;
-  int32_t* cur = sh + S;
+constexpr int kBucketThreads = 1024;
+
+// One workgroup per (token chunk, tree): counts of the chunk's tokens per
+// level-k node (LDS atomics), their exclusive scan into the bucket offsets,
+// then each token's id scattered to its bucket.  Tokens of a bucket land in
+// an arbitrary order; every token's result is independent of its neighbours
+// in a bucket, so the order changes no output.
+__global__ __launch_bounds__(kBucketThreads) void bucket_kernel(const int32_t* __restrict__ rec_next,
+                                                                int32_t* __restrict__ perm,
+                                                                int32_t* __restrict__ offs, int T,
+                                                                int P, int k, int chunk) {
+  __shared__ int32_t cnt[256];
+  __shared__ int32_t cur[256];
+  const int S = 1 << k;  // k <= 8
   const int c = blockIdx.x / P;
   const int p = blockIdx.x - c * P;
   const int t0 = c * chunk;
   const int t1 = min(T, t0 + chunk);
-  const int lane = threadIdx.x & (kWave - 1);
   const int32_t* nx = rec_next + static_cast<int64_t>(p) * T;
-  for (int i = threadIdx.x; i < S; i += blockDim.x) cnt[i] = 0;
+  for (int i = threadIdx.x; i < S; i += kBucketThreads) cnt[i] = 0;
   __syncthreads();
-
-  // Pass 1: counts.  Pass 2: positions.  Both walk the chunk in the same
-  // order with the same wavefront matching.
-  for (int pass = 0; pass < 2; ++pass) {
-    int32_t* ctr = pass == 0 ? cnt : cur;
-    for (int base = t0; base < t1; base += blockDim.x) {
-      const int t = base + threadIdx.x;
-      const bool valid = t < t1;
-      const int s = valid ? nx[t] - (S - 1) : -1;
-      uint64_t active = __ballot(valid);
-      int pos = 0;
-      while (active) {
-        const int leader = __ffsll(static_cast<unsigned long long>(active)) - 1;
-        const int ls = __shfl(s, leader);
-        const uint64_t mask = __ballot(valid && s == ls);
-        int got = 0;
-        if (lane == leader) got = atomicAdd(&ctr[ls], __popcll(mask));
-        got = __shfl(got, leader);
-        if (valid && s == ls) pos = got + __popcll(mask & lanemask_lt(lane));
-        active &= ~mask;
-      }
-      if (pass == 1 && valid) perm[static_cast<int64_t>(p) * T + t0 + pos] = t;
+  for (int t = t0 + threadIdx.x; t < t1; t += kBucketThreads) atomicAdd(&cnt[nx[t] - (S - 1)], 1);
+  __syncthreads();
+  if (threadIdx.x < kWave) {
+    // Exclusive scan of S <= 256 counts: four per lane, then across lanes.
+    const int lane = threadIdx.x;
+    int v[4], sum = 0;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int i = lane * 4 + u;
+      v[u] = i < S ? cnt[i] : 0;
+      sum += v[u];
     }
-    __syncthreads();
-    if (pass == 0) {
-      if (threadIdx.x == 0) {
-        int32_t* o = offs + (static_cast<int64_t>(c) * P + p) * (S + 1);
-        int run = 0;
-        for (int i = 0; i < S; ++i) {
-          o[i] = run;
-          cur[i] = run;
-          run += cnt[i];
-        }
-        o[S] = run;
-      }
-      __syncthreads();
+    int incl = sum;
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+      const int o = __shfl_up(incl, off);
+      if (lane >= off) incl += o;
     }
+    int run = incl - sum;
+    int32_t* ob = offs + (static_cast<int64_t>(c) * P + p) * (S + 1);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int i = lane * 4 + u;
+      if (i < S) {
+        ob[i] = run;
+        cur[i] = run;
+      }
+      run += v[u];
+    }
+    if (lane == kWave - 1) ob[S] = incl;
   }
+  __syncthreads();
+  int32_t* pp = perm + static_cast<int64_t>(p) * T + t0;
+  for (int t = t0 + threadIdx.x; t < t1; t += kBucketThreads)
+    pp[atomicAdd(&cur[nx[t] - (S - 1)], 1)] = t;
 }
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
 
 // LDS layout of deep_kernel (bytes, in order):
-//   Wsub  kSubRows x (d + 8) bf16   subtree w_n rows (rows >= used are zero)
+//   Wsub  kSubRows x (d + 8) bf16   subtree w_n rows (rows >= used are not
+//                                   written; their products are never read)
 //   Vsub  kSubRows x h bf16         subtree v_n rows
 //   Vtop  k x h bf16                v_n rows of the top path shared by the bucket
+//   part  kDeepWaves x 16 x 16 f32  per-wave partial logits [wave][row][token]
+//   topl  16 x k f32                recorded top-level logits of a group's tokens
 //   bsub  kSubRows fp32             subtree biases
 //   asub  kSubRows int32            1 = subtree node alive (static pruning)
+constexpr int kDeepWaves = 8;
+constexpr int kDeepSteps = 8;  // 32-wide k steps per wave: d <= 32 * 8 * 8
 struct DeepLds {
-  size_t w, vsub, vtop, bsub, asub, total;
+  size_t w, vsub, vtop, part, topl, bsub, asub, total;
 };
 __host__ __device__ inline DeepLds deep_lds(int d, int h, int k) {
   DeepLds L;
   L.w = 0;
   L.vsub = L.w + size_t(kSubRows) * (d + 8) * 2;
   L.vtop = L.vsub + size_t(kSubRows) * h * 2;
-  L.bsub = L.vtop + size_t(k) * h * 2;
+  L.part = L.vtop + size_t(k) * h * 2;
+  L.topl = L.part + size_t(kDeepWaves) * 16 * 16 * 4;
+  L.bsub = L.topl + size_t(16) * k * 4;
   L.asub = L.bsub + kSubRows * 4;
   L.total = L.asub + kSubRows * 4;
   return L;
 }
 
-template <int WAVES>
-__global__ __launch_bounds__(WAVES * 64, 2) void deep_kernel(
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_of(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
+}
+// Buffer loads: an offset past the buffer (kOob) returns zeros, so loads
+// need no per-lane branch.
+constexpr uint32_t kOob = 0x80000000u;
+__device__ __forceinline__ uint4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+__device__ __forceinline__ float buffer_load_f32(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+}
+
+// Workgroup barrier for LDS data only: waits for this wave's LDS operations,
+// not for its global loads still in flight (__syncthreads() would).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt and expcnt unconstrained
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// One workgroup per (chunk, tree p, level-k node s): the tokens of the
+// bucket go through the subtree below s in groups of 16.  The subtree's w_n
+// and v_n rows (and the v_n rows of the path above s) are copied straight
+// into LDS once.  For a group, the eight waves split the model width: wave w
+// loads its d/8 columns of the 16 token rows (one round of loads, issued a
+// group ahead) and forms the partial logits of all 16 subtree rows with
+// v_mfma_f32_16x16x32_bf16; the partials are summed in wave order through
+// LDS.  Then wave w takes tokens 2w and 2w + 1, 32 lanes each: every lane
+// walks its token through the subtree and forms h/32 consecutive columns of
+//     H[t, p*h : (p+1)*h] = sum over all D+1 visited nodes of GELU(a) * v_n
+// (GELU before the sum: explainer page, section 3.C; FFFpost applies it to
+// the sum), the top levels' terms from the logits the top-level kernel
+// recorded, so H is written exactly once; lane 0 writes path_out.
+__global__ __launch_bounds__(kDeepWaves * 64, 2) void deep_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ W, const uint16_t* __restrict__ b,
     const uint16_t* __restrict__ V, const float* __restrict__ rec_logit,
     const int32_t* __restrict__ perm, const int32_t* __restrict__ offs, uint16_t* __restrict__ H,
@@ -172,162 +209,191 @@ __global__ __launch_bounds__(WAVES * 64, 2) void deep_kernel(
   const int used = (1 << sub_levels) - 1;       // subtree nodes
   const int64_t r = (int64_t(1) << k) - 1 + s;  // subtree root (heap id)
   const DeepLds L = deep_lds(d, h, k);
-  uint16_t* Wsub = reinterpret_cast<uint16_t*>(lds + L.w);
-  uint16_t* Vsub = reinterpret_cast<uint16_t*>(lds + L.vsub);
-  uint16_t* Vtop = reinterpret_cast<uint16_t*>(lds + L.vtop);
+  const uint16_t* Wsub = reinterpret_cast<const uint16_t*>(lds + L.w);
+  const uint16_t* Vsub = reinterpret_cast<const uint16_t*>(lds + L.vsub);
+  const uint16_t* Vtop = reinterpret_cast<const uint16_t*>(lds + L.vtop);
+  float* part = reinterpret_cast<float*>(lds + L.part);
+  float* topl = reinterpret_cast<float*>(lds + L.topl);
   float* bsub = reinterpret_cast<float*>(lds + L.bsub);
   int32_t* asub = reinterpret_cast<int32_t*>(lds + L.asub);
   const int ld = d + 8;
   const uint16_t* Wp = W + static_cast<int64_t>(p) * N * d;
   const uint16_t* Vp = V + static_cast<int64_t>(p) * N * h;
-
-  // Stage the subtree (and the top path's v rows) once.
-  const int wchunks = d / 8;
-  for (int e = threadIdx.x; e < kSubRows * wchunks; e += blockDim.x) {
-    const int j = e / wchunks;
-    const int cc = e - j * wchunks;
-    uint4 v = make_uint4(0, 0, 0, 0);
-    if (j < used) v = ldg16_stream(Wp + subtree_global(r, j) * d + cc * 8);
-    *reinterpret_cast<uint4*>(Wsub + j * ld + cc * 8) = v;
-  }
-  const int hchunks = h / 8;
-  for (int e = threadIdx.x; e < (kSubRows + k) * hchunks; e += blockDim.x) {
-    const int j = e / hchunks;
-    const int cc = e - j * hchunks;
-    if (j < kSubRows) {
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (j < used) v = ldg16(Vp + subtree_global(r, j) * h + cc * 8);
-      *reinterpret_cast<uint4*>(Vsub + j * h + cc * 8) = v;
-    } else {
-      const int l = j - kSubRows;                   // top level l < k
-      const int64_t n = ((r + 1) >> (k - l)) - 1;  // ancestor of r at level l
-      *reinterpret_cast<uint4*>(Vtop + l * h + cc * 8) = ldg16(Vp + n * h + cc * 8);
-    }
-  }
-  for (int j = threadIdx.x; j < kSubRows; j += blockDim.x) {
-    const int64_t g = static_cast<int64_t>(p) * N + (j < used ? subtree_global(r, j) : 0);
-    bsub[j] = j < used ? bf16_to_f32(b[g]) : 0.0f;
-    asub[j] = j < used && (!alive || alive[g]);
-  }
-  __syncthreads();
-
-  const int lane = threadIdx.x & (kWave - 1);
-  const int wave = threadIdx.x / kWave;
-  const int m = lane & 15;  // token within the group (and subtree node row for W)
-  const int q = lane >> 4;  // k sub-block of the operands; h quarter of the output
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = tid / kWave;
+  const int m = lane & 15;  // subtree row (A) / token of the group (B)
+  const int q = lane >> 4;  // 8-wide k group within each 32-wide step
+  const int tt = 2 * wave + (lane >> 5);  // token of the group this lane walks
+  const int c32 = lane & 31;              // its h/32-column piece of H
   const int ngroups = (ntok + 15) / 16;
-  const int my_groups = wave < ngroups ? (ngroups - wave + WAVES - 1) / WAVES : 0;
-  const int nb = d / 256;  // batches of 4 k-steps (64 k each) per token group
-  const int total = my_groups * nb;
-  const uint16_t* wrow = Wsub + m * ld + q * 16;
-  const int hq = h / 4;  // outputs per lane
+  const int nks = d / (32 * kDeepWaves);  // k steps of each wave's slice
+  const int kw = wave * (d / kDeepWaves); // first column of the slice
+  const __amdgpu_buffer_rsrc_t xbuf = buffer_of(x, uint32_t(T) * d * 2);
+  const __amdgpu_buffer_rsrc_t lbuf = buffer_of(rec_logit, uint32_t(P) * T * k * 4);
 
-  // x rows are read with 32 contiguous bytes per lane (k = 64 s + 16 q + 0..15;
-  // the four lanes of a token cover one 128-byte line per step), double
-  // buffered one batch (4 steps, 8 loads) ahead, across group boundaries.
-  auto tok_of = [&](int i) {  // token id of this lane's row in the wave's i-th group
-    const int idx = (wave + WAVES * i) * 16 + m;
-    return toks[idx < ntok ? idx : ntok - 1];
+  // Token id of lane m's row of group g (the last token past the bucket's
+  // end: loads stay valid, results unused).
+  auto tok_id = [&](int g) {
+    const int i = g * 16 + m;
+    return toks[i < ntok ? i : ntok - 1];
   };
-  int issue_tok = total > 0 ? tok_of(0) : 0;
-  auto issue = [&](uint4 (&xa)[4], uint4 (&xb)[4], int f) {
-    const int i = f / nb;
-    const int bb = f - i * nb;
-    if (bb == 0 && i > 0) issue_tok = tok_of(i);
-    const uint16_t* xr = x + static_cast<int64_t>(issue_tok) * d + q * 16 + bb * 256;
+  auto load_x = [&](uint4 (&xr)[kDeepSteps], int id) {
+    const uint32_t base = uint32_t(id * d + kw + q * 8) * 2;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      xa[u] = ldg16(xr + u * 64);
-      xb[u] = ldg16(xr + u * 64 + 8);
-    }
+    for (int u = 0; u < kDeepSteps; ++u) xr[u] = buffer_load16(xbuf, u < nks ? base + u * 64 : kOob);
+  };
+  // Recorded logits of the top levels of a group's tokens (16 x k floats,
+  // token-major like the record): element i = wave * 64 + lane of waves 0
+  // and 1 (a zero elsewhere), written to LDS when the group is computed.
+  const int ti = (wave * kWave + lane) / k;
+  const bool top_lane = wave * kWave + lane < 16 * k;
+  auto load_top = [&](int id) {
+    const int tok = __shfl(id, ti < 16 ? ti : 15);
+    const int i = wave * kWave + lane;
+    return buffer_load_f32(
+        lbuf, top_lane ? uint32_t((static_cast<int64_t>(p) * T + tok) * k + (i - ti * k)) * 4 : kOob);
   };
 
-  f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
-  auto finish = [&](int i) {
-    const int idx = (wave + WAVES * i) * 16 + m;
-    const bool valid = idx < ntok;
-    const int tok = toks[valid ? idx : ntok - 1];
-    // Walk the subtree.  Node j of token m lives in lane m + 16*(j/4), register j%4.
-    float gv[kSubRows / 4 + 1];
-    int jv[kSubRows / 4 + 1];
+  // First group's loads, then the subtree's rows straight into LDS (1 KB
+  // per wave-wide load, lane i at byte 16 i; all in flight together).
+  int id0 = tok_id(0);
+  int id1 = tok_id(ngroups > 1 ? 1 : 0);
+  uint4 x0[kDeepSteps], x1[kDeepSteps];
+  load_x(x0, id0);
+  float tv0 = load_top(id0), tv1 = 0.0f;
+  {
+    const int row_bytes = d * 2;
+    const int pieces = (row_bytes + 1023) >> 10;
+    for (int i = wave; i < used * pieces; i += kDeepWaves) {
+      const int j = i / pieces;
+      const int pc = i - j * pieces;
+      const int off = pc * 1024 + lane * 16;
+      if (off < row_bytes)
+        __builtin_amdgcn_global_load_lds(Wp + subtree_global(r, j) * d + (off >> 1),
+                                         lds + L.w + size_t(j) * ld * 2 + pc * 1024, 16, 0, 0);
+    }
+    const int vrow = h * 2;  // <= 1 KB
+    for (int i = wave; i < used + k; i += kDeepWaves) {
+      int64_t n;
+      size_t dst;
+      if (i < used) {
+        n = subtree_global(r, i);
+        dst = L.vsub + size_t(i) * vrow;
+      } else {
+        const int l = i - used;      // top level l < k
+        n = ((r + 1) >> (k - l)) - 1;  // ancestor of r at level l
+        dst = L.vtop + size_t(l) * vrow;
+      }
+      if (lane * 16 < vrow)
+        __builtin_amdgcn_global_load_lds(Vp + n * h + lane * 8, lds + dst, 16, 0, 0);
+    }
+  }
+  if (tid < kSubRows) {
+    const int j = tid;
+    const int64_t g = static_cast<int64_t>(p) * N + (j < used ? subtree_global(r, j) : 0);
+    const __amdgpu_buffer_rsrc_t abuf = buffer_of(alive ? static_cast<const void*>(alive) : x,
+                                                  alive ? uint32_t(P * N) : 0);
+    const uint16_t braw = b[g];
+    const uint32_t al = __builtin_amdgcn_raw_buffer_load_b8(abuf, uint32_t(g), 0, 0);
+    bsub[j] = j < used ? bf16_to_f32(braw) : 0.0f;
+    asub[j] = j < used && (!alive || al != 0);
+  }
+  wait_vmcnt<0>();  // this wave's copies into LDS have landed
+  lds_barrier();
+
+  const uint16_t* wrow = Wsub + m * ld + kw + q * 8;
+  const int hq = h / 32;
+  // One group: partial logits of this wave's slice, their sum, the walk and
+  // the token's H piece.
+  auto compute = [&](int g, const uint4 (&xr)[kDeepSteps], float tv, int id) {
+    f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int u = 0; u < kDeepSteps; ++u) {
+      if (u < nks) {
+        const uint4 wv = *reinterpret_cast<const uint4*>(wrow + u * 32);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(wv), as_bf16x8(xr[u]), acc, 0, 0,
+                                                      0);
+      }
+    }
+    // acc[rr] = this wave's part of row 4q + rr for token m.
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) part[(wave * 16 + 4 * q + rr) * 16 + m] = acc[rr];
+    if (top_lane) topl[wave * kWave + lane] = tv;
+    lds_barrier();
+    const int idx = g * 16 + tt;
+    const int tok = __shfl(id, tt);
+    float gv[4];
+    int jv[4];
     int j = 0;
-    for (int lv = 0; lv < sub_levels; ++lv) {
-      const int src = m + 16 * (j >> 2);
-      const float v0 = __shfl(acc[0], src);
-      const float v1 = __shfl(acc[1], src);
-      const float v2 = __shfl(acc[2], src);
-      const float v3 = __shfl(acc[3], src);
-      const int rr = j & 3;
-      const float a = (rr == 0 ? v0 : rr == 1 ? v1 : rr == 2 ? v2 : v3) + bsub[j];
-      gv[lv] = post ? a : gelu_tanh(a);
-      jv[lv] = j;
-      if (lv + 1 < sub_levels) {
-        int rr2 = go_right(a);
-        if (!asub[2 * j + 1 + rr2]) rr2 ^= 1;  // pruned child: its sibling
-        j = 2 * j + 1 + rr2;
-      }
-    }
-    if (!valid) return;
-    // H slice of this lane: columns [q*hq, (q+1)*hq) of tree p.
-    const float* tl = rec_logit + (static_cast<int64_t>(p) * T + tok) * k;
-    float gt[8];
-    for (int l = 0; l < k; ++l) gt[l] = post ? tl[l] : gelu_tanh(tl[l]);
-    uint16_t* out = H + static_cast<int64_t>(tok) * P * h + static_cast<int64_t>(p) * h + q * hq;
-    for (int c8 = 0; c8 < hq; c8 += 8) {
-      float a8[8] = {};
-      for (int l = 0; l < k; ++l) {
-        const uint4 v = *reinterpret_cast<const uint4*>(Vtop + l * h + q * hq + c8);
-        const float gg = gt[l];
-        a8[0] += gg * bf16lo(v.x); a8[1] += gg * bf16hi(v.x);
-        a8[2] += gg * bf16lo(v.y); a8[3] += gg * bf16hi(v.y);
-        a8[4] += gg * bf16lo(v.z); a8[5] += gg * bf16hi(v.z);
-        a8[6] += gg * bf16lo(v.w); a8[7] += gg * bf16hi(v.w);
-      }
-      for (int lv = 0; lv < sub_levels; ++lv) {
-        const uint4 v = *reinterpret_cast<const uint4*>(Vsub + jv[lv] * h + q * hq + c8);
-        const float gg = gv[lv];
-        a8[0] += gg * bf16lo(v.x); a8[1] += gg * bf16hi(v.x);
-        a8[2] += gg * bf16lo(v.y); a8[3] += gg * bf16hi(v.y);
-        a8[4] += gg * bf16lo(v.z); a8[5] += gg * bf16hi(v.z);
-        a8[6] += gg * bf16lo(v.w); a8[7] += gg * bf16hi(v.w);
-      }
-      if (post) {
 #pragma unroll
-        for (int u = 0; u < 8; ++u) a8[u] = gelu_tanh(a8[u]);
-      }
-      const u32x4_t packed = {pack_bf16x2(a8[0], a8[1]), pack_bf16x2(a8[2], a8[3]),
-                              pack_bf16x2(a8[4], a8[5]), pack_bf16x2(a8[6], a8[7])};
-      __builtin_nontemporal_store(packed, reinterpret_cast<u32x4_t*>(out + c8));
-    }
-    if (q == 0 && path_out) {
-      const int64_t leaf = subtree_global(r, jv[sub_levels - 1]);
-      path_out[static_cast<int64_t>(tok) * P + p] =
-          static_cast<int32_t>(leaf - ((int64_t(1) << D) - 1));
-    }
-  };
-  auto consume = [&](const uint4 (&xa)[4], const uint4 (&xb)[4], int f) {
-    const int i = f / nb;
-    const int bb = f - i * nb;
-    if (bb == 0) acc = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-    const uint16_t* w = wrow + bb * 256;
+    for (int lv = 0; lv < 4; ++lv) {
+      if (lv < sub_levels) {
+        float a = part[j * 16 + tt];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const uint4 wa = *reinterpret_cast<const uint4*>(w + u * 64);
-      const uint4 wb = *reinterpret_cast<const uint4*>(w + u * 64 + 8);
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(wa), as_bf16x8(xa[u]), acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(wb), as_bf16x8(xb[u]), acc, 0, 0, 0);
+        for (int w = 1; w < kDeepWaves; ++w) a += part[(w * 16 + j) * 16 + tt];
+        a += bsub[j];
+        gv[lv] = post ? a : gelu_tanh(a);
+        jv[lv] = j;
+        if (lv + 1 < sub_levels) {
+          int rr = go_right(a);
+          if (!asub[2 * j + 1 + rr]) rr ^= 1;  // pruned child: its sibling
+          j = 2 * j + 1 + rr;
+        }
+      }
     }
-    if (bb == nb - 1) finish(i);
+    if (idx < ntok) {
+      const float* tl = topl + tt * k;
+      float gt[8];
+#pragma unroll
+      for (int l = 0; l < 8; ++l) gt[l] = l < k ? (post ? tl[l] : gelu_tanh(tl[l])) : 0.0f;
+      uint16_t* out =
+          H + static_cast<int64_t>(tok) * P * h + static_cast<int64_t>(p) * h + c32 * hq;
+      for (int cc = 0; cc < hq; cc += 2) {
+        float a0 = 0.0f, a1 = 0.0f;
+        for (int l = 0; l < k; ++l) {
+          const uint32_t v = *reinterpret_cast<const uint32_t*>(Vtop + l * h + c32 * hq + cc);
+          a0 += gt[l] * bf16lo(v);
+          a1 += gt[l] * bf16hi(v);
+        }
+#pragma unroll
+        for (int lv = 0; lv < 4; ++lv) {
+          if (lv < sub_levels) {
+            const uint32_t v =
+                *reinterpret_cast<const uint32_t*>(Vsub + jv[lv] * h + c32 * hq + cc);
+            a0 += gv[lv] * bf16lo(v);
+            a1 += gv[lv] * bf16hi(v);
+          }
+        }
+        if (post) {
+          a0 = gelu_tanh(a0);
+          a1 = gelu_tanh(a1);
+        }
+        *reinterpret_cast<uint32_t*>(out + cc) = pack_bf16x2(a0, a1);
+      }
+      if (c32 == 0 && path_out) {
+        const int64_t leaf = subtree_global(r, jv[sub_levels - 1]);
+        path_out[static_cast<int64_t>(tok) * P + p] =
+            static_cast<int32_t>(leaf - ((int64_t(1) << D) - 1));
+      }
+    }
+    lds_barrier();  // part is rewritten by the next group
   };
 
-  uint4 xa0[4], xb0[4], xa1[4], xb1[4];
-  if (total > 0) issue(xa0, xb0, 0);
-  for (int f = 0; f < total; f += 2) {
-    if (f + 1 < total) issue(xa1, xb1, f + 1);
-    consume(xa0, xb0, f);
-    if (f + 1 < total) {
-      if (f + 2 < total) issue(xa0, xb0, f + 2);
-      consume(xa1, xb1, f + 1);
+  // Groups in pairs over two register buffers; each group's loads are issued
+  // one group ahead (past the last group they reload a valid token, unused).
+  for (int g = 0; g < ngroups; g += 2) {
+    load_x(x1, id1);
+    tv1 = load_top(id1);
+    const int id2 = tok_id(g + 2 < ngroups ? g + 2 : ngroups - 1);
+    compute(g, x0, tv0, id0);
+    if (g + 1 < ngroups) {
+      load_x(x0, id2);
+      tv0 = load_top(id2);
+      const int id3 = tok_id(g + 3 < ngroups ? g + 3 : ngroups - 1);
+      compute(g + 1, x1, tv1, id1);
+      id0 = id2;
+      id1 = id3;
     }
   }
 }
@@ -335,22 +401,26 @@ __global__ __launch_bounds__(WAVES * 64, 2) void deep_kernel(
 }  // namespace
 
 bool deep_supported(const Dims& s, int k) {
+  // Each wave's slice of the width fits kDeepSteps k steps; V rows fit one
+  // wave-wide copy and pair up per lane; byte offsets of x and of the
+  // recorded logits fit the 32-bit buffer range.
   return s.dtype == 1 && k >= 1 && k <= 8 && k <= s.D && s.D - k + 1 <= 4 && s.d % 256 == 0 &&
-         s.h % 32 == 0 && deep_lds(s.d, s.h, k).total <= 80 * 1024;
+         s.d <= 32 * kDeepWaves * kDeepSteps && s.h % 64 == 0 && s.h <= 512 &&
+         deep_lds(s.d, s.h, k).total <= 80 * 1024 && s.T * int64_t(s.d) * 2 < (int64_t(1) << 31) &&
+         int64_t(s.P) * s.T * k * 4 < (int64_t(1) << 31);
 }
 
 size_t deep_chunk(const Dims& s, int k) {
-  // Tokens per chunk: about 16 MB of x rows, and at least 32 tokens per
-  // level-k bucket on average so that the staged subtree rows serve whole
+  // Tokens per chunk: about 32 MB of x rows, and at least 64 tokens per
+  // level-k bucket on average so that the staged subtree rows serve several
   // 16-token groups.  Each chunk restages every subtree's rows, so small
   // chunks cost W_node traffic; large ones lose the x rows' cache reuse
   // across trees.  Measured at d = 2048, P = 32, h = 128, T = 16384 (ms per
-  // forward, chunks of 1024 / 2048 / 4096 / 8192 / 16384 tokens): D = 8:
-  // 1.09 / 0.98 / 1.00 / 1.05 / 1.28; D = 9: 1.79 / 1.25 / 1.16 / 1.27 / 1.54;
-  // D = 10: 3.17 / 2.04 / 1.55 / 1.54 / 1.89; D = 11: 5.99 / 3.62 / 2.51 /
-  // 2.09 / 2.35.
-  int64_t c = (16 << 20) / (int64_t(s.d) * 2);
-  const int64_t per_bucket = int64_t(32) << k;
+  // forward, chunks of 2048 / 4096 / 8192 / 16384 tokens): D = 8: 0.83 /
+  // 0.78 / 0.78 / 0.82; D = 9: 1.01 / 0.91 / 0.88 / 0.89; D = 10: 1.37 /
+  // 1.16 / 1.07 / 1.05; D = 11: 2.06 / 1.65 / 1.45 / 1.36.
+  int64_t c = (int64_t(32) << 20) / (int64_t(s.d) * 2);
+  const int64_t per_bucket = int64_t(64) << k;
   c = c < per_bucket ? per_bucket : c;
   c = c < 64 ? 64 : c;
   return static_cast<size_t>(c < s.T ? c : s.T);
@@ -359,9 +429,8 @@ size_t deep_chunk(const Dims& s, int k) {
 hipError_t launch_bucket(const Dims& s, int k, const int32_t* rec_next, int32_t* perm,
                          int32_t* offs, int chunk, hipStream_t st) {
   const int nchunks = static_cast<int>((s.T + chunk - 1) / chunk);
-  const size_t lds = 2 * sizeof(int32_t) * (size_t(1) << k);
-  bucket_kernel<<<dim3(nchunks * s.P), dim3(256), lds, st>>>(rec_next, perm, offs,
-                                                             static_cast<int>(s.T), s.P, k, chunk);
+  bucket_kernel<<<dim3(nchunks * s.P), dim3(kBucketThreads), 0, st>>>(
+      rec_next, perm, offs, static_cast<int>(s.T), s.P, k, chunk);
   return hipGetLastError();
 }
 
@@ -376,13 +445,13 @@ hipError_t launch_deep(const Dims& s, int k, const void* x, const void* W, const
   const int per_xcd = nchunks >= 8 ? ((nchunks + 7) / 8) * ipc
                                    : (ipc + 8 / nchunks - 1) / (8 / nchunks);
   const DeepLds L = deep_lds(s.d, s.h, k);
-  auto kern = deep_kernel<8>;
+  auto kern = deep_kernel;
   {
     const hipError_t e =
         ensure_lds_limit(reinterpret_cast<const void*>(kern), 80 * 1024);
     if (e != hipSuccess) return e;
   }
-  kern<<<dim3(8 * per_xcd), dim3(8 * 64), L.total, st>>>(
+  kern<<<dim3(8 * per_xcd), dim3(kDeepWaves * 64), L.total, st>>>(
       static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(W),
       static_cast<const uint16_t*>(b), static_cast<const uint16_t*>(V), rec_logit, perm, offs,
       static_cast<uint16_t*>(H), path_out, static_cast<int>(s.T), s.d, s.P, s.D, s.h, s.N, k,

@@ -144,16 +144,16 @@ def test_plans(lib):
 
 
 def test_deep_chunk_rule():
-    # Bucketed deep levels: about 16 MB of x rows per chunk, at least 32
+    # Bucketed deep levels: about 32 MB of x rows per chunk, at least 64
     # tokens per level-k bucket on average, at most T.
     wide = dict(T=16384, d=2048, P=32, h=128)
-    for D, k, chunk in ((8, 5, 4096), (9, 6, 4096), (10, 7, 4096), (11, 8, 8192)):
+    for D, k, chunk in ((8, 5, 8192), (9, 6, 8192), (10, 7, 8192), (11, 8, 16384)):
         r = fff.resolve_plan(_shape(D=D, **wide), fff.make_plan("prefill"))
         assert (r.split_level, r.chunk_tokens) == (k, chunk), (D, r.split_level, r.chunk_tokens)
     r = fff.resolve_plan(_shape(T=300, d=512, P=8, D=11, h=128), fff.make_plan("prefill"))
     assert (r.split_level, r.chunk_tokens) == (8, 300)
     r = fff.resolve_plan(_shape(T=100000, d=512, P=8, D=9, h=128), fff.make_plan("prefill"))
-    assert r.chunk_tokens == 16384  # 16 MB of 1 KB rows
+    assert r.chunk_tokens == 32768  # 32 MB of 1 KB rows
 
 
 def test_project_validation(lib):
