@@ -297,26 +297,62 @@ __global__ __launch_bounds__(256) void hbuild_kernel(const float* __restrict__ r
   unsigned char* vs = hb_lds;                                               // N x h
   float* gl = reinterpret_cast<float*>(hb_lds + size_t(N) * h * kEsz);     // kHbTok x L
   int32_t* leaf = reinterpret_cast<int32_t*>(gl + kHbTok * L);             // kHbTok
+  static_assert(kHbTok == 256, "one token per thread of the 256-thread workgroup");
   const uint16_t* Vp = V + static_cast<int64_t>(p) * N * h;
-  for (int e = threadIdx.x; e < static_cast<int>(N) * (h / 8); e += blockDim.x) {
-    const uint4 v = ldg16(Vp + static_cast<size_t>(e) * 8);
-    if constexpr (F32) {
-      float4* dst = reinterpret_cast<float4*>(vs + static_cast<size_t>(e) * 32);
-      dst[0] = make_float4(bf16lo(v.x), bf16hi(v.x), bf16lo(v.y), bf16hi(v.y));
-      dst[1] = make_float4(bf16lo(v.z), bf16hi(v.z), bf16lo(v.w), bf16hi(v.w));
-    } else {
-      *reinterpret_cast<uint4*>(vs + static_cast<size_t>(e) * 16) = v;
+  // Every load of the staging phase is issued before any is waited for (a
+  // loop of load, wait and store would cost one memory round trip per
+  // iteration).
+  if constexpr (F32) {
+    // Small trees (N * h * 4 <= 32 KB: at most 4 pieces per thread),
+    // widened to fp32.
+    constexpr int kPer = 4;
+    const int pieces = static_cast<int>(N) * (h / 8);
+    uint4 v[kPer];
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const int e = threadIdx.x + u * kHbTok;
+      v[u] = ldg16(Vp + static_cast<size_t>(e < pieces ? e : 0) * 8);
     }
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const int e = threadIdx.x + u * kHbTok;
+      if (e < pieces) {
+        float4* dst = reinterpret_cast<float4*>(vs + static_cast<size_t>(e) * 32);
+        dst[0] = make_float4(bf16lo(v[u].x), bf16hi(v[u].x), bf16lo(v[u].y), bf16hi(v[u].y));
+        dst[1] = make_float4(bf16lo(v[u].z), bf16hi(v[u].z), bf16lo(v[u].w), bf16hi(v[u].w));
+      }
+    }
+  } else {
+    // The tree's V rows are contiguous: copied straight into LDS, 1 KB per
+    // wave-wide load (lane i at byte 16 i).
+    const unsigned char* src = reinterpret_cast<const unsigned char*>(Vp);
+    const int total = static_cast<int>(N) * h * 2;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x / kWave;
+    for (int base = wave * 1024; base < total; base += (kHbTok / kWave) * 1024)
+      if (base + lane * 16 < total)
+        __builtin_amdgcn_global_load_lds(src + base + lane * 16, vs + base, 16, 0, 0);
   }
-  const float* rl = rec_logit + (static_cast<int64_t>(p) * T + t0) * L;
   // Per-node weights of the V rows: GELU(a) per node, or a itself when GELU is
   // applied to the summed vector instead.
-  for (int i = threadIdx.x; i < ntok * L; i += blockDim.x) gl[i] = post ? rl[i] : gelu_tanh(rl[i]);
-  for (int i = threadIdx.x; i < ntok; i += blockDim.x) {
-    const int32_t n = rec_next[static_cast<int64_t>(p) * T + t0 + i];
-    leaf[i] = n;
-    if (path_out) path_out[static_cast<int64_t>(t0 + i) * P + p] = n - ((1 << D) - 1);
+  const float* rl = rec_logit + (static_cast<int64_t>(p) * T + t0) * L;
+  float lv[L];
+#pragma unroll
+  for (int u = 0; u < L; ++u) {
+    const int i = threadIdx.x + u * kHbTok;
+    lv[u] = rl[i < ntok * L ? i : 0];
   }
+  const int32_t nl = rec_next[static_cast<int64_t>(p) * T + t0 + (threadIdx.x < ntok ? threadIdx.x : 0)];
+#pragma unroll
+  for (int u = 0; u < L; ++u) {
+    const int i = threadIdx.x + u * kHbTok;
+    if (i < ntok * L) gl[i] = post ? lv[u] : gelu_tanh(lv[u]);
+  }
+  if (threadIdx.x < ntok) {
+    leaf[threadIdx.x] = nl;
+    if (path_out) path_out[static_cast<int64_t>(t0 + threadIdx.x) * P + p] = nl - ((1 << D) - 1);
+  }
+  wait_vmcnt<0>();  // the copies into LDS have landed
   __syncthreads();
   uint16_t* Hp = H + static_cast<int64_t>(p) * h;
   for (int e = threadIdx.x; e < (ntok << HSHIFT); e += blockDim.x) {
