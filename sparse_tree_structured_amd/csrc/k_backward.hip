@@ -370,9 +370,20 @@ __global__ __launch_bounds__(256) void bwd_paths_kernel(
   const int p = blockIdx.y;
   const int t = blockIdx.x * 256 + threadIdx.x;
   const uint16_t* Vp = V + static_cast<int64_t>(p) * N * h;
-  for (int e = threadIdx.x; e < static_cast<int>(N) * (h / 8); e += 256)
-    *reinterpret_cast<uint4*>(Vs + static_cast<size_t>(e) * 8) = ldg16(Vp + static_cast<size_t>(e) * 8);
+  // The tree's V rows are contiguous: copied straight into LDS, 1 KB per
+  // wave-wide load (lane i at byte 16 i), all in flight together.
+  {
+    const unsigned char* src = reinterpret_cast<const unsigned char*>(Vp);
+    const int total = static_cast<int>(N) * h * 2;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x / kWave;
+    for (int base = wave * 1024; base < total; base += 4 * 1024)
+      if (base + lane * 16 < total)
+        __builtin_amdgcn_global_load_lds(src + base + lane * 16,
+                                         reinterpret_cast<unsigned char*>(Vs) + base, 16, 0, 0);
+  }
   for (int c = threadIdx.x; c < cpt; c += 256) dbs[c] = 0.0f;
+  wait_vmcnt<0>();
   __syncthreads();
 
   const bool live = t < T;

@@ -72,9 +72,38 @@ struct NodeRowLoader {
 // Walk epilogue shared by the top-level kernels.  acc holds the tile's
 // logits without bias (transposed-block layout of mfma_tile.hpp); `lg` is
 // LDS of at least WM * (BN + 4) + 2 * BN floats, free for reuse.
+// Per tile column: the node's bias and, pruned, its children's columns and
+// alive flags.  Thread c < BN loads column c before the main loop so that
+// the loads are long done when the epilogue stages them.
+struct ColMeta {
+  float bias;
+  uint32_t info;
+};
+template <class C>
+__device__ __forceinline__ ColMeta load_col_meta(const uint16_t* __restrict__ b, int P, int L,
+                                                 int64_t N, int n0, const PruneView& pv) {
+  static_assert(C::kThreads >= C::BN, "one thread per tile column");
+  ColMeta cm{0.0f, 0u};
+  const int c = threadIdx.x;
+  if (c < C::BN) {
+    int64_t g = -1;  // heap row p*N + n of column c
+    if (pv.alive) {
+      g = pv.colmap[n0 + c];
+      cm.info = pv.colinfo[n0 + c];
+    } else {
+      const int cpt = 1 << L;
+      const int p = (n0 + c) >> L;
+      const int n = (n0 + c) & (cpt - 1);
+      if (p < P && n < cpt - 1) g = static_cast<int64_t>(p) * N + n;
+    }
+    cm.bias = g >= 0 ? bf16_to_f32(b[g]) : 0.0f;
+  }
+  return cm;
+}
+
 template <class C>
 __device__ __forceinline__ void top_walk_epilogue(const f32x16_t (&acc)[C::kTm][C::kTn], float* lg,
-                                                  const uint16_t* __restrict__ b,
+                                                  const ColMeta& cm,
                                                   float* __restrict__ rec_logit,
                                                   int32_t* __restrict__ rec_next, int T, int P,
                                                   int D, int L, int64_t N, int m0, int n0,
@@ -99,17 +128,9 @@ __device__ __forceinline__ void top_walk_epilogue(const f32x16_t (&acc)[C::kTm][
   // global memory per level (visible after the first pass's barrier).
   float* bias_s = lg + kRows * kPitch;
   uint32_t* info_s = reinterpret_cast<uint32_t*>(bias_s + C::BN);
-  for (int c = tid; c < C::BN; c += C::kThreads) {
-    int64_t g = -1;  // heap row p*N + n of column c
-    if (pv.alive) {
-      g = pv.colmap[n0 + c];
-      info_s[c] = pv.colinfo[n0 + c];
-    } else {
-      const int p = (n0 + c) >> L;
-      const int n = (n0 + c) & (cpt - 1);
-      if (p < P && n < cpt - 1) g = static_cast<int64_t>(p) * N + n;
-    }
-    bias_s[c] = g >= 0 ? bf16_to_f32(b[g]) : 0.0f;
+  if (tid < C::BN) {
+    bias_s[tid] = cm.bias;
+    info_s[tid] = cm.info;
   }
 #pragma unroll 1
   for (int half = 0; half < C::kWavesM; ++half) {
@@ -199,10 +220,11 @@ __global__ __launch_bounds__(C::kThreads) void route_top_kernel(
   lb.n0 = n0;
   lb.tid = threadIdx.x;
   lb.N = N;
+  const ColMeta cm = load_col_meta<C>(b, P, L, N, n0, pv);
   f32x16_t acc[C::kTm][C::kTn];
   gemm_mainloop<C>(acc, smem, d, la, lb);
-  top_walk_epilogue<C>(acc, reinterpret_cast<float*>(smem), b, rec_logit, rec_next, T, P, D, L, N,
-                       m0, n0, pv);
+  top_walk_epilogue<C>(acc, reinterpret_cast<float*>(smem), cm, rec_logit, rec_next, T, P, D, L,
+                       N, m0, n0, pv);
 }
 
 // Same product through the direct-to-LDS multi-stage main loop.
@@ -230,10 +252,11 @@ __global__ __launch_bounds__(C::kThreads) void route_top_direct_kernel(
     const bool used = p < P && n < cmask;
     return W + (used ? (static_cast<int64_t>(p) * N + n) * d : 0);
   };
+  const ColMeta cm = load_col_meta<C>(b, P, L, N, n0, pv);
   f32x16_t acc[C::kTm][C::kTn];
   gemm_mainloop_direct<C>(acc, lds, d, a_row, b_row);
-  top_walk_epilogue<C>(acc, reinterpret_cast<float*>(lds), b, rec_logit, rec_next, T, P, D, L, N,
-                       m0, n0, pv);
+  top_walk_epilogue<C>(acc, reinterpret_cast<float*>(lds), cm, rec_logit, rec_next, T, P, D, L,
+                       N, m0, n0, pv);
 }
 
 // H for fully routed paths (L = D+1).  One workgroup per (tile of kHbTok
