@@ -351,14 +351,16 @@ __global__ __launch_bounds__(256) void transpose_rows_kernel(
                                                 w[12] | (uint32_t(w[13]) << 16), w[14] | (uint32_t(w[15]) << 16));
 }
 
-// One thread per (tree p, token t < Tp): from the routing records, dH (fp32) and
-// the tree's v rows (staged in LDS), the path's da and GELU terms; writes
+// One thread per (tree p, token t < Tp): from the routing records, dH^T
+// (fp32 [K][Tp], so that the lanes of a wave read consecutive tokens of one
+// column) and the tree's v rows (staged in LDS), the path's da and GELU
+// terms; writes
 // the masked rows DA[t][p*2^L ..], the transposed columns DA^T, G^T, H^T
 // and dS^T at token t (zeros for padding tokens t >= T), and db through an
 // LDS reduction per node.
 __global__ __launch_bounds__(256) void bwd_paths_kernel(
     const float* __restrict__ rec_logit, const int32_t* __restrict__ rec_next,
-    const uint16_t* __restrict__ V, const float* __restrict__ dH, uint16_t* __restrict__ DA,
+    const uint16_t* __restrict__ V, const float* __restrict__ dHt, uint16_t* __restrict__ DA,
     uint16_t* __restrict__ DAt, uint16_t* __restrict__ Gt, uint16_t* __restrict__ Ht,
     uint16_t* __restrict__ dSt, float* __restrict__ db, int T, int Tp, int P, int D, int h,
     int64_t N, int post) {
@@ -387,7 +389,6 @@ __global__ __launch_bounds__(256) void bwd_paths_kernel(
   __syncthreads();
 
   const bool live = t < T;
-  const int64_t K = static_cast<int64_t>(P) * h;
   int node[8];
   float a[8], g[8];
   const int leaf = live ? rec_next[static_cast<int64_t>(p) * T + t] : 0;
@@ -397,15 +398,17 @@ __global__ __launch_bounds__(256) void bwd_paths_kernel(
     a[l] = (live && l < L) ? rec_logit[(static_cast<int64_t>(p) * T + t) * L + l] : 0.0f;
     g[l] = 0.0f;
   }
-  const float* dHt = dH + static_cast<int64_t>(t) * K + static_cast<int64_t>(p) * h;
+  // Weight of each level's v row: GELU(a), or a itself for FFFpost; formed
+  // once per level and reused by every column below.
+  float gw[8];
+#pragma unroll
+  for (int l = 0; l < 8; ++l) gw[l] = post ? a[l] : gelu_tanh(a[l]);
+  const float* dHp = dHt + static_cast<int64_t>(p) * h * Tp + (live ? t : 0);
   for (int j0 = 0; j0 < h; j0 += 8) {
     float dj[8], hj[8];
-    if (live) {
-      const float4 u0 = *reinterpret_cast<const float4*>(dHt + j0);
-      const float4 u1 = *reinterpret_cast<const float4*>(dHt + j0 + 4);
-      dj[0] = u0.x; dj[1] = u0.y; dj[2] = u0.z; dj[3] = u0.w;
-      dj[4] = u1.x; dj[5] = u1.y; dj[6] = u1.z; dj[7] = u1.w;
-    } else {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) dj[e] = dHp[static_cast<int64_t>(j0 + e) * Tp];
+    if (!live) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) dj[e] = 0.0f;
     }
@@ -418,9 +421,8 @@ __global__ __launch_bounds__(256) void bwd_paths_kernel(
       const uint4 u = *reinterpret_cast<const uint4*>(Vs + static_cast<size_t>(node[l]) * h + j0);
       const float v[8] = {bf16lo(u.x), bf16hi(u.x), bf16lo(u.y), bf16hi(u.y),
                           bf16lo(u.z), bf16hi(u.z), bf16lo(u.w), bf16hi(u.w)};
-      const float w = post ? a[l] : gelu_tanh(a[l]);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) sj[e] += w * v[e];
+      for (int e = 0; e < 8; ++e) sj[e] += gw[l] * v[e];
     }
     // FFF: sj is H; FFF-post: sj is s, H = GELU(s), dS = GELU'(s) dH.
 #pragma unroll
@@ -462,7 +464,7 @@ __global__ __launch_bounds__(256) void bwd_paths_kernel(
       for (int l = 0; l < 8; ++l)
         if (l == lvl && l < L && node[l] == c) {
           vd = da[l];
-          vg = post ? a[l] : gelu_tanh(a[l]);
+          vg = gw[l];
         }
       if (!live) vd = vg = 0.0f;
       dv[e] = f32_to_bf16(vd);
@@ -580,7 +582,7 @@ BwdMfmaLayout backward_mfma_layout(const Dims& s) {
   B.next = off;   off = up(off + size_t(s.T) * s.P * 4);
   B.xT = off;     off = up(off + size_t(s.d) * Tp * 2);
   B.dyT = off;    off = up(off + size_t(s.d) * Tp * 2);
-  B.dH = off;     off = up(off + size_t(s.T) * size_t(s.K) * 4);
+  B.dH = off;     off = up(off + size_t(s.K) * Tp * 4);  // dH^T
   B.DA = off;     off = up(off + size_t(s.T) * cols * 2);
   B.DAt = off;    off = up(off + cols * Tp * 2);
   B.Gt = off;     off = up(off + cols * Tp * 2);
@@ -635,9 +637,9 @@ hipError_t launch_backward_mfma(const Dims& s, const void* x, const void* W, con
   FFF_TRY(transpose_rows(static_cast<const uint16_t*>(W), s.d, WTn, cols, cols, cols, s.d, L, s.N,
                          s.P, st));
   GemmArgs g{};
-  // dH = dy . W_out^T  [T, K]
-  g.A = dy16; g.lda = s.d; g.B = static_cast<const uint16_t*>(Wout); g.ldb = s.d;
-  g.C = dH; g.ldc = s.K; g.M = static_cast<int>(s.T); g.N = static_cast<int>(s.K); g.Kk = s.d;
+  // dH^T = W_out . dy^T  [K, Tp] (columns t >= T are not written and not read)
+  g.A = static_cast<const uint16_t*>(Wout); g.lda = s.d; g.B = dy16; g.ldb = s.d;
+  g.C = dH; g.ldc = Tp; g.M = static_cast<int>(s.K); g.N = static_cast<int>(s.T); g.Kk = s.d;
   g.ksplit = 1;
   FFF_TRY(launch_gemm_nt<BwdTile, kF32>(g, 1, st));
   bwd_paths_kernel<<<dim3(static_cast<unsigned>(Tp / 256), static_cast<unsigned>(s.P)), 256,

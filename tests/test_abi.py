@@ -267,7 +267,7 @@ def test_backward_plans_and_workspace():
     s = _shape(T=16384, d=2048, P=32, D=6, h=128)
     assert fff.backward_workspace_size(s) == fff.backward_workspace_size(s, fff.make_plan("prefill"))
     T, Tp, cols, K, d = 16384, 16384, 32 * 128, 32 * 128, 2048
-    expect = (up(T * 32 * 7 * 4) + up(T * 32 * 4) + 2 * up(d * Tp * 2) + up(T * K * 4) +
+    expect = (up(T * 32 * 7 * 4) + up(T * 32 * 4) + 2 * up(d * Tp * 2) + up(K * Tp * 4) +
               up(T * cols * 2) + 2 * up(cols * Tp * 2) + 2 * up(K * Tp * 2) + up(d * cols * 2) +
               up(max(2 * 32 * 127 * d, 2 * K * d, 8 * 32 * 127 * 128) * 4))  # split partials
     assert fff.backward_workspace_size(s) == expect
