@@ -264,40 +264,27 @@ __global__ __launch_bounds__(C::kThreads) void route_top_direct_kernel(
 // when they fit in 32 KB, else kept bf16) and reused by every token of the
 // tile (the top levels' rows are shared by all of them); the tile's GELU(a)
 // values and leaves come from the routing records.  Each thread then forms
-// 16 consecutive outputs of
+// 16 outputs, 8 in each half of the token's row, of
 //     H[t, p*h : (p+1)*h] = sum over l of GELU(a_l) * V_node[p, n_l, :]
 // (GELU before the sum: explainer section 3.C) as two 16-byte stores; the
-// h/16 threads of a token write its 2h-byte segment contiguously.  The work
+// h/16 threads of a token read consecutive 16-byte pieces of each staged
+// half row (free of LDS bank conflicts) and write its 2h-byte segment.  The work
 // is vector-ALU bound: the depth and the chunk count per token are template
 // parameters (all per-level reads issue together; index math is shifts).
 constexpr int kHbTok = 256;
 
+// Eight consecutive V values of row-major staged rows (fp32 or bf16).
 template <bool F32>
-__device__ __forceinline__ void load_v16(const unsigned char* vs, size_t elem, float (&v)[16]) {
+__device__ __forceinline__ void load_v8(const unsigned char* vs, size_t elem, float* v) {
   if constexpr (F32) {
     const float4* src = reinterpret_cast<const float4*>(vs + elem * 4);
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const float4 f = src[q];
-      v[4 * q] = f.x;
-      v[4 * q + 1] = f.y;
-      v[4 * q + 2] = f.z;
-      v[4 * q + 3] = f.w;
-    }
+    const float4 f0 = src[0], f1 = src[1];
+    v[0] = f0.x; v[1] = f0.y; v[2] = f0.z; v[3] = f0.w;
+    v[4] = f1.x; v[5] = f1.y; v[6] = f1.z; v[7] = f1.w;
   } else {
-    const uint4* src = reinterpret_cast<const uint4*>(vs + elem * 2);
-#pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      const uint4 u = src[q];
-      v[8 * q] = bf16lo(u.x);
-      v[8 * q + 1] = bf16hi(u.x);
-      v[8 * q + 2] = bf16lo(u.y);
-      v[8 * q + 3] = bf16hi(u.y);
-      v[8 * q + 4] = bf16lo(u.z);
-      v[8 * q + 5] = bf16hi(u.z);
-      v[8 * q + 6] = bf16lo(u.w);
-      v[8 * q + 7] = bf16hi(u.w);
-    }
+    const uint4 u = *reinterpret_cast<const uint4*>(vs + elem * 2);
+    v[0] = bf16lo(u.x); v[1] = bf16hi(u.x); v[2] = bf16lo(u.y); v[3] = bf16hi(u.y);
+    v[4] = bf16lo(u.z); v[5] = bf16hi(u.z); v[6] = bf16lo(u.w); v[7] = bf16hi(u.w);
   }
 }
 
@@ -380,7 +367,10 @@ __global__ __launch_bounds__(256) void hbuild_kernel(const float* __restrict__ r
   uint16_t* Hp = H + static_cast<int64_t>(p) * h;
   for (int e = threadIdx.x; e < (ntok << HSHIFT); e += blockDim.x) {
     const int i = e >> HSHIFT;
-    const int j0 = (e & (kChunks - 1)) * 16;
+    // Columns ja..ja+7 and jb..jb+7: the lanes of a token read consecutive
+    // pieces of each half row (no LDS bank conflicts), and write them.
+    const int ja = (e & (kChunks - 1)) * 8;
+    const int jb = h / 2 + ja;
     const int32_t lf = leaf[i];
     const float* g = gl + i * L;
     float acc[16];
@@ -390,7 +380,8 @@ __global__ __launch_bounds__(256) void hbuild_kernel(const float* __restrict__ r
     for (int l = 0; l < L; ++l) {
       const int n = ((lf + 1) >> (D - l)) - 1;  // ancestor of the leaf at level l
       float v[16];
-      load_v16<F32>(vs, static_cast<size_t>(n) * h + j0, v);
+      load_v8<F32>(vs, static_cast<size_t>(n) * h + ja, v);
+      load_v8<F32>(vs, static_cast<size_t>(n) * h + jb, v + 8);
       const float gg = g[l];
 #pragma unroll
       for (int q = 0; q < 16; ++q) acc[q] += gg * v[q];
@@ -399,11 +390,13 @@ __global__ __launch_bounds__(256) void hbuild_kernel(const float* __restrict__ r
 #pragma unroll
       for (int q = 0; q < 16; ++q) acc[q] = gelu_tanh(acc[q]);
     }
-    uint4* dst = reinterpret_cast<uint4*>(Hp + static_cast<int64_t>(t0 + i) * P * h + j0);
-    dst[0] = make_uint4(pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]),
-                        pack_bf16x2(acc[4], acc[5]), pack_bf16x2(acc[6], acc[7]));
-    dst[1] = make_uint4(pack_bf16x2(acc[8], acc[9]), pack_bf16x2(acc[10], acc[11]),
-                        pack_bf16x2(acc[12], acc[13]), pack_bf16x2(acc[14], acc[15]));
+    uint16_t* row = Hp + static_cast<int64_t>(t0 + i) * P * h;
+    *reinterpret_cast<uint4*>(row + ja) =
+        make_uint4(pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]),
+                   pack_bf16x2(acc[4], acc[5]), pack_bf16x2(acc[6], acc[7]));
+    *reinterpret_cast<uint4*>(row + jb) =
+        make_uint4(pack_bf16x2(acc[8], acc[9]), pack_bf16x2(acc[10], acc[11]),
+                   pack_bf16x2(acc[12], acc[13]), pack_bf16x2(acc[14], acc[15]));
   }
 }
 
