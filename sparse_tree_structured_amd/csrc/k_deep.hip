@@ -7,9 +7,11 @@
 // subtree share its weights, so:
 //
 //  bucket_kernel  groups, per (token chunk, tree), the chunk's tokens by
-//                 their level-k node: counts with LDS atomics, an exclusive
-//                 scan into bucket offsets, token ids scattered into a
-//                 permutation.
+//                 their level-k node: within a wavefront, lanes with equal
+//                 nodes find each other with one ballot per node bit, rank
+//                 by a masked popcount and make one LDS atomic per
+//                 (wavefront, bucket); counts are scanned into offsets and
+//                 token ids scattered into a permutation.
 //
 //  deep_kernel    one workgroup per (chunk, tree, subtree): copies the
 //                 subtree's w_n and v_n rows (plus the v_n rows of the shared
@@ -51,11 +53,29 @@ __device__ __forceinline__ int64_t subtree_global(int64_t r, int j) {
 
 constexpr int kBucketThreads = 1024;
 
-// One workgroup per (token chunk, tree): counts of the chunk's tokens per
-// level-k node (LDS atomics), their exclusive scan into the bucket offsets,
-// then each token's id scattered to its bucket.  Tokens of a bucket land in
-// an arbitrary order; every token's result is independent of its neighbours
-// in a bucket, so the order changes no output.
+__device__ __forceinline__ uint64_t lanemask_lt(int lane) { return (uint64_t(1) << lane) - 1; }
+
+// Lanes of this wavefront whose `valid` token has the same key (self
+// included): one ballot per key bit, kept where the lane's own bit agrees.
+__device__ __forceinline__ uint64_t same_key_lanes(bool valid, int key, int bits) {
+  uint64_t peers = __ballot(valid);
+  for (int b = 0; b < bits; ++b) {
+    const bool on = (key >> b) & 1;
+    const uint64_t m = __ballot(valid && on);
+    peers &= on ? m : ~m;
+  }
+  return valid ? peers : 0;
+}
+
+// One workgroup per (token chunk, tree) groups the chunk's tokens by their
+// level-k node.  Per wavefront of 64 tokens, the lanes with equal nodes find
+// each other with k ballots; a lane's rank among them is a masked popcount,
+// and their lowest lane makes the one LDS atomic of the (wavefront, bucket)
+// pair.  Pass 1 counts, a wave-level exclusive scan turns the counts into
+// bucket offsets, pass 2 scatters token ids.  Buckets keep each wavefront's
+// tokens in order; wavefronts land in arbitrary order, and every token's
+// result is independent of its neighbours in a bucket, so that order changes
+// no output.
 __global__ __launch_bounds__(kBucketThreads) void bucket_kernel(const int32_t* __restrict__ rec_next,
                                                                 int32_t* __restrict__ perm,
                                                                 int32_t* __restrict__ offs, int T,
@@ -67,14 +87,24 @@ __global__ __launch_bounds__(kBucketThreads) void bucket_kernel(const int32_t* _
   const int p = blockIdx.x - c * P;
   const int t0 = c * chunk;
   const int t1 = min(T, t0 + chunk);
+  const int lane = threadIdx.x & (kWave - 1);
   const int32_t* nx = rec_next + static_cast<int64_t>(p) * T;
   for (int i = threadIdx.x; i < S; i += kBucketThreads) cnt[i] = 0;
   __syncthreads();
-  for (int t = t0 + threadIdx.x; t < t1; t += kBucketThreads) atomicAdd(&cnt[nx[t] - (S - 1)], 1);
+  // The loop bound is uniform across the workgroup: every lane takes part
+  // in the ballots, past the chunk's end as an invalid lane.
+  const int span = (t1 - t0 + kBucketThreads - 1) / kBucketThreads * kBucketThreads;
+  for (int o = threadIdx.x; o < span; o += kBucketThreads) {
+    const int t = t0 + o;
+    const bool valid = t < t1;
+    const int key = valid ? nx[t] - (S - 1) : 0;
+    const uint64_t peers = same_key_lanes(valid, key, k);
+    if (valid && lane == __ffsll(static_cast<unsigned long long>(peers)) - 1)
+      atomicAdd(&cnt[key], __popcll(peers));
+  }
   __syncthreads();
   if (threadIdx.x < kWave) {
     // Exclusive scan of S <= 256 counts: four per lane, then across lanes.
-    const int lane = threadIdx.x;
     int v[4], sum = 0;
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
@@ -103,8 +133,17 @@ __global__ __launch_bounds__(kBucketThreads) void bucket_kernel(const int32_t* _
   }
   __syncthreads();
   int32_t* pp = perm + static_cast<int64_t>(p) * T + t0;
-  for (int t = t0 + threadIdx.x; t < t1; t += kBucketThreads)
-    pp[atomicAdd(&cur[nx[t] - (S - 1)], 1)] = t;
+  for (int o = threadIdx.x; o < span; o += kBucketThreads) {
+    const int t = t0 + o;
+    const bool valid = t < t1;
+    const int key = valid ? nx[t] - (S - 1) : 0;
+    const uint64_t peers = same_key_lanes(valid, key, k);
+    const int leader = valid ? __ffsll(static_cast<unsigned long long>(peers)) - 1 : lane;
+    int base = 0;
+    if (valid && lane == leader) base = atomicAdd(&cur[key], __popcll(peers));
+    base = __shfl(base, leader);
+    if (valid) pp[base + __popcll(peers & lanemask_lt(lane))] = t;
+  }
 }
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
