@@ -313,3 +313,22 @@ def test_maximum_depth_generic():
     inp = workloads.random_inputs(50, 8, 1, 20, 2, "f32", seed=14, unit_rms_x=True)
     y, path = run(inp)
     check(inp, y, path)
+
+
+# Wide node outputs through the bucketed deep levels (v rows of 512 and
+# 1024 bytes copied into LDS, h/32 columns per lane) and the dense H pass.
+WIDE = [
+    # T, d, P, D, h, split level (-1: AUTO)
+    (300, 256, 3, 7, 256, 4),
+    (200, 512, 2, 5, 512, 2),
+    (300, 128, 4, 3, 256, -1),
+]
+
+
+@needs_gpu
+@pytest.mark.parametrize("shape", WIDE, ids=[str(s) for s in WIDE])
+def test_wide_nodes(shape):
+    T, d, P, D, h, k = shape
+    inp = workloads.random_inputs(T, d, P, D, h, "bf16", seed=61 + D, unit_rms_x=True)
+    y, path = run(inp, algo="prefill", split_level=k)
+    check(inp, y, path)
