@@ -155,12 +155,13 @@ __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_ca
 //   Vtop  k x h bf16                v_n rows of the top path shared by the bucket
 //   part  kDeepWaves x 16 x 16 f32  per-wave partial logits [wave][row][token]
 //   topl  16 x k f32                recorded top-level logits of a group's tokens
+//   wgt   16 x 12 f32               v-row weights of a group's tokens (k + 4 <= 12)
 //   bsub  kSubRows fp32             subtree biases
 //   asub  kSubRows int32            1 = subtree node alive (static pruning)
 constexpr int kDeepWaves = 8;
 constexpr int kDeepSteps = 8;  // 32-wide k steps per wave: d <= 32 * 8 * 8
 struct DeepLds {
-  size_t w, vsub, vtop, part, topl, bsub, asub, total;
+  size_t w, vsub, vtop, part, topl, wgt, bsub, asub, total;
 };
 __host__ __device__ inline DeepLds deep_lds(int d, int h, int k) {
   DeepLds L;
@@ -169,7 +170,8 @@ __host__ __device__ inline DeepLds deep_lds(int d, int h, int k) {
   L.vtop = L.vsub + size_t(kSubRows) * h * 2;
   L.part = L.vtop + size_t(k) * h * 2;
   L.topl = L.part + size_t(kDeepWaves) * 16 * 16 * 4;
-  L.bsub = L.topl + size_t(16) * k * 4;
+  L.wgt = L.topl + size_t(16) * k * 4;
+  L.bsub = L.wgt + size_t(16) * 12 * 4;
   L.asub = L.bsub + kSubRows * 4;
   L.total = L.asub + kSubRows * 4;
   return L;
@@ -253,6 +255,7 @@ __global__ __launch_bounds__(kDeepWaves * 64, 2) void deep_kernel(
   const uint16_t* Vtop = reinterpret_cast<const uint16_t*>(lds + L.vtop);
   float* part = reinterpret_cast<float*>(lds + L.part);
   float* topl = reinterpret_cast<float*>(lds + L.topl);
+  float* wgt = reinterpret_cast<float*>(lds + L.wgt);
   float* bsub = reinterpret_cast<float*>(lds + L.bsub);
   int32_t* asub = reinterpret_cast<int32_t*>(lds + L.asub);
   const int ld = d + 8;
@@ -362,7 +365,8 @@ __global__ __launch_bounds__(kDeepWaves * 64, 2) void deep_kernel(
     lds_barrier();
     const int idx = g * 16 + tt;
     const int tok = __shfl(id, tt);
-    float gv[4];
+    // Walk (every lane of the token: sums of the wave partials, no GELU).
+    float av[4] = {0.0f, 0.0f, 0.0f, 0.0f};
     int jv[4];
     int j = 0;
 #pragma unroll
@@ -372,7 +376,7 @@ __global__ __launch_bounds__(kDeepWaves * 64, 2) void deep_kernel(
 #pragma unroll
         for (int w = 1; w < kDeepWaves; ++w) a += part[(w * 16 + j) * 16 + tt];
         a += bsub[j];
-        gv[lv] = post ? a : gelu_tanh(a);
+        av[lv] = a;
         jv[lv] = j;
         if (lv + 1 < sub_levels) {
           int rr = go_right(a);
@@ -381,27 +385,41 @@ __global__ __launch_bounds__(kDeepWaves * 64, 2) void deep_kernel(
         }
       }
     }
+    // Weights of the token's D+1 v rows: lane l of its 32 forms level l's
+    // (the recorded logit below level k, the walked one from k on) into LDS,
+    // where the token's other lanes (same wavefront) read it: one GELU per
+    // lane instead of one per level.
+    float* wt = wgt + tt * 12;
+    {
+      float src;
+      if (c32 < k) {
+        src = topl[tt * k + c32];
+      } else {
+        const int lv = c32 - k;
+        src = lv == 0 ? av[0] : lv == 1 ? av[1] : lv == 2 ? av[2] : av[3];
+      }
+      const float mine = post ? src : gelu_tanh(src);
+      if (c32 < k + sub_levels) wt[c32] = mine;
+    }
     if (idx < ntok) {
-      const float* tl = topl + tt * k;
-      float gt[8];
-#pragma unroll
-      for (int l = 0; l < 8; ++l) gt[l] = l < k ? (post ? tl[l] : gelu_tanh(tl[l])) : 0.0f;
       uint16_t* out =
           H + static_cast<int64_t>(tok) * P * h + static_cast<int64_t>(p) * h + c32 * hq;
       for (int cc = 0; cc < hq; cc += 2) {
         float a0 = 0.0f, a1 = 0.0f;
         for (int l = 0; l < k; ++l) {
           const uint32_t v = *reinterpret_cast<const uint32_t*>(Vtop + l * h + c32 * hq + cc);
-          a0 += gt[l] * bf16lo(v);
-          a1 += gt[l] * bf16hi(v);
+          const float w = wt[l];
+          a0 += w * bf16lo(v);
+          a1 += w * bf16hi(v);
         }
 #pragma unroll
         for (int lv = 0; lv < 4; ++lv) {
           if (lv < sub_levels) {
             const uint32_t v =
                 *reinterpret_cast<const uint32_t*>(Vsub + jv[lv] * h + c32 * hq + cc);
-            a0 += gv[lv] * bf16lo(v);
-            a1 += gv[lv] * bf16hi(v);
+            const float w = wt[k + lv];
+            a0 += w * bf16lo(v);
+            a1 += w * bf16hi(v);
           }
         }
         if (post) {
