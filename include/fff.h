@@ -105,7 +105,10 @@ typedef struct fff_shape {
 /* Algorithms.  AUTO picks by shape; the others force one (for tests and
  * measurement).  GENERIC takes any shape and dtype.  PREFILL needs bf16,
  * d % 64 == 0, h % 64 == 0 and either 2^(D+1) <= 256 (every level dense) or
- * a split level k with 2^k <= 256 and D-k <= 3.  DECODE (one kernel for
+ * a split level k with 1 <= k <= 8 and D-k <= 3 for which d % 256 == 0,
+ * d <= 2048 and h <= 512 (bucketed deep levels).  AUTO evaluates every level
+ * densely up to depth 6 and buckets the last three levels at depth 7, the
+ * last four from depth 8.  DECODE (one kernel for
  * the whole layer, routing overlapped with the stream of W_out) needs bf16,
  * 1 <= T <= 64, d % 128 == 0, d <= 2048, h % 8 == 0, h <= 256,
  * P*h % 512 == 0 and D <= 15; AUTO takes it whenever the shape allows.
@@ -129,8 +132,9 @@ typedef struct fff_plan {
                              densely.  -1 = choose by shape; ignored by other
                              algorithms */
     int32_t chunk_tokens; /* PREFILL with k <= D: tokens per bucketing chunk
-                             (each chunk's x rows are reused from one XCD's
-                             L2 across all trees); 0 = choose by shape */
+                             (a chunk's x rows are reread from cache by all
+                             trees; each chunk restages every subtree's
+                             rows); 0 = choose by shape */
 } fff_plan_t;
 
 /* Optional events recorded on `stream` at stage boundaries (each may be

@@ -55,15 +55,18 @@ bool split_ok(const Dims& s, int k) {
   return k >= 1 && k <= s.D && fff::route_top_supported(s, k) && fff::deep_supported(s, k);
 }
 
-// Every level dense whenever the tile fits a whole tree (2^(D+1) <= 256):
-// on MI355X the bucketed deep levels gather each token's x row once per tree
-// with little L2 reuse and measure slower than the dense product for the
-// shapes up to depth 7.  Deeper trees evaluate their last four levels per
-// token bucket.
+// Every level dense up to depth 6: the dense product (about 1 PFLOP/s) beats
+// the bucketed deep levels, which gather each token's x row once per tree.
+// From depth 7 the bucketed levels win: measured at T = 16384, d = 2048,
+// P = 32, h = 128 (ms per forward): D = 6 dense 0.54, k = 5 0.68; D = 7 dense
+// 0.81, k = 5 0.69, k = 4 0.74; D = 8 k = 5 0.75, k = 6 0.79.  So depth 7
+// buckets its last three levels and deeper trees their last four; a shape
+// the bucketed kernels do not cover stays dense where the tile fits a tree.
 int default_split(const Dims& s) {
-  if (split_ok(s, s.D + 1)) return s.D + 1;
-  const int k = s.D - 3 > 1 ? s.D - 3 : 1;
-  return split_ok(s, k) ? k : -1;
+  if (s.D <= 6 && split_ok(s, s.D + 1)) return s.D + 1;
+  const int k = s.D == 7 ? 5 : (s.D - 3 > 1 ? s.D - 3 : 1);
+  if (k <= s.D && split_ok(s, k)) return k;
+  return split_ok(s, s.D + 1) ? s.D + 1 : -1;
 }
 
 bool prefill_fits(const Dims& s) {
