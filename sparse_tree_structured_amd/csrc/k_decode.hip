@@ -600,10 +600,16 @@ bool decode_supported(const Dims& s) {
 // below n distinct current nodes it takes the deepest subtree with
 // n (2^levels - 1) rows that fit, so with at most 2 tokens per item every
 // round after the first covers 3 levels (a depth-6 walk takes 2 rounds, not
-// the 4 of a 16-token item whose tokens spread over 16 nodes).  Small
-// batches use 2 while the items fit half of a 256-CU grid; larger ones 16.
+// the 4 of a 16-token item whose tokens spread over 16 nodes).  Items must
+// also fit half of a 256-CU grid at once (a routing workgroup that loops
+// over items serializes their rounds): 2 tokens while that holds, else 8,
+// else 16.  Measured at d = 2048, P = 32, D = 6: T = 64 takes 31.5 us with
+// 16 tokens per item, 30.5 us with 8 and 39 us with 4 (512 items, two per
+// routing workgroup).
 static int tokens_per_item(const Dims& s) {
-  return s.T <= 16 && int64_t(s.P) * ((s.T + 1) / 2) <= 256 ? 2 : kDecTok;
+  if (s.T <= 16 && int64_t(s.P) * ((s.T + 1) / 2) <= 256) return 2;
+  if (int64_t(s.P) * ((s.T + 7) / 8) <= 256) return 8;
+  return kDecTok;
 }
 
 size_t decode_workspace(const Dims& s) {

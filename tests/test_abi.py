@@ -195,10 +195,14 @@ def test_decode_workspace_covers_route(lib):
     # H [8, 4096] bf16, 32 x 8 arrival slots and 8 K-chunk partials of y
     # [8, 2048] fp32.
     assert dec == 32 * 4 * 8 + 8 * 4096 * 2 + 32 * 8 * 8 + 8 * 8 * 2048 * 4
-    # 64 tokens: 16 per item, 4 items per tree.
+    # 64 tokens: 8 per item, 8 items per tree (256 items fit half of the grid).
     s64 = _shape(T=64, d=2048, P=32, D=6, h=128)
     assert fff.workspace_size(s64, fff.make_plan("decode")) == \
-        32 * 4 * 8 + 64 * 4096 * 2 + 32 * 8 * 8 + 8 * 64 * 2048 * 4
+        32 * 8 * 8 + 64 * 4096 * 2 + 32 * 8 * 8 + 8 * 64 * 2048 * 4
+    # 64 tokens on 64 trees: 16 per item (8-token items would be 512).
+    w64 = _shape(T=64, d=2048, P=64, D=6, h=128)
+    assert fff.workspace_size(w64, fff.make_plan("decode")) == \
+        64 * 4 * 8 + 64 * 8192 * 2 + 32 * 16 * 8 + 16 * 64 * 2048 * 4
     st = lib.fff_route(ctypes.byref(s), ctypes.byref(fff.make_plan("decode")), FAKE, FAKE, FAKE,
                        FAKE, FAKE, FAKE, FAKE, 1 << 40, None)
     assert st == fff.ERROR_NOT_SUPPORTED

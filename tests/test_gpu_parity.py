@@ -214,7 +214,7 @@ DECODE_SHAPES = [
     # T, d, P, D, h (bf16)
     (1, 256, 2, 0, 256),       # a single level
     (5, 256, 4, 3, 128),       # ragged T
-    (17, 512, 8, 5, 64),       # a second token group holding one token
+    (17, 512, 8, 5, 64),       # a last routing item holding one token
     (64, 2048, 32, 6, 128),    # unskewed: later rounds see up to 16 distinct nodes
     (33, 768, 4, 9, 128),      # three rounds
     (40, 256, 320, 3, 8),      # more routing items than workgroups
