@@ -268,10 +268,14 @@ __global__ __launch_bounds__(C::kThreads) void route_top_direct_kernel(
 //     H[t, p*h : (p+1)*h] = sum over l of GELU(a_l) * V_node[p, n_l, :]
 // (GELU before the sum: explainer section 3.C) as two 16-byte stores; the
 // h/16 threads of a token read consecutive 16-byte pieces of each staged
-// half row (free of LDS bank conflicts) and write its 2h-byte segment.  The work
-// is vector-ALU bound: the depth and the chunk count per token are template
-// parameters (all per-level reads issue together; index math is shifts).
+// half row and write its 2h-byte segment.  The depth and the chunk count per
+// token are template parameters (all per-level reads issue together; index
+// math is shifts).  kHbThreads = 2 kHbTok threads share the tile's tokens:
+// the LDS of a tile (about 40 KB at h = 128) allows four workgroups per
+// compute unit, and twice the tile's token count in threads keeps eight
+// waves per SIMD in flight.
 constexpr int kHbTok = 256;
+constexpr int kHbThreads = 512;
 
 // Eight consecutive V values of row-major staged rows (fp32 or bf16).
 template <bool F32>
@@ -289,7 +293,7 @@ __device__ __forceinline__ void load_v8(const unsigned char* vs, size_t elem, fl
 }
 
 template <int LEVELS, int HSHIFT, bool F32>
-__global__ __launch_bounds__(256) void hbuild_kernel(const float* __restrict__ rec_logit,
+__global__ __launch_bounds__(kHbThreads) void hbuild_kernel(const float* __restrict__ rec_logit,
                                                      const int32_t* __restrict__ rec_next,
                                                      const uint16_t* __restrict__ V,
                                                      uint16_t* __restrict__ H,
@@ -301,31 +305,34 @@ __global__ __launch_bounds__(256) void hbuild_kernel(const float* __restrict__ r
   constexpr int kChunks = 1 << HSHIFT;  // 16-output chunks per token
   constexpr int kEsz = F32 ? 4 : 2;
   extern __shared__ __align__(16) unsigned char hb_lds[];
-  const int p = blockIdx.y;
-  const int t0 = blockIdx.x * kHbTok;
+  // Workgroups launched together cover all trees of the same token block,
+  // so the stores in flight fill whole rows of H, and workgroup b runs on
+  // XCD b % 8, which then stages only its own trees' V rows.
+  const int p = static_cast<int>(blockIdx.x % static_cast<unsigned>(P));
+  const int t0 = static_cast<int>(blockIdx.x / static_cast<unsigned>(P)) * kHbTok;
   const int ntok = min(kHbTok, T - t0);
   unsigned char* vs = hb_lds;                                               // N x h
   float* gl = reinterpret_cast<float*>(hb_lds + size_t(N) * h * kEsz);     // kHbTok x L
   int32_t* leaf = reinterpret_cast<int32_t*>(gl + kHbTok * L);             // kHbTok
-  static_assert(kHbTok == 256, "one token per thread of the 256-thread workgroup");
+  static_assert(kHbThreads >= kHbTok, "one thread per token for the tile's leaves");
   const uint16_t* Vp = V + static_cast<int64_t>(p) * N * h;
   // Every load of the staging phase is issued before any is waited for (a
   // loop of load, wait and store would cost one memory round trip per
   // iteration).
   if constexpr (F32) {
-    // Small trees (N * h * 4 <= 32 KB: at most 4 pieces per thread),
+    // Small trees (N * h * 4 <= 32 KB: at most 1024 16-byte pieces),
     // widened to fp32.
-    constexpr int kPer = 4;
+    constexpr int kPer = 1024 / kHbThreads;
     const int pieces = static_cast<int>(N) * (h / 8);
     uint4 v[kPer];
 #pragma unroll
     for (int u = 0; u < kPer; ++u) {
-      const int e = threadIdx.x + u * kHbTok;
+      const int e = threadIdx.x + u * kHbThreads;
       v[u] = ldg16(Vp + static_cast<size_t>(e < pieces ? e : 0) * 8);
     }
 #pragma unroll
     for (int u = 0; u < kPer; ++u) {
-      const int e = threadIdx.x + u * kHbTok;
+      const int e = threadIdx.x + u * kHbThreads;
       if (e < pieces) {
         float4* dst = reinterpret_cast<float4*>(vs + static_cast<size_t>(e) * 32);
         dst[0] = make_float4(bf16lo(v[u].x), bf16hi(v[u].x), bf16lo(v[u].y), bf16hi(v[u].y));
@@ -339,23 +346,24 @@ __global__ __launch_bounds__(256) void hbuild_kernel(const float* __restrict__ r
     const int total = static_cast<int>(N) * h * 2;
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x / kWave;
-    for (int base = wave * 1024; base < total; base += (kHbTok / kWave) * 1024)
+    for (int base = wave * 1024; base < total; base += (kHbThreads / kWave) * 1024)
       if (base + lane * 16 < total)
         __builtin_amdgcn_global_load_lds(src + base + lane * 16, vs + base, 16, 0, 0);
   }
   // Per-node weights of the V rows: GELU(a) per node, or a itself when GELU is
   // applied to the summed vector instead.
   const float* rl = rec_logit + (static_cast<int64_t>(p) * T + t0) * L;
-  float lv[L];
+  constexpr int kRec = (kHbTok * L + kHbThreads - 1) / kHbThreads;
+  float lv[kRec];
 #pragma unroll
-  for (int u = 0; u < L; ++u) {
-    const int i = threadIdx.x + u * kHbTok;
+  for (int u = 0; u < kRec; ++u) {
+    const int i = threadIdx.x + u * kHbThreads;
     lv[u] = rl[i < ntok * L ? i : 0];
   }
   const int32_t nl = rec_next[static_cast<int64_t>(p) * T + t0 + (threadIdx.x < ntok ? threadIdx.x : 0)];
 #pragma unroll
-  for (int u = 0; u < L; ++u) {
-    const int i = threadIdx.x + u * kHbTok;
+  for (int u = 0; u < kRec; ++u) {
+    const int i = threadIdx.x + u * kHbThreads;
     if (i < ntok * L) gl[i] = post ? lv[u] : gelu_tanh(lv[u]);
   }
   if (threadIdx.x < ntok) {
@@ -499,8 +507,9 @@ hipError_t launch_hbuild_l(const Dims& s, const float* rec_logit, const int32_t*
         ensure_lds_limit(reinterpret_cast<const void*>(kern), 160 * 1024);
     if (e != hipSuccess) return e;
   }
-  const dim3 grid(static_cast<unsigned>((s.T + kHbTok - 1) / kHbTok), static_cast<unsigned>(s.P));
-  kern<<<grid, dim3(256), lds, st>>>(rec_logit, rec_next, static_cast<const uint16_t*>(V),
+  const int64_t blocks = (s.T + kHbTok - 1) / kHbTok * s.P;
+  if (blocks > INT32_MAX) return hipErrorInvalidConfiguration;
+  kern<<<dim3(static_cast<unsigned>(blocks)), dim3(kHbThreads), lds, st>>>(rec_logit, rec_next, static_cast<const uint16_t*>(V),
                                      static_cast<uint16_t*>(H), path_out, static_cast<int>(s.T),
                                      s.P, s.N, s.variant);
   return hipGetLastError();
