@@ -124,11 +124,12 @@ fff_status_t resolve_plan(const Dims& s, const fff_plan_t* in, fff_plan_t* out,
 //   leaf    per (tree, token) int32 node state
 //   perm    per (tree, token) int32 token ids grouped by bucket (prefill, k <= D)
 //   offs    per (chunk, tree) bucket offsets, 2^k + 1 int32 each
+//   cnt     per (chunk, tree, slice) bucket counts, 2^k int32 each
 //   H       concatenated tree outputs [T, P*h] in the layer dtype
 //   WT      W_out transposed to [d, P*h] for the direct-to-LDS projection
 //           (prefill, large products only)
 struct Layout {
-  size_t logits = 0, leaf = 0, perm = 0, offs = 0, H = 0, WT = 0;  // offsets
+  size_t logits = 0, leaf = 0, perm = 0, offs = 0, cnt = 0, H = 0, WT = 0;  // offsets
   bool use_wt = false;
   size_t total = 0;
 };
@@ -157,6 +158,8 @@ Layout layout_for(const Dims& s, const fff_plan_t& p) {
     const size_t nchunks = (size_t(s.T) + p.chunk_tokens - 1) / p.chunk_tokens;
     off = align_up(off + nchunks * s.P * ((size_t(1) << p.split_level) + 1) * sizeof(int32_t));
   }
+  L.cnt = off;
+  if (deep) off = align_up(off + fff::bucket_count_bytes(s, p.split_level, p.chunk_tokens));
   L.H = off;
   off = align_up(off + size_t(s.T) * size_t(s.K) * s.esize);
   L.WT = off;
@@ -228,7 +231,8 @@ fff_status_t run_route(const Dims& s, const fff_plan_t& p, const Layout& L, cons
     if (k == s.D + 1) return hip_status(fff::launch_hbuild(s, logits, leaf, V, H, path_out, st));
     int32_t* perm = reinterpret_cast<int32_t*>(ws + L.perm);
     int32_t* offs = reinterpret_cast<int32_t*>(ws + L.offs);
-    e = fff::launch_bucket(s, k, leaf, perm, offs, p.chunk_tokens, st);
+    int32_t* cnt = reinterpret_cast<int32_t*>(ws + L.cnt);
+    e = fff::launch_bucket(s, k, leaf, perm, offs, cnt, p.chunk_tokens, st);
     if (e != hipSuccess) return FFF_ERROR_HIP;
     return hip_status(fff::launch_deep(s, k, x, W, b, V, logits, perm, offs, H, path_out,
                                        p.chunk_tokens, st));

@@ -6,12 +6,14 @@
 // evaluated by the layer (explainer page, section 2), but tokens of one
 // subtree share its weights, so:
 //
-//  bucket_kernel  groups, per (token chunk, tree), the chunk's tokens by
+//  bucket_count_kernel, bucket_scatter_kernel
+//                 group, per (token chunk, tree), the chunk's tokens by
 //                 their level-k node: within a wavefront, lanes with equal
 //                 nodes find each other with one ballot per node bit, rank
 //                 by a masked popcount and make one LDS atomic per
-//                 (wavefront, bucket); counts are scanned into offsets and
-//                 token ids scattered into a permutation.
+//                 (wavefront, bucket); the counts of a chunk's slices are
+//                 scanned into offsets and token ids scattered into a
+//                 permutation.
 //
 //  deep_kernel    one workgroup per (chunk, tree, subtree): copies the
 //                 subtree's w_n and v_n rows (plus the v_n rows of the shared
@@ -52,6 +54,7 @@ __device__ __forceinline__ int64_t subtree_global(int64_t r, int j) {
 }
 
 constexpr int kBucketThreads = 1024;
+constexpr int kBucketMaxSlices = 16;  // slices per (chunk, tree)
 
 __device__ __forceinline__ uint64_t lanemask_lt(int lane) { return (uint64_t(1) << lane) - 1; }
 
@@ -67,49 +70,95 @@ __device__ __forceinline__ uint64_t same_key_lanes(bool valid, int key, int bits
   return valid ? peers : 0;
 }
 
-// One workgroup per (token chunk, tree) groups the chunk's tokens by their
-// level-k node.  Per wavefront of 64 tokens, the lanes with equal nodes find
-// each other with k ballots; a lane's rank among them is a masked popcount,
-// and their lowest lane makes the one LDS atomic of the (wavefront, bucket)
-// pair.  Pass 1 counts, a wave-level exclusive scan turns the counts into
-// bucket offsets, pass 2 scatters token ids.  Buckets keep each wavefront's
-// tokens in order; wavefronts land in arbitrary order, and every token's
+// Each (token chunk, tree) is split into G slices of consecutive tokens, one
+// workgroup per (chunk, tree, slice) in two launches, so that the grid covers
+// the compute units even when chunks are few.  Per wavefront of 64 tokens,
+// the lanes with equal level-k nodes find each other with k ballots; a lane's
+// rank among them is a masked popcount, and their lowest lane makes the one
+// LDS atomic of the (wavefront, bucket) pair.
+//   bucket_count_kernel    counts its slice per bucket into cnt[chunk][tree][slice][S];
+//   bucket_scatter_kernel  turns the counts of all slices of its (chunk, tree)
+//                          into bucket offsets (written by slice 0) and its
+//                          own slice's start in each bucket, and scatters its
+//                          token ids there.
+// Buckets keep each wavefront's tokens in order and the slices in slice
+// order; wavefronts of one slice land in arbitrary order, and every token's
 // result is independent of its neighbours in a bucket, so that order changes
 // no output.
-__global__ __launch_bounds__(kBucketThreads) void bucket_kernel(const int32_t* __restrict__ rec_next,
-                                                                int32_t* __restrict__ perm,
-                                                                int32_t* __restrict__ offs, int T,
-                                                                int P, int k, int chunk) {
+struct BucketSlice {
+  int c, p, g, t0, t1;
+};
+__device__ __forceinline__ BucketSlice bucket_slice(int T, int P, int chunk, int G) {
+  BucketSlice b;
+  const int cp = blockIdx.x / G;
+  b.g = blockIdx.x - cp * G;
+  b.c = cp / P;
+  b.p = cp - b.c * P;
+  const int c0 = b.c * chunk;
+  const int c1 = min(T, c0 + chunk);
+  const int slice = (chunk + G - 1) / G;
+  b.t0 = min(c1, c0 + b.g * slice);
+  b.t1 = min(c1, b.t0 + slice);
+  return b;
+}
+
+__global__ __launch_bounds__(kBucketThreads) void bucket_count_kernel(const int32_t* __restrict__ rec_next,
+                                                                      int32_t* __restrict__ cnt_out,
+                                                                      int T, int P, int k, int chunk,
+                                                                      int G) {
   __shared__ int32_t cnt[256];
-  __shared__ int32_t cur[256];
   const int S = 1 << k;  // k <= 8
-  const int c = blockIdx.x / P;
-  const int p = blockIdx.x - c * P;
-  const int t0 = c * chunk;
-  const int t1 = min(T, t0 + chunk);
+  const BucketSlice b = bucket_slice(T, P, chunk, G);
   const int lane = threadIdx.x & (kWave - 1);
-  const int32_t* nx = rec_next + static_cast<int64_t>(p) * T;
+  const int32_t* nx = rec_next + static_cast<int64_t>(b.p) * T;
   for (int i = threadIdx.x; i < S; i += kBucketThreads) cnt[i] = 0;
   __syncthreads();
   // The loop bound is uniform across the workgroup: every lane takes part
-  // in the ballots, past the chunk's end as an invalid lane.
-  const int span = (t1 - t0 + kBucketThreads - 1) / kBucketThreads * kBucketThreads;
+  // in the ballots, past the slice's end as an invalid lane.
+  const int span = (b.t1 - b.t0 + kBucketThreads - 1) / kBucketThreads * kBucketThreads;
   for (int o = threadIdx.x; o < span; o += kBucketThreads) {
-    const int t = t0 + o;
-    const bool valid = t < t1;
+    const int t = b.t0 + o;
+    const bool valid = t < b.t1;
     const int key = valid ? nx[t] - (S - 1) : 0;
     const uint64_t peers = same_key_lanes(valid, key, k);
     if (valid && lane == __ffsll(static_cast<unsigned long long>(peers)) - 1)
       atomicAdd(&cnt[key], __popcll(peers));
   }
   __syncthreads();
+  int32_t* out = cnt_out + static_cast<int64_t>(blockIdx.x) * S;
+  for (int i = threadIdx.x; i < S; i += kBucketThreads) out[i] = cnt[i];
+}
+
+__global__ __launch_bounds__(kBucketThreads) void bucket_scatter_kernel(const int32_t* __restrict__ rec_next,
+                                                                        const int32_t* __restrict__ cnt_in,
+                                                                        int32_t* __restrict__ perm,
+                                                                        int32_t* __restrict__ offs, int T,
+                                                                        int P, int k, int chunk, int G) {
+  __shared__ int32_t tot[256];
+  __shared__ int32_t cur[256];
+  const int S = 1 << k;  // k <= 8
+  const BucketSlice b = bucket_slice(T, P, chunk, G);
+  const int lane = threadIdx.x & (kWave - 1);
+  // Per bucket: the tokens of all slices, and those of the slices before this one.
+  const int32_t* cin = cnt_in + static_cast<int64_t>(blockIdx.x - b.g) * S;
+  for (int i = threadIdx.x; i < S; i += kBucketThreads) {
+    int all = 0, before = 0;
+    for (int g = 0; g < G; ++g) {
+      const int v = cin[static_cast<int64_t>(g) * S + i];
+      all += v;
+      before += g < b.g ? v : 0;
+    }
+    tot[i] = all;
+    cur[i] = before;
+  }
+  __syncthreads();
   if (threadIdx.x < kWave) {
-    // Exclusive scan of S <= 256 counts: four per lane, then across lanes.
+    // Exclusive scan of S <= 256 totals: four per lane, then across lanes.
     int v[4], sum = 0;
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int i = lane * 4 + u;
-      v[u] = i < S ? cnt[i] : 0;
+      v[u] = i < S ? tot[i] : 0;
       sum += v[u];
     }
     int incl = sum;
@@ -119,23 +168,25 @@ __global__ __launch_bounds__(kBucketThreads) void bucket_kernel(const int32_t* _
       if (lane >= off) incl += o;
     }
     int run = incl - sum;
-    int32_t* ob = offs + (static_cast<int64_t>(c) * P + p) * (S + 1);
+    int32_t* ob = offs + (static_cast<int64_t>(b.c) * P + b.p) * (S + 1);
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int i = lane * 4 + u;
       if (i < S) {
-        ob[i] = run;
-        cur[i] = run;
+        if (b.g == 0) ob[i] = run;
+        cur[i] += run;
       }
       run += v[u];
     }
-    if (lane == kWave - 1) ob[S] = incl;
+    if (b.g == 0 && lane == kWave - 1) ob[S] = incl;
   }
   __syncthreads();
-  int32_t* pp = perm + static_cast<int64_t>(p) * T + t0;
+  const int32_t* nx = rec_next + static_cast<int64_t>(b.p) * T;
+  int32_t* pp = perm + static_cast<int64_t>(b.p) * T + static_cast<int64_t>(b.c) * chunk;
+  const int span = (b.t1 - b.t0 + kBucketThreads - 1) / kBucketThreads * kBucketThreads;
   for (int o = threadIdx.x; o < span; o += kBucketThreads) {
-    const int t = t0 + o;
-    const bool valid = t < t1;
+    const int t = b.t0 + o;
+    const bool valid = t < b.t1;
     const int key = valid ? nx[t] - (S - 1) : 0;
     const uint64_t peers = same_key_lanes(valid, key, k);
     const int leader = valid ? __ffsll(static_cast<unsigned long long>(peers)) - 1 : lane;
@@ -483,11 +534,35 @@ size_t deep_chunk(const Dims& s, int k) {
   return static_cast<size_t>(c < s.T ? c : s.T);
 }
 
+// Slices per (chunk, tree): about 512 workgroups in all, each slice at least
+// one pass of a workgroup (kBucketThreads tokens), at most 16 slices.  With
+// one workgroup per (chunk, tree) the two depth-8 and -11 headline shapes ran
+// on 64 and 32 workgroups: 14 and 33 us.
+int bucket_slices(const Dims& s, int chunk) {
+  const int64_t groups = (s.T + chunk - 1) / chunk * s.P;
+  int64_t g = (512 + groups - 1) / groups;
+  const int64_t len = chunk < s.T ? chunk : s.T;
+  const int64_t max_g = (len + kBucketThreads - 1) / kBucketThreads;
+  g = g < max_g ? g : max_g;
+  g = g < kBucketMaxSlices ? g : kBucketMaxSlices;
+  return static_cast<int>(g < 1 ? 1 : g);
+}
+
+size_t bucket_count_bytes(const Dims& s, int k, int chunk) {
+  const size_t nchunks = (size_t(s.T) + chunk - 1) / chunk;
+  return nchunks * s.P * bucket_slices(s, chunk) * (size_t(1) << k) * sizeof(int32_t);
+}
+
 hipError_t launch_bucket(const Dims& s, int k, const int32_t* rec_next, int32_t* perm,
-                         int32_t* offs, int chunk, hipStream_t st) {
+                         int32_t* offs, int32_t* cnt, int chunk, hipStream_t st) {
   const int nchunks = static_cast<int>((s.T + chunk - 1) / chunk);
-  bucket_kernel<<<dim3(nchunks * s.P), dim3(kBucketThreads), 0, st>>>(
-      rec_next, perm, offs, static_cast<int>(s.T), s.P, k, chunk);
+  const int G = bucket_slices(s, chunk);
+  const int64_t blocks = int64_t(nchunks) * s.P * G;
+  if (blocks > INT32_MAX) return hipErrorInvalidConfiguration;
+  bucket_count_kernel<<<dim3(static_cast<unsigned>(blocks)), dim3(kBucketThreads), 0, st>>>(
+      rec_next, cnt, static_cast<int>(s.T), s.P, k, chunk, G);
+  bucket_scatter_kernel<<<dim3(static_cast<unsigned>(blocks)), dim3(kBucketThreads), 0, st>>>(
+      rec_next, cnt, perm, offs, static_cast<int>(s.T), s.P, k, chunk, G);
   return hipGetLastError();
 }
 

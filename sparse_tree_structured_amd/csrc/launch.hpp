@@ -97,8 +97,9 @@ hipError_t launch_hbuild(const Dims& s, const float* rec_logit, const int32_t* r
 // Deep levels k..D per token bucket (bf16; D-k <= 3).
 bool deep_supported(const Dims& s, int k);
 size_t deep_chunk(const Dims& s, int k);  // default tokens per bucket chunk
+size_t bucket_count_bytes(const Dims& s, int k, int chunk);  // per-slice bucket counts
 hipError_t launch_bucket(const Dims& s, int k, const int32_t* rec_next, int32_t* perm,
-                         int32_t* offs, int chunk, hipStream_t st);
+                         int32_t* offs, int32_t* cnt, int chunk, hipStream_t st);
 hipError_t launch_deep(const Dims& s, int k, const void* x, const void* W, const void* b,
                        const void* V, const float* rec_logit, const int32_t* perm,
                        const int32_t* offs, void* H, int32_t* path_out, int chunk,

@@ -286,3 +286,19 @@ def test_backward_plans_and_workspace():
         fff.backward_workspace_size(s, fff.make_plan("decode"))
     with pytest.raises(fff.FFFError):
         fff.backward_workspace_size(s, fff.make_plan("prefill", 4))
+
+
+@pytest.mark.parametrize("D,k,chunk,slices", [(8, 5, 8192, 8), (11, 8, 16384, 16), (7, 5, 8192, 8)])
+def test_bucketed_plan_workspace(D, k, chunk, slices):
+    # Bucketed plans carve per-(chunk, tree) offsets and per-(chunk, tree,
+    # slice) counts; the slices per chunk aim at about 512 workgroups of
+    # 1024 tokens at most each, at most 16.
+    up = lambda v: (v + 255) // 256 * 256  # noqa: E731
+    T, d, P, h = 16384, 2048, 32, 128
+    s = _shape(T=T, d=d, P=P, D=D, h=h)
+    plan = fff.resolve_plan(s, fff.make_plan())
+    assert (plan.algo, plan.split_level, plan.chunk_tokens) == (fff.ALGO_PREFILL, k, chunk)
+    nch = T // chunk
+    expect = (up(T * P * k * 4) + up(T * P * 4) + up(T * P * 4) + up(nch * P * (2 ** k + 1) * 4)
+              + up(nch * P * slices * 2 ** k * 4) + up(T * P * h * 2) + up(d * P * h * 2))
+    assert fff.workspace_size(s) == expect
