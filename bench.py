@@ -223,25 +223,29 @@ def depth_sweep(args):
                       "tokens_per_s": T / (t_dense * 1e-3),
                       "tflops": dense_flops / (t_dense * 1e-3) / 1e12,
                       "impl": "torch linear (hipBLASLt) + tanh GELU, bf16"}), flush=True)
-    # The same block with this library's matrix-core product (fff_project,
-    # y = H . W with W row-major [K, N]) for both products; bias and GELU in
+    # The same block with this library's matrix-core product (fff_project_ws,
+    # y = H . W with W row-major [K, N], W transposed into the workspace as
+    # the layer's own projection does) for both products; bias and GELU in
     # torch between them.
     w1t, w2t = w1.t().contiguous(), w2.t().contiguous()
     hid = torch.empty((T, dff), dtype=torch.bfloat16, device=dev)
     yd = torch.empty((T, d), dtype=torch.bfloat16, device=dev)
+    pws = max(fff.project_workspace_size(fff.make_shape(T, dff, 1, 0, d, fff.DTYPE_BF16)),
+              fff.project_workspace_size(fff.make_shape(T, d, 1, 0, dff, fff.DTYPE_BF16)))
+    pws = torch.empty(pws, dtype=torch.uint8, device=dev) if pws else None
 
     def dense_ours(i):
-        fff.project(xs[i % len(xs)], w1t, y=hid)
+        fff.project(xs[i % len(xs)], w1t, y=hid, workspace=pws)
         h2 = torch.nn.functional.gelu(hid + b1, approximate="tanh")
-        fff.project(h2, w2t, y=yd)
+        fff.project(h2, w2t, y=yd, workspace=pws)
 
     t_ours = _events_ms(torch, dense_ours, steps, warmup)
     print(json.dumps({"sweep": "dense_ff_ours", "d_ff": dff, "T": T, "d": d, "ms": t_ours,
                       "tokens_per_s": T / (t_ours * 1e-3),
                       "tflops": dense_flops / (t_ours * 1e-3) / 1e12,
-                      "impl": "fff_project (matrix-core) x2 + torch bias and tanh GELU, bf16"}),
+                      "impl": "fff_project_ws (matrix-core) x2 + torch bias and tanh GELU, bf16"}),
           flush=True)
-    del xs, hid, yd, w1t, w2t
+    del xs, hid, yd, w1t, w2t, pws
 
     for D in depths:
         shape = dataclasses_replace(base, D=D)

@@ -199,6 +199,29 @@ fff_status_t fff_project(const fff_shape_t *shape, int32_t algo, const void *H,
                          const void *W_out, void *y, hipStream_t stream);
 
 /*
+ * Workspace bytes of fff_project_ws for this shape and algo: d*K*dtype-size
+ * (rounded up to 256) where the direct-to-LDS matrix-core product applies
+ * (bf16, K % 32 == 0 and at least 256 output tiles of 256 x 256), else 0.
+ * `bytes` must not be NULL.  Same shape and algo rules as fff_project.
+ */
+fff_status_t fff_project_workspace_size(const fff_shape_t *shape, int32_t algo, size_t *bytes);
+
+/*
+ * fff_project with a caller workspace (device, 256-byte aligned, at least
+ * fff_project_workspace_size() bytes; may be NULL when that size is 0).
+ * Where the size is nonzero, W_out is transposed into the workspace and the
+ * product runs the kernel fff_forward uses for its projection (the same
+ * results as fff_forward's y for the same H); else it runs as fff_project.
+ * Returns FFF_ERROR_WORKSPACE for a missing or too small workspace, and
+ * FFF_ERROR_INVALID_VALUE for a misaligned one.  The product is the layer's
+ * final linear projection of the concatenated tree outputs (the paper's page,
+ * Figure 1(c) caption).
+ */
+fff_status_t fff_project_ws(const fff_shape_t *shape, int32_t algo, const void *H,
+                            const void *W_out, void *y, void *workspace, size_t workspace_bytes,
+                            hipStream_t stream);
+
+/*
  * Static path pruning
  * -------------------
  * The paper's page (Figure 4) removes paths of trained trees permanently at

@@ -67,7 +67,8 @@ class FFFError(RuntimeError):
 
 
 EXPORTS = ("fff_plan_default", "fff_plan_resolve", "fff_workspace_size", "fff_forward",
-           "fff_route", "fff_project", "fff_status_string", "fff_algo_name",
+           "fff_route", "fff_project", "fff_project_workspace_size", "fff_project_ws",
+           "fff_status_string", "fff_algo_name",
            "fff_prune_table_size", "fff_prune_prepare", "fff_forward_pruned",
            "fff_backward_workspace_size", "fff_backward")
 
@@ -93,6 +94,8 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
                                 ctypes.POINTER(StageEvents)]
     lib.fff_route.argtypes = [SP, PP, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.fff_project.argtypes = [SP, ctypes.c_int32, vp, vp, vp, vp]
+    lib.fff_project_workspace_size.argtypes = [SP, ctypes.c_int32, ctypes.POINTER(sz)]
+    lib.fff_project_ws.argtypes = [SP, ctypes.c_int32, vp, vp, vp, vp, sz, vp]
     PrP = ctypes.POINTER(Pruning)
     lib.fff_prune_table_size.argtypes = [SP, PP, ctypes.POINTER(sz)]
     lib.fff_prune_prepare.argtypes = [SP, PP, vp, vp, vp, sz, vp, PrP]
@@ -105,7 +108,8 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.fff_algo_name.argtypes = [ctypes.c_int32]
     lib.fff_algo_name.restype = ctypes.c_char_p
     for name in ("fff_plan_default", "fff_plan_resolve", "fff_workspace_size", "fff_forward",
-                 "fff_route", "fff_project", "fff_prune_table_size", "fff_prune_prepare",
+                 "fff_route", "fff_project", "fff_project_workspace_size", "fff_project_ws",
+                 "fff_prune_table_size", "fff_prune_prepare",
                  "fff_forward_pruned", "fff_backward_workspace_size", "fff_backward"):
         getattr(lib, name).restype = ctypes.c_int
     if path is None:
@@ -257,8 +261,24 @@ def route(x, W_node, b_node, V_node, *, algo=ALGO_AUTO, split_level: int = -1,
     return H, path
 
 
-def project(H, W_out, *, algo=ALGO_AUTO, stream=None, y=None):
-    """y = H . W_out (fp32 accumulation)."""
+def project_workspace_size(shape: Shape, algo=ALGO_AUTO) -> int:
+    """Workspace bytes of fff_project_ws (0 where it needs none)."""
+    if isinstance(algo, str):
+        algo = ALGOS[algo]
+    n = ctypes.c_size_t()
+    st = load_library().fff_project_workspace_size(ctypes.byref(shape), int(algo), ctypes.byref(n))
+    if st != SUCCESS:
+        raise FFFError(st, "fff_project_workspace_size")
+    return n.value
+
+
+def project(H, W_out, *, algo=ALGO_AUTO, stream=None, y=None, workspace=None,
+            use_workspace: bool = True):
+    """y = H . W_out (fp32 accumulation).
+
+    With ``use_workspace`` (default) the call goes through fff_project_ws,
+    allocating its workspace when none is given, so large bf16 products take
+    the same kernel as fff_forward's projection; else through fff_project."""
     torch = _torch()
     T, K = H.shape
     K2, d = W_out.shape
@@ -271,10 +291,22 @@ def project(H, W_out, *, algo=ALGO_AUTO, stream=None, y=None):
         y = torch.empty((T, d), dtype=H.dtype, device=H.device)
     if isinstance(algo, str):
         algo = ALGOS[algo]
-    st = load_library().fff_project(ctypes.byref(shape), int(algo), H.data_ptr(), W_out.data_ptr(),
-                                    y.data_ptr(), _stream_handle(stream))
+    lib = load_library()
+    if not use_workspace:
+        st = lib.fff_project(ctypes.byref(shape), int(algo), H.data_ptr(), W_out.data_ptr(),
+                             y.data_ptr(), _stream_handle(stream))
+        if st != SUCCESS:
+            raise FFFError(st, "fff_project")
+        return y
+    if workspace is None:
+        nbytes = project_workspace_size(shape, algo)
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=H.device) if nbytes else None
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = lib.fff_project_ws(ctypes.byref(shape), int(algo), H.data_ptr(), W_out.data_ptr(),
+                            y.data_ptr(), ws_ptr, ws_bytes, _stream_handle(stream))
     if st != SUCCESS:
-        raise FFFError(st, "fff_project")
+        raise FFFError(st, "fff_project_ws")
     return y
 
 

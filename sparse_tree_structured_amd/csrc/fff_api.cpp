@@ -253,6 +253,13 @@ fff_status_t run_project(const Dims& s, int32_t algo, const void* H, const void*
   return hip_status(e);
 }
 
+// fff_project_ws: W_out transposed into the workspace for the direct-to-LDS
+// product where that kernel applies (large bf16 products), else nothing.
+size_t project_ws_bytes(const Dims& s, int32_t algo) {
+  if (algo == FFF_ALGO_GENERIC || !fff::project_direct_supported(s)) return 0;
+  return align_up(size_t(s.d) * size_t(s.K) * s.esize);
+}
+
 fff_status_t check_inputs(const Dims& s, const void* x, const void* W, const void* b,
                           const void* V) {
   if (!x || !W || !b || !V) return FFF_ERROR_INVALID_VALUE;
@@ -659,6 +666,37 @@ fff_status_t fff_project(const fff_shape_t* shape, int32_t algo, const void* H, 
   if (!H || !W_out || !y || !aligned(H, 16) || !aligned(W_out, 16) || !aligned(y, 16))
     return FFF_ERROR_INVALID_VALUE;
   return run_project(s, algo, H, W_out, y, stream);
+}
+
+fff_status_t fff_project_workspace_size(const fff_shape_t* shape, int32_t algo, size_t* bytes) {
+  if (!bytes) return FFF_ERROR_INVALID_VALUE;
+  Dims s;
+  fff_status_t st = check_shape(shape, &s);
+  if (st != FFF_SUCCESS) return st;
+  if (algo != FFF_ALGO_AUTO && algo != FFF_ALGO_GENERIC && algo != FFF_ALGO_PREFILL)
+    return FFF_ERROR_INVALID_VALUE;
+  *bytes = project_ws_bytes(s, algo);
+  return FFF_SUCCESS;
+}
+
+fff_status_t fff_project_ws(const fff_shape_t* shape, int32_t algo, const void* H,
+                            const void* W_out, void* y, void* workspace, size_t workspace_bytes,
+                            hipStream_t stream) {
+  Dims s;
+  fff_status_t st = check_shape(shape, &s);
+  if (st != FFF_SUCCESS) return st;
+  if (algo != FFF_ALGO_AUTO && algo != FFF_ALGO_GENERIC && algo != FFF_ALGO_PREFILL)
+    return FFF_ERROR_INVALID_VALUE;
+  if (algo == FFF_ALGO_PREFILL && !fff::project_mfma_supported(s)) return FFF_ERROR_NOT_SUPPORTED;
+  if (s.T == 0) return FFF_SUCCESS;
+  if (!H || !W_out || !y || !aligned(H, 16) || !aligned(W_out, 16) || !aligned(y, 16))
+    return FFF_ERROR_INVALID_VALUE;
+  const size_t need = project_ws_bytes(s, algo);
+  if (need == 0) return run_project(s, algo, H, W_out, y, stream);
+  if (!workspace || workspace_bytes < need) return FFF_ERROR_WORKSPACE;
+  if (!aligned(workspace, kWsAlign)) return FFF_ERROR_INVALID_VALUE;
+  if (fff::launch_transpose(W_out, workspace, s.K, s.d, stream) != hipSuccess) return FFF_ERROR_HIP;
+  return hip_status(fff::launch_project_direct(s, H, workspace, y, stream));
 }
 
 const char* fff_status_string(fff_status_t status) {

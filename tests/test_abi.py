@@ -302,3 +302,34 @@ def test_bucketed_plan_workspace(D, k, chunk, slices):
     expect = (up(T * P * k * 4) + up(T * P * 4) + up(T * P * 4) + up(nch * P * (2 ** k + 1) * 4)
               + up(nch * P * slices * 2 ** k * 4) + up(T * P * h * 2) + up(d * P * h * 2))
     assert fff.workspace_size(s) == expect
+
+
+def test_project_ws_sizes_and_validation(lib):
+    n = ctypes.c_size_t()
+    big = fff.make_shape(16384, 2048, 1, 0, 4096, fff.DTYPE_BF16)   # y = H[16384,4096] . W[4096,2048]
+    assert fff.project_workspace_size(big) == 2048 * 4096 * 2      # W_out transposed
+    assert fff.project_workspace_size(big, "prefill") == 2048 * 4096 * 2
+    assert fff.project_workspace_size(big, "generic") == 0
+    small = fff.make_shape(1000, 768, 1, 0, 1024, fff.DTYPE_BF16)  # too few output tiles
+    assert fff.project_workspace_size(small) == 0
+    f32 = fff.make_shape(16384, 2048, 1, 0, 4096, fff.DTYPE_F32)
+    assert fff.project_workspace_size(f32) == 0
+    assert lib.fff_project_workspace_size(ctypes.byref(big), 7, ctypes.byref(n)) == \
+        fff.ERROR_INVALID_VALUE
+    assert lib.fff_project_workspace_size(ctypes.byref(big), fff.ALGO_AUTO, None) == \
+        fff.ERROR_INVALID_VALUE
+    # All of these fail validation before any HIP call.
+    ws = lib.fff_project_ws
+    assert ws(ctypes.byref(big), 7, FAKE, FAKE, FAKE, FAKE, 1 << 30, None) == fff.ERROR_INVALID_VALUE
+    assert ws(ctypes.byref(big), fff.ALGO_AUTO, None, FAKE, FAKE, FAKE, 1 << 30, None) == \
+        fff.ERROR_INVALID_VALUE
+    assert ws(ctypes.byref(f32), fff.ALGO_PREFILL, FAKE, FAKE, FAKE, None, 0, None) == \
+        fff.ERROR_NOT_SUPPORTED
+    assert ws(ctypes.byref(big), fff.ALGO_AUTO, FAKE, FAKE, FAKE, None, 0, None) == \
+        fff.ERROR_WORKSPACE
+    assert ws(ctypes.byref(big), fff.ALGO_AUTO, FAKE, FAKE, FAKE, FAKE, 2048 * 4096 * 2 - 1, None) == \
+        fff.ERROR_WORKSPACE
+    assert ws(ctypes.byref(big), fff.ALGO_AUTO, FAKE, FAKE, FAKE, FAKE + 16, 2048 * 4096 * 2, None) == \
+        fff.ERROR_INVALID_VALUE  # workspace not 256-byte aligned
+    empty = fff.make_shape(0, 2048, 1, 0, 4096, fff.DTYPE_BF16)
+    assert ws(ctypes.byref(empty), fff.ALGO_AUTO, None, None, None, None, 0, None) == fff.SUCCESS

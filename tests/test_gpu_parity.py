@@ -159,11 +159,12 @@ def test_projection_matches_fp64(M, K, N):
     for algo in ("prefill", "generic"):
         if algo == "prefill" and K % 64:
             continue
-        y = fff.project(H.cuda(), Wo.cuda(), algo=algo)
-        torch.cuda.synchronize()
-        got = to_f64(y)[rows]
-        err = np.abs(got - ref.numpy()) / np.maximum(np.abs(ref.numpy()), 1e-2)
-        assert err.max() < 2e-2, (algo, err.max())
+        for use_ws in (True, False):  # fff_project_ws (direct-to-LDS where large) and fff_project
+            y = fff.project(H.cuda(), Wo.cuda(), algo=algo, use_workspace=use_ws)
+            torch.cuda.synchronize()
+            got = to_f64(y)[rows]
+            err = np.abs(got - ref.numpy()) / np.maximum(np.abs(ref.numpy()), 1e-2)
+            assert err.max() < 2e-2, (algo, use_ws, err.max())
 
 
 SPLITS = [
@@ -197,10 +198,12 @@ def test_prefill_split_levels(name, k, chunk):
 
 
 @needs_gpu
-def test_route_matches_forward_h():
-    # fff_route exposes H; projecting it must give fff_forward's y exactly.
+@pytest.mark.parametrize("name", ["gpt125m", "opt1p3b_d6"])
+def test_route_matches_forward_h(name):
+    # fff_route exposes H; projecting it must give fff_forward's y exactly
+    # (at the OPT-1.3B shape through fff_project_ws's direct-to-LDS product).
     import sparse_tree_structured_amd as fff
-    inp = wl("gpt125m")
+    inp = wl(name)
     T = to_device(inp)
     H, path = fff.route(T["x"], T["W_node"], T["b_node"], T["V_node"])
     y2 = fff.project(H, T["W_out"])
