@@ -177,6 +177,7 @@ SPLITS = [
     ("opt1p3b_d4", 5, 0),
     ("gpt125m", 2, 0),
     ("gpt125m", 3, 256),
+    ("gpt125m", 3, 3000),      # bucketing slices of 1000 tokens; last chunk 2192 tokens
     ("gpt125m", 6, 0),
     ("decode_skew_t64", 3, 16),
     ("decode_skew_t8", 6, 0),
