@@ -182,20 +182,70 @@ def _dtype_code(t) -> int:
     raise TypeError(f"unsupported dtype {t.dtype}")
 
 
+def _dims(t, n, what):
+    if t.dim() != n:
+        raise ValueError(f"{what} must have {n} dimensions, got shape {tuple(t.shape)}")
+    return tuple(int(v) for v in t.shape)
+
+
 def shape_of(x, W_node, V_node, variant=VARIANT_FFF) -> Shape:
-    T, d = x.shape
-    P, N, d2 = W_node.shape
-    h = V_node.shape[2]
+    T, d = _dims(x, 2, "x [T,d]")
+    P, N, d2 = _dims(W_node, 3, "W_node [P,N,d]")
+    _dims(V_node, 3, "V_node [P,N,h]")
+    h = int(V_node.shape[2])
     D = N.bit_length() - 1
-    if d2 != d or (1 << (D + 1)) - 1 != N:
-        raise ValueError("W_node must be [P, 2^(D+1)-1, d]")
+    if d2 != d or N < 1 or (1 << (D + 1)) - 1 != N:
+        raise ValueError(f"W_node must be [P, 2^(D+1)-1, d={d}], got {tuple(W_node.shape)}")
     return make_shape(T, d, P, D, h, _dtype_code(x), variant)
 
 
+def _want(t, shape, what):
+    if tuple(int(v) for v in t.shape) != tuple(shape):
+        raise ValueError(f"{what} must be {list(shape)}, got {list(t.shape)}")
+
+
 def _check(tensors, dtype, device):
+    """Every tensor contiguous, of `dtype`, on `device`, which must be a GPU
+    (the library takes device pointers only)."""
     for t in tensors:
         if t.dtype != dtype or t.device != device or not t.is_contiguous():
             raise ValueError("all tensors must be contiguous, on one device, of one dtype")
+    if device.type != "cuda":
+        raise ValueError(f"tensors must be on a GPU, not {device}")
+
+
+def _check_layer(shape: Shape, x, W_node, b_node, V_node, W_out=None, extra=(), y=None,
+                 path_out=None, workspace=None):
+    """Full shapes of the layer's tensors against `shape` (W_out in the
+    library's [P*h, d] layout, not nn.Linear's [d, P*h]), of the optional
+    outputs y [T,d], path_out [T,P] and a flat workspace; then dtype (the
+    layer's, int32 for path_out, uint8 for the workspace), device and
+    contiguity.  Raises ValueError before anything reaches the library."""
+    torch = _torch()
+    N = (1 << (shape.D + 1)) - 1
+    _want(x, (shape.T, shape.d), "x [T,d]")
+    _want(W_node, (shape.P, N, shape.d), "W_node [P,N,d]")
+    _want(b_node, (shape.P, N), "b_node [P,N]")
+    _want(V_node, (shape.P, N, shape.h), "V_node [P,N,h]")
+    same = [x, W_node, b_node, V_node]
+    if W_out is not None:
+        _want(W_out, (shape.P * shape.h, shape.d), "W_out [P*h,d]")
+        same.append(W_out)
+    for t, want, what in extra:
+        _want(t, want, what)
+        same.append(t)
+    if y is not None:
+        _want(y, (shape.T, shape.d), "y [T,d]")
+        same.append(y)
+    if path_out is not None:
+        _want(path_out, (shape.T, shape.P), "path_out [T,P]")
+    if workspace is not None and workspace.dim() != 1:
+        raise ValueError("workspace must be a flat uint8 tensor")
+    _check(same, x.dtype, x.device)
+    if path_out is not None:
+        _check([path_out], torch.int32, x.device)
+    if workspace is not None:
+        _check([workspace], torch.uint8, x.device)
 
 
 def _stream_handle(stream) -> int:
@@ -221,7 +271,8 @@ def forward(x, W_node, b_node, V_node, W_out, *, algo=ALGO_AUTO, split_level: in
     (1) applies it to each element of a tree's summed output instead."""
     torch = _torch()
     shape = shape_of(x, W_node, V_node, variant)
-    _check([x, W_node, b_node, V_node, W_out], x.dtype, x.device)
+    _check_layer(shape, x, W_node, b_node, V_node, W_out, y=y, path_out=path_out,
+                 workspace=workspace)
     plan = make_plan(algo, split_level, chunk_tokens)
     if workspace is None:
         workspace, nbytes = alloc_workspace(shape, plan, x.device)
@@ -247,7 +298,7 @@ def route(x, W_node, b_node, V_node, *, algo=ALGO_AUTO, split_level: int = -1,
     """Routing only: returns (H[T, P*h], path_out[T,P])."""
     torch = _torch()
     shape = shape_of(x, W_node, V_node, variant)
-    _check([x, W_node, b_node, V_node], x.dtype, x.device)
+    _check_layer(shape, x, W_node, b_node, V_node)
     plan = make_plan(algo, split_level, chunk_tokens)
     workspace, nbytes = alloc_workspace(shape, plan, x.device)
     H = torch.empty((shape.T, shape.P * shape.h), dtype=x.dtype, device=x.device)
@@ -280,11 +331,15 @@ def project(H, W_out, *, algo=ALGO_AUTO, stream=None, y=None, workspace=None,
     allocating its workspace when none is given, so large bf16 products take
     the same kernel as fff_forward's projection; else through fff_project."""
     torch = _torch()
-    T, K = H.shape
-    K2, d = W_out.shape
+    T, K = _dims(H, 2, "H [T,K]")
+    K2, d = _dims(W_out, 2, "W_out [K,d]")
     if K2 != K:
-        raise ValueError("H and W_out disagree on K")
-    _check([H, W_out], H.dtype, H.device)
+        raise ValueError(f"H {list(H.shape)} and W_out {list(W_out.shape)} disagree on K")
+    if y is not None:
+        _want(y, (T, d), "y [T,d]")
+    _check([H, W_out] + ([y] if y is not None else []), H.dtype, H.device)
+    if workspace is not None:
+        _check([workspace], torch.uint8, H.device)
     # K = P*h with P=1, h=K describes the product for the library.
     shape = make_shape(T, d, 1, 0, K, _dtype_code(H))
     if y is None:
@@ -356,7 +411,8 @@ def forward_pruned(x, W_node, b_node, V_node, W_out, pruning: Pruning, *, algo=A
     """fff_forward_pruned: y and path_out of the pruned trees."""
     torch = _torch()
     shape = shape_of(x, W_node, V_node, variant)
-    _check([x, W_node, b_node, V_node, W_out], x.dtype, x.device)
+    _check_layer(shape, x, W_node, b_node, V_node, W_out, y=y, path_out=path_out,
+                 workspace=workspace)
     plan = make_plan(algo, split_level, chunk_tokens)
     if workspace is None:
         workspace, nbytes = alloc_workspace(shape, plan, x.device)
@@ -391,7 +447,19 @@ def backward(x, W_node, b_node, V_node, W_out, dy, *, algo=ALGO_AUTO, split_leve
     a dict: dx (dtype of x), dW_node, db_node, dV_node, dW_out (float32)."""
     torch = _torch()
     shape = shape_of(x, W_node, V_node, variant)
-    _check([x, W_node, b_node, V_node, W_out, dy], x.dtype, x.device)
+    N = (1 << (shape.D + 1)) - 1
+    want = {"dx": ((shape.T, shape.d), x.dtype), "dW_node": ((shape.P, N, shape.d), torch.float32),
+            "db_node": ((shape.P, N), torch.float32),
+            "dV_node": ((shape.P, N, shape.h), torch.float32),
+            "dW_out": ((shape.P * shape.h, shape.d), torch.float32)}
+    if out is not None:
+        for k, (shp, _) in want.items():
+            _want(out[k], shp, k)
+    _check_layer(shape, x, W_node, b_node, V_node, W_out,
+                 extra=[(dy, (shape.T, shape.d), "dy [T,d]")], workspace=workspace)
+    if out is not None:
+        for k, (_, dt) in want.items():
+            _check([out[k]], dt, x.device)
     plan = make_plan(algo, split_level, 0)
     if workspace is None:
         n = backward_workspace_size(shape, plan)

@@ -1,9 +1,11 @@
 """Parity of the HIP path with the CPU oracle, through the C ABI, on the GPU.
 
-Paths: every token, bit-exact except counted near-ties.  y: every token for
-the small workloads, sampled tokens (including the first and last) at full
-size; tolerance 1e-4 for fp32 and 2e-2 for bf16 (max elementwise relative
-error with the denominator floored at the row RMS).
+Paths: every token, bit-exact except counted near-ties; a flipped token's
+device path is re-evaluated by the oracle and every decision on it must
+follow its logit's sign.  y: every token, at every size (flipped tokens
+against the oracle along the device's paths); tolerance 1e-4 for fp32 and
+2e-2 for bf16 (max elementwise relative error with the denominator floored
+at the row RMS).
 """
 import functools
 
@@ -13,7 +15,7 @@ import torch
 
 import oracle
 import workloads
-from gpu_helpers import check, run, sample_rows, to_device, to_f64
+from gpu_helpers import check, run, to_device, to_f64
 
 pytestmark = pytest.mark.gpu
 
@@ -34,8 +36,7 @@ ALL = ["tiny", "gpt125m", "opt1p3b_d4", "opt1p3b_d6", "decode_skew_t1", "decode_
 def test_workload_default_plan(name):
     inp = wl(name)
     y, path = run(inp)
-    sample = None if inp.shape.T <= 1024 else sample_rows(inp.shape.T)
-    r = check(inp, y, path, sample=sample)
+    r = check(inp, y, path)
     print(name, r)
 
 
@@ -44,8 +45,7 @@ def test_workload_default_plan(name):
 def test_workload_generic(name):
     inp = wl(name)
     y, path = run(inp, algo="generic")
-    sample = None if inp.shape.T <= 1024 else sample_rows(inp.shape.T, n=32)
-    check(inp, y, path, sample=sample)
+    check(inp, y, path)
 
 
 SHAPES = [
@@ -154,15 +154,14 @@ def test_projection_matches_fp64(M, K, N):
     g = torch.Generator().manual_seed(M + K + N)
     H = torch.randn(M, K, generator=g).to(torch.bfloat16)
     Wo = (torch.randn(K, N, generator=g) / K ** 0.5).to(torch.bfloat16)
-    rows = sample_rows(M, n=64)
-    ref = H[rows].double() @ Wo.double()
+    ref = H.double() @ Wo.double()  # every row, in float64 on the CPU
     for algo in ("prefill", "generic"):
         if algo == "prefill" and K % 64:
             continue
         for use_ws in (True, False):  # fff_project_ws (direct-to-LDS where large) and fff_project
             y = fff.project(H.cuda(), Wo.cuda(), algo=algo, use_workspace=use_ws)
             torch.cuda.synchronize()
-            got = to_f64(y)[rows]
+            got = to_f64(y)
             err = np.abs(got - ref.numpy()) / np.maximum(np.abs(ref.numpy()), 1e-2)
             assert err.max() < 2e-2, (algo, use_ws, err.max())
 
@@ -194,8 +193,7 @@ def test_prefill_split_levels(name, k, chunk):
     y, path = fff.forward(T["x"], T["W_node"], T["b_node"], T["V_node"], T["W_out"],
                           algo="prefill", split_level=k, chunk_tokens=chunk)
     torch.cuda.synchronize()
-    sample = None if inp.shape.T <= 1024 else sample_rows(inp.shape.T, n=48)
-    check(inp, to_f64(y), path.cpu().numpy(), sample=sample)
+    print(name, k, chunk, check(inp, to_f64(y), path.cpu().numpy()))
 
 
 @needs_gpu

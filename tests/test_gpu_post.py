@@ -13,7 +13,7 @@ import torch
 
 import oracle
 import workloads
-from gpu_helpers import check, run, sample_rows, to_device, to_f64
+from gpu_helpers import check, run, to_device, to_f64
 from oracle.compare import y_error
 
 pytestmark = pytest.mark.gpu
@@ -61,8 +61,7 @@ def test_post_shapes(case):
 def test_post_workloads(name):
     inp = wl(name)
     y, path = run(inp, variant=POST)
-    sample = None if inp.shape.T <= 1024 else sample_rows(inp.shape.T, n=48)
-    check(inp, y, path, sample=sample, variant=POST)
+    check(inp, y, path, variant=POST)
 
 
 @needs_gpu

@@ -9,7 +9,7 @@ import torch
 
 import workloads
 import sparse_tree_structured_amd as fff
-from gpu_helpers import check, sample_rows, to_device, to_f64
+from gpu_helpers import check, to_device, to_f64
 
 pytestmark = pytest.mark.gpu
 
@@ -109,11 +109,11 @@ def test_all_alive_equals_unpruned(algo):
 @needs_gpu
 def test_pruned_headline_shape():
     # The OPT-1.3B-shaped depth-6 layer with half of the paths pruned at
-    # random (sampled tokens for y, every token for paths).
+    # random (paths and y of every token).
     inp = workloads.workload("opt1p3b_d6")
     mask = random_mask(np.random.default_rng(7), 32, 6, 0.5)
     y, path = run_pruned(inp, mask)
-    check(inp, y, path, sample=sample_rows(inp.shape.T, n=48), leaf_alive=mask)
+    check(inp, y, path, leaf_alive=mask)
 
 
 @needs_gpu
