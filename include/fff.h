@@ -313,6 +313,29 @@ fff_status_t fff_backward(const fff_shape_t *shape, const fff_plan_t *plan, cons
                           float *db_node, float *dV_node, float *dW_out, void *workspace,
                           size_t workspace_bytes, hipStream_t stream);
 
+/*
+ * Allocation-free forward, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc).  fff_forward with the library's own fixed scratch region as
+ * the workspace: a device array of FFF_STATIC_SCRATCH_BYTES bytes that each
+ * GPU the library runs on holds from the first call until the process ends.
+ * The caller passes inputs and outputs as for fff_forward; the call makes no
+ * allocation of any kind.
+ *
+ * Shapes whose fff_workspace_size() exceeds FFF_STATIC_SCRATCH_BYTES return
+ * FFF_ERROR_WORKSPACE before any HIP call (so do the other validation
+ * errors of fff_forward).  Every call on one GPU uses the same region and
+ * leaves its contents behind; nothing in it needs to start at zero.  Calls
+ * that overlap on one GPU (concurrent streams or host threads) race on it
+ * and must be serialized by the caller.
+ */
+#define FFF_STATIC_SCRATCH_BYTES ((size_t)32 << 20)
+fff_status_t fff_forward_static(const fff_shape_t *shape, const fff_plan_t *plan,
+                                const void *x, const void *W_node, const void *b_node,
+                                const void *V_node, const void *W_out, void *y,
+                                int32_t *path_out, hipStream_t stream,
+                                const fff_stage_events_t *events);
+
 /* Static, human-readable text for a status code. */
 const char *fff_status_string(fff_status_t status);
 

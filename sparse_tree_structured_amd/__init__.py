@@ -70,7 +70,8 @@ EXPORTS = ("fff_plan_default", "fff_plan_resolve", "fff_workspace_size", "fff_fo
            "fff_route", "fff_project", "fff_project_workspace_size", "fff_project_ws",
            "fff_status_string", "fff_algo_name",
            "fff_prune_table_size", "fff_prune_prepare", "fff_forward_pruned",
-           "fff_backward_workspace_size", "fff_backward")
+           "fff_backward_workspace_size", "fff_backward", "fff_forward_static")
+STATIC_SCRATCH_BYTES = 32 << 20  # FFF_STATIC_SCRATCH_BYTES
 
 _lib: Optional[ctypes.CDLL] = None
 
@@ -103,6 +104,8 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
                                        ctypes.POINTER(StageEvents)]
     lib.fff_backward_workspace_size.argtypes = [SP, PP, ctypes.POINTER(sz)]
     lib.fff_backward.argtypes = [SP, PP, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.fff_forward_static.argtypes = [SP, PP, vp, vp, vp, vp, vp, vp, vp, vp,
+                                       ctypes.POINTER(StageEvents)]
     lib.fff_status_string.argtypes = [ctypes.c_int]
     lib.fff_status_string.restype = ctypes.c_char_p
     lib.fff_algo_name.argtypes = [ctypes.c_int32]
@@ -110,7 +113,8 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     for name in ("fff_plan_default", "fff_plan_resolve", "fff_workspace_size", "fff_forward",
                  "fff_route", "fff_project", "fff_project_workspace_size", "fff_project_ws",
                  "fff_prune_table_size", "fff_prune_prepare",
-                 "fff_forward_pruned", "fff_backward_workspace_size", "fff_backward"):
+                 "fff_forward_pruned", "fff_backward_workspace_size", "fff_backward",
+                 "fff_forward_static"):
         getattr(lib, name).restype = ctypes.c_int
     if path is None:
         _lib = lib
@@ -290,6 +294,25 @@ def forward(x, W_node, b_node, V_node, W_out, *, algo=ALGO_AUTO, split_level: in
         ctypes.byref(events) if events is not None else None)
     if st != SUCCESS:
         raise FFFError(st, "fff_forward")
+    return y, path_out
+
+
+def forward_static(x, W_node, b_node, V_node, W_out, y, path_out=None, *, algo=ALGO_AUTO,
+                   split_level: int = -1, chunk_tokens: int = 0, stream=None,
+                   events: Optional[StageEvents] = None, variant=VARIANT_FFF):
+    """fff_forward_static: the layer with the library's fixed scratch region
+    as its workspace.  The caller passes y [T,d] (and path_out [T,P] int32,
+    or None); nothing is allocated."""
+    shape = shape_of(x, W_node, V_node, variant)
+    _check_layer(shape, x, W_node, b_node, V_node, W_out, y=y, path_out=path_out)
+    plan = make_plan(algo, split_level, chunk_tokens)
+    st = load_library().fff_forward_static(
+        ctypes.byref(shape), ctypes.byref(plan), x.data_ptr(), W_node.data_ptr(),
+        b_node.data_ptr(), V_node.data_ptr(), W_out.data_ptr(), y.data_ptr(),
+        path_out.data_ptr() if path_out is not None else None, _stream_handle(stream),
+        ctypes.byref(events) if events is not None else None)
+    if st != SUCCESS:
+        raise FFFError(st, "fff_forward_static")
     return y, path_out
 
 

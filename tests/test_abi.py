@@ -333,3 +333,19 @@ def test_project_ws_sizes_and_validation(lib):
         fff.ERROR_INVALID_VALUE  # workspace not 256-byte aligned
     empty = fff.make_shape(0, 2048, 1, 0, 4096, fff.DTYPE_BF16)
     assert ws(ctypes.byref(empty), fff.ALGO_AUTO, None, None, None, None, 0, None) == fff.SUCCESS
+
+
+def test_static_forward_validation(lib):
+    # fff_forward_static: validation, and a workspace beyond the fixed region,
+    # return before any HIP call (FAKE pointers are never touched).
+    def call(shape, plan=None):
+        return lib.fff_forward_static(ctypes.byref(shape), ctypes.byref(plan) if plan else None,
+                                      FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None)
+    assert call(_shape(T=-1)) == fff.ERROR_INVALID_VALUE
+    assert call(_shape(dtype=7)) == fff.ERROR_NOT_SUPPORTED
+    big = _shape(T=65536, d=64, P=4, D=3, h=128)
+    n = ctypes.c_size_t()
+    assert lib.fff_workspace_size(ctypes.byref(big), None, ctypes.byref(n)) == fff.SUCCESS
+    assert n.value > fff.STATIC_SCRATCH_BYTES
+    assert call(big) == fff.ERROR_WORKSPACE
+    assert call(_shape(T=0)) == fff.SUCCESS
