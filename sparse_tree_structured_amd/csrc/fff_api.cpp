@@ -49,10 +49,18 @@ fff_status_t check_shape(const fff_shape_t* s, Dims* out) {
   return FFF_SUCCESS;
 }
 
+// Deep levels through the token-tile subtree kernel (its records then feed
+// the H pass, which needs the whole path: D+1 <= 8).
+bool tile_ok(const Dims& s, int k) {
+  return k >= 1 && k <= s.D && fff::route_top_supported(s, k) && fff::subtree_supported(s, k) &&
+         fff::hbuild_supported(s);
+}
+
 // Split levels the prefill algorithm can take for this shape.
 bool split_ok(const Dims& s, int k) {
   if (k == s.D + 1) return fff::route_top_supported(s, k);
-  return k >= 1 && k <= s.D && fff::route_top_supported(s, k) && fff::deep_supported(s, k);
+  return k >= 1 && k <= s.D && fff::route_top_supported(s, k) &&
+         (fff::deep_supported(s, k) || tile_ok(s, k));
 }
 
 // Every level dense up to depth 6: the dense product (about 1 PFLOP/s) beats
@@ -99,7 +107,11 @@ fff_status_t resolve_plan(const Dims& s, const fff_plan_t* in, fff_plan_t* out,
       if (!split_ok(s, p.split_level)) return FFF_ERROR_NOT_SUPPORTED;
       if (p.chunk_tokens < 0) return FFF_ERROR_INVALID_VALUE;
       if (p.split_level <= s.D) {
-        if (p.chunk_tokens == 0)
+        // chunk_tokens 0: the token-tile kernel where it applies (it stays 0
+        // in the resolved plan); > 0: bucketing in chunks of that many tokens.
+        const bool tile = p.chunk_tokens == 0 && tile_ok(s, p.split_level);
+        if (!tile && !fff::deep_supported(s, p.split_level)) return FFF_ERROR_NOT_SUPPORTED;
+        if (!tile && p.chunk_tokens == 0)
           p.chunk_tokens = static_cast<int32_t>(fff::deep_chunk(s, p.split_level));
         if (p.chunk_tokens > s.T) p.chunk_tokens = static_cast<int32_t>(s.T > 0 ? s.T : 1);
       } else {
@@ -120,7 +132,7 @@ fff_status_t resolve_plan(const Dims& s, const fff_plan_t* in, fff_plan_t* out,
 
 // Workspace carve-up.  Offsets are multiples of kWsAlign.
 //   logits  per (tree, token) fp32 logits of the densely evaluated levels
-//           (all D+1 levels on the generic path)
+//           (all D+1 levels on the generic path and the token-tile path)
 //   leaf    per (tree, token) int32 node state
 //   perm    per (tree, token) int32 token ids grouped by bucket (prefill, k <= D)
 //   offs    per (chunk, tree) bucket offsets, 2^k + 1 int32 each
@@ -131,6 +143,7 @@ fff_status_t resolve_plan(const Dims& s, const fff_plan_t* in, fff_plan_t* out,
 struct Layout {
   size_t logits = 0, leaf = 0, perm = 0, offs = 0, cnt = 0, H = 0, WT = 0;  // offsets
   bool use_wt = false;
+  bool tile = false;  // deep levels through the token-tile kernel (records of all D+1 levels)
   size_t total = 0;
 };
 
@@ -143,9 +156,11 @@ Layout layout_for(const Dims& s, const fff_plan_t& p) {
     return L;
   }
   const bool prefill = p.algo == FFF_ALGO_PREFILL;
-  const int levels = prefill ? p.split_level : s.D + 1;
-  const bool deep = prefill && p.split_level <= s.D;
+  const bool tile = prefill && p.split_level <= s.D && p.chunk_tokens == 0;
+  const int levels = prefill && !tile ? p.split_level : s.D + 1;
+  const bool deep = prefill && p.split_level <= s.D && !tile;
   Layout L;
+  L.tile = tile;
   size_t off = 0;
   L.logits = off;
   off = align_up(off + size_t(s.T) * s.P * levels * sizeof(float));
@@ -226,9 +241,14 @@ fff_status_t run_route(const Dims& s, const fff_plan_t& p, const Layout& L, cons
   hipError_t e;
   if (p.algo == FFF_ALGO_PREFILL) {
     const int k = p.split_level;
-    e = fff::launch_route_top(s, k, x, W, b, logits, leaf, st);
+    e = fff::launch_route_top(s, k, L.tile ? s.D + 1 : k, x, W, b, logits, leaf, st);
     if (e != hipSuccess) return FFF_ERROR_HIP;
     if (k == s.D + 1) return hip_status(fff::launch_hbuild(s, logits, leaf, V, H, path_out, st));
+    if (L.tile) {
+      e = fff::launch_subtree(s, k, x, W, b, logits, leaf, st);
+      if (e != hipSuccess) return FFF_ERROR_HIP;
+      return hip_status(fff::launch_hbuild(s, logits, leaf, V, H, path_out, st));
+    }
     int32_t* perm = reinterpret_cast<int32_t*>(ws + L.perm);
     int32_t* offs = reinterpret_cast<int32_t*>(ws + L.offs);
     int32_t* cnt = reinterpret_cast<int32_t*>(ws + L.cnt);

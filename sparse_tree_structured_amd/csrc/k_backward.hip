@@ -631,7 +631,7 @@ hipError_t launch_backward_mfma(const Dims& s, const void* x, const void* W, con
   const int64_t nW = int64_t(s.P) * s.N * s.d, nO = s.K * s.d, nV = int64_t(s.P) * s.N * s.h;
   // db gathers atomically; dW, dW_out and dV are written in full below.
   FFF_TRY(launch_fill_f32(db, int64_t(s.P) * s.N, st));
-  FFF_TRY(launch_route_top(s, L, x, W, b, logits, next, st));
+  FFF_TRY(launch_route_top(s, L, L, x, W, b, logits, next, st));
   FFF_TRY(transpose_rows(x16, s.d, xT, Tp, s.T, Tp, s.d, 0, 0, 0, st));
   FFF_TRY(transpose_rows(dy16, s.d, dyT, Tp, s.T, Tp, s.d, 0, 0, 0, st));
   FFF_TRY(transpose_rows(static_cast<const uint16_t*>(W), s.d, WTn, cols, cols, cols, s.d, L, s.N,

@@ -106,8 +106,8 @@ __device__ __forceinline__ void top_walk_epilogue(const f32x16_t (&acc)[C::kTm][
                                                   const ColMeta& cm,
                                                   float* __restrict__ rec_logit,
                                                   int32_t* __restrict__ rec_next, int T, int P,
-                                                  int D, int L, int64_t N, int m0, int n0,
-                                                  const PruneView& pv) {
+                                                  int D, int L, int stride, int64_t N, int m0,
+                                                  int n0, const PruneView& pv) {
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = tid / kWave;
@@ -155,7 +155,7 @@ __device__ __forceinline__ void top_walk_epilogue(const f32x16_t (&acc)[C::kTm][
       const int t = m0 + half * kRows + tr;
       const int p = p_base + tp;
       if (t >= T || p >= P) continue;
-      float* out = rec_logit + (static_cast<int64_t>(p) * T + t) * L;
+      float* out = rec_logit + (static_cast<int64_t>(p) * T + t) * stride;
       const float* row = lg + tr * kPitch;
       int n = 0;
       if (!pv.alive) {
@@ -198,7 +198,7 @@ template <class C>
 __global__ __launch_bounds__(C::kThreads) void route_top_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ W, const uint16_t* __restrict__ b,
     float* __restrict__ rec_logit, int32_t* __restrict__ rec_next, int T, int d, int P, int D,
-    int L, int64_t N, int tiles_n, PruneView pv) {
+    int L, int stride, int64_t N, int tiles_n, PruneView pv) {
   extern __shared__ __align__(16) uint16_t smem[];
   const int logical = xcd_logical_tile(blockIdx.x, gridDim.x);
   const int tn = logical % tiles_n;
@@ -224,7 +224,7 @@ __global__ __launch_bounds__(C::kThreads) void route_top_kernel(
   f32x16_t acc[C::kTm][C::kTn];
   gemm_mainloop<C>(acc, smem, d, la, lb);
   top_walk_epilogue<C>(acc, reinterpret_cast<float*>(smem), cm, rec_logit, rec_next, T, P, D, L,
-                       N, m0, n0, pv);
+                       stride, N, m0, n0, pv);
 }
 
 // Same product through the direct-to-LDS multi-stage main loop.
@@ -232,7 +232,7 @@ template <class C>
 __global__ __launch_bounds__(C::kThreads) void route_top_direct_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ W, const uint16_t* __restrict__ b,
     float* __restrict__ rec_logit, int32_t* __restrict__ rec_next, int T, int d, int P, int D,
-    int L, int64_t N, int tiles_n, PruneView pv) {
+    int L, int stride, int64_t N, int tiles_n, PruneView pv) {
   extern __shared__ __align__(16) unsigned char lds[];
   const int logical = xcd_logical_tile(blockIdx.x, gridDim.x);
   const int tn = logical % tiles_n;
@@ -256,7 +256,7 @@ __global__ __launch_bounds__(C::kThreads) void route_top_direct_kernel(
   f32x16_t acc[C::kTm][C::kTn];
   gemm_mainloop_direct<C>(acc, lds, d, a_row, b_row);
   top_walk_epilogue<C>(acc, reinterpret_cast<float*>(lds), cm, rec_logit, rec_next, T, P, D, L,
-                       N, m0, n0, pv);
+                       stride, N, m0, n0, pv);
 }
 
 // H for fully routed paths (L = D+1).  One workgroup per (tile of kHbTok
@@ -423,13 +423,13 @@ int top_col_tiles(const Dims& s, int L) {
 }
 
 template <class C, bool kDirect>
-hipError_t launch_top_cfg(const Dims& s, int L, const void* x, const void* W, const void* b,
-                          float* rec_logit, int32_t* rec_next, hipStream_t st) {
+hipError_t launch_top_cfg(const Dims& s, int L, int stride, const void* x, const void* W,
+                          const void* b, float* rec_logit, int32_t* rec_next, hipStream_t st) {
   const int tiles_m = static_cast<int>((s.T + C::BM - 1) / C::BM);
   const int tiles_n = top_col_tiles(s, L);
   const PruneView pv = s.prune ? *s.prune : PruneView{};
   void (*kern)(const uint16_t*, const uint16_t*, const uint16_t*, float*, int32_t*, int, int, int,
-               int, int, int64_t, int, PruneView);
+               int, int, int, int64_t, int, PruneView);
   if constexpr (kDirect)
     kern = route_top_direct_kernel<C>;
   else
@@ -443,7 +443,7 @@ hipError_t launch_top_cfg(const Dims& s, int L, const void* x, const void* W, co
   kern<<<dim3(tiles_m * tiles_n), dim3(C::kThreads), lds, st>>>(
       static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(W),
       static_cast<const uint16_t*>(b), rec_logit, rec_next, static_cast<int>(s.T), s.d, s.P, s.D,
-      L, s.N, tiles_n, pv);
+      L, stride, s.N, tiles_n, pv);
   return hipGetLastError();
 }
 
@@ -475,25 +475,24 @@ hipError_t launch_prune_pack(const void* W, const int32_t* colmap, void* packed,
   return hipGetLastError();
 }
 
-bool hbuild_supported(const Dims& s);
-
 bool route_top_supported(const Dims& s, int L) {
   return s.dtype == 1 && s.d % TopTile::BK == 0 && s.h % 8 == 0 && L >= 1 && L <= s.D + 1 &&
          (1 << L) <= TopTile::BN && (L <= s.D || hbuild_supported(s));
 }
 
-hipError_t launch_route_top(const Dims& s, int L, const void* x, const void* W, const void* b,
-                            float* rec_logit, int32_t* rec_next, hipStream_t st) {
+hipError_t launch_route_top(const Dims& s, int L, int stride, const void* x, const void* W,
+                            const void* b, float* rec_logit, int32_t* rec_next, hipStream_t st) {
+  if (stride < L) return hipErrorInvalidValue;
   // A pruning table packs the rows of one split level only.
   if (s.prune && s.prune->L != L) return hipErrorInvalidValue;
   // Enough tiles to cover the 256 compute units: shrink the token tile when
   // the column count is small (few trees or few levels).
   const int64_t tiles_n = top_col_tiles(s, L);
   if ((1 << L) <= TopDirect::BN && ((s.T + 255) / 256) * tiles_n >= 256)
-    return launch_top_cfg<TopDirect, true>(s, L, x, W, b, rec_logit, rec_next, st);
+    return launch_top_cfg<TopDirect, true>(s, L, stride, x, W, b, rec_logit, rec_next, st);
   if (((s.T + 127) / 128) * tiles_n >= 256)
-    return launch_top_cfg<MidTile, false>(s, L, x, W, b, rec_logit, rec_next, st);
-  return launch_top_cfg<SmallTile, false>(s, L, x, W, b, rec_logit, rec_next, st);
+    return launch_top_cfg<MidTile, false>(s, L, stride, x, W, b, rec_logit, rec_next, st);
+  return launch_top_cfg<SmallTile, false>(s, L, stride, x, W, b, rec_logit, rec_next, st);
 }
 
 namespace {

@@ -85,14 +85,23 @@ hipError_t launch_project_direct(const Dims& s, const void* H, const void* WT, v
 
 // ---- prefill routing (bf16) ----
 // Dense evaluation of tree levels 0..L-1 (L <= 8) with the walk over them:
-// rec_logit[p][t][l] (fp32) and rec_next[p][t] (heap id at level L, or the
-// leaf when L = D+1).
+// rec_logit[p][t][l] (fp32, record stride `stride` >= L floats) and
+// rec_next[p][t] (heap id at level L, or the leaf when L = D+1).
 bool route_top_supported(const Dims& s, int L);
-hipError_t launch_route_top(const Dims& s, int L, const void* x, const void* W, const void* b,
-                            float* rec_logit, int32_t* rec_next, hipStream_t st);
+hipError_t launch_route_top(const Dims& s, int L, int stride, const void* x, const void* W,
+                            const void* b, float* rec_logit, int32_t* rec_next, hipStream_t st);
+// H and path_out need the whole path's records (L = D+1 levels, stride D+1).
+bool hbuild_supported(const Dims& s);
 // H and path_out from fully routed records (L = D+1).
 hipError_t launch_hbuild(const Dims& s, const float* rec_logit, const int32_t* rec_next,
                          const void* V, void* H, int32_t* path_out, hipStream_t st);
+
+// Deep levels k..D per token tile (bf16; D-k <= 3, 1 <= k <= 5): for each
+// token and tree, the 16-node block of its own level-k subtree on the matrix
+// cores; completes rec_logit (levels k..D, stride D+1) and rec_next (leaf).
+bool subtree_supported(const Dims& s, int k);
+hipError_t launch_subtree(const Dims& s, int k, const void* x, const void* W, const void* b,
+                          float* rec_logit, int32_t* rec_next, hipStream_t st);
 
 // Deep levels k..D per token bucket (bf16; D-k <= 3).
 bool deep_supported(const Dims& s, int k);

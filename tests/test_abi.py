@@ -288,7 +288,7 @@ def test_backward_plans_and_workspace():
         fff.backward_workspace_size(s, fff.make_plan("prefill", 4))
 
 
-@pytest.mark.parametrize("D,k,chunk,slices", [(8, 5, 8192, 8), (11, 8, 16384, 16), (7, 5, 8192, 8)])
+@pytest.mark.parametrize("D,k,chunk,slices", [(8, 5, 8192, 8), (11, 8, 16384, 16)])
 def test_bucketed_plan_workspace(D, k, chunk, slices):
     # Bucketed plans carve per-(chunk, tree) offsets and per-(chunk, tree,
     # slice) counts; the slices per chunk aim at about 512 workgroups of
@@ -349,3 +349,29 @@ def test_static_forward_validation(lib):
     assert n.value > fff.STATIC_SCRATCH_BYTES
     assert call(big) == fff.ERROR_WORKSPACE
     assert call(_shape(T=0)) == fff.SUCCESS
+
+
+def test_token_tile_plans():
+    # Split plans with chunk 0 take the token-tile subtree kernel where it
+    # applies (1 <= k <= 5, at most four levels below k, every level's
+    # records feeding the H pass: D + 1 <= 8); the resolved chunk stays 0 and
+    # the workspace holds all D + 1 logits per (tree, token).  An explicit
+    # chunk keeps the bucketed kernels.
+    up = lambda v: (v + 255) // 256 * 256  # noqa: E731
+    T, d, P, h = 16384, 2048, 32, 128
+    s = _shape(T=T, d=d, P=P, D=6, h=h)
+    r = fff.resolve_plan(s, fff.make_plan("prefill", 3, 0))
+    assert (r.split_level, r.chunk_tokens) == (3, 0)
+    expect = up(T * P * 7 * 4) + up(T * P * 4) + up(T * P * h * 2) + up(d * P * h * 2)
+    assert fff.workspace_size(s, r) == expect
+    r = fff.resolve_plan(s, fff.make_plan("prefill", 3, 4096))
+    assert (r.split_level, r.chunk_tokens) == (3, 4096)
+    # k = 6 > 5 at depth 6: bucketed
+    r = fff.resolve_plan(s, fff.make_plan("prefill", 6, 0))
+    assert r.chunk_tokens > 0
+    # depth 7, AUTO's split level 5: the token-tile kernel
+    r = fff.resolve_plan(_shape(T=T, d=d, P=P, D=7, h=h), fff.make_plan())
+    assert (r.algo, r.split_level, r.chunk_tokens) == (fff.ALGO_PREFILL, 5, 0)
+    # depth 8 needs the bucketed kernels (the H pass takes at most 8 levels)
+    r = fff.resolve_plan(_shape(T=T, d=d, P=P, D=8, h=h), fff.make_plan("prefill", 5, 0))
+    assert r.chunk_tokens > 0

@@ -172,6 +172,7 @@ SPLITS = [
     ("opt1p3b_d6", 7, 0),      # every level dense
     ("opt1p3b_d6", 4, 0),
     ("opt1p3b_d6", 3, 1000),   # chunks that do not divide T
+    ("opt1p3b_d6", 3, 4096),   # bucketed (an explicit chunk) beside the token-tile path (chunk 0)
     ("opt1p3b_d4", 1, 0),
     ("opt1p3b_d4", 5, 0),
     ("gpt125m", 2, 0),
@@ -315,6 +316,52 @@ def test_maximum_depth_generic():
     inp = workloads.random_inputs(50, 8, 1, 20, 2, "f32", seed=14, unit_rms_x=True)
     y, path = run(inp)
     check(inp, y, path)
+
+
+# The token-tile subtree kernel (split level k, chunk 0): every subtree
+# count it instantiates (2^k for k = 1..5), 1 to 4 subtree levels, token
+# counts that leave a ragged last tile, tree counts that leave a partial
+# last tree group, and one token.
+TILE = [
+    # T, d, P, D, h, k
+    (1000, 256, 5, 6, 128, 3),   # 512-token tiles, 4-tree groups: both ragged
+    (300, 128, 3, 5, 64, 2),     # 256-token tiles of 8 trees
+    (777, 256, 4, 4, 64, 1),     # 128-token tiles of 16 trees
+    (600, 512, 2, 7, 128, 4),    # 16 subtrees per tree
+    (513, 256, 3, 5, 64, 5),     # 32 subtrees of one level (the leaves)
+    (400, 256, 6, 5, 128, 3),    # three-level subtrees
+    (64, 2048, 32, 6, 128, 3),   # the decode workload's widths through the prefill path
+    (1, 64, 1, 1, 64, 1),
+    (2048, 2048, 32, 6, 128, 3),  # the headline widths, four full tiles
+]
+
+
+@needs_gpu
+@pytest.mark.parametrize("shape", TILE, ids=[str(s) for s in TILE])
+def test_subtree_tiles(shape):
+    import sparse_tree_structured_amd as fff
+    T, d, P, D, h, k = shape
+    inp = workloads.random_inputs(T, d, P, D, h, "bf16", seed=90 + k, unit_rms_x=True)
+    Td = to_device(inp)
+    plan = fff.resolve_plan(fff.shape_of(Td["x"], Td["W_node"], Td["V_node"]),
+                            fff.make_plan("prefill", k, 0))
+    assert plan.split_level == k and plan.chunk_tokens == 0  # the token-tile path
+    y, path = run(inp, algo="prefill", split_level=k)
+    print(shape, check(inp, y, path))
+
+
+@needs_gpu
+@pytest.mark.parametrize("name,k", [("opt1p3b_d6", 3), ("gpt125m", 2), ("opt1p3b_d4", 1)])
+def test_subtree_matches_dense_paths(name, k):
+    # The token-tile path and the all-dense path take the same decisions
+    # (bit for bit: the logits differ only in fp32 summation order, and no
+    # decision of these workloads lies that close to zero); their y agree
+    # to the bf16 tolerance.
+    inp = wl(name)
+    y1, p1 = run(inp, algo="prefill", split_level=k)
+    y2, p2 = run(inp, algo="prefill", split_level=inp.shape.D + 1)
+    np.testing.assert_array_equal(p1, p2)
+    assert np.abs(y1 - y2).max() <= 2e-2 * np.sqrt(np.mean(y2 ** 2))
 
 
 # Wide node outputs through the bucketed deep levels (v rows of 512 and

@@ -56,7 +56,8 @@ CASES = [
     (700, 256, 8, 6, 128, "bf16", "prefill", -1, 0.3),
     (700, 256, 8, 6, 128, "bf16", "prefill", -1, 0.9),     # a few paths left
     (500, 256, 40, 7, 64, "bf16", "prefill", -1, 0.6),     # trees packed across many tiles
-    (400, 256, 3, 6, 64, "bf16", "prefill", 3, 0.5),       # bucketed deep levels
+    (400, 256, 3, 6, 64, "bf16", "prefill", 3, 0.5),       # token-tile deep levels
+    (1100, 256, 9, 6, 128, "bf16", "prefill", 3, 0.7),     # ragged tiles and tree groups
     (300, 512, 4, 9, 64, "bf16", "prefill", 6, 0.7),
     (9, 256, 8, 5, 64, "bf16", "decode", -1, 0.5),
     (64, 1024, 16, 7, 64, "bf16", "decode", -1, 0.7),
@@ -72,6 +73,15 @@ def test_pruned_shapes(case):
     mask = random_mask(np.random.default_rng(T + D), P, D, frac)
     y, path = run_pruned(inp, mask, algo=algo, split_level=k)
     assert mask[np.arange(P)[None, :], path].all(), "every path ends at an alive leaf"
+    check(inp, y, path, leaf_alive=mask)
+
+
+@needs_gpu
+def test_pruned_bucketed_deep_levels():
+    # Bucketing (an explicit chunk) on pruned trees.
+    inp = workloads.random_inputs(400, 256, 3, 6, 64, "bf16", seed=35, unit_rms_x=True)
+    mask = random_mask(np.random.default_rng(9), 3, 6, 0.5)
+    y, path = run_pruned(inp, mask, algo="prefill", split_level=3, chunk_tokens=256)
     check(inp, y, path, leaf_alive=mask)
 
 
