@@ -63,14 +63,20 @@ bool split_ok(const Dims& s, int k) {
          (fff::deep_supported(s, k) || tile_ok(s, k));
 }
 
-// Every level dense up to depth 6: the dense product (about 1 PFLOP/s) beats
-// the bucketed deep levels, which gather each token's x row once per tree.
-// From depth 7 the bucketed levels win: measured at T = 16384, d = 2048,
-// P = 32, h = 128 (ms per forward): D = 6 dense 0.54, k = 5 0.68; D = 7 dense
-// 0.81, k = 5 0.69, k = 4 0.74; D = 8 k = 5 0.75, k = 6 0.79.  So depth 7
-// buckets its last three levels and deeper trees their last four; a shape
-// the bucketed kernels do not cover stays dense where the tile fits a tree.
+// Up to depth 5 every level is dense: with at most 64 columns per tree the
+// dense product beats the token-tile kernel (measured at the GPT-125M shape,
+// depth 5: 107 against 72 M tokens/s; OPT-1.3B shape, depth 4: 38 against
+// 35 M tokens/s).  At depths 6 and 7 the dense product would evaluate 128 or
+// 256 columns per tree for D + 1 nodes on a path; the top D - 3 levels stay
+// dense and the last four go through the token-tile kernel (depth 6 at the
+// OPT-1.3B shape: 32.6 against 26.7 M tokens/s all dense).  From depth 8 the
+// H pass cannot take the whole path's records, and the bucketed kernels take
+// the last levels (depth 8 and beyond, measured at T = 16384, d = 2048,
+// P = 32, h = 128, ms per forward: D = 8 k = 5 0.75, k = 6 0.79).  A shape a
+// kernel does not cover falls back to the next choice.
 int default_split(const Dims& s) {
+  if (s.D <= 5 && split_ok(s, s.D + 1)) return s.D + 1;
+  if (s.D >= 3 && tile_ok(s, s.D - 3)) return s.D - 3;
   if (s.D <= 6 && split_ok(s, s.D + 1)) return s.D + 1;
   const int k = s.D == 7 ? 5 : (s.D - 3 > 1 ? s.D - 3 : 1);
   if (k <= s.D && split_ok(s, k)) return k;

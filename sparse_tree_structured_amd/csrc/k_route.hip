@@ -450,6 +450,11 @@ hipError_t launch_top_cfg(const Dims& s, int L, int stride, const void* x, const
 using MidTile = TileCfg<128, 256, 64, 64, 128>;
 using SmallTile = TileCfg<64, 256, 64, 64, 64>;
 using TopDirect = DirectCfg<256, 256, 128, 64, 4>;
+// 64 tokens x 256 columns on four waves: 80 KB of stages, so two
+// workgroups share a compute unit; for few column tiles (the top three
+// levels of 32 trees are one tile) it fills the chip where 256-token tiles
+// would leave most compute units idle.
+using TopDirect64 = DirectCfg<64, 256, 64, 64, 4>;
 
 
 // One workgroup per packed row: packed[i] = W row colmap[i] (zeros for -1).
@@ -490,6 +495,8 @@ hipError_t launch_route_top(const Dims& s, int L, int stride, const void* x, con
   const int64_t tiles_n = top_col_tiles(s, L);
   if ((1 << L) <= TopDirect::BN && ((s.T + 255) / 256) * tiles_n >= 256)
     return launch_top_cfg<TopDirect, true>(s, L, stride, x, W, b, rec_logit, rec_next, st);
+  if ((1 << L) <= TopDirect64::BN && ((s.T + 63) / 64) * tiles_n >= 256)
+    return launch_top_cfg<TopDirect64, true>(s, L, stride, x, W, b, rec_logit, rec_next, st);
   if (((s.T + 127) / 128) * tiles_n >= 256)
     return launch_top_cfg<MidTile, false>(s, L, stride, x, W, b, rec_logit, rec_next, st);
   return launch_top_cfg<SmallTile, false>(s, L, stride, x, W, b, rec_logit, rec_next, st);

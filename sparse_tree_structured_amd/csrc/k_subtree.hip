@@ -28,8 +28,9 @@
 // Within a subtree the order of a group's tokens is free (every token's
 // result is its own).  Tokens are ordered so that a group's 16 rows differ
 // in their low four row bits where the counts allow: the operand read of a
-// group is then free of LDS bank conflicts under the XOR swizzle of the
-// direct-to-LDS loads.
+// group is then free of LDS bank conflicts under the rows' XOR swizzle
+// (chunk c of row r at slot c ^ ((r >> 1) & 3); with bits 2-3, as the
+// 32 x 32 x 16 products use, every such read measured 2-way conflicts).
 #include "common.hpp"
 #include "launch.hpp"
 #include "mfma_tile.hpp"
@@ -38,6 +39,11 @@ namespace fff {
 namespace {
 
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+// Chunk swizzle of the staged rows: chunk c of row r at slot c ^ ((r >> 1) & 3),
+// conflict-free for the 16-row operand fetches below when the 16 rows differ
+// in their low four bits.
+constexpr int kSwz = 1;
 
 template <int M_, int G_, int S_>
 struct SubCfg {
@@ -271,9 +277,9 @@ __global__ __launch_bounds__(C::kThreads, 1) void subtree_kernel(
     const int slot = e & 0xffff;
     int row = perm[tl * C::kSlots + slot + m];
     row = row < 0 ? 0 : row;
-    addrA[g] = static_cast<uint32_t>(row * C::kRowBytes + ((q ^ lds_swz(row)) << 4));
+    addrA[g] = static_cast<uint32_t>(row * C::kRowBytes + ((q ^ lds_swz_s<kSwz>(row)) << 4));
     const int brow = (tl * S + s) * 16 + m;
-    addrB[g] = static_cast<uint32_t>(brow * C::kRowBytes + ((q ^ lds_swz(brow)) << 4));
+    addrB[g] = static_cast<uint32_t>(brow * C::kRowBytes + ((q ^ lds_swz_s<kSwz>(brow)) << 4));
   }
   f32x4_t acc[C::kMaxG];
 #pragma unroll
@@ -282,7 +288,7 @@ __global__ __launch_bounds__(C::kThreads, 1) void subtree_kernel(
   // ---- main loop: two stages, one barrier per K step ----
   // Iteration ks issues the loads of stage ks+1 into buffer (ks+1) % 2, then
   // works on stage ks; iteration -1 only issues stage 0.  Each wave-wide
-  // load fills 16 rows of 64 bytes, XOR-swizzled (mfma_tile.hpp).
+  // load fills 16 rows of 64 bytes, chunks XOR-swizzled by row bits 1-2.
   for (int ks = -1; ks < nk; ++ks) {
     if (ks >= 0) {
       wait_vmcnt<0>();   // this wave's loads of stage ks have landed
@@ -290,8 +296,10 @@ __global__ __launch_bounds__(C::kThreads, 1) void subtree_kernel(
     }
     if (ks + 1 < nk) {
       const int buf = (ks + 1) & 1;
-      direct_load_rows<C, M>(lds, C::kOffX + buf * C::kXBytes, x_row, (ks + 1) * 32, wave, lane);
-      direct_load_rows<C, C::R>(lds, C::kOffW + buf * C::kWBytes, w_row, (ks + 1) * 32, wave, lane);
+      direct_load_rows_s<C, M, kSwz>(lds, C::kOffX + buf * C::kXBytes, x_row, (ks + 1) * 32, wave,
+                                     lane);
+      direct_load_rows_s<C, C::R, kSwz>(lds, C::kOffW + buf * C::kWBytes, w_row, (ks + 1) * 32,
+                                        wave, lane);
     }
     if (ks < 0) continue;
     const unsigned char* xs = lds + C::kOffX + (ks & 1) * C::kXBytes;

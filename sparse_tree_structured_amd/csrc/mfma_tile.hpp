@@ -209,6 +209,29 @@ __device__ __forceinline__ void direct_load_rows(unsigned char* lds, int base, c
   }
 }
 
+// The same loads with the 16-byte chunks swizzled by row bits SHIFT and
+// SHIFT+1: chunk c of row r at slot c ^ ((r >> SHIFT) & 3).  For the
+// 16 x 16 x 32 operand fetch (16 rows, one chunk per 16 lanes) SHIFT = 1 is
+// the bank-conflict-free choice on gfx950 for any 16 rows whose low four
+// bits differ (measured with SQ_LDS_BANK_CONFLICT; SHIFT = 2 gives 2-way
+// conflicts there).
+template <int SHIFT>
+__device__ __forceinline__ int lds_swz_s(int r) { return (r >> SHIFT) & 3; }
+
+template <class C, int ROWS, int SHIFT, class RowPtr>
+__device__ __forceinline__ void direct_load_rows_s(unsigned char* lds, int base, const RowPtr& row_ptr,
+                                                   int k0, int wave, int lane) {
+  constexpr int kLoads = ROWS / 16 / C::kWaves;
+#pragma unroll
+  for (int j = 0; j < kLoads; ++j) {
+    const int r0 = (wave * kLoads + j) * 16;
+    const int r = r0 + (lane >> 2);
+    const int chunk = (lane & 3) ^ lds_swz_s<SHIFT>(r);
+    const uint16_t* g = row_ptr(r) + k0 + chunk * 8;
+    __builtin_amdgcn_global_load_lds(g, lds + base + r0 * C::kRowBytes, 16, 0, 0);
+  }
+}
+
 // Operand fragments of one 16-wide k sub-step (kk = 0 or 1) of a stage.
 template <class C>
 struct Frags {

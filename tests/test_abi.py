@@ -369,9 +369,14 @@ def test_token_tile_plans():
     # k = 6 > 5 at depth 6: bucketed
     r = fff.resolve_plan(s, fff.make_plan("prefill", 6, 0))
     assert r.chunk_tokens > 0
-    # depth 7, AUTO's split level 5: the token-tile kernel
-    r = fff.resolve_plan(_shape(T=T, d=d, P=P, D=7, h=h), fff.make_plan())
-    assert (r.algo, r.split_level, r.chunk_tokens) == (fff.ALGO_PREFILL, 5, 0)
+    # AUTO: depth 6 and 7 keep the last four levels for the token-tile kernel
+    for D in (6, 7):
+        r = fff.resolve_plan(_shape(T=T, d=d, P=P, D=D, h=h), fff.make_plan())
+        assert (r.algo, r.split_level, r.chunk_tokens) == (fff.ALGO_PREFILL, D - 3, 0)
+    # depths 4 and 5 stay dense
+    for D in (4, 5):
+        r = fff.resolve_plan(_shape(T=T, d=d, P=P, D=D, h=h), fff.make_plan())
+        assert (r.algo, r.split_level) == (fff.ALGO_PREFILL, D + 1)
     # depth 8 needs the bucketed kernels (the H pass takes at most 8 levels)
     r = fff.resolve_plan(_shape(T=T, d=d, P=P, D=8, h=h), fff.make_plan("prefill", 5, 0))
     assert r.chunk_tokens > 0
