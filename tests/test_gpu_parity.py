@@ -356,12 +356,13 @@ def test_subtree_matches_dense_paths(name, k):
     # The token-tile path and the all-dense path take the same decisions
     # (bit for bit: the logits differ only in fp32 summation order, and no
     # decision of these workloads lies that close to zero); their y agree
-    # to the bf16 tolerance.
+    # to the bf16 tolerance (a rounding of H may land one bf16 step apart).
+    from oracle.compare import y_error
     inp = wl(name)
     y1, p1 = run(inp, algo="prefill", split_level=k)
     y2, p2 = run(inp, algo="prefill", split_level=inp.shape.D + 1)
     np.testing.assert_array_equal(p1, p2)
-    assert np.abs(y1 - y2).max() <= 2e-2 * np.sqrt(np.mean(y2 ** 2))
+    assert y_error(y1, y2)["err"] <= 2e-2
 
 
 # Wide node outputs through the bucketed deep levels (v rows of 512 and
