@@ -5,11 +5,15 @@ GELU*v accumulation into the concatenated buffer, the output projection)
 over one batch of synthetic tokens already resident in HBM.  The default
 workload is the OPT-1.3B-shaped depth-6 layer (T=16384, d=2048, P=32, D=6,
 h=128, bf16).  Input sets are rotated between steps so that the 256 MB
-Infinity Cache cannot serve a repeated call.
+Infinity Cache cannot serve a repeated call; a second, shorter pass on one
+input set gives the warm figure beside it.
 
-Prints one JSON line: tokens/s, the dominant kernel's roofline (measured live
-with HIP events recorded by the library around that kernel, on the stream it
-is launched on) and the CPU oracle's throughput on a bounded token sample.
+Prints one JSON line: tokens/s; the roofline of the dominant kernel, picked
+by measured time among the stages the library brackets with HIP events on
+the stream it launches on (W_out transpose, dense top levels, deep levels,
+H build, projection), with every stage's roofline beside it; and the CPU
+oracle's throughput on the same workload, whose output also gives the
+run's routing flips and y error.
 """
 from __future__ import annotations
 
@@ -44,7 +48,8 @@ def parse():
     ap.add_argument("--prune", type=float, default=0.0,
                     help="statically prune this fraction of each tree's paths (seeded random "
                          "leaf mask) and run fff_forward_pruned")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="oracle sample budget")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="oracle budget: three timed runs of about a third of this each")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--backward", action="store_true",
                     help="time fff_backward (gradients of sum(y * dy)) on the workload instead")
@@ -76,6 +81,9 @@ def algorithmic_work(s, U):
 KERNEL_SOURCES = {
     "proj_direct": ("k_proj.hip", "mfma_tile.hpp", "common.hpp"),
     "decode": ("k_decode.hip", "mfma_tile.hpp", "common.hpp"),
+    "subtree": ("k_subtree.hip", "mfma_tile.hpp", "common.hpp"),
+    "route_top": ("k_route.hip", "mfma_tile.hpp", "common.hpp"),
+    "hbuild": ("k_route.hip", "mfma_tile.hpp", "common.hpp"),
 }
 
 
@@ -118,7 +126,11 @@ def calibrate_copy():
     print(json.dumps({"copy_bytes_each_way": n, "dispatches": 3}), flush=True)
 
 
-def cpu_baseline(inp, budget_s, variant=0):
+def cpu_baseline(inp, budget_s, variant=0, leaf_alive=None):
+    """The CPU oracle (plain float64 C, every host thread) on the first n
+    tokens of the workload, n chosen so that three runs take about
+    `budget_s`; returns the median of the three and the oracle output of the
+    last run (for the parity figures)."""
     import numpy as np
 
     import oracle
@@ -127,16 +139,17 @@ def cpu_baseline(inp, budget_s, variant=0):
     threads = oracle.default_threads()
     T = inp.shape.T
 
-    def timed(n):
+    def run(n, **kw):
         t0 = time.perf_counter()
-        oracle.forward(f["x"][:n], f["W_node"], f["b_node"], f["V_node"], f["W_out"], nthreads=threads,
-                       variant=variant)
-        return time.perf_counter() - t0
+        r = oracle.forward(f["x"][:n], f["W_node"], f["b_node"], f["V_node"], f["W_out"],
+                           nthreads=threads, variant=variant, leaf_alive=leaf_alive, **kw)
+        return time.perf_counter() - t0, r
 
-    pilot = min(T, max(threads, 16))
-    tp = timed(pilot)
-    n = int(min(T, max(pilot, pilot * budget_s / max(tp, 1e-6))))
-    dt = timed(n) if n > pilot else tp
+    pilot = min(T, max(threads, 256))
+    tp, _ = run(pilot)
+    n = int(min(T, max(pilot, pilot * (budget_s / 3) / max(tp, 1e-6))))
+    times = [run(n)[0] for _ in range(3)]
+    dt = float(np.median(times))
     cpu = "unknown"
     try:
         with open("/proc/cpuinfo") as fh:
@@ -146,10 +159,39 @@ def cpu_baseline(inp, budget_s, variant=0):
                     break
     except OSError:
         pass
+    _, ref = run(n, want_records=True)
     return {"value": n / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "sample": f"first {n} of {T} tokens of the same workload (seed 0), full forward "
-                      f"(routing + projection) in float64, {dt:.2f} s wall on {cpu}",
-            "seconds": dt}
+                      f"(routing + projection) in float64, median of 3 runs "
+                      f"({', '.join(f'{t:.2f}' for t in times)} s) on {cpu}",
+            "seconds": dt, "tokens": n}, ref
+
+
+def parity_figures(inp, ref, n, path_dev, y_dev, variant=0, leaf_alive=None):
+    """Routing flips and y error of the device output on the oracle's tokens
+    (flipped tokens checked along the device's own paths)."""
+    import numpy as np
+
+    import oracle
+    from oracle.compare import check_path_signs, classify_paths, node_alive_from_leaves, y_error
+
+    s = inp.shape
+    cls = classify_paths(path_dev[:n], ref, s.D)
+    err = y_error(y_dev[:n], ref["y"], cls["tokens_ok"])
+    flipped = np.flatnonzero(~cls["tokens_ok"])
+    out = {"tokens_checked": int(n), "flips_near_tie": int(cls["flips_near_tie"]),
+           "mismatches_beyond_tie": len(cls["bad"]), "tokens_excluded": 0,
+           "tokens_flipped": int(len(flipped)), "y_err": err["err"],
+           "y_err_unfloored": err["err_unfloored"], "y_err_normwise": err["normwise"]}
+    if len(flipped):
+        f = inp.as_f64()
+        fr = oracle.forward(f["x"][flipped], f["W_node"], f["b_node"], f["V_node"], f["W_out"],
+                            forced=np.ascontiguousarray(path_dev[flipped], dtype=np.int32),
+                            want_records=True, variant=variant)
+        alive = node_alive_from_leaves(leaf_alive, s.D) if leaf_alive is not None else None
+        out["flipped_paths_valid"] = not check_path_signs(path_dev[flipped], fr, s.D, alive)
+        out["y_err_flipped"] = y_error(y_dev[flipped], fr["y"])["err"]
+    return out
 
 
 def _events_ms(torch, fn, steps, warmup):
@@ -432,32 +474,43 @@ def main():
     torch.cuda.synchronize()
 
     # HIP events (torch-created, so profilers see ordinary events) that the
-    # library records on `stream` around its stages.  Record each once so the
-    # underlying event exists before its handle is passed on.
-    evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in range(args.steps)]
-    for trio in evs:
-        for e in trio:
-            e.record(stream)
-    torch.cuda.synchronize()
-    sev = [fff.StageEvents(a.cuda_event, b.cuda_event, c.cuda_event) for a, b, c in evs]
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(i, sev[i])
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
+    # library records on `stream` at its stage boundaries.  Record each once
+    # so the underlying event exists before its handle is passed on.
+    nev = len(fff.StageEvents.NAMES)
 
-    route_ms = [a.elapsed_time(b) for a, b, _ in evs]
-    proj_ms = [b.elapsed_time(c) for _, b, c in evs]
-    fwd_ms = [a.elapsed_time(c) for a, _, c in evs]
+    def timed_pass(nsteps, rotating):
+        evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(nev))
+               for _ in range(nsteps)]
+        for ev in evs:
+            for e in ev:
+                e.record(stream)
+        torch.cuda.synchronize()
+        sev = [fff.StageEvents(*[e.cuda_event for e in ev]) for ev in evs]
+        t0 = time.perf_counter()
+        for i in range(nsteps):
+            step(i if rotating else 0, sev[i])
+        torch.cuda.synchronize()
+        elapsed = time.perf_counter() - t0
+        # per step: the intervals between consecutive stage events (ms)
+        stages = np.array([[ev[j].elapsed_time(ev[j + 1]) for j in range(nev - 1)] for ev in evs])
+        fwd = np.array([ev[0].elapsed_time(ev[-1]) for ev in evs])
+        return elapsed, stages, fwd
 
-    # Distinct visited (tree, node) pairs for the algorithmic byte count,
-    # from the device's own paths on input set 0.
+    elapsed, stages_ms, fwd_ms = timed_pass(args.steps, True)
+    _, _, warm_ms = timed_pass(max(5, args.steps // 2), False)
+
+    # Device output on input set 0 (paths for the distinct visited nodes, the
+    # empty-leaf fraction and the parity figures).
     step(0)
     torch.cuda.synchronize()
     leaves = path.cpu().numpy().astype(np.int64)
+    y0 = y.float().cpu().numpy().astype(np.float64)
     visited = set()
+    used_leaves = 0
     for p in range(shape.P):
-        for lf in np.unique(leaves[:, p]):
+        lfs = np.unique(leaves[:, p])
+        used_leaves += len(lfs)
+        for lf in lfs:
             n = int(lf) + (1 << shape.D) - 1
             while True:
                 visited.add((p, n))
@@ -465,31 +518,66 @@ def main():
                     break
                 n = (n - 1) // 2
     U = len(visited)
+    empty_leaf_frac = 1.0 - used_leaves / float(shape.P << shape.D)
     f_route, f_proj, b_alg = algorithmic_work(shape, U)
     ms_step = 1e3 * elapsed / args.steps
     tokens_per_s = shape.T * args.steps / elapsed
 
+    # Stage rooflines.  Work per stage is what the method itself needs there:
+    # the routing stages' logits only along the paths (T*P per level, 2d
+    # flops each) and each stage's own operand and result bytes (the H build:
+    # its records in, H out; the projection: H, W_out and y).
+    e = 2 if shape.dtype == "bf16" else 4
+    T, d, P, D, h, K = shape.T, shape.d, shape.P, shape.D, shape.h, shape.P * shape.h
+    k = plan.split_level if plan.algo == fff.ALGO_PREFILL else D + 1
+    k = min(k, D + 1)
+    x_bytes = T * d * e
+    rows_top = P * ((1 << k) - 1)
+    rows_deep = P * ((1 << (D + 1)) - (1 << k))
+    stage_work = {
+        # name: (flops, bytes)
+        "prepare": (0, 2 * K * d * e),
+        "top": (2 * T * P * k * d, x_bytes + rows_top * (d + 1) * e + 4 * T * P * (k + 1)),
+        "deep": (2 * T * P * (D + 1 - k) * d,
+                 x_bytes + rows_deep * (d + 1) * e + 4 * T * P * (D + 2 - k)),
+        "hbuild": (2 * T * P * (D + 1) * h,
+                   4 * T * P * (D + 2) + P * shape.N * h * e + T * K * e + 4 * T * P),
+        "proj": (f_proj, T * K * e + K * d * e + T * d * e),
+    }
     fused = plan.algo == fff.ALGO_DECODE
-    if fused:
-        # One kernel is the whole layer: its bytes are the layer's.  The
-        # library records `start` before and `routed` right after that one
-        # launch (`done` follows as a second, back-to-back event record).
-        t_dom = float(np.mean(route_ms)) * 1e-3
-        achieved = b_alg / t_dom / 1e9
-        roof = {"bound": "hbm", "kernel": "decode", "achieved": achieved,
-                "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": achieved / PEAK_HBM_GBPS,
-                "traffic": measured_traffic("decode", args.workload),
-                "per_launch": {"bytes": b_alg, "avg_us": t_dom * 1e6}}
+    names = ["prepare", "top", "deep", "hbuild", "proj"]
+    stage_us = {n: float(np.mean(stages_ms[:, j])) * 1e3 for j, n in enumerate(names)}
+    if fused:  # one kernel: its time sits in the first interval
+        stage_us = {"decode": float(np.mean(stages_ms[:, 0])) * 1e3}
+        stage_work = {"decode": (f_route + f_proj, b_alg)}
+    stages = {}
+    for n, us in stage_us.items():
+        fl, by = stage_work[n]
+        t_mfma = fl / (PEAK_MFMA_BF16_TFLOPS * 1e12)
+        t_hbm = by / (PEAK_HBM_GBPS * 1e9)
+        bound = "mfma" if t_mfma >= t_hbm else "hbm"
+        t = max(us, 1e-3) * 1e-6
+        stages[n] = {"us": us, "flops": fl, "bytes": by, "bound": bound,
+                     "tflops": fl / t / 1e12, "gbps": by / t / 1e9,
+                     "frac": max(t_mfma, t_hbm) / t}
+    dom = max(stages, key=lambda n: stages[n]["us"])
+    ds = stages[dom]
+    kernel_of = {"prepare": "transpose", "top": "route_top", "deep": "subtree", "hbuild": "hbuild",
+                 "proj": "proj_direct", "decode": "decode"}
+    traffic = measured_traffic(kernel_of[dom], args.workload)
+    if ds["bound"] == "mfma":
+        roof = {"bound": "mfma", "kernel": kernel_of[dom], "stage": dom, "achieved": ds["tflops"],
+                "peak": PEAK_MFMA_BF16_TFLOPS, "unit": "TFLOP/s", "frac": ds["frac"],
+                "traffic": traffic, "per_launch": {"flops": ds["flops"], "avg_us": ds["us"]}}
     else:
-        t_dom = float(np.mean(proj_ms)) * 1e-3
-        achieved = f_proj / t_dom / 1e12
-        roof = {"bound": "mfma", "kernel": "proj_direct", "achieved": achieved,
-                "peak": PEAK_MFMA_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": achieved / PEAK_MFMA_BF16_TFLOPS,
-                "traffic": measured_traffic("proj_direct", args.workload),
-                "per_launch": {"flops": f_proj, "avg_us": t_dom * 1e6}}
+        roof = {"bound": "hbm", "kernel": kernel_of[dom], "stage": dom, "achieved": ds["gbps"],
+                "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": ds["frac"], "traffic": traffic,
+                "per_launch": {"bytes": ds["bytes"], "avg_us": ds["us"]}}
+    if traffic:
+        roof["traffic_gbps"] = traffic / (ds["us"] * 1e-6) / 1e9
 
     t_roof = max(b_alg / (PEAK_HBM_GBPS * 1e9), (f_route + f_proj) / (PEAK_MFMA_BF16_TFLOPS * 1e12))
+    t_med = float(np.median(fwd_ms)) * 1e-3
     out = {
         "metric": METRIC,
         "value": tokens_per_s,
@@ -515,17 +603,28 @@ def main():
                                    if plan.algo == fff.ALGO_PREFILL else None}}
                       if prunings is not None else {})},
         "roofline": roof,
+        "stages": stages,
         "layer": {"F_alg": f_route + f_proj, "B_alg": b_alg, "U": U,
                   "t_roof_us": t_roof * 1e6, "roof_frac": t_roof / (ms_step * 1e-3),
-                  "route_us": float(np.mean(route_ms)) * 1e3,
-                  "proj_us": float(np.mean(proj_ms)) * 1e3,
-                  "forward_us_median": float(np.median(fwd_ms)) * 1e3,
-                  "forward_us_p10": float(np.percentile(fwd_ms, 10)) * 1e3,
-                  "forward_us_p90": float(np.percentile(fwd_ms, 90)) * 1e3},
+                  "hbm_frac": b_alg / (ms_step * 1e-3) / (PEAK_HBM_GBPS * 1e9),
+                  "mfma_frac_proj": stages["proj"]["frac"] if "proj" in stages else None,
+                  "empty_leaf_frac": empty_leaf_frac,
+                  "route_us": float(np.mean(stages_ms[:, :4].sum(axis=1))) * 1e3,
+                  "proj_us": float(np.mean(stages_ms[:, 4])) * 1e3,
+                  "t_us_median": t_med * 1e6,
+                  "t_us_p10": float(np.percentile(fwd_ms, 10)) * 1e3,
+                  "t_us_p90": float(np.percentile(fwd_ms, 90)) * 1e3,
+                  "rotated": True,
+                  "warm_t_us_median": float(np.median(warm_ms)) * 1e3,
+                  "warm_tokens_per_s": shape.T / (float(np.median(warm_ms)) * 1e-3)},
         "host": platform.node(),
     }
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(inp0, args.cpu_seconds, variant)
+        cb, ref = cpu_baseline(inp0, args.cpu_seconds, variant,
+                               mask if prunings is not None else None)
+        out["cpu_baseline"] = cb
+        out["parity"] = parity_figures(inp0, ref, cb["tokens"], leaves, y0, variant,
+                                       mask if prunings is not None else None)
     print(json.dumps(out), flush=True)
 
 

@@ -142,11 +142,25 @@ typedef struct fff_plan {
 } fff_plan_t;
 
 /* Optional events recorded on `stream` at stage boundaries (each may be
- * NULL): `start` before the first kernel, `routed` once the concatenated tree
- * outputs are complete, `done` after the projection.  Algorithms that fuse
- * routing and projection record `routed` together with `done`. */
+ * NULL), in this order:
+ *   start     before the first kernel
+ *   prepared  after W_out is transposed for the projection (PREFILL plans
+ *             with the direct-to-LDS projection; elsewhere with `start`)
+ *   top       after the densely evaluated levels (GENERIC: every level's
+ *             logits)
+ *   deep      after the deep levels (the token-tile or bucketed kernels;
+ *             with `top` where every level is dense)
+ *   routed    once the concatenated tree outputs H are complete
+ *   done      after the projection
+ * A stage a plan does not have is recorded together with the previous
+ * event; DECODE (one kernel for the whole layer) records `start` before it
+ * and every other event after it.  The interval between two consecutive
+ * events is that stage's time on the stream. */
 typedef struct fff_stage_events {
     hipEvent_t start;
+    hipEvent_t prepared;
+    hipEvent_t top;
+    hipEvent_t deep;
     hipEvent_t routed;
     hipEvent_t done;
 } fff_stage_events_t;

@@ -49,7 +49,10 @@ class Plan(ctypes.Structure):
 
 
 class StageEvents(ctypes.Structure):
-    _fields_ = [("start", ctypes.c_void_p), ("routed", ctypes.c_void_p), ("done", ctypes.c_void_p)]
+    """fff_stage_events_t: HIP events recorded at the stage boundaries."""
+    _fields_ = [("start", ctypes.c_void_p), ("prepared", ctypes.c_void_p), ("top", ctypes.c_void_p),
+                ("deep", ctypes.c_void_p), ("routed", ctypes.c_void_p), ("done", ctypes.c_void_p)]
+    NAMES = ("start", "prepared", "top", "deep", "routed", "done")
 
 
 class Pruning(ctypes.Structure):

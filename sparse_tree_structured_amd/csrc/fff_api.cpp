@@ -238,21 +238,30 @@ fff_status_t record(hipEvent_t ev, hipStream_t st) {
   return hip_status(hipEventRecord(ev, st));
 }
 
-// Routing stage into H (caller or workspace buffer).
+// Routing stage into H (caller or workspace buffer); records the `top` and
+// `deep` events (NULL events: none).
 fff_status_t run_route(const Dims& s, const fff_plan_t& p, const Layout& L, const void* x,
                        const void* W, const void* b, const void* V, void* H, int32_t* path_out,
-                       char* ws, hipStream_t st) {
+                       char* ws, hipStream_t st, const fff_stage_events_t* ev) {
   float* logits = reinterpret_cast<float*>(ws + L.logits);
   int32_t* leaf = reinterpret_cast<int32_t*>(ws + L.leaf);
+  const fff_stage_events_t none{};
+  const fff_stage_events_t& E = ev ? *ev : none;
   hipError_t e;
+  fff_status_t r;
   if (p.algo == FFF_ALGO_PREFILL) {
     const int k = p.split_level;
     e = fff::launch_route_top(s, k, L.tile ? s.D + 1 : k, x, W, b, logits, leaf, st);
     if (e != hipSuccess) return FFF_ERROR_HIP;
-    if (k == s.D + 1) return hip_status(fff::launch_hbuild(s, logits, leaf, V, H, path_out, st));
+    if ((r = record(E.top, st)) != FFF_SUCCESS) return r;
+    if (k == s.D + 1) {
+      if ((r = record(E.deep, st)) != FFF_SUCCESS) return r;
+      return hip_status(fff::launch_hbuild(s, logits, leaf, V, H, path_out, st));
+    }
     if (L.tile) {
       e = fff::launch_subtree(s, k, x, W, b, logits, leaf, st);
       if (e != hipSuccess) return FFF_ERROR_HIP;
+      if ((r = record(E.deep, st)) != FFF_SUCCESS) return r;
       return hip_status(fff::launch_hbuild(s, logits, leaf, V, H, path_out, st));
     }
     int32_t* perm = reinterpret_cast<int32_t*>(ws + L.perm);
@@ -260,11 +269,14 @@ fff_status_t run_route(const Dims& s, const fff_plan_t& p, const Layout& L, cons
     int32_t* cnt = reinterpret_cast<int32_t*>(ws + L.cnt);
     e = fff::launch_bucket(s, k, leaf, perm, offs, cnt, p.chunk_tokens, st);
     if (e != hipSuccess) return FFF_ERROR_HIP;
-    return hip_status(fff::launch_deep(s, k, x, W, b, V, logits, perm, offs, H, path_out,
-                                       p.chunk_tokens, st));
+    e = fff::launch_deep(s, k, x, W, b, V, logits, perm, offs, H, path_out, p.chunk_tokens, st);
+    if (e != hipSuccess) return FFF_ERROR_HIP;
+    return record(E.deep, st);  // the deep kernel writes H itself
   }
   e = fff::launch_route_generic(s, x, W, b, logits, path_out, leaf, st);
   if (e != hipSuccess) return FFF_ERROR_HIP;
+  if ((r = record(E.top, st)) != FFF_SUCCESS) return r;
+  if ((r = record(E.deep, st)) != FFF_SUCCESS) return r;
   e = fff::launch_hbuild_generic(s, logits, leaf, V, H, st);
   return hip_status(e);
 }
@@ -313,28 +325,31 @@ fff_status_t forward_impl(const Dims& s, const fff_plan_t& p, const void* x, con
 
   char* ws = static_cast<char*>(workspace);
   void* H = ws + L.H;
-  if (events && (st = record(events->start, stream)) != FFF_SUCCESS) return st;
+  const fff_stage_events_t none{};
+  const fff_stage_events_t& E = events ? *events : none;
+  if ((st = record(E.start, stream)) != FFF_SUCCESS) return st;
   if (p.algo == FFF_ALGO_DECODE) {
     st = hip_status(fff::launch_decode(s, x, W_node, b_node, V_node, W_out, y, path_out, ws,
                                        stream));
     if (st != FFF_SUCCESS) return st;
-    if (events && (st = record(events->routed, stream)) != FFF_SUCCESS) return st;
-    if (events && (st = record(events->done, stream)) != FFF_SUCCESS) return st;
+    for (hipEvent_t ev : {E.prepared, E.top, E.deep, E.routed, E.done})
+      if ((st = record(ev, stream)) != FFF_SUCCESS) return st;
     return FFF_SUCCESS;
   }
   // The projection's transposed W_out is prepared first, so that the
   // projection stage is the matrix product alone.
   if (L.use_wt && fff::launch_transpose(W_out, ws + L.WT, s.K, s.d, stream) != hipSuccess)
     return FFF_ERROR_HIP;
-  st = run_route(s, p, L, x, W_node, b_node, V_node, H, path_out, ws, stream);
+  if ((st = record(E.prepared, stream)) != FFF_SUCCESS) return st;
+  st = run_route(s, p, L, x, W_node, b_node, V_node, H, path_out, ws, stream, &E);
   if (st != FFF_SUCCESS) return st;
-  if (events && (st = record(events->routed, stream)) != FFF_SUCCESS) return st;
+  if ((st = record(E.routed, stream)) != FFF_SUCCESS) return st;
   if (L.use_wt)
     st = hip_status(fff::launch_project_direct(s, H, ws + L.WT, y, stream));
   else
     st = run_project(s, p.algo, H, W_out, y, stream);
   if (st != FFF_SUCCESS) return st;
-  if (events && (st = record(events->done, stream)) != FFF_SUCCESS) return st;
+  if ((st = record(E.done, stream)) != FFF_SUCCESS) return st;
   return FFF_SUCCESS;
 }
 
@@ -677,7 +692,7 @@ fff_status_t fff_route(const fff_shape_t* shape, const fff_plan_t* plan, const v
   if (L.total > 0 && (!workspace || workspace_bytes < L.total)) return FFF_ERROR_WORKSPACE;
   if (workspace && !aligned(workspace, kWsAlign)) return FFF_ERROR_INVALID_VALUE;
   return run_route(s, p, L, x, W_node, b_node, V_node, H, path_out, static_cast<char*>(workspace),
-                   stream);
+                   stream, nullptr);
 }
 
 fff_status_t fff_project(const fff_shape_t* shape, int32_t algo, const void* H, const void* W_out,
