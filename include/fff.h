@@ -113,10 +113,26 @@ typedef struct fff_shape {
  * the whole layer, routing overlapped with the stream of W_out) needs bf16,
  * 1 <= T <= 64, d % 128 == 0, d <= 2048, h % 8 == 0, h <= 256,
  * P*h % 512 == 0 and D <= 15; AUTO takes it whenever the shape allows.
- * DECODE tags its cross-workgroup slots with a fresh per-call value passed
- * from the host, so a DECODE call must not be captured into a HIP graph and
- * replayed (a replay would reuse the value); capture PREFILL or GENERIC
- * plans instead, which launch only ordinary kernels (no memset nodes). */
+ *
+ * DECODE hands data between workgroups through slots in the workspace,
+ * tagged with a per-call epoch; nothing needs clearing between calls.  An
+ * ordinary call takes a fresh epoch from the host.  A call captured into a
+ * HIP graph (the stream is capturing when fff_forward is called) takes its
+ * epoch from a header word in the workspace instead: the call reads it at
+ * entry and the last workgroup to finish advances it, so every replay gets a
+ * new epoch.  Replays of one workspace must not overlap (one stream, or
+ * ordered streams).  PREFILL and GENERIC plans launch only ordinary kernels
+ * (no memset nodes) and capture as they are.
+ *
+ * DECODE assumes its workgroups are resident together (the grid is sized
+ * from the device's occupancy); a workgroup that waits for another polls a
+ * bounded number of times (about 0.1 s).  If a wait gives up, the columns
+ * of y that depend on it come out NaN, for every token, and the kernel
+ * still ends normally.  In a captured call a give-up also marks the
+ * workspace header: every later captured call on that workspace then
+ * writes NaN to all of y (and leaves path_out as it was), without waiting,
+ * until an ordinary (uncaptured) DECODE call on the workspace, or clearing
+ * the workspace's first 256 bytes, resets it. */
 typedef enum fff_algo {
     FFF_ALGO_AUTO = 0,
     FFF_ALGO_GENERIC = 1,
@@ -139,7 +155,15 @@ typedef struct fff_plan {
                              this many tokens (a chunk's x rows are reread
                              from cache by all trees; each chunk restages
                              every subtree's rows) */
+    int32_t flags;        /* 0, or FFF_PLAN_* bits below; other bits are
+                             FFF_ERROR_INVALID_VALUE */
 } fff_plan_t;
+
+/* For tests of the decode wait's give-up only: DECODE's routing workgroups
+ * do not publish their items, and the projection's waits poll a few times
+ * instead of about 0.1 s, so every wait gives up and y comes out NaN (see
+ * the DECODE notes above).  Other algorithms ignore it. */
+#define FFF_PLAN_TEST_DECODE_NO_PUBLISH 1
 
 /* Optional events recorded on `stream` at stage boundaries (each may be
  * NULL), in this order:

@@ -30,6 +30,8 @@ ALGO_GENERIC = 1
 ALGO_PREFILL = 2
 ALGO_DECODE = 3
 ALGOS = {"auto": ALGO_AUTO, "generic": ALGO_GENERIC, "prefill": ALGO_PREFILL, "decode": ALGO_DECODE}
+# fff_plan_t flags
+PLAN_TEST_DECODE_NO_PUBLISH = 1
 # fff_variant_t
 VARIANT_FFF = 0
 VARIANT_POST = 1
@@ -45,7 +47,7 @@ class Shape(ctypes.Structure):
 
 class Plan(ctypes.Structure):
     _fields_ = [("algo", ctypes.c_int32), ("split_level", ctypes.c_int32),
-                ("chunk_tokens", ctypes.c_int32)]
+                ("chunk_tokens", ctypes.c_int32), ("flags", ctypes.c_int32)]
 
 
 class StageEvents(ctypes.Structure):
@@ -140,10 +142,11 @@ def make_shape(T: int, d: int, P: int, D: int, h: int, dtype: int, variant=VARIA
     return Shape(int(T), int(d), int(P), int(D), int(h), int(dtype), _variant_code(variant))
 
 
-def make_plan(algo=ALGO_AUTO, split_level: int = -1, chunk_tokens: int = 0) -> Plan:
+def make_plan(algo=ALGO_AUTO, split_level: int = -1, chunk_tokens: int = 0,
+              flags: int = 0) -> Plan:
     if isinstance(algo, str):
         algo = ALGOS[algo]
-    return Plan(int(algo), int(split_level), int(chunk_tokens))
+    return Plan(int(algo), int(split_level), int(chunk_tokens), int(flags))
 
 
 def plan_default(shape: Shape) -> Plan:
@@ -271,16 +274,17 @@ def alloc_workspace(shape: Shape, plan: Optional[Plan], device):
 def forward(x, W_node, b_node, V_node, W_out, *, algo=ALGO_AUTO, split_level: int = -1,
             chunk_tokens: int = 0, want_path: bool = True, workspace=None, y=None, path_out=None,
             stream=None, events: Optional[StageEvents] = None,
-            variant=VARIANT_FFF) -> Tuple[object, Optional[object]]:
+            variant=VARIANT_FFF, plan_flags: int = 0) -> Tuple[object, Optional[object]]:
     """y = FFF(x); returns (y, path_out[T,P] int32 or None).
 
     ``variant`` "fff" (0) applies GELU to each visited node's logit; "post"
-    (1) applies it to each element of a tree's summed output instead."""
+    (1) applies it to each element of a tree's summed output instead.
+    ``plan_flags``: fff_plan_t flags (PLAN_TEST_DECODE_NO_PUBLISH, tests only)."""
     torch = _torch()
     shape = shape_of(x, W_node, V_node, variant)
     _check_layer(shape, x, W_node, b_node, V_node, W_out, y=y, path_out=path_out,
                  workspace=workspace)
-    plan = make_plan(algo, split_level, chunk_tokens)
+    plan = make_plan(algo, split_level, chunk_tokens, plan_flags)
     if workspace is None:
         workspace, nbytes = alloc_workspace(shape, plan, x.device)
     else:
@@ -302,13 +306,14 @@ def forward(x, W_node, b_node, V_node, W_out, *, algo=ALGO_AUTO, split_level: in
 
 def forward_static(x, W_node, b_node, V_node, W_out, y, path_out=None, *, algo=ALGO_AUTO,
                    split_level: int = -1, chunk_tokens: int = 0, stream=None,
-                   events: Optional[StageEvents] = None, variant=VARIANT_FFF):
+                   events: Optional[StageEvents] = None, variant=VARIANT_FFF,
+                   plan_flags: int = 0):
     """fff_forward_static: the layer with the library's fixed scratch region
     as its workspace.  The caller passes y [T,d] (and path_out [T,P] int32,
     or None); nothing is allocated."""
     shape = shape_of(x, W_node, V_node, variant)
     _check_layer(shape, x, W_node, b_node, V_node, W_out, y=y, path_out=path_out)
-    plan = make_plan(algo, split_level, chunk_tokens)
+    plan = make_plan(algo, split_level, chunk_tokens, plan_flags)
     st = load_library().fff_forward_static(
         ctypes.byref(shape), ctypes.byref(plan), x.data_ptr(), W_node.data_ptr(),
         b_node.data_ptr(), V_node.data_ptr(), W_out.data_ptr(), y.data_ptr(),

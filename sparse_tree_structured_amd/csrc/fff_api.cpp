@@ -17,6 +17,7 @@ using fff::Dims;
 
 constexpr int64_t kMaxElems = int64_t(1) << 40;
 constexpr size_t kWsAlign = 256;
+constexpr int32_t kPlanFlags = FFF_PLAN_TEST_DECODE_NO_PUBLISH;  // every defined plan flag
 
 bool mul_ok(int64_t a, int64_t b, int64_t limit) { return a == 0 || b <= limit / a; }
 
@@ -96,6 +97,8 @@ fff_status_t resolve_plan(const Dims& s, const fff_plan_t* in, fff_plan_t* out,
   p.algo = in ? in->algo : FFF_ALGO_AUTO;
   p.split_level = in ? in->split_level : -1;
   p.chunk_tokens = in ? in->chunk_tokens : 0;
+  p.flags = in ? in->flags : 0;
+  if (p.flags & ~kPlanFlags) return FFF_ERROR_INVALID_VALUE;
   if (p.algo == FFF_ALGO_AUTO) {
     if (!staged && fff::decode_supported(s))
       p.algo = FFF_ALGO_DECODE;
@@ -330,7 +333,7 @@ fff_status_t forward_impl(const Dims& s, const fff_plan_t& p, const void* x, con
   if ((st = record(E.start, stream)) != FFF_SUCCESS) return st;
   if (p.algo == FFF_ALGO_DECODE) {
     st = hip_status(fff::launch_decode(s, x, W_node, b_node, V_node, W_out, y, path_out, ws,
-                                       stream));
+                                       p.flags, stream));
     if (st != FFF_SUCCESS) return st;
     for (hipEvent_t ev : {E.prepared, E.top, E.deep, E.routed, E.done})
       if ((st = record(ev, stream)) != FFF_SUCCESS) return st;
@@ -362,6 +365,8 @@ fff_status_t resolve_bwd_plan(const Dims& s, const fff_plan_t* in, fff_plan_t* o
   p.algo = in ? in->algo : FFF_ALGO_AUTO;
   p.split_level = in ? in->split_level : -1;
   p.chunk_tokens = 0;
+  p.flags = in ? in->flags : 0;
+  if (p.flags & ~kPlanFlags) return FFF_ERROR_INVALID_VALUE;
   if (p.algo == FFF_ALGO_AUTO) p.algo = bwd_mfma_fits(s) ? FFF_ALGO_PREFILL : FFF_ALGO_GENERIC;
   switch (p.algo) {
     case FFF_ALGO_GENERIC:

@@ -36,16 +36,33 @@
 // until its stores have completed, then publishes by storing the call's
 // epoch into a slot of its own (routing items; split-K partials).  A slot
 // that does not hold the current epoch counts as not done, so nothing needs
-// clearing between calls or before the first one.  Epochs come from a per-process counter started at a random
-// point.  A projection workgroup only waits on routing workgroups, which
-// have lower block ids, never wait themselves and are all resident (the
-// grid is capped at what the device holds at once); the wait is also
-// bounded.
+// clearing between calls or before the first one.
+//
+// Epochs.  An ordinary call gets a fresh one from the host (a per-process
+// counter started at a random point) and records it in the workspace
+// header.  A call captured into a graph cannot take a new value from the
+// host on each replay, so it reads the header at entry instead and uses the
+// next value; the workgroup that sees every partial of the call arrived
+// (which implies every workgroup has read the header) stores the call's
+// epoch back.  A header that fails its check word (a fresh workspace) gives
+// the launch's own value.
+//
+// A projection workgroup only waits on routing workgroups, which have lower
+// block ids, never wait themselves and are all resident (the grid is capped
+// at what the device holds at once); the wait is also bounded.  A wait that
+// gives up poisons the workgroup's partial with NaN (so the columns of y it
+// feeds come out NaN) and marks its arrival slot.  In a captured call that
+// mark turns the header into a poisoned state: a routing workgroup that
+// starts only after the call was finished off would otherwise read the
+// advanced header and publish with the next replay's epoch; in the poisoned
+// state every workgroup only writes NaN to y, until an ordinary call
+// rewrites the header.
 #include <atomic>
 #include <chrono>
 #include <random>
 
 #include "common.hpp"
+#include "fff.h"
 #include "launch.hpp"
 #include "mfma_tile.hpp"
 
@@ -66,8 +83,18 @@ constexpr int kMaxD = 2048;       // model width: 16 k-steps per wave slice
 constexpr int kMaxH = 256;        // node output width: 2 H pieces per thread
 constexpr int kHPieces = kDecTok * (kMaxH / 8) / kDecThreads;
 constexpr int kWtPitch = kKc + 8;
-constexpr uint64_t kEpochMask = (uint64_t(1) << 40) - 1;
+// Epochs are 62-bit and never 0.  Those of ordinary calls have bit 61 set
+// (random values), those a captured call derives from the header have it
+// clear, so the two kinds never meet.
+constexpr uint64_t kEpochMask = (uint64_t(1) << 62) - 1;
+constexpr uint64_t kDeviceEpochMask = (uint64_t(1) << 61) - 1;
+constexpr uint64_t kHostEpochBit = uint64_t(1) << 61;
+constexpr uint64_t kGaveUp = uint64_t(1) << 63;  // arrival slot: the partial's wait gave up
+// Header check words: header[1] = header[0] ^ one of these.
+constexpr uint64_t kHdrValid = 0x6A09E667F3BCC908ull;
+constexpr uint64_t kHdrPoison = 0xBB67AE8584CAA73Bull;
 constexpr int kSpinLimit = 1 << 22;
+constexpr int kTestSpinLimit = 64;
 constexpr int kSc1 = 16;  // buffer cache policy: device scope (sc1)
 
 struct DecodeArgs {
@@ -81,8 +108,14 @@ struct DecodeArgs {
   uint16_t* H;       // workspace [T, K] bf16
   float* partial;    // workspace [K / kKc, T, d] fp32
   uint64_t* done;    // workspace [routing items] epoch of the call that routed it
-  uint64_t* arrive;  // workspace [d / kColSlice][K / kKc] epoch of the call whose partial arrived
-  uint64_t epoch;
+  uint64_t* arrive;  // workspace [d / kColSlice][K / kKc] epoch of the call whose partial
+                     // arrived, | kGaveUp if its wait gave up
+  uint64_t* hdr;     // workspace header: [0] epoch of the last call, [1] check word
+  uint64_t seed;     // the call's epoch (ordinary call), or the one to use when the header
+                     // fails its check (captured call)
+  int device_epoch;  // 1: captured call, epoch from the header
+  int publish;       // 0: routing items are not published (give-up test)
+  int spin_limit;    // polls of a projection wait
   int T, d, P, D, h, K;
   int64_t N;
   int n_route_wg, n_proj_wg;
@@ -133,16 +166,18 @@ __device__ __forceinline__ void coherent_store16(__amdgpu_buffer_rsrc_t r, uint3
   __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v), r, off, 0, kSc1);
 }
 
-// One wave waits (bounded) until slots [first, first + n) all hold `epoch`.
-__device__ void wait_slots(const uint64_t* done, int first, int n, uint64_t epoch) {
+// One wave waits (at most `limit` polls) until slots [first, first + n) all
+// hold `epoch`; false if it gave up.
+__device__ bool wait_slots(const uint64_t* done, int first, int n, uint64_t epoch, int limit) {
   const int lane = threadIdx.x & (kWave - 1);
-  for (int it = 0; it < kSpinLimit; ++it) {
+  for (int it = 0; it < limit; ++it) {
     bool ok = true;
     for (int i = lane; i < n; i += kWave)
       ok &= __hip_atomic_load(done + first + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == epoch;
-    if (__all(ok)) break;
+    if (__all(ok)) return true;
     __builtin_amdgcn_s_sleep(1);
   }
+  return false;
 }
 
 // LDS: the two roles overlay one allocation.
@@ -196,9 +231,9 @@ __device__ __forceinline__ void add_h_terms(const unsigned char* lds, const uint
   }
 }
 
-// Routing of one item: tree p, tokens [t0, t0 + nt).
+// Routing of one item: tree p, tokens [t0, t0 + nt), published with epoch e.
 __device__ void route_item(const DecodeArgs& a, unsigned char* lds, int item, int p, int t0,
-                           int nt) {
+                           int nt, uint64_t e) {
   float* part = reinterpret_cast<float*>(lds + RouteLds::part);
   float* lgs = reinterpret_cast<float*>(lds + RouteLds::lgs);
   uint16_t* vc = reinterpret_cast<uint16_t*>(lds + RouteLds::vc);
@@ -414,8 +449,8 @@ __device__ void route_item(const DecodeArgs& a, unsigned char* lds, int item, in
   // Publish the item once every thread's stores have completed.
   wait_vmcnt<0>();
   __syncthreads();
-  if (tid == 0)
-    __hip_atomic_store(a.done + item, a.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (tid == 0 && a.publish)
+    __hip_atomic_store(a.done + item, e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // W_out block (K chunk kc, column slice cs) into LDS as wt[n][k].  A thread
@@ -456,9 +491,11 @@ __device__ void load_wout_block(const DecodeArgs& a, unsigned char* lds, int kc,
   }
 }
 
-// Partial product of item (kc, cs): partial[kc][t][cs*64 + c].  Wave w takes
-// token block w (T <= 64) and all four 16-column groups.
-__device__ void project_split(const DecodeArgs& a, unsigned char* lds, int kc, int cs) {
+// Partial product of item (kc, cs): partial[kc][t][cs*64 + c] (NaN when
+// `poison`: the H it would read may be incomplete).  Wave w takes token
+// block w (T <= 64) and all four 16-column groups.
+__device__ void project_split(const DecodeArgs& a, unsigned char* lds, int kc, int cs,
+                              bool poison) {
   const uint16_t* wt = reinterpret_cast<const uint16_t*>(lds + ProjLds::wt);
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
@@ -483,6 +520,8 @@ __device__ void project_split(const DecodeArgs& a, unsigned char* lds, int kc, i
       acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(wv), as_bf16x8(hf[s]), acc, 0, 0, 0);
     }
     // acc[r]: column cg*16 + 4q + r, token tb + n.
+    if (poison) acc = f32x4_t{__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""),
+                              __builtin_nanf("")};
     if (tb + n < a.T)
       coherent_store16(pbuf,
                        uint32_t((kc * a.T + tb + n) * a.d + cs * kColSlice + cg * 16 + q * 4) * 4,
@@ -512,26 +551,63 @@ __device__ void reduce_slice(const DecodeArgs& a, int cs) {
   }
 }
 
+// y columns of slice cs set to NaN for every token (poisoned header).
+__device__ void nan_slice(const DecodeArgs& a, int cs) {
+  const uint32_t qnan = 0x7FC07FC0u;  // two bf16 quiet NaNs
+  for (int e = threadIdx.x; e < a.T * (kColSlice / 4); e += kDecThreads) {
+    const int t = e / (kColSlice / 4);
+    const int c = cs * kColSlice + (e - t * (kColSlice / 4)) * 4;
+    *reinterpret_cast<uint2*>(a.y + static_cast<int64_t>(t) * a.d + c) = make_uint2(qnan, qnan);
+  }
+}
+
 __global__ __launch_bounds__(kDecThreads, 2) void decode_kernel(DecodeArgs a) {
   extern __shared__ __align__(16) unsigned char lds[];
-  __shared__ int last;
+  __shared__ int last, waited;
   const int per_tree = (a.T + a.tok - 1) / a.tok;
   const int nroute = a.P * per_tree;
   const int g = blockIdx.x;
+  const int nkc = a.K / kKc;
+  const int ncs = a.d / kColSlice;
+
+  // The call's epoch.
+  uint64_t e = a.seed;
+  bool poisoned = false;
+  if (a.device_epoch) {
+    const uint64_t h0 = __hip_atomic_load(a.hdr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const uint64_t h1 = __hip_atomic_load(a.hdr + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (h0 != 0 && h0 <= kEpochMask) {
+      if (h1 == (h0 ^ kHdrValid)) {
+        e = (h0 + 1) & kDeviceEpochMask;
+        e = e ? e : 1;
+      } else if (h1 == (h0 ^ kHdrPoison)) {
+        poisoned = true;
+      }
+    }
+  } else if (g == 0 && threadIdx.x == 0) {
+    // Recorded for a later captured call; nothing in this call reads it.
+    __hip_atomic_store(a.hdr, e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(a.hdr + 1, e ^ kHdrValid, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+
   if (g < a.n_route_wg) {
+    if (poisoned) return;
     for (int it = g; it < nroute; it += a.n_route_wg) {
       const int p = it / per_tree;
       const int t0 = (it - p * per_tree) * a.tok;
-      route_item(a, lds, it, p, t0, min(a.tok, a.T - t0));
+      route_item(a, lds, it, p, t0, min(a.tok, a.T - t0), e);
     }
     return;
   }
   const int j = g - a.n_route_wg;
-  const int nkc = a.K / kKc;
-  const int nproj = nkc * (a.d / kColSlice);
+  const int nproj = nkc * ncs;
   for (int it = j; it < nproj; it += a.n_proj_wg) {
     const int kc = it % nkc;
     const int cs = it / nkc;
+    if (poisoned) {
+      if (kc == 0) nan_slice(a, cs);
+      continue;
+    }
     __syncthreads();  // LDS of a previous item is no longer read
     load_wout_block(a, lds, kc, cs);
     if (threadIdx.x < kWave) {
@@ -540,26 +616,49 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_kernel(DecodeArgs a) {
       const int p_lo = kc * kKc / a.h;
       int p_hi = (kc * kKc + kKc - 1) / a.h;
       if (p_hi > a.P - 1) p_hi = a.P - 1;
-      wait_slots(a.done, p_lo * per_tree, (p_hi - p_lo + 1) * per_tree, a.epoch);
+      const bool ok =
+          wait_slots(a.done, p_lo * per_tree, (p_hi - p_lo + 1) * per_tree, e, a.spin_limit);
+      if (threadIdx.x == 0) waited = ok;
     }
     __syncthreads();
-    project_split(a, lds, kc, cs);
+    const bool gave_up = !waited;
+    project_split(a, lds, kc, cs, gave_up);
     // Arrival: store this chunk's slot once the partial stores have
     // completed, wait for that store, then read the slice's slots.  The
     // workgroup whose slot store completes last sees every slot set; more
-    // than one may, and each then writes the same y values.
+    // than one may, and each then writes the same y values.  A captured call
+    // reads every slice's slots: the workgroup that sees all of them set
+    // stores the header (more than one may, with the same values).
     wait_vmcnt<0>();
     __syncthreads();
     if (threadIdx.x < kWave) {
-      uint64_t* slots = a.arrive + static_cast<int64_t>(cs) * nkc;
       if (threadIdx.x == 0)
-        __hip_atomic_store(slots + kc, a.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(a.arrive + static_cast<int64_t>(cs) * nkc + kc,
+                           e | (gave_up ? kGaveUp : 0), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
       wait_vmcnt<0>();
-      bool ok = true;
-      for (int i = threadIdx.x; i < nkc; i += kWave)
-        ok &= __hip_atomic_load(slots + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == a.epoch;
-      ok = __all(ok);
-      if (threadIdx.x == 0) last = ok;
+      const int first = a.device_epoch ? 0 : cs * nkc;
+      const int n = a.device_epoch ? ncs * nkc : nkc;
+      bool ok_slice = true, ok_all = true, any_gave_up = false;
+      for (int i = threadIdx.x; i < n; i += kWave) {
+        const uint64_t v =
+            __hip_atomic_load(a.arrive + first + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const bool set = (v & kEpochMask) == e;
+        ok_all &= set;
+        if ((first + i) / nkc == cs) ok_slice &= set;
+        any_gave_up |= (v & kGaveUp) != 0;
+      }
+      ok_slice = __all(ok_slice);
+      ok_all = __all(ok_all);
+      any_gave_up = __any(any_gave_up);
+      if (threadIdx.x == 0) {
+        last = ok_slice;
+        if (a.device_epoch && ok_all) {
+          __hip_atomic_store(a.hdr, e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          __hip_atomic_store(a.hdr + 1, e ^ (any_gave_up ? kHdrPoison : kHdrValid),
+                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+      }
     }
     __syncthreads();
     if (last) reduce_slice(a, cs);
@@ -573,8 +672,13 @@ struct DeviceInfo {
 
 size_t up256(size_t v) { return (v + 255) / 256 * 256; }
 
-// Per-call epochs: distinct within a process, and starting from a random
-// point so that words left by other processes do not match.
+// Epochs of ordinary calls: a per-process counter started at a random point
+// (so that words left by other processes do not match), each value passed
+// through the SplitMix64 finaliser (Steele, Lea and Flood, "Fast splittable
+// pseudorandom number generators", 2014) so that the runs of consecutive
+// epochs a captured call derives from one of them do not overlap those of
+// the next.  61 random bits: a repeat within a process is vanishingly
+// unlikely (the finaliser is a bijection of the 64-bit counter).
 uint64_t next_epoch() {
   static std::atomic<uint64_t> counter{[] {
     std::random_device rd;
@@ -582,8 +686,11 @@ uint64_t next_epoch() {
         std::chrono::steady_clock::now().time_since_epoch().count());
     return (uint64_t(rd()) << 32) ^ uint64_t(rd()) ^ (t * 0x9E3779B97F4A7C15ull);
   }()};
-  uint64_t e = counter.fetch_add(1, std::memory_order_relaxed) & kEpochMask;
-  return e ? e : 1;
+  uint64_t z = counter.fetch_add(1, std::memory_order_relaxed);
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  z ^= z >> 31;
+  return (z & kDeviceEpochMask) | kHostEpochBit;
 }
 
 }  // namespace
@@ -614,13 +721,13 @@ static int tokens_per_item(const Dims& s) {
 
 size_t decode_workspace(const Dims& s) {
   const size_t items = size_t(s.P) * ((s.T + tokens_per_item(s) - 1) / tokens_per_item(s));
-  return up256(items * 8) + up256(size_t(s.T) * s.K * 2) +
+  return 256 + up256(items * 8) + up256(size_t(s.T) * s.K * 2) +
          up256(size_t(s.d / kColSlice) * (s.K / kKc) * 8) + up256(size_t(s.K / kKc) * s.T * s.d * 4);
 }
 
 hipError_t launch_decode(const Dims& s, const void* x, const void* W, const void* b,
                          const void* V, const void* Wout, void* y, int32_t* path_out, void* ws,
-                         hipStream_t st) {
+                         int flags, hipStream_t st) {
   DecodeArgs a;
   a.x = static_cast<const uint16_t*>(x);
   a.W = static_cast<const uint16_t*>(W);
@@ -632,6 +739,8 @@ hipError_t launch_decode(const Dims& s, const void* x, const void* W, const void
   a.tok = tokens_per_item(s);
   const int nroute = s.P * static_cast<int>((s.T + a.tok - 1) / a.tok);
   char* w = static_cast<char*>(ws);
+  a.hdr = reinterpret_cast<uint64_t*>(w);
+  w += 256;
   a.done = reinterpret_cast<uint64_t*>(w);
   w += up256(size_t(nroute) * 8);
   a.H = reinterpret_cast<uint16_t*>(w);
@@ -673,7 +782,15 @@ hipError_t launch_decode(const Dims& s, const void* x, const void* W, const void
   a.n_route_wg = nroute < cap / 2 ? nroute : cap / 2;
   a.n_proj_wg = nproj < cap - a.n_route_wg ? nproj : cap - a.n_route_wg;
   if (a.n_proj_wg < 1) return hipErrorInvalidConfiguration;
-  a.epoch = next_epoch();
+  // A captured call takes its epoch from the workspace header (see above).
+  hipStreamCaptureStatus capture = hipStreamCaptureStatusNone;
+  e = hipStreamIsCapturing(st, &capture);
+  if (e != hipSuccess) return e;
+  a.device_epoch = capture == hipStreamCaptureStatusActive ? 1 : 0;
+  a.seed = next_epoch();
+  const bool test_no_publish = (flags & FFF_PLAN_TEST_DECODE_NO_PUBLISH) != 0;
+  a.publish = test_no_publish ? 0 : 1;
+  a.spin_limit = test_no_publish ? kTestSpinLimit : kSpinLimit;
   hipLaunchKernelGGL(decode_kernel, dim3(a.n_route_wg + a.n_proj_wg), dim3(kDecThreads), kDecLds,
                      st, a);
   return hipGetLastError();

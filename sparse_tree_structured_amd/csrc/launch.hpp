@@ -120,12 +120,13 @@ hipError_t launch_prune_pack(const void* W, const int32_t* colmap, void* packed,
                              hipStream_t st);
 
 // ---- decode (bf16, 1 <= T <= 64): one kernel for the whole layer ----
-// Workspace: H [T,K] bf16, fp32 K-chunk partials of y, per-slice counters.
+// Workspace: an epoch header, per-item and per-partial slots, H [T,K] bf16
+// and fp32 K-chunk partials of y.  `flags`: fff_plan_t flags.
 bool decode_supported(const Dims& s);
 size_t decode_workspace(const Dims& s);
 hipError_t launch_decode(const Dims& s, const void* x, const void* W, const void* b,
                          const void* V, const void* Wout, void* y, int32_t* path_out, void* ws,
-                         hipStream_t st);
+                         int flags, hipStream_t st);
 
 // ---- backward pass (gradients of sum(y * dy), paths held fixed) ----
 hipError_t launch_fill_f32(float* p, int64_t n, hipStream_t st);

@@ -141,6 +141,15 @@ def test_plans(lib):
     assert _forward(lib, _shape(dtype=fff.DTYPE_F32), plan=bad) == fff.ERROR_NOT_SUPPORTED
     assert _forward(lib, _shape(d=72), plan=bad) == fff.ERROR_NOT_SUPPORTED
     assert _forward(lib, _shape(), plan=fff.make_plan(9)) == fff.ERROR_INVALID_VALUE
+    # Plan flags: the defined bit passes through resolution; others are invalid.
+    dec = _shape(T=8, d=2048, P=32, D=6, h=128)
+    r = fff.resolve_plan(dec, fff.make_plan("decode", flags=fff.PLAN_TEST_DECODE_NO_PUBLISH))
+    assert r.algo == fff.ALGO_DECODE and r.flags == fff.PLAN_TEST_DECODE_NO_PUBLISH
+    assert fff.resolve_plan(dec, fff.make_plan()).flags == 0
+    for flags in (2, 1 << 30, -1):
+        assert _forward(lib, dec, plan=fff.make_plan(flags=flags)) == fff.ERROR_INVALID_VALUE
+        assert lib.fff_plan_resolve(ctypes.byref(dec), ctypes.byref(fff.make_plan(flags=flags)),
+                                    ctypes.byref(fff.Plan())) == fff.ERROR_INVALID_VALUE
 
 
 def test_deep_chunk_rule():
@@ -191,18 +200,18 @@ def test_decode_workspace_covers_route(lib):
     dec = fff.workspace_size(s, fff.make_plan("decode"))
     pre = fff.workspace_size(s, fff.make_plan("prefill"))
     assert auto >= dec > 0 and auto >= pre > 0
-    # 128 routing-item slots (2 tokens per item at 8 tokens; 64-bit each),
-    # H [8, 4096] bf16, 32 x 8 arrival slots and 8 K-chunk partials of y
-    # [8, 2048] fp32.
-    assert dec == 32 * 4 * 8 + 8 * 4096 * 2 + 32 * 8 * 8 + 8 * 8 * 2048 * 4
+    # A 256-byte epoch header, 128 routing-item slots (2 tokens per item at
+    # 8 tokens; 64-bit each), H [8, 4096] bf16, 32 x 8 arrival slots and 8
+    # K-chunk partials of y [8, 2048] fp32.
+    assert dec == 256 + 32 * 4 * 8 + 8 * 4096 * 2 + 32 * 8 * 8 + 8 * 8 * 2048 * 4
     # 64 tokens: 8 per item, 8 items per tree (256 items fit half of the grid).
     s64 = _shape(T=64, d=2048, P=32, D=6, h=128)
     assert fff.workspace_size(s64, fff.make_plan("decode")) == \
-        32 * 8 * 8 + 64 * 4096 * 2 + 32 * 8 * 8 + 8 * 64 * 2048 * 4
+        256 + 32 * 8 * 8 + 64 * 4096 * 2 + 32 * 8 * 8 + 8 * 64 * 2048 * 4
     # 64 tokens on 64 trees: 16 per item (8-token items would be 512).
     w64 = _shape(T=64, d=2048, P=64, D=6, h=128)
     assert fff.workspace_size(w64, fff.make_plan("decode")) == \
-        64 * 4 * 8 + 64 * 8192 * 2 + 32 * 16 * 8 + 16 * 64 * 2048 * 4
+        256 + 64 * 4 * 8 + 64 * 8192 * 2 + 32 * 16 * 8 + 16 * 64 * 2048 * 4
     st = lib.fff_route(ctypes.byref(s), ctypes.byref(fff.make_plan("decode")), FAKE, FAKE, FAKE,
                        FAKE, FAKE, FAKE, FAKE, 1 << 40, None)
     assert st == fff.ERROR_NOT_SUPPORTED
