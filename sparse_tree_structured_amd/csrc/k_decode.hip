@@ -415,6 +415,11 @@ __device__ void route_item(const DecodeArgs& a, unsigned char* lds, int item, in
         }
       }
     }
+    // Every load of this round has been consumed (some only by some waves
+    // or lanes): wait for all of them here, so that the compiler, which
+    // cannot tell, does not make the loop head wait for outstanding loads;
+    // on entry that would hold round 1's node rows behind the token rows.
+    wait_vmcnt<0>();
     __syncthreads();
     lev += rl;
     prev_rl = rl;

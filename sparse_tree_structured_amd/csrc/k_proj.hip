@@ -248,6 +248,12 @@ hipError_t launch_cfg(const Dims& s, const void* H, const void* Wout, void* y, h
 using BigTile = TileCfg<256, 256, 64, 128, 128>;
 using SmallTile = TileCfg<128, 128, 64, 64, 64>;
 using BigDirect = DirectCfg<256, 256, 128, 64, 4>;
+// Products with fewer than 256 big tiles (the GPT-125M shape's 8192 x 768
+// output makes 96): 128 x 128 tiles, two workgroups per compute unit.
+using MidDirect = DirectCfg<128, 128, 64, 64, 4>;
+
+int64_t big_direct_tiles(const Dims& s) { return ((s.T + 255) / 256) * ((s.d + 255) / 256); }
+int64_t mid_direct_tiles(const Dims& s) { return ((s.T + 127) / 128) * ((s.d + 127) / 128); }
 
 }  // namespace
 
@@ -266,7 +272,7 @@ hipError_t launch_project_mfma(const Dims& s, const void* H, const void* Wout, v
 
 bool project_direct_supported(const Dims& s) {
   return project_mfma_supported(s) && s.K % 32 == 0 &&
-         ((s.T + 255) / 256) * ((s.d + 255) / 256) >= 256;
+         (big_direct_tiles(s) >= 256 || mid_direct_tiles(s) >= 256);
 }
 
 hipError_t launch_transpose(const void* W, void* WT, int64_t K, int Nc, hipStream_t st) {
@@ -275,9 +281,9 @@ hipError_t launch_transpose(const void* W, void* WT, int64_t K, int Nc, hipStrea
   return hipGetLastError();
 }
 
-hipError_t launch_project_direct(const Dims& s, const void* H, const void* WT, void* y,
-                                 hipStream_t st) {
-  using C = BigDirect;
+template <class C>
+hipError_t launch_direct_cfg(const Dims& s, const void* H, const void* WT, void* y,
+                             hipStream_t st) {
   const int tiles_m = static_cast<int>((s.T + C::BM - 1) / C::BM);
   const int tiles_n = (s.d + C::BN - 1) / C::BN;
   auto kern = proj_direct_kernel<C>;
@@ -290,6 +296,12 @@ hipError_t launch_project_direct(const Dims& s, const void* H, const void* WT, v
       static_cast<const uint16_t*>(H), static_cast<const uint16_t*>(WT), static_cast<uint16_t*>(y),
       static_cast<int>(s.T), static_cast<int>(s.K), s.d, tiles_n);
   return hipGetLastError();
+}
+
+hipError_t launch_project_direct(const Dims& s, const void* H, const void* WT, void* y,
+                                 hipStream_t st) {
+  if (big_direct_tiles(s) >= 256) return launch_direct_cfg<BigDirect>(s, H, WT, y, st);
+  return launch_direct_cfg<MidDirect>(s, H, WT, y, st);
 }
 
 }  // namespace fff
