@@ -148,7 +148,11 @@ def test_zero_tokens():
 
 
 @needs_gpu
-@pytest.mark.parametrize("M,K,N", [(16384, 4096, 2048), (1000, 1024, 768), (1, 64, 8), (129, 192, 72)])
+@pytest.mark.parametrize("M,K,N", [(16384, 4096, 2048), (1000, 1024, 768), (1, 64, 8), (129, 192, 72),
+                                   # direct-to-LDS with 128 x 128 tiles: a ragged last
+                                   # column tile (and transpose tile) of 8 columns, and
+                                   # ragged rows
+                                   (8192, 1024, 776), (4000, 4096, 2048)])
 def test_projection_matches_fp64(M, K, N):
     import sparse_tree_structured_amd as fff
     g = torch.Generator().manual_seed(M + K + N)
