@@ -11,7 +11,7 @@ input set gives the warm figure beside it.
 Prints one JSON line: tokens/s from K steps with nothing else on the
 stream; the roofline of the dominant kernel, picked by measured time among
 the stages the library brackets with HIP events on the stream it launches
-on (W_out transpose, dense top levels, deep levels, H build, projection), in
+on (dense top levels, deep levels, H build, projection), in
 a second pass of the same K steps (each event costs about 3 us of GPU time,
 so the headline pass carries none), with every stage's roofline beside it;
 and the CPU oracle's throughput on the same workload, whose output also
@@ -268,9 +268,8 @@ def depth_sweep(args):
                       "tflops": dense_flops / (t_dense * 1e-3) / 1e12,
                       "impl": "torch linear (hipBLASLt) + tanh GELU, bf16"}), flush=True)
     # The same block with this library's matrix-core product (fff_project_ws,
-    # y = H . W with W row-major [K, N], W transposed into the workspace as
-    # the layer's own projection does) for both products; bias and GELU in
-    # torch between them.
+    # y = H . W with W row-major [K, N], the kernel of the layer's own
+    # projection) for both products; bias and GELU in torch between them.
     w1t, w2t = w1.t().contiguous(), w2.t().contiguous()
     hid = torch.empty((T, dff), dtype=torch.bfloat16, device=dev)
     yd = torch.empty((T, d), dtype=torch.bfloat16, device=dev)
@@ -550,7 +549,6 @@ def main():
     rows_deep = P * ((1 << (D + 1)) - (1 << k))
     stage_work = {
         # name: (flops, bytes)
-        "prepare": (0, 2 * K * d * e),
         "top": (2 * T * P * k * d, x_bytes + rows_top * (d + 1) * e + 4 * T * P * (k + 1)),
         "deep": (2 * T * P * (D + 1 - k) * d,
                  x_bytes + rows_deep * (d + 1) * e + 4 * T * P * (D + 2 - k)),
@@ -559,8 +557,12 @@ def main():
         "proj": (f_proj, T * K * e + K * d * e + T * d * e),
     }
     fused = plan.algo == fff.ALGO_DECODE
-    names = ["prepare", "top", "deep", "hbuild", "proj"]
-    stage_us = {n: float(np.mean(stages_ms[:, j])) * 1e3 for j, n in enumerate(names)}
+    # Intervals between the library's events: start-prepared (nothing is
+    # prepared: the two events are recorded back to back, so it is counted
+    # with the top levels), prepared-top, top-deep, deep-routed, routed-done.
+    intervals = {"top": (0, 2), "deep": (2, 3), "hbuild": (3, 4), "proj": (4, 5)}
+    stage_us = {n: float(np.mean(stages_ms[:, a:b].sum(axis=1))) * 1e3
+                for n, (a, b) in intervals.items()}
     if fused:  # one kernel: its time sits in the first interval
         stage_us = {"decode": float(np.mean(stages_ms[:, 0])) * 1e3}
         stage_work = {"decode": (f_route + f_proj, b_alg)}
@@ -576,7 +578,7 @@ def main():
                      "frac": max(t_mfma, t_hbm) / t}
     dom = max(stages, key=lambda n: stages[n]["us"])
     ds = stages[dom]
-    kernel_of = {"prepare": "transpose", "top": "route_top", "deep": "subtree", "hbuild": "hbuild",
+    kernel_of = {"top": "route_top", "deep": "subtree", "hbuild": "hbuild",
                  "proj": "proj_direct", "decode": "decode"}
     traffic = measured_traffic(kernel_of[dom], args.workload)
     if ds["bound"] == "mfma":

@@ -168,8 +168,9 @@ typedef struct fff_plan {
 /* Optional events recorded on `stream` at stage boundaries (each may be
  * NULL), in this order:
  *   start     before the first kernel
- *   prepared  after W_out is transposed for the projection (PREFILL plans
- *             with the direct-to-LDS projection; elsewhere with `start`)
+ *   prepared  with `start` (no plan prepares anything before routing: every
+ *             projection kernel reads W_out in its own layout); kept so
+ *             that the list of stages stays the same
  *   top       after the densely evaluated levels (GENERIC: every level's
  *             logits)
  *   deep      after the deep levels (the token-tile or bucketed kernels;
@@ -235,28 +236,27 @@ fff_status_t fff_route(const fff_shape_t *shape, const fff_plan_t *plan,
 /*
  * Projection only: y[T,d] = H[T,K] . W_out[K,d] with K = P*h, fp32
  * accumulation, output rounded to dtype.  `algo` selects the kernel family
- * (AUTO, GENERIC, or PREFILL for the matrix-core kernel).  Needs no workspace.
+ * (AUTO, GENERIC, or PREFILL for the matrix-core kernels; where the
+ * direct-to-LDS product applies (bf16, K % 32 == 0 and at least 256 output
+ * tiles of 256 x 256 or 128 x 128) it is the kernel fff_forward uses for its
+ * projection, so y equals fff_forward's y for the same H).  Needs no
+ * workspace.
  */
 fff_status_t fff_project(const fff_shape_t *shape, int32_t algo, const void *H,
                          const void *W_out, void *y, hipStream_t stream);
 
 /*
- * Workspace bytes of fff_project_ws for this shape and algo: d*K*dtype-size
- * (rounded up to 256) where the direct-to-LDS matrix-core product applies
- * (bf16, K % 32 == 0 and at least 256 output tiles of 256 x 256), else 0.
- * `bytes` must not be NULL.  Same shape and algo rules as fff_project.
+ * Workspace bytes of fff_project_ws for this shape and algo: always 0 (no
+ * projection kernel needs workspace).  `bytes` must not be NULL.  Same
+ * shape and algo rules as fff_project.
  */
 fff_status_t fff_project_workspace_size(const fff_shape_t *shape, int32_t algo, size_t *bytes);
 
 /*
- * fff_project with a caller workspace (device, 256-byte aligned, at least
- * fff_project_workspace_size() bytes; may be NULL when that size is 0).
- * Where the size is nonzero, W_out is transposed into the workspace and the
- * product runs the kernel fff_forward uses for its projection (the same
- * results as fff_forward's y for the same H); else it runs as fff_project.
- * Returns FFF_ERROR_WORKSPACE for a missing or too small workspace, and
- * FFF_ERROR_INVALID_VALUE for a misaligned one.  The product is the layer's
- * final linear projection of the concatenated tree outputs (the paper's page,
+ * fff_project with a caller workspace, which no kernel uses any more
+ * (fff_project_workspace_size() is 0; the workspace may be NULL): the same
+ * kernels and results as fff_project.  The product is the layer's final
+ * linear projection of the concatenated tree outputs (the paper's page,
  * Figure 1(c) caption).
  */
 fff_status_t fff_project_ws(const fff_shape_t *shape, int32_t algo, const void *H,

@@ -358,9 +358,9 @@ def project(H, W_out, *, algo=ALGO_AUTO, stream=None, y=None, workspace=None,
             use_workspace: bool = True):
     """y = H . W_out (fp32 accumulation).
 
-    With ``use_workspace`` (default) the call goes through fff_project_ws,
-    allocating its workspace when none is given, so large bf16 products take
-    the same kernel as fff_forward's projection; else through fff_project."""
+    With ``use_workspace`` (default) the call goes through fff_project_ws
+    (whose workspace size is 0: it may be None), else through fff_project;
+    both run the kernel fff_forward's projection uses for the same shape."""
     torch = _torch()
     T, K = _dims(H, 2, "H [T,K]")
     K2, d = _dims(W_out, 2, "W_out [K,d]")

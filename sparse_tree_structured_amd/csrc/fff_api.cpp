@@ -147,11 +147,8 @@ fff_status_t resolve_plan(const Dims& s, const fff_plan_t* in, fff_plan_t* out,
 //   offs    per (chunk, tree) bucket offsets, 2^k + 1 int32 each
 //   cnt     per (chunk, tree, slice) bucket counts, 2^k int32 each
 //   H       concatenated tree outputs [T, P*h] in the layer dtype
-//   WT      W_out transposed to [d, P*h] for the direct-to-LDS projection
-//           (prefill, large products only)
 struct Layout {
-  size_t logits = 0, leaf = 0, perm = 0, offs = 0, cnt = 0, H = 0, WT = 0;  // offsets
-  bool use_wt = false;
+  size_t logits = 0, leaf = 0, perm = 0, offs = 0, cnt = 0, H = 0;  // offsets
   bool tile = false;  // deep levels through the token-tile kernel (records of all D+1 levels)
   size_t total = 0;
 };
@@ -186,9 +183,6 @@ Layout layout_for(const Dims& s, const fff_plan_t& p) {
   if (deep) off = align_up(off + fff::bucket_count_bytes(s, p.split_level, p.chunk_tokens));
   L.H = off;
   off = align_up(off + size_t(s.T) * size_t(s.K) * s.esize);
-  L.WT = off;
-  L.use_wt = prefill && fff::project_direct_supported(s);
-  if (L.use_wt) off = align_up(off + size_t(s.d) * size_t(s.K) * s.esize);
   L.total = off;
   return L;
 }
@@ -287,19 +281,18 @@ fff_status_t run_route(const Dims& s, const fff_plan_t& p, const Layout& L, cons
 fff_status_t run_project(const Dims& s, int32_t algo, const void* H, const void* Wout, void* y,
                          hipStream_t st) {
   hipError_t e;
-  if (algo != FFF_ALGO_GENERIC && fff::project_mfma_supported(s))
+  if (algo != FFF_ALGO_GENERIC && fff::project_direct_supported(s))
+    e = fff::launch_project_direct(s, H, Wout, y, st);
+  else if (algo != FFF_ALGO_GENERIC && fff::project_mfma_supported(s))
     e = fff::launch_project_mfma(s, H, Wout, y, st);
   else
     e = fff::launch_project_generic(s, H, Wout, y, st);
   return hip_status(e);
 }
 
-// fff_project_ws: W_out transposed into the workspace for the direct-to-LDS
-// product where that kernel applies (large bf16 products), else nothing.
-size_t project_ws_bytes(const Dims& s, int32_t algo) {
-  if (algo == FFF_ALGO_GENERIC || !fff::project_direct_supported(s)) return 0;
-  return align_up(size_t(s.d) * size_t(s.K) * s.esize);
-}
+// fff_project_ws: every projection kernel reads W_out in its own layout, so
+// none needs workspace.
+size_t project_ws_bytes(const Dims&, int32_t) { return 0; }
 
 fff_status_t check_inputs(const Dims& s, const void* x, const void* W, const void* b,
                           const void* V) {
@@ -339,18 +332,13 @@ fff_status_t forward_impl(const Dims& s, const fff_plan_t& p, const void* x, con
       if ((st = record(ev, stream)) != FFF_SUCCESS) return st;
     return FFF_SUCCESS;
   }
-  // The projection's transposed W_out is prepared first, so that the
-  // projection stage is the matrix product alone.
-  if (L.use_wt && fff::launch_transpose(W_out, ws + L.WT, s.K, s.d, stream) != hipSuccess)
-    return FFF_ERROR_HIP;
+  // Nothing is prepared before routing (W_out is used in its own layout):
+  // `prepared` follows `start` directly.
   if ((st = record(E.prepared, stream)) != FFF_SUCCESS) return st;
   st = run_route(s, p, L, x, W_node, b_node, V_node, H, path_out, ws, stream, &E);
   if (st != FFF_SUCCESS) return st;
   if ((st = record(E.routed, stream)) != FFF_SUCCESS) return st;
-  if (L.use_wt)
-    st = hip_status(fff::launch_project_direct(s, H, ws + L.WT, y, stream));
-  else
-    st = run_project(s, p.algo, H, W_out, y, stream);
+  st = run_project(s, p.algo, H, W_out, y, stream);
   if (st != FFF_SUCCESS) return st;
   if ((st = record(E.done, stream)) != FFF_SUCCESS) return st;
   return FFF_SUCCESS;
@@ -737,12 +725,9 @@ fff_status_t fff_project_ws(const fff_shape_t* shape, int32_t algo, const void* 
   if (s.T == 0) return FFF_SUCCESS;
   if (!H || !W_out || !y || !aligned(H, 16) || !aligned(W_out, 16) || !aligned(y, 16))
     return FFF_ERROR_INVALID_VALUE;
-  const size_t need = project_ws_bytes(s, algo);
-  if (need == 0) return run_project(s, algo, H, W_out, y, stream);
-  if (!workspace || workspace_bytes < need) return FFF_ERROR_WORKSPACE;
-  if (!aligned(workspace, kWsAlign)) return FFF_ERROR_INVALID_VALUE;
-  if (fff::launch_transpose(W_out, workspace, s.K, s.d, stream) != hipSuccess) return FFF_ERROR_HIP;
-  return hip_status(fff::launch_project_direct(s, H, workspace, y, stream));
+  (void)workspace;  // no projection kernel needs one (project_ws_bytes is 0)
+  (void)workspace_bytes;
+  return run_project(s, algo, H, W_out, y, stream);
 }
 
 const char* fff_status_string(fff_status_t status) {

@@ -21,6 +21,12 @@
 // Accumulator blocks are transposed y blocks, so a lane holds four
 // consecutive output columns of one row, packed into one 8-byte store.
 //
+// Large products take the multi-stage direct-to-LDS kernel instead: both
+// operands go from global memory straight into LDS (H rows as they are,
+// W_out as k rows of the tile's columns), and the W_out fragments are read
+// out of LDS with ds_read_b64_tr_b16, which transposes 16-bit elements
+// across lanes, so W_out is used in its own layout with no preparation pass.
+//
 // XCD-aware tile order: each XCD owns a contiguous range of row panels, so H
 // is fetched once in total and W_out once per XCD.
 #include "common.hpp"
@@ -182,11 +188,13 @@ __device__ __forceinline__ void store_y_tile_lds(const f32x16_t (&acc)[C::kTm][C
   }
 }
 
-// y = H . W_out with W_out supplied transposed (WT[d][K], K-contiguous), both
-// operands loaded straight into LDS by the multi-stage main loop.
+// y = H . W_out with both operands loaded straight into LDS by the
+// multi-stage main loop: H rows K-contiguous, W_out in its own k-major layout
+// (W_out[k][n]), whose fragments the main loop reads with transposing LDS
+// reads, so W_out needs no preparation.
 template <class C>
 __global__ __launch_bounds__(C::kThreads) void proj_direct_kernel(
-    const uint16_t* __restrict__ H, const uint16_t* __restrict__ WT, uint16_t* __restrict__ y,
+    const uint16_t* __restrict__ H, const uint16_t* __restrict__ Wout, uint16_t* __restrict__ y,
     int M, int K, int Nc, int tiles_n) {
   extern __shared__ __align__(16) unsigned char lds[];
   const int logical = xcd_logical_tile(blockIdx.x, gridDim.x);
@@ -198,51 +206,10 @@ __global__ __launch_bounds__(C::kThreads) void proj_direct_kernel(
     const int r = m0 + i < M ? m0 + i : M - 1;
     return H + static_cast<size_t>(r) * K;
   };
-  auto b_row = [&](int j) {
-    const int c = n0 + j < Nc ? n0 + j : Nc - 1;
-    return WT + static_cast<size_t>(c) * K;
-  };
+  const KMajorBOp<C> bop{KMajorB{Wout + n0, Nc, Nc - n0}};
   f32x16_t acc[C::kTm][C::kTn];
-  gemm_mainloop_direct<C>(acc, lds, K, a_row, b_row);
+  gemm_mainloop_direct_op<C>(acc, lds, K, a_row, bop);
   store_y_tile_lds<C>(acc, lds, y, M, Nc, m0, n0);
-}
-
-// WT[n][k] = W[k][n] for a [K x Nc] bf16 matrix, 64 x 64 tiles through LDS.
-__global__ __launch_bounds__(256) void transpose_kernel(const uint16_t* __restrict__ W,
-                                                        uint16_t* __restrict__ WT, int K, int Nc) {
-  __shared__ uint16_t tile[64][64 + 2];
-  const int k0 = blockIdx.y * 64;
-  const int n0 = blockIdx.x * 64;
-  const int t = threadIdx.x;
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int r = t / 8 + 32 * i;  // k within tile
-    const int c8 = (t % 8) * 8;    // n within tile
-    if (k0 + r < K && n0 + c8 < Nc) {
-      const uint4 v = ldg16(W + static_cast<size_t>(k0 + r) * Nc + n0 + c8);
-      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        tile[r][c8 + 2 * e] = static_cast<uint16_t>(w[e] & 0xffffu);
-        tile[r][c8 + 2 * e + 1] = static_cast<uint16_t>(w[e] >> 16);
-      }
-    }
-  }
-  __syncthreads();
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int rn = t / 8 + 32 * i;  // n within tile
-    const int k8 = (t % 8) * 8;     // k within tile
-    if (n0 + rn < Nc && k0 + k8 < K) {
-      uint32_t w[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        w[e] = static_cast<uint32_t>(tile[k8 + 2 * e][rn]) |
-               (static_cast<uint32_t>(tile[k8 + 2 * e + 1][rn]) << 16);
-      *reinterpret_cast<uint4*>(WT + static_cast<size_t>(n0 + rn) * K + k0 + k8) =
-          make_uint4(w[0], w[1], w[2], w[3]);
-    }
-  }
 }
 
 template <class C>
@@ -298,12 +265,22 @@ hipError_t launch_cfg(const Dims& s, const void* H, const void* Wout, void* y, h
 using BigTile = TileCfg<256, 256, 64, 128, 128>;
 using SmallTile = TileCfg<128, 128, 64, 64, 64>;
 using BigDirect = DirectCfg<256, 256, 128, 64, 4>;
-// Products with fewer than 256 big tiles (the GPT-125M shape's 8192 x 768
-// output makes 96): 128 x 128 tiles, two workgroups per compute unit.
+// Smaller products (the GPT-125M shape's 8192 x 768 output makes 96 big
+// tiles): 256 x 128 or 128 x 128 tiles (the latter two workgroups per
+// compute unit).
+using WideDirect = DirectCfg<256, 128, 64, 64, 4>;
 using MidDirect = DirectCfg<128, 128, 64, 64, 4>;
 
 int64_t big_direct_tiles(const Dims& s) { return ((s.T + 255) / 256) * ((s.d + 255) / 256); }
 int64_t mid_direct_tiles(const Dims& s) { return ((s.T + 127) / 128) * ((s.d + 127) / 128); }
+
+// Output area the busiest compute unit computes with bm x bn tiles spread
+// over the 256 units: the time model the tile choice minimises (ties go to
+// the larger tile, which reuses each operand byte more).
+int64_t cu_area(int64_t rows, int64_t cols, int bm, int bn) {
+  const int64_t tiles = ((rows + bm - 1) / bm) * ((cols + bn - 1) / bn);
+  return (tiles + 255) / 256 * bm * bn;
+}
 
 }  // namespace
 
@@ -325,14 +302,8 @@ bool project_direct_supported(const Dims& s) {
          (big_direct_tiles(s) >= 256 || mid_direct_tiles(s) >= 256);
 }
 
-hipError_t launch_transpose(const void* W, void* WT, int64_t K, int Nc, hipStream_t st) {
-  transpose_kernel<<<dim3((Nc + 63) / 64, static_cast<unsigned>((K + 63) / 64)), dim3(256), 0, st>>>(
-      static_cast<const uint16_t*>(W), static_cast<uint16_t*>(WT), static_cast<int>(K), Nc);
-  return hipGetLastError();
-}
-
 template <class C>
-hipError_t launch_direct_cfg(const Dims& s, const void* H, const void* WT, void* y,
+hipError_t launch_direct_cfg(const Dims& s, const void* H, const void* Wout, void* y,
                              hipStream_t st) {
   const int tiles_m = static_cast<int>((s.T + C::BM - 1) / C::BM);
   const int tiles_n = (s.d + C::BN - 1) / C::BN;
@@ -344,15 +315,19 @@ hipError_t launch_direct_cfg(const Dims& s, const void* H, const void* WT, void*
     if (e != hipSuccess) return e;
   }
   kern<<<dim3(tiles_m * tiles_n), dim3(C::kThreads), lds, st>>>(
-      static_cast<const uint16_t*>(H), static_cast<const uint16_t*>(WT), static_cast<uint16_t*>(y),
+      static_cast<const uint16_t*>(H), static_cast<const uint16_t*>(Wout), static_cast<uint16_t*>(y),
       static_cast<int>(s.T), static_cast<int>(s.K), s.d, tiles_n);
   return hipGetLastError();
 }
 
-hipError_t launch_project_direct(const Dims& s, const void* H, const void* WT, void* y,
+hipError_t launch_project_direct(const Dims& s, const void* H, const void* Wout, void* y,
                                  hipStream_t st) {
-  if (big_direct_tiles(s) >= 256) return launch_direct_cfg<BigDirect>(s, H, WT, y, st);
-  return launch_direct_cfg<MidDirect>(s, H, WT, y, st);
+  const int64_t big = cu_area(s.T, s.d, 256, 256);
+  const int64_t wide = cu_area(s.T, s.d, 256, 128);
+  const int64_t mid = cu_area(s.T, s.d, 128, 128);
+  if (big <= wide && big <= mid) return launch_direct_cfg<BigDirect>(s, H, Wout, y, st);
+  if (wide <= mid) return launch_direct_cfg<WideDirect>(s, H, Wout, y, st);
+  return launch_direct_cfg<MidDirect>(s, H, Wout, y, st);
 }
 
 }  // namespace fff

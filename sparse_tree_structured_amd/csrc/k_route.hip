@@ -314,7 +314,7 @@ __global__ __launch_bounds__(kHbThreads) void hbuild_kernel(const float* __restr
   unsigned char* vs = hb_lds;                                               // N x h
   float* gl = reinterpret_cast<float*>(hb_lds + size_t(N) * h * kEsz);     // kHbTok x L
   int32_t* leaf = reinterpret_cast<int32_t*>(gl + kHbTok * L);             // kHbTok
-  static_assert(kHbThreads >= kHbTok, "one thread per token for the tile's leaves");
+  static_assert(kHbTok % kHbThreads == 0 || kHbThreads % kHbTok == 0, "token loop");
   const uint16_t* Vp = V + static_cast<int64_t>(p) * N * h;
   // Every load of the staging phase is issued before any is waited for (a
   // loop of load, wait and store would cost one memory round trip per
@@ -360,15 +360,25 @@ __global__ __launch_bounds__(kHbThreads) void hbuild_kernel(const float* __restr
     const int i = threadIdx.x + u * kHbThreads;
     lv[u] = rl[i < ntok * L ? i : 0];
   }
-  const int32_t nl = rec_next[static_cast<int64_t>(p) * T + t0 + (threadIdx.x < ntok ? threadIdx.x : 0)];
+  constexpr int kLeafPer = (kHbTok + kHbThreads - 1) / kHbThreads;
+  int32_t nl[kLeafPer];
+#pragma unroll
+  for (int u = 0; u < kLeafPer; ++u) {
+    const int i = threadIdx.x + u * kHbThreads;
+    nl[u] = rec_next[static_cast<int64_t>(p) * T + t0 + (i < ntok ? i : 0)];
+  }
 #pragma unroll
   for (int u = 0; u < kRec; ++u) {
     const int i = threadIdx.x + u * kHbThreads;
     if (i < ntok * L) gl[i] = post ? lv[u] : gelu_tanh(lv[u]);
   }
-  if (threadIdx.x < ntok) {
-    leaf[threadIdx.x] = nl;
-    if (path_out) path_out[static_cast<int64_t>(t0 + threadIdx.x) * P + p] = nl - ((1 << D) - 1);
+#pragma unroll
+  for (int u = 0; u < kLeafPer; ++u) {
+    const int i = threadIdx.x + u * kHbThreads;
+    if (i < ntok) {
+      leaf[i] = nl[u];
+      if (path_out) path_out[static_cast<int64_t>(t0 + i) * P + p] = nl[u] - ((1 << D) - 1);
+    }
   }
   wait_vmcnt<0>();  // the copies into LDS have landed
   __syncthreads();
@@ -455,6 +465,8 @@ using TopDirect = DirectCfg<256, 256, 128, 64, 4>;
 // levels of 32 trees are one tile) it fills the chip where 256-token tiles
 // would leave most compute units idle.
 using TopDirect64 = DirectCfg<64, 256, 64, 64, 4>;
+// 128 tokens x 256 columns on eight waves (96 KB of stages).
+using TopDirect128 = DirectCfg<128, 256, 64, 64, 4>;
 
 
 // One workgroup per packed row: packed[i] = W row colmap[i] (zeros for -1).
@@ -493,9 +505,24 @@ hipError_t launch_route_top(const Dims& s, int L, int stride, const void* x, con
   // Enough tiles to cover the 256 compute units: shrink the token tile when
   // the column count is small (few trees or few levels).
   const int64_t tiles_n = top_col_tiles(s, L);
-  if ((1 << L) <= TopDirect::BN && ((s.T + 255) / 256) * tiles_n >= 256)
+  // Direct-to-LDS tiles of 256, 128 or 64 tokens (each at least 256 tiles):
+  // the one whose busiest compute unit has the least output area (tiles per
+  // unit x tile area), ties to the larger tile.
+  int64_t best = INT64_MAX;
+  int pick = 0;
+  for (int bm : {256, 128, 64}) {
+    const int64_t tiles = (s.T + bm - 1) / bm * tiles_n;
+    const int64_t area = (tiles + 255) / 256 * bm;
+    if ((1 << L) <= TopDirect::BN && tiles >= 256 && area < best) {
+      best = area;
+      pick = bm;
+    }
+  }
+  if (pick == 256)
     return launch_top_cfg<TopDirect, true>(s, L, stride, x, W, b, rec_logit, rec_next, st);
-  if ((1 << L) <= TopDirect64::BN && ((s.T + 63) / 64) * tiles_n >= 256)
+  if (pick == 128)
+    return launch_top_cfg<TopDirect128, true>(s, L, stride, x, W, b, rec_logit, rec_next, st);
+  if (pick == 64)
     return launch_top_cfg<TopDirect64, true>(s, L, stride, x, W, b, rec_logit, rec_next, st);
   if (((s.T + 127) / 128) * tiles_n >= 256)
     return launch_top_cfg<MidTile, false>(s, L, stride, x, W, b, rec_logit, rec_next, st);

@@ -11,13 +11,13 @@
 //   (M x 64 bytes) and the G trees' subtree rows (G x S x 16 rows) go
 //   straight into LDS (global_load_lds, two stages), so x is read once per
 //   tree group instead of once per tree.  Before the main loop the tile's
-//   tokens are grouped, per tree, by their level-k node: groups of 16
-//   tokens that share a subtree (the last one of a subtree padded).  A group
-//   is one v_mfma_f32_16x16x32_bf16 per K step: its 16 x rows, read from LDS
-//   through the group's row list (the permutation costs nothing there),
-//   against the 16 rows of its subtree.  The groups of the workgroup are
-//   split evenly over the eight waves; a wave rereads a subtree's rows only
-//   when its next group changes subtree.
+//   tokens are grouped, per tree, by their level-k node: units of 32 tokens
+//   that share a subtree (the last one of a subtree padded), each unit two
+//   groups of 16.  A group is one v_mfma_f32_16x16x32_bf16 per K step: its
+//   16 x rows, read from LDS through the group's row list (the permutation
+//   costs nothing there), against the 16 rows of its subtree, which are read
+//   once per unit for both of its groups.  Whole units are split evenly over
+//   the eight waves.
 //
 // The epilogue walks each token through its subtree (a = logit + b_n; left
 // iff a < 0; NaN and zeros right) and records the logits of levels k..D in
@@ -26,11 +26,14 @@
 // complete records.
 //
 // Within a subtree the order of a group's tokens is free (every token's
-// result is its own).  Tokens are ordered so that a group's 16 rows differ
-// in their low four row bits where the counts allow: the operand read of a
-// group is then free of LDS bank conflicts under the rows' XOR swizzle
-// (chunk c of row r at slot c ^ ((r >> 1) & 3); with bits 2-3, as the
-// 32 x 32 x 16 products use, every such read measured 2-way conflicts).
+// result is its own).  Tokens are ordered by (rank within their class,
+// class), the class being the low three bits of the token's row, so that
+// each eight consecutive rows of a group take distinct classes where the
+// counts allow: the operand read, which the LDS serves eight lanes at a
+// time, is then free of bank conflicts under the rows' XOR swizzle (chunk c
+// of row r at slot c ^ ((r >> 1) & 3), a function of row bits 0-2 together
+// with the row's bank offset; with bits 2-3, as the 32 x 32 x 16 products
+// use, every such read measured 2-way conflicts).
 #include "common.hpp"
 #include "launch.hpp"
 #include "mfma_tile.hpp"
@@ -45,6 +48,17 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 // in their low four bits.
 constexpr int kSwz = 1;
 
+// Token classes for the operand-read order: row bits 0-2 (the bits the
+// swizzle above and the row's bank offset depend on).  A 16 x 16 x 32
+// operand read is served eight lanes (eight rows) at a time, so eight rows
+// with distinct classes read without bank conflicts.
+constexpr int kClasses = 8;
+// Tokens per subtree are padded to whole units of kUnit = 16 * kPair tokens;
+// the kPair groups of a unit share their subtree, so one read of its node
+// rows serves kPair matrix-core products.
+constexpr int kPair = 2;
+constexpr int kUnit = 16 * kPair;
+
 template <int M_, int G_, int S_>
 struct SubCfg {
   static constexpr int M = M_;  // tokens per tile
@@ -56,12 +70,13 @@ struct SubCfg {
   static constexpr int R = G * S * 16;             // subtree rows per stage
   static constexpr int kXBytes = M * kRowBytes;    // x rows of one stage
   static constexpr int kWBytes = R * kRowBytes;    // node rows of one stage
-  static constexpr int kSlots = M + 16 * S;        // group slots per tree (bound)
-  static constexpr int kMaxGroups = G * (M / 16 + S);
-  static constexpr int kMaxG = (kMaxGroups + kWaves - 1) / kWaves;  // per wave
+  static constexpr int kSlots = M + kUnit * S;     // group slots per tree (bound)
+  static constexpr int kMaxGroups = G * (M / 16 + kPair * S);
+  static constexpr int kMaxUnits = kMaxGroups / kPair;
+  static constexpr int kMaxG = kPair * ((kMaxUnits + kWaves - 1) / kWaves);  // per wave
   static constexpr int kXLoads = M / 16 / kWaves;  // wave-wide loads per stage
   static constexpr int kWLoads = R / 16 / kWaves;
-  static constexpr int kKeys = S * 16;             // (subtree, row residue) keys
+  static constexpr int kKeys = S * kClasses;       // (subtree, token class) keys
   static constexpr int kChunks = M / kWave;        // 64-token chunks of the tile
   static_assert(M % (16 * kWaves) == 0 && R % (16 * kWaves) == 0, "loads split over waves");
   static_assert(M <= kThreads && M % kWave == 0, "one thread per token while grouping");
@@ -166,7 +181,7 @@ __global__ __launch_bounds__(C::kThreads, 1) void subtree_kernel(
   // group at once: the token's subtree s and row residue form the key
   // s * 16 + residue; equal keys within a wavefront find each other by
   // ballots, and per-wavefront counts go to LDS.
-  constexpr int kKeyBits = __builtin_ctz(S) + 4;
+  constexpr int kKeyBits = __builtin_ctz(S) + __builtin_ctz(kClasses);
   const int t = t0 + tid;
   const bool tok_ok = tid < M && t < T;
   int sub[G];
@@ -187,13 +202,13 @@ __global__ __launch_bounds__(C::kThreads, 1) void subtree_kernel(
     bias[i] = v;
   }
   __syncthreads();
-  const int res = tid & 15;
+  const int res = tid & (kClasses - 1);
   const int chunk = tid / kWave;
   int rank[G];
 #pragma unroll
   for (int tl = 0; tl < G; ++tl) {
     const bool valid = sub[tl] >= 0;
-    const int key = (valid ? sub[tl] : 0) * 16 + res;
+    const int key = (valid ? sub[tl] : 0) * kClasses + res;
     const uint64_t peers = peers_with_key(valid, key, kKeyBits);
     rank[tl] = __popcll(peers & lanes_below(lane));
     if (valid && rank[tl] == 0)
@@ -215,15 +230,15 @@ __global__ __launch_bounds__(C::kThreads, 1) void subtree_kernel(
   }
   __syncthreads();
   // Groups: lane i of wave 0 takes item i = (tree i / S, subtree i % S); its
-  // token count padded to whole groups of 16; a scan within the tree gives
-  // the subtree's first slot, a scan over all items its first group.
+  // token count padded to whole units; a scan within the tree gives the
+  // subtree's first slot, a scan over all items its first group.
   if (tid < 32) {
     const int tl = tid / S;
     const int s = tid % S;
     int n = 0;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) n += cnt[tl * C::kKeys + s * 16 + r];
-    const int pad = (n + 15) & ~15;
+    for (int r = 0; r < kClasses; ++r) n += cnt[tl * C::kKeys + s * kClasses + r];
+    const int pad = (n + kUnit - 1) & ~(kUnit - 1);
     int slot = pad, gi = pad / 16;  // inclusive scans
 #pragma unroll
     for (int off = 1; off < 32; off <<= 1) {
@@ -239,18 +254,18 @@ __global__ __launch_bounds__(C::kThreads, 1) void subtree_kernel(
     if (tid == 31) misc[0] = gi + pad / 16;
   }
   __syncthreads();
-  // Each token's slot: order within its subtree by (rank within the
-  // residue, residue), so that consecutive slots take distinct residues
-  // while the counts allow.
+  // Each token's slot: order within its subtree by (rank within the class,
+  // class), so that consecutive slots take distinct classes while the
+  // counts allow.
 #pragma unroll
   for (int tl = 0; tl < G; ++tl) {
     if (sub[tl] >= 0) {
-      const int key = sub[tl] * 16 + res;
+      const int key = sub[tl] * kClasses + res;
       const int r = wcnt[(tl * C::kChunks + chunk) * C::kKeys + key] + rank[tl];
-      const int32_t* cs = cnt + tl * C::kKeys + sub[tl] * 16;
+      const int32_t* cs = cnt + tl * C::kKeys + sub[tl] * kClasses;
       int pos = sbase[tl * S + sub[tl]];
 #pragma unroll
-      for (int qq = 0; qq < 16; ++qq) {
+      for (int qq = 0; qq < kClasses; ++qq) {
         const int c = cs[qq];
         pos += c < r ? c : r;
         pos += (qq < res && c > r) ? 1 : 0;
@@ -263,9 +278,11 @@ __global__ __launch_bounds__(C::kThreads, 1) void subtree_kernel(
   // ---- this wave's groups: operand addresses ----
   // Slots past the wave's count read valid rows and their products are
   // dropped, so the K loop has no branch.
-  const int ng_all = misc[0];
-  const int gbeg = (wave * ng_all) / C::kWaves;
-  const int ng = ((wave + 1) * ng_all) / C::kWaves - gbeg;
+  // Whole units per wave (a unit's groups share their subtree rows).
+  const int nu_all = misc[0] / kPair;
+  const int ubeg = (wave * nu_all) / C::kWaves;
+  const int gbeg = kPair * ubeg;
+  const int ng = kPair * (((wave + 1) * nu_all) / C::kWaves - ubeg);
   const int m = lane & 15;
   const int q = lane >> 4;
   uint32_t addrA[C::kMaxG], addrB[C::kMaxG];
@@ -305,11 +322,14 @@ __global__ __launch_bounds__(C::kThreads, 1) void subtree_kernel(
     const unsigned char* xs = lds + C::kOffX + (ks & 1) * C::kXBytes;
     const unsigned char* ws = lds + C::kOffW + (ks & 1) * C::kWBytes;
 #pragma unroll
-    for (int g = 0; g < C::kMaxG; ++g) {
-      const bf16x8_t afrag = *reinterpret_cast<const bf16x8_t*>(xs + addrA[g]);
-      const bf16x8_t bfrag = *reinterpret_cast<const bf16x8_t*>(ws + addrB[g]);
-      // D[token][node]: lane l holds tokens 4(l/16)+i of node l%16.
-      acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afrag, bfrag, acc[g], 0, 0, 0);
+    for (int u = 0; u < C::kMaxG; u += kPair) {
+      const bf16x8_t bfrag = *reinterpret_cast<const bf16x8_t*>(ws + addrB[u]);
+#pragma unroll
+      for (int g = u; g < u + kPair; ++g) {
+        const bf16x8_t afrag = *reinterpret_cast<const bf16x8_t*>(xs + addrA[g]);
+        // D[token][node]: lane l holds tokens 4(l/16)+i of node l%16.
+        acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afrag, bfrag, acc[g], 0, 0, 0);
+      }
     }
   }
   __syncthreads();  // stage buffers free for the epilogue

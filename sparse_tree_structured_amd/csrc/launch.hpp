@@ -77,10 +77,9 @@ bool project_mfma_supported(const Dims& s);
 hipError_t launch_project_mfma(const Dims& s, const void* H, const void* Wout, void* y,
                                hipStream_t st);
 
-// Multi-stage direct-to-LDS projection; W_out supplied transposed (WT[d][K]).
+// Multi-stage direct-to-LDS projection (W_out in its own [K][d] layout).
 bool project_direct_supported(const Dims& s);
-hipError_t launch_transpose(const void* W, void* WT, int64_t K, int Nc, hipStream_t st);
-hipError_t launch_project_direct(const Dims& s, const void* H, const void* WT, void* y,
+hipError_t launch_project_direct(const Dims& s, const void* H, const void* Wout, void* y,
                                  hipStream_t st);
 
 // ---- prefill routing (bf16) ----

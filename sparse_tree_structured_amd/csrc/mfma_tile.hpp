@@ -209,6 +209,46 @@ __device__ __forceinline__ void direct_load_rows(unsigned char* lds, int base, c
   }
 }
 
+// The same copy (16 bytes per lane into lds_dst + 16 * lane, lds_dst
+// wave-uniform) written as inline assembly.  The compiler then does not know
+// that the instruction writes LDS, so it does not hold later LDS reads
+// behind it (it does so, with a full vmcnt(0), before every
+// ds_read_b64_tr_b16 that follows a global_load_lds it issued itself); the
+// caller waits for the copies with explicit s_waitcnt vmcnt, as the
+// pipelined loops below do anyway.  M0 holds the LDS base during the copy
+// and is restored afterwards; one wait state separates the M0 write from
+// the copy.  The asm has no outputs but the saved M0, so no register is
+// left pending.
+__device__ __forceinline__ void dma16_asm(const void* g, const unsigned char* lds_dst) {
+  // The low 32 bits of a generic LDS address are its LDS offset.
+  const uint32_t m =
+      __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds_dst)));
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(g), "s"(m)
+      : "memory");
+}
+
+template <class C, int ROWS, class RowPtr>
+__device__ __forceinline__ void direct_load_rows_asm(unsigned char* lds, int base,
+                                                     const RowPtr& row_ptr, int k0, int wave,
+                                                     int lane) {
+  constexpr int kLoads = ROWS / 16 / C::kWaves;
+#pragma unroll
+  for (int j = 0; j < kLoads; ++j) {
+    const int r0 = (wave * kLoads + j) * 16;
+    const int r = r0 + (lane >> 2);
+    const int chunk = (lane & 3) ^ lds_swz(r);
+    dma16_asm(row_ptr(r) + k0 + chunk * 8, lds + base + r0 * C::kRowBytes);
+  }
+}
+
 // The same loads with the 16-byte chunks swizzled by row bits SHIFT and
 // SHIFT+1: chunk c of row r at slot c ^ ((r >> SHIFT) & 3).  For the
 // 16 x 16 x 32 operand fetch (16 rows, one chunk per 16 lanes) SHIFT = 1 is
@@ -238,9 +278,84 @@ struct Frags {
   bf16x8_t a[C::kTm], b[C::kTn];
 };
 
+// B operand held as rows of the output columns (B^T, K-contiguous): row j of
+// the stage's B block is output column j, 64 bytes of k.  row_ptr(j) gives
+// column j's K-contiguous start (already clamped to valid memory).
+template <class C, class RowPtr>
+struct RowsB {
+  static constexpr bool kAsmDma = false;  // A and B copies through the builtin
+  const RowPtr& row_ptr;
+  __device__ __forceinline__ void issue(unsigned char* lds, int base, int k0, int wave,
+                                        int lane) const {
+    direct_load_rows<C, C::BN>(lds, base, row_ptr, k0, wave, lane);
+  }
+  __device__ __forceinline__ bf16x8_t frag(const unsigned char* Bs, int kk, int wn, int j,
+                                           int lane) const {
+    const int r = wn * C::WN + j * 32 + (lane & 31);
+    const int chunk = kk * 2 + (lane >> 5);
+    return *reinterpret_cast<const bf16x8_t*>(Bs + r * C::kRowBytes + ((chunk ^ lds_swz(r)) << 4));
+  }
+};
+
+// B operand in its natural k-major layout (row k holds consecutive output
+// columns, row stride ld elements), as y = H . W_out has it.  The stage's B
+// block is BK = 32 rows of BN columns (BN * 2 bytes each, whole 128-byte
+// lines per load); 16-byte chunk c of row r sits at slot c ^ 4 (r & 3).
+// A fragment wants eight k-consecutive values of one column per lane, which
+// ds_read_b64_tr_b16 assembles from a k-major tile: within each 16-lane
+// group, lane 4 jj + a addresses row kb + jj at columns cb + 4 a .. cb + 4 a + 3,
+// and lane i receives element i % 4 of the words of lanes i / 4, 4 + i / 4,
+// 8 + i / 4 and 12 + i / 4, i.e. column cb + i at rows kb .. kb + 3.  Two
+// such reads (rows kb and kb + 4) make the eight values.  With the swizzle,
+// the 32 lanes of a half wavefront read 64 distinct banks.
+struct KMajorB {
+  const uint16_t* p;  // element (k = 0, column n0) of the tile
+  int ld;             // row stride in elements
+  int ncols;          // valid columns from n0 (chunks past it read column n0)
+};
+
 template <class C>
+struct KMajorBOp {
+  static constexpr bool kAsmDma = true;  // A and B copies through dma16_asm
+  static constexpr int kRow = C::BN * 2;       // LDS bytes per k row
+  static constexpr int kLoads = C::BN / 16 / C::kWaves;  // 1 KB loads per wave per stage
+  static_assert(C::BN >= 128 && (C::BN * 2) % 256 == 0, "swizzle spans 16 chunks per row");
+  static_assert(C::BK * C::BN * 2 == C::BN * C::kRowBytes, "stage B block size");
+  KMajorB b;
+  __device__ __forceinline__ static int swz(int r) { return (r & 3) << 2; }
+  __device__ __forceinline__ void issue(unsigned char* lds, int base, int k0, int wave,
+                                        int lane) const {
+#pragma unroll
+    for (int j = 0; j < kLoads; ++j) {
+      const int q = wave * kLoads + j;  // 1 KB piece of the stage's B block
+      const int byte = q * 1024 + lane * 16;
+      const int r = byte / kRow;
+      const int c = ((byte % kRow) >> 4) ^ swz(r);
+      const int col = c * 8 < b.ncols ? c * 8 : 0;
+      dma16_asm(b.p + static_cast<size_t>(k0 + r) * b.ld + col, lds + base + q * 1024);
+    }
+  }
+  __device__ __forceinline__ bf16x8_t frag(const unsigned char* Bs, int kk, int wn, int j,
+                                           int lane) const {
+    typedef short v4i16_t __attribute__((ext_vector_type(4)));
+    typedef short v8i16_t __attribute__((ext_vector_type(8)));
+    const int cb = wn * C::WN + j * 32 + (lane & 16);  // group's first column
+    const int kb = kk * 16 + ((lane >> 5) << 3);       // group's first row
+    const int jj = (lane >> 2) & 3;
+    const int col = cb + ((lane & 3) << 2);
+    const int r = kb + jj;  // (r + 4) & 3 == r & 3: one swizzle for both reads
+    const int off = r * kRow + (((col >> 3) ^ swz(r)) << 4) + ((col & 7) << 1);
+    typedef __attribute__((address_space(3))) v4i16_t* lds_v4_t;
+    const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4_t)(Bs + off));
+    const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4_t)(Bs + off + 4 * kRow));
+    const v8i16_t v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    return __builtin_bit_cast(bf16x8_t, v);
+  }
+};
+
+template <class C, class BOp>
 __device__ __forceinline__ void read_frags(Frags<C>& f, const unsigned char* stage, int kk, int wm,
-                                           int wn, int lane) {
+                                           int wn, int lane, const BOp& bop) {
   const unsigned char* As = stage;
   const unsigned char* Bs = stage + C::BM * C::kRowBytes;
   const int lrow = lane & 31;
@@ -251,10 +366,7 @@ __device__ __forceinline__ void read_frags(Frags<C>& f, const unsigned char* sta
     f.a[i] = *reinterpret_cast<const bf16x8_t*>(As + r * C::kRowBytes + ((chunk ^ lds_swz(r)) << 4));
   }
 #pragma unroll
-  for (int j = 0; j < C::kTn; ++j) {
-    const int r = wn * C::WN + j * 32 + lrow;
-    f.b[j] = *reinterpret_cast<const bf16x8_t*>(Bs + r * C::kRowBytes + ((chunk ^ lds_swz(r)) << 4));
-  }
+  for (int j = 0; j < C::kTn; ++j) f.b[j] = bop.frag(Bs, kk, wn, j, lane);
 }
 
 template <class C>
@@ -275,8 +387,9 @@ __device__ __forceinline__ void stage_barrier() {
   asm volatile("" ::: "memory");
 }
 
-// Full K loop (K % 32 == 0).  a_row(i), i < BM, and b_row(j), j < BN, return
-// K-contiguous row starts (already clamped to valid memory).
+// Full K loop (K % 32 == 0).  a_row(i), i < BM, returns a K-contiguous row
+// start (already clamped to valid memory); bop stages and reads the B
+// operand (RowsB or KMajorBOp).
 //
 // Schedule of iteration ks (stage buffer ks % S):
 //   read fragments (ks, kk=1)            -- LDS reads overlap the MFMAs below
@@ -286,10 +399,10 @@ __device__ __forceinline__ void stage_barrier() {
 //   MFMAs on fragments (ks, kk=1)
 // so every fragment is read one MFMA group (16 MFMAs) before its use and the
 // loads of a stage are issued S-2 iterations before it is needed.
-template <class C, class ARow, class BRow>
-__device__ __forceinline__ void gemm_mainloop_direct(f32x16_t (&acc)[C::kTm][C::kTn],
-                                                     unsigned char* lds, int K, const ARow& a_row,
-                                                     const BRow& b_row) {
+template <class C, class ARow, class BOp>
+__device__ __forceinline__ void gemm_mainloop_direct_op(f32x16_t (&acc)[C::kTm][C::kTn],
+                                                        unsigned char* lds, int K,
+                                                        const ARow& a_row, const BOp& bop) {
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = tid / kWave;
@@ -302,8 +415,11 @@ __device__ __forceinline__ void gemm_mainloop_direct(f32x16_t (&acc)[C::kTm][C::
   const int nk = K / C::BK;
   auto issue = [&](int ks) {
     const int base = (ks % S) * C::kStageBytes;
-    direct_load_rows<C, C::BM>(lds, base, a_row, ks * C::BK, wave, lane);
-    direct_load_rows<C, C::BN>(lds, base + C::BM * C::kRowBytes, b_row, ks * C::BK, wave, lane);
+    if constexpr (BOp::kAsmDma)
+      direct_load_rows_asm<C, C::BM>(lds, base, a_row, ks * C::BK, wave, lane);
+    else
+      direct_load_rows<C, C::BM>(lds, base, a_row, ks * C::BK, wave, lane);
+    bop.issue(lds, base + C::BM * C::kRowBytes, ks * C::BK, wave, lane);
   };
 #pragma unroll
   for (int s = 0; s < S - 1; ++s)
@@ -312,10 +428,10 @@ __device__ __forceinline__ void gemm_mainloop_direct(f32x16_t (&acc)[C::kTm][C::
   wait_stages<kPerStage, S - 2>(nk - 1);
   stage_barrier();
   Frags<C> f0, f1;
-  read_frags<C>(f0, lds, 0, wm, wn, lane);
+  read_frags<C>(f0, lds, 0, wm, wn, lane, bop);
   for (int ks = 0; ks < nk; ++ks) {
     const unsigned char* cur = lds + (ks % S) * C::kStageBytes;
-    read_frags<C>(f1, cur, 1, wm, wn, lane);
+    read_frags<C>(f1, cur, 1, wm, wn, lane, bop);
     asm volatile("" ::: "memory");  // keep these reads ahead of the MFMAs below
     mma_frags<C>(acc, f0);
     if (ks + 1 < nk) {
@@ -327,11 +443,20 @@ __device__ __forceinline__ void gemm_mainloop_direct(f32x16_t (&acc)[C::kTm][C::
     // Unconditional (after the last stage it reads a stale buffer and the
     // values go unused), so the wait before the MFMAs below can leave these
     // eight reads in flight on every path.
-    read_frags<C>(f0, lds + ((ks + 1) % S) * C::kStageBytes, 0, wm, wn, lane);
+    read_frags<C>(f0, lds + ((ks + 1) % S) * C::kStageBytes, 0, wm, wn, lane, bop);
     asm volatile("" ::: "memory");
     mma_frags<C>(acc, f1);
   }
   __syncthreads();
+}
+
+// Both operands K-contiguous: b_row(j), j < BN, returns output column j's
+// row start (already clamped to valid memory).
+template <class C, class ARow, class BRow>
+__device__ __forceinline__ void gemm_mainloop_direct(f32x16_t (&acc)[C::kTm][C::kTn],
+                                                     unsigned char* lds, int K, const ARow& a_row,
+                                                     const BRow& b_row) {
+  gemm_mainloop_direct_op<C>(acc, lds, K, a_row, RowsB<C, BRow>{b_row});
 }
 
 // XCD-aware tile order: hardware sends workgroup b to XCD b % 8.  Each XCD

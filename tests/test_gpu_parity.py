@@ -150,8 +150,7 @@ def test_zero_tokens():
 @needs_gpu
 @pytest.mark.parametrize("M,K,N", [(16384, 4096, 2048), (1000, 1024, 768), (1, 64, 8), (129, 192, 72),
                                    # direct-to-LDS with 128 x 128 tiles: a ragged last
-                                   # column tile (and transpose tile) of 8 columns, and
-                                   # ragged rows
+                                   # column tile of 8 columns, and ragged rows
                                    (8192, 1024, 776), (4000, 4096, 2048)])
 def test_projection_matches_fp64(M, K, N):
     import sparse_tree_structured_amd as fff
@@ -162,7 +161,7 @@ def test_projection_matches_fp64(M, K, N):
     for algo in ("prefill", "generic"):
         if algo == "prefill" and K % 64:
             continue
-        for use_ws in (True, False):  # fff_project_ws (direct-to-LDS where large) and fff_project
+        for use_ws in (True, False):  # fff_project_ws and fff_project
             y = fff.project(H.cuda(), Wo.cuda(), algo=algo, use_workspace=use_ws)
             torch.cuda.synchronize()
             got = to_f64(y)
@@ -205,7 +204,7 @@ def test_prefill_split_levels(name, k, chunk):
 @pytest.mark.parametrize("name", ["gpt125m", "opt1p3b_d6"])
 def test_route_matches_forward_h(name):
     # fff_route exposes H; projecting it must give fff_forward's y exactly
-    # (at the OPT-1.3B shape through fff_project_ws's direct-to-LDS product).
+    # (at the OPT-1.3B shape through the direct-to-LDS product).
     import sparse_tree_structured_amd as fff
     inp = wl(name)
     T = to_device(inp)
