@@ -235,11 +235,21 @@ fff_status_t record(hipEvent_t ev, hipStream_t st) {
   return hip_status(hipEventRecord(ev, st));
 }
 
-// Routing stage into H (caller or workspace buffer); records the `top` and
-// `deep` events (NULL events: none).
+// Whether the routing stage of a plan writes H through hbuild_kernel (the
+// dense and token-tile prefill plans) and the direct-to-LDS projection takes
+// it: then fff_forward keeps H K-blocked, so that each projection stage
+// reads whole 128-byte lines.
+bool h_blocked(const Dims& s, const fff_plan_t& p, const Layout& L) {
+  return p.algo == FFF_ALGO_PREFILL && (L.tile || p.split_level == s.D + 1) &&
+         fff::project_direct_supported(s);
+}
+
+// Routing stage into H (caller or workspace buffer; K-blocked with
+// `blocked`, which needs a plan for which h_blocked() holds); records the
+// `top` and `deep` events (NULL events: none).
 fff_status_t run_route(const Dims& s, const fff_plan_t& p, const Layout& L, const void* x,
                        const void* W, const void* b, const void* V, void* H, int32_t* path_out,
-                       char* ws, hipStream_t st, const fff_stage_events_t* ev) {
+                       char* ws, bool blocked, hipStream_t st, const fff_stage_events_t* ev) {
   float* logits = reinterpret_cast<float*>(ws + L.logits);
   int32_t* leaf = reinterpret_cast<int32_t*>(ws + L.leaf);
   const fff_stage_events_t none{};
@@ -253,13 +263,13 @@ fff_status_t run_route(const Dims& s, const fff_plan_t& p, const Layout& L, cons
     if ((r = record(E.top, st)) != FFF_SUCCESS) return r;
     if (k == s.D + 1) {
       if ((r = record(E.deep, st)) != FFF_SUCCESS) return r;
-      return hip_status(fff::launch_hbuild(s, logits, leaf, V, H, path_out, st));
+      return hip_status(fff::launch_hbuild(s, logits, leaf, V, H, path_out, blocked, st));
     }
     if (L.tile) {
       e = fff::launch_subtree(s, k, x, W, b, logits, leaf, st);
       if (e != hipSuccess) return FFF_ERROR_HIP;
       if ((r = record(E.deep, st)) != FFF_SUCCESS) return r;
-      return hip_status(fff::launch_hbuild(s, logits, leaf, V, H, path_out, st));
+      return hip_status(fff::launch_hbuild(s, logits, leaf, V, H, path_out, blocked, st));
     }
     int32_t* perm = reinterpret_cast<int32_t*>(ws + L.perm);
     int32_t* offs = reinterpret_cast<int32_t*>(ws + L.offs);
@@ -282,7 +292,7 @@ fff_status_t run_project(const Dims& s, int32_t algo, const void* H, const void*
                          hipStream_t st) {
   hipError_t e;
   if (algo != FFF_ALGO_GENERIC && fff::project_direct_supported(s))
-    e = fff::launch_project_direct(s, H, Wout, y, st);
+    e = fff::launch_project_direct(s, H, Wout, y, false, st);
   else if (algo != FFF_ALGO_GENERIC && fff::project_mfma_supported(s))
     e = fff::launch_project_mfma(s, H, Wout, y, st);
   else
@@ -335,10 +345,14 @@ fff_status_t forward_impl(const Dims& s, const fff_plan_t& p, const void* x, con
   // Nothing is prepared before routing (W_out is used in its own layout):
   // `prepared` follows `start` directly.
   if ((st = record(E.prepared, stream)) != FFF_SUCCESS) return st;
-  st = run_route(s, p, L, x, W_node, b_node, V_node, H, path_out, ws, stream, &E);
+  const bool blk = h_blocked(s, p, L);
+  st = run_route(s, p, L, x, W_node, b_node, V_node, H, path_out, ws, blk, stream, &E);
   if (st != FFF_SUCCESS) return st;
   if ((st = record(E.routed, stream)) != FFF_SUCCESS) return st;
-  st = run_project(s, p.algo, H, W_out, y, stream);
+  if (blk)
+    st = hip_status(fff::launch_project_direct(s, H, W_out, y, true, stream));
+  else
+    st = run_project(s, p.algo, H, W_out, y, stream);
   if (st != FFF_SUCCESS) return st;
   if ((st = record(E.done, stream)) != FFF_SUCCESS) return st;
   return FFF_SUCCESS;
@@ -684,8 +698,9 @@ fff_status_t fff_route(const fff_shape_t* shape, const fff_plan_t* plan, const v
   const Layout L = layout_for(s, p);
   if (L.total > 0 && (!workspace || workspace_bytes < L.total)) return FFF_ERROR_WORKSPACE;
   if (workspace && !aligned(workspace, kWsAlign)) return FFF_ERROR_INVALID_VALUE;
+  // fff_route hands H to the caller: row-major, as fff.h documents it.
   return run_route(s, p, L, x, W_node, b_node, V_node, H, path_out, static_cast<char*>(workspace),
-                   stream, nullptr);
+                   false, stream, nullptr);
 }
 
 fff_status_t fff_project(const fff_shape_t* shape, int32_t algo, const void* H, const void* W_out,

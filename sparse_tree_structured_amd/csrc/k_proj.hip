@@ -189,10 +189,13 @@ __device__ __forceinline__ void store_y_tile_lds(const f32x16_t (&acc)[C::kTm][C
 }
 
 // y = H . W_out with both operands loaded straight into LDS by the
-// multi-stage main loop: H rows K-contiguous, W_out in its own k-major layout
-// (W_out[k][n]), whose fragments the main loop reads with transposing LDS
-// reads, so W_out needs no preparation.
-template <class C>
+// multi-stage main loop: W_out in its own k-major layout (W_out[k][n]), whose
+// fragments the main loop reads with transposing LDS reads, so W_out needs no
+// preparation; H row-major, or K-blocked (HBLK: element (t, k) at
+// ((k / 32) * M + t) * 32 + k % 32, as the H pass writes it inside the
+// layer), where each stage's A tile is one contiguous block and every load
+// fetches whole 128-byte lines.
+template <class C, bool HBLK>
 __global__ __launch_bounds__(C::kThreads) void proj_direct_kernel(
     const uint16_t* __restrict__ H, const uint16_t* __restrict__ Wout, uint16_t* __restrict__ y,
     int M, int K, int Nc, int tiles_n) {
@@ -204,11 +207,11 @@ __global__ __launch_bounds__(C::kThreads) void proj_direct_kernel(
   const int n0 = tn * C::BN;
   auto a_row = [&](int i) {
     const int r = m0 + i < M ? m0 + i : M - 1;
-    return H + static_cast<size_t>(r) * K;
+    return H + static_cast<size_t>(r) * (HBLK ? 32 : K);
   };
   const KMajorBOp<C> bop{KMajorB{Wout + n0, Nc, Nc - n0}};
   f32x16_t acc[C::kTm][C::kTn];
-  gemm_mainloop_direct_op<C>(acc, lds, K, a_row, bop);
+  gemm_mainloop_direct_op<C>(acc, lds, K, a_row, bop, HBLK ? static_cast<int64_t>(M) : 1);
   store_y_tile_lds<C>(acc, lds, y, M, Nc, m0, n0);
 }
 
@@ -302,12 +305,12 @@ bool project_direct_supported(const Dims& s) {
          (big_direct_tiles(s) >= 256 || mid_direct_tiles(s) >= 256);
 }
 
-template <class C>
+template <class C, bool HBLK>
 hipError_t launch_direct_cfg(const Dims& s, const void* H, const void* Wout, void* y,
                              hipStream_t st) {
   const int tiles_m = static_cast<int>((s.T + C::BM - 1) / C::BM);
   const int tiles_n = (s.d + C::BN - 1) / C::BN;
-  auto kern = proj_direct_kernel<C>;
+  auto kern = proj_direct_kernel<C, HBLK>;
   constexpr size_t lds = proj_lds_bytes<C>();
   {
     const hipError_t e =
@@ -320,14 +323,21 @@ hipError_t launch_direct_cfg(const Dims& s, const void* H, const void* Wout, voi
   return hipGetLastError();
 }
 
-hipError_t launch_project_direct(const Dims& s, const void* H, const void* Wout, void* y,
-                                 hipStream_t st) {
+template <bool HBLK>
+hipError_t launch_direct_pick(const Dims& s, const void* H, const void* Wout, void* y,
+                              hipStream_t st) {
   const int64_t big = cu_area(s.T, s.d, 256, 256);
   const int64_t wide = cu_area(s.T, s.d, 256, 128);
   const int64_t mid = cu_area(s.T, s.d, 128, 128);
-  if (big <= wide && big <= mid) return launch_direct_cfg<BigDirect>(s, H, Wout, y, st);
-  if (wide <= mid) return launch_direct_cfg<WideDirect>(s, H, Wout, y, st);
-  return launch_direct_cfg<MidDirect>(s, H, Wout, y, st);
+  if (big <= wide && big <= mid) return launch_direct_cfg<BigDirect, HBLK>(s, H, Wout, y, st);
+  if (wide <= mid) return launch_direct_cfg<WideDirect, HBLK>(s, H, Wout, y, st);
+  return launch_direct_cfg<MidDirect, HBLK>(s, H, Wout, y, st);
+}
+
+hipError_t launch_project_direct(const Dims& s, const void* H, const void* Wout, void* y,
+                                 bool h_blocked, hipStream_t st) {
+  if (h_blocked) return launch_direct_pick<true>(s, H, Wout, y, st);
+  return launch_direct_pick<false>(s, H, Wout, y, st);
 }
 
 }  // namespace fff

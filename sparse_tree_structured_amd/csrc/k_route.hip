@@ -298,7 +298,7 @@ __global__ __launch_bounds__(kHbThreads) void hbuild_kernel(const float* __restr
                                                      const uint16_t* __restrict__ V,
                                                      uint16_t* __restrict__ H,
                                                      int32_t* __restrict__ path_out, int T, int P,
-                                                     int64_t N, int post) {
+                                                     int64_t N, int post, int blocked) {
   constexpr int L = LEVELS;
   constexpr int D = LEVELS - 1;
   constexpr int h = 16 << HSHIFT;     // node output width
@@ -408,11 +408,22 @@ __global__ __launch_bounds__(kHbThreads) void hbuild_kernel(const float* __restr
 #pragma unroll
       for (int q = 0; q < 16; ++q) acc[q] = gelu_tanh(acc[q]);
     }
-    uint16_t* row = Hp + static_cast<int64_t>(t0 + i) * P * h;
-    *reinterpret_cast<uint4*>(row + ja) =
+    uint16_t* pa;
+    uint16_t* pb;
+    if (blocked) {  // element (t, k) at ((k / 32) * T + t) * 32 + k % 32
+      const int64_t ka = static_cast<int64_t>(p) * h + ja, kb = ka + h / 2;
+      const int64_t tt = static_cast<int64_t>(t0 + i) * 32;
+      pa = H + (ka >> 5) * (static_cast<int64_t>(T) << 5) + tt + (ka & 31);
+      pb = H + (kb >> 5) * (static_cast<int64_t>(T) << 5) + tt + (kb & 31);
+    } else {
+      uint16_t* row = Hp + static_cast<int64_t>(t0 + i) * P * h;
+      pa = row + ja;
+      pb = row + jb;
+    }
+    *reinterpret_cast<uint4*>(pa) =
         make_uint4(pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]),
                    pack_bf16x2(acc[4], acc[5]), pack_bf16x2(acc[6], acc[7]));
-    *reinterpret_cast<uint4*>(row + jb) =
+    *reinterpret_cast<uint4*>(pb) =
         make_uint4(pack_bf16x2(acc[8], acc[9]), pack_bf16x2(acc[10], acc[11]),
                    pack_bf16x2(acc[12], acc[13]), pack_bf16x2(acc[14], acc[15]));
   }
@@ -532,7 +543,8 @@ hipError_t launch_route_top(const Dims& s, int L, int stride, const void* x, con
 namespace {
 template <int LEVELS, int HSHIFT, bool F32>
 hipError_t launch_hbuild_l(const Dims& s, const float* rec_logit, const int32_t* rec_next,
-                           const void* V, void* H, int32_t* path_out, hipStream_t st) {
+                           const void* V, void* H, int32_t* path_out, bool blocked,
+                           hipStream_t st) {
   const size_t lds = hbuild_lds_bytes(s);
   auto kern = hbuild_kernel<LEVELS, HSHIFT, F32>;
   {
@@ -544,26 +556,28 @@ hipError_t launch_hbuild_l(const Dims& s, const float* rec_logit, const int32_t*
   if (blocks > INT32_MAX) return hipErrorInvalidConfiguration;
   kern<<<dim3(static_cast<unsigned>(blocks)), dim3(kHbThreads), lds, st>>>(rec_logit, rec_next, static_cast<const uint16_t*>(V),
                                      static_cast<uint16_t*>(H), path_out, static_cast<int>(s.T),
-                                     s.P, s.N, s.variant);
+                                     s.P, s.N, s.variant, blocked ? 1 : 0);
   return hipGetLastError();
 }
 
 template <int LEVELS, int HSHIFT>
 hipError_t launch_hbuild_h(const Dims& s, const float* rec_logit, const int32_t* rec_next,
-                           const void* V, void* H, int32_t* path_out, hipStream_t st) {
+                           const void* V, void* H, int32_t* path_out, bool blocked,
+                           hipStream_t st) {
   if (hbuild_f32(s))
-    return launch_hbuild_l<LEVELS, HSHIFT, true>(s, rec_logit, rec_next, V, H, path_out, st);
-  return launch_hbuild_l<LEVELS, HSHIFT, false>(s, rec_logit, rec_next, V, H, path_out, st);
+    return launch_hbuild_l<LEVELS, HSHIFT, true>(s, rec_logit, rec_next, V, H, path_out, blocked, st);
+  return launch_hbuild_l<LEVELS, HSHIFT, false>(s, rec_logit, rec_next, V, H, path_out, blocked, st);
 }
 
 template <int LEVELS>
 hipError_t launch_hbuild_d(const Dims& s, const float* rec_logit, const int32_t* rec_next,
-                           const void* V, void* H, int32_t* path_out, hipStream_t st) {
+                           const void* V, void* H, int32_t* path_out, bool blocked,
+                           hipStream_t st) {
   switch (s.h) {
-    case 64: return launch_hbuild_h<LEVELS, 2>(s, rec_logit, rec_next, V, H, path_out, st);
-    case 128: return launch_hbuild_h<LEVELS, 3>(s, rec_logit, rec_next, V, H, path_out, st);
-    case 256: return launch_hbuild_h<LEVELS, 4>(s, rec_logit, rec_next, V, H, path_out, st);
-    case 512: return launch_hbuild_h<LEVELS, 5>(s, rec_logit, rec_next, V, H, path_out, st);
+    case 64: return launch_hbuild_h<LEVELS, 2>(s, rec_logit, rec_next, V, H, path_out, blocked, st);
+    case 128: return launch_hbuild_h<LEVELS, 3>(s, rec_logit, rec_next, V, H, path_out, blocked, st);
+    case 256: return launch_hbuild_h<LEVELS, 4>(s, rec_logit, rec_next, V, H, path_out, blocked, st);
+    case 512: return launch_hbuild_h<LEVELS, 5>(s, rec_logit, rec_next, V, H, path_out, blocked, st);
     default: return hipErrorInvalidValue;  // hbuild_supported() excludes other widths
   }
 }
@@ -575,16 +589,17 @@ bool hbuild_supported(const Dims& s) {
 }
 
 hipError_t launch_hbuild(const Dims& s, const float* rec_logit, const int32_t* rec_next,
-                         const void* V, void* H, int32_t* path_out, hipStream_t st) {
+                         const void* V, void* H, int32_t* path_out, bool blocked,
+                         hipStream_t st) {
   switch (s.D + 1) {
-    case 1: return launch_hbuild_d<1>(s, rec_logit, rec_next, V, H, path_out, st);
-    case 2: return launch_hbuild_d<2>(s, rec_logit, rec_next, V, H, path_out, st);
-    case 3: return launch_hbuild_d<3>(s, rec_logit, rec_next, V, H, path_out, st);
-    case 4: return launch_hbuild_d<4>(s, rec_logit, rec_next, V, H, path_out, st);
-    case 5: return launch_hbuild_d<5>(s, rec_logit, rec_next, V, H, path_out, st);
-    case 6: return launch_hbuild_d<6>(s, rec_logit, rec_next, V, H, path_out, st);
-    case 7: return launch_hbuild_d<7>(s, rec_logit, rec_next, V, H, path_out, st);
-    case 8: return launch_hbuild_d<8>(s, rec_logit, rec_next, V, H, path_out, st);
+    case 1: return launch_hbuild_d<1>(s, rec_logit, rec_next, V, H, path_out, blocked, st);
+    case 2: return launch_hbuild_d<2>(s, rec_logit, rec_next, V, H, path_out, blocked, st);
+    case 3: return launch_hbuild_d<3>(s, rec_logit, rec_next, V, H, path_out, blocked, st);
+    case 4: return launch_hbuild_d<4>(s, rec_logit, rec_next, V, H, path_out, blocked, st);
+    case 5: return launch_hbuild_d<5>(s, rec_logit, rec_next, V, H, path_out, blocked, st);
+    case 6: return launch_hbuild_d<6>(s, rec_logit, rec_next, V, H, path_out, blocked, st);
+    case 7: return launch_hbuild_d<7>(s, rec_logit, rec_next, V, H, path_out, blocked, st);
+    case 8: return launch_hbuild_d<8>(s, rec_logit, rec_next, V, H, path_out, blocked, st);
     default: return hipErrorInvalidValue;  // the dense path covers D+1 <= 8 only
   }
 }

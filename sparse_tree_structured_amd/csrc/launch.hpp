@@ -77,10 +77,11 @@ bool project_mfma_supported(const Dims& s);
 hipError_t launch_project_mfma(const Dims& s, const void* H, const void* Wout, void* y,
                                hipStream_t st);
 
-// Multi-stage direct-to-LDS projection (W_out in its own [K][d] layout).
+// Multi-stage direct-to-LDS projection (W_out in its own [K][d] layout; H
+// row-major, or K-blocked as launch_hbuild writes it with `h_blocked`).
 bool project_direct_supported(const Dims& s);
 hipError_t launch_project_direct(const Dims& s, const void* H, const void* Wout, void* y,
-                                 hipStream_t st);
+                                 bool h_blocked, hipStream_t st);
 
 // ---- prefill routing (bf16) ----
 // Dense evaluation of tree levels 0..L-1 (L <= 8) with the walk over them:
@@ -91,9 +92,13 @@ hipError_t launch_route_top(const Dims& s, int L, int stride, const void* x, con
                             const void* b, float* rec_logit, int32_t* rec_next, hipStream_t st);
 // H and path_out need the whole path's records (L = D+1 levels, stride D+1).
 bool hbuild_supported(const Dims& s);
-// H and path_out from fully routed records (L = D+1).
+// H and path_out from fully routed records (L = D+1).  H row-major
+// [T][K], or, with `blocked` (K % 32 == 0), K-blocked: element (t, k) at
+// ((k / 32) * T + t) * 32 + k % 32, so that the 32-column K slice of a
+// token tile is contiguous for the projection.
 hipError_t launch_hbuild(const Dims& s, const float* rec_logit, const int32_t* rec_next,
-                         const void* V, void* H, int32_t* path_out, hipStream_t st);
+                         const void* V, void* H, int32_t* path_out, bool blocked,
+                         hipStream_t st);
 
 // Deep levels k..D per token tile (bf16; D-k <= 3, 1 <= k <= 5): for each
 // token and tree, the 16-node block of its own level-k subtree on the matrix

@@ -238,14 +238,14 @@ __device__ __forceinline__ void dma16_asm(const void* g, const unsigned char* ld
 template <class C, int ROWS, class RowPtr>
 __device__ __forceinline__ void direct_load_rows_asm(unsigned char* lds, int base,
                                                      const RowPtr& row_ptr, int k0, int wave,
-                                                     int lane) {
+                                                     int lane, int64_t kmul) {
   constexpr int kLoads = ROWS / 16 / C::kWaves;
 #pragma unroll
   for (int j = 0; j < kLoads; ++j) {
     const int r0 = (wave * kLoads + j) * 16;
     const int r = r0 + (lane >> 2);
     const int chunk = (lane & 3) ^ lds_swz(r);
-    dma16_asm(row_ptr(r) + k0 + chunk * 8, lds + base + r0 * C::kRowBytes);
+    dma16_asm(row_ptr(r) + k0 * kmul + chunk * 8, lds + base + r0 * C::kRowBytes);
   }
 }
 
@@ -387,9 +387,11 @@ __device__ __forceinline__ void stage_barrier() {
   asm volatile("" ::: "memory");
 }
 
-// Full K loop (K % 32 == 0).  a_row(i), i < BM, returns a K-contiguous row
-// start (already clamped to valid memory); bop stages and reads the B
-// operand (RowsB or KMajorBOp).
+// Full K loop (K % 32 == 0).  a_row(i), i < BM, returns the start of A row
+// i (already clamped to valid memory), whose K step k0 begins k0 * a_kmul
+// elements further (1 for K-contiguous rows; with the asm copies only, the
+// row count for K-blocked rows, where each 32-wide K slice of every row is
+// contiguous); bop stages and reads the B operand (RowsB or KMajorBOp).
 //
 // Schedule of iteration ks (stage buffer ks % S):
 //   read fragments (ks, kk=1)            -- LDS reads overlap the MFMAs below
@@ -402,7 +404,8 @@ __device__ __forceinline__ void stage_barrier() {
 template <class C, class ARow, class BOp>
 __device__ __forceinline__ void gemm_mainloop_direct_op(f32x16_t (&acc)[C::kTm][C::kTn],
                                                         unsigned char* lds, int K,
-                                                        const ARow& a_row, const BOp& bop) {
+                                                        const ARow& a_row, const BOp& bop,
+                                                        int64_t a_kmul = 1) {
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = tid / kWave;
@@ -416,7 +419,7 @@ __device__ __forceinline__ void gemm_mainloop_direct_op(f32x16_t (&acc)[C::kTm][
   auto issue = [&](int ks) {
     const int base = (ks % S) * C::kStageBytes;
     if constexpr (BOp::kAsmDma)
-      direct_load_rows_asm<C, C::BM>(lds, base, a_row, ks * C::BK, wave, lane);
+      direct_load_rows_asm<C, C::BM>(lds, base, a_row, ks * C::BK, wave, lane, a_kmul);
     else
       direct_load_rows<C, C::BM>(lds, base, a_row, ks * C::BK, wave, lane);
     bop.issue(lds, base + C::BM * C::kRowBytes, ks * C::BK, wave, lane);
