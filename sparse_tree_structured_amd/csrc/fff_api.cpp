@@ -150,6 +150,8 @@ fff_status_t resolve_plan(const Dims& s, const fff_plan_t* in, fff_plan_t* out,
 struct Layout {
   size_t logits = 0, leaf = 0, perm = 0, offs = 0, cnt = 0, H = 0;  // offsets
   bool tile = false;  // deep levels through the token-tile kernel (records of all D+1 levels)
+  bool split = false;  // token-tile plan whose dense levels run as two K halves
+  size_t part = 0;     // their fp32 logits (split only)
   size_t total = 0;
 };
 
@@ -183,6 +185,9 @@ Layout layout_for(const Dims& s, const fff_plan_t& p) {
   if (deep) off = align_up(off + fff::bucket_count_bytes(s, p.split_level, p.chunk_tokens));
   L.H = off;
   off = align_up(off + size_t(s.T) * size_t(s.K) * s.esize);
+  L.split = tile && fff::route_top_split_wanted(s, p.split_level);
+  L.part = off;
+  if (L.split) off = align_up(off + fff::route_top_split_bytes(s, p.split_level));
   L.total = off;
   return L;
 }
@@ -258,6 +263,18 @@ fff_status_t run_route(const Dims& s, const fff_plan_t& p, const Layout& L, cons
   fff_status_t r;
   if (p.algo == FFF_ALGO_PREFILL) {
     const int k = p.split_level;
+    if (L.split) {
+      // Dense levels as two K halves; the token-tile kernel walks them.
+      float* part = reinterpret_cast<float*>(ws + L.part);
+      e = fff::launch_route_top_split(s, k, x, W, part, st);
+      if (e != hipSuccess) return FFF_ERROR_HIP;
+      if ((r = record(E.top, st)) != FFF_SUCCESS) return r;
+      e = fff::launch_subtree(s, k, x, W, b, logits, leaf, part,
+                              fff::route_top_split_cols(s, k), st);
+      if (e != hipSuccess) return FFF_ERROR_HIP;
+      if ((r = record(E.deep, st)) != FFF_SUCCESS) return r;
+      return hip_status(fff::launch_hbuild(s, logits, leaf, V, H, path_out, blocked, st));
+    }
     e = fff::launch_route_top(s, k, L.tile ? s.D + 1 : k, x, W, b, logits, leaf, st);
     if (e != hipSuccess) return FFF_ERROR_HIP;
     if ((r = record(E.top, st)) != FFF_SUCCESS) return r;
@@ -266,7 +283,7 @@ fff_status_t run_route(const Dims& s, const fff_plan_t& p, const Layout& L, cons
       return hip_status(fff::launch_hbuild(s, logits, leaf, V, H, path_out, blocked, st));
     }
     if (L.tile) {
-      e = fff::launch_subtree(s, k, x, W, b, logits, leaf, st);
+      e = fff::launch_subtree(s, k, x, W, b, logits, leaf, nullptr, 0, st);
       if (e != hipSuccess) return FFF_ERROR_HIP;
       if ((r = record(E.deep, st)) != FFF_SUCCESS) return r;
       return hip_status(fff::launch_hbuild(s, logits, leaf, V, H, path_out, blocked, st));

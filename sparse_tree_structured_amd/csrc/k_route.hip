@@ -259,6 +259,69 @@ __global__ __launch_bounds__(C::kThreads) void route_top_direct_kernel(
                        stride, N, m0, n0, pv);
 }
 
+// The same product split in two halves of K, for shapes whose few column
+// tiles leave too few token tiles to fill the chip (the top three levels of
+// 32 trees are one 256-column tile): each workgroup reads half of x's row
+// tile and half of the node rows, so the node rows, which every token tile
+// needs, are streamed from L2 half as often per workgroup.  No walk here:
+// the raw fp32 logits of each half go to part[(half * ncols + col) * T + t]
+// (token-fastest, ncols = tiles_n * BN), and the token-tile kernel that
+// takes the deep levels sums the halves, adds the bias and walks.  Logical
+// tiles are half-major, so the workgroups of one XCD share one half of the
+// node rows in its L2.
+template <class C>
+__global__ __launch_bounds__(C::kThreads) void route_top_part_kernel(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ W, float* __restrict__ part,
+    int T, int d, int P, int L, int64_t N, int tiles_m, int tiles_n) {
+  extern __shared__ __align__(16) unsigned char lds[];
+  const int logical = xcd_logical_tile(blockIdx.x, gridDim.x);
+  const int per = tiles_m * tiles_n;
+  const int half = logical / per;
+  const int rem = logical - half * per;
+  const int tn = rem % tiles_n;
+  const int tm = rem / tiles_n;
+  const int m0 = tm * C::BM;
+  const int n0 = tn * C::BN;
+  const int cmask = (1 << L) - 1;
+  const int kh = d / 2;
+  const int64_t k0 = static_cast<int64_t>(half) * kh;
+  auto a_row = [&](int i) {
+    const int r = m0 + i < T ? m0 + i : T - 1;
+    return x + static_cast<size_t>(r) * d + k0;
+  };
+  auto b_row = [&](int j) {
+    const int gc = n0 + j;
+    const int p = gc >> L;
+    const int n = gc & cmask;
+    const bool used = p < P && n < cmask;
+    return W + (used ? (static_cast<int64_t>(p) * N + n) * d : 0) + k0;
+  };
+  f32x16_t acc[C::kTm][C::kTn];
+  gemm_mainloop_direct<C>(acc, lds, kh, a_row, b_row);
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x / kWave;
+  const int wm = wave / C::kWavesN;
+  const int wn = wave % C::kWavesN;
+  const int ncols = tiles_n * C::BN;
+  float* out = part + static_cast<int64_t>(half) * ncols * T;
+  // Lane l holds token row (block row + l % 32) and columns
+  // 8 (r / 4) + 4 (l / 32) + r % 4: a store instruction writes 32
+  // consecutive tokens of two columns.
+#pragma unroll
+  for (int i = 0; i < C::kTm; ++i) {
+    const int t = m0 + wm * C::WM + i * 32 + (lane & 31);
+    if (t < T) {
+#pragma unroll
+      for (int j = 0; j < C::kTn; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int col = n0 + wn * C::WN + j * 32 + 8 * (r / 4) + 4 * (lane >> 5) + (r % 4);
+          out[static_cast<int64_t>(col) * T + t] = acc[i][j][r];
+        }
+    }
+  }
+}
+
 // H for fully routed paths (L = D+1).  One workgroup per (tile of kHbTok
 // tokens, tree p): the tree's v rows are staged in LDS once (widened to fp32
 // when they fit in 32 KB, else kept bf16) and reused by every token of the
@@ -500,6 +563,38 @@ hipError_t launch_prune_pack(const void* W, const int32_t* colmap, void* packed,
   if (rows <= 0) return hipSuccess;
   prune_pack_kernel<<<dim3(rows), dim3(256), 0, st>>>(static_cast<const uint16_t*>(W), colmap,
                                                       static_cast<uint16_t*>(packed), d);
+  return hipGetLastError();
+}
+
+// The split form is taken for unpruned token-tile plans (the deep kernel
+// walks the top levels) when 128-token tiles alone give fewer than 256
+// workgroups and the two K halves at least 256.
+bool route_top_split_wanted(const Dims& s, int L) {
+  if (s.prune || s.dtype != 1 || s.d % 64 != 0 || (1 << L) > TopDirect128::BN) return false;
+  const int64_t tiles = (s.T + TopDirect128::BM - 1) / TopDirect128::BM * top_col_tiles(s, L);
+  return tiles < 256 && 2 * tiles >= 256;
+}
+
+size_t route_top_split_bytes(const Dims& s, int L) {
+  return size_t(2) * size_t(top_col_tiles(s, L)) * TopDirect128::BN * size_t(s.T) * 4;
+}
+
+int route_top_split_cols(const Dims& s, int L) { return top_col_tiles(s, L) * TopDirect128::BN; }
+
+hipError_t launch_route_top_split(const Dims& s, int L, const void* x, const void* W,
+                                  float* part, hipStream_t st) {
+  using C = TopDirect128;
+  const int tiles_m = static_cast<int>((s.T + C::BM - 1) / C::BM);
+  const int tiles_n = top_col_tiles(s, L);
+  auto kern = route_top_part_kernel<C>;
+  {
+    const hipError_t e =
+        ensure_lds_limit(reinterpret_cast<const void*>(kern), static_cast<int>(C::kLdsBytes));
+    if (e != hipSuccess) return e;
+  }
+  kern<<<dim3(2 * tiles_m * tiles_n), dim3(C::kThreads), C::kLdsBytes, st>>>(
+      static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(W), part,
+      static_cast<int>(s.T), s.d, s.P, L, s.N, tiles_m, tiles_n);
   return hipGetLastError();
 }
 

@@ -136,8 +136,8 @@ template <class C, int SL>
 __global__ __launch_bounds__(C::kThreads, 1) void subtree_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ W, const uint16_t* __restrict__ b,
     float* __restrict__ rec_logit, int32_t* __restrict__ rec_next,
-    const uint8_t* __restrict__ alive, int T, int d, int P, int D, int k, int64_t N,
-    int tree_groups) {
+    const uint8_t* __restrict__ alive, const float* __restrict__ part, int ncols, int T, int d,
+    int P, int D, int k, int64_t N, int tree_groups) {
   extern __shared__ __align__(16) unsigned char lds[];
   constexpr int M = C::M, G = C::G, S = C::S;
   const int tid = threadIdx.x;
@@ -175,6 +175,10 @@ __global__ __launch_bounds__(C::kThreads, 1) void subtree_kernel(
     return W + (static_cast<int64_t>(p) * N + sub_global(first_sub + s, jj)) * d;
   };
   const int nk = d / 32;
+  // Stage 0's loads do not depend on the grouping: issued first, so that
+  // they are in flight together with the grouping's own reads.
+  direct_load_rows_s<C, M, kSwz>(lds, C::kOffX, x_row, 0, wave, lane);
+  direct_load_rows_s<C, C::R, kSwz>(lds, C::kOffW, w_row, 0, wave, lane);
 
   // ---- grouping: per tree, the tile's tokens by level-k node ----
   // One thread per token of the tile (M <= threads).  For every tree of the
@@ -185,11 +189,54 @@ __global__ __launch_bounds__(C::kThreads, 1) void subtree_kernel(
   const int t = t0 + tid;
   const bool tok_ok = tid < M && t < T;
   int sub[G];
+  if (part) {
+    // Levels 0..k-1 from the dense product's two K halves (column p*S + n
+    // of tree p's node n, token-fastest: part[(half*ncols + col)*T + t]):
+    // logits summed, bias added and walked here, as the dense product's own
+    // epilogue does otherwise; their records written beside levels k..D.
+    float tb[G][S];  // top nodes' biases (the same for every token)
 #pragma unroll
-  for (int tl = 0; tl < G; ++tl)
-    sub[tl] = tok_ok && p0 + tl < P
-                  ? rec_next[static_cast<int64_t>(p0 + tl) * T + t] - static_cast<int>(first_sub)
-                  : -1;
+    for (int tl = 0; tl < G; ++tl)
+#pragma unroll
+      for (int n = 0; n < S; ++n) {
+        const int p = p0 + tl < P ? p0 + tl : P - 1;
+        tb[tl][n] = n < S - 1 ? bf16_to_f32(b[static_cast<int64_t>(p) * N + n]) : 0.0f;
+      }
+    float lg[G][S];
+    const int tt = tok_ok ? t : 0;
+#pragma unroll
+    for (int tl = 0; tl < G; ++tl)
+#pragma unroll
+      for (int n = 0; n < S; ++n) {
+        const int p = p0 + tl < P ? p0 + tl : P - 1;
+        const int64_t c = static_cast<int64_t>(p) * S + n;
+        lg[tl][n] = part[c * T + tt] + part[(ncols + c) * T + tt];
+      }
+#pragma unroll
+    for (int tl = 0; tl < G; ++tl) {
+      sub[tl] = -1;
+      if (tok_ok && p0 + tl < P) {
+        float* out = rec_logit + (static_cast<int64_t>(p0 + tl) * T + t) * (D + 1);
+        int n = 0;
+#pragma unroll
+        for (int lv = 0; lv < __builtin_ctz(S); ++lv) {  // S = 2^k
+          float a = 0.0f;
+#pragma unroll
+          for (int j = 0; j < S - 1; ++j)
+            if (j == n) a = lg[tl][j] + tb[tl][j];
+          out[lv] = a;
+          n = 2 * n + 1 + go_right(a);
+        }
+        sub[tl] = n - static_cast<int>(first_sub);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int tl = 0; tl < G; ++tl)
+      sub[tl] = tok_ok && p0 + tl < P
+                    ? rec_next[static_cast<int64_t>(p0 + tl) * T + t] - static_cast<int>(first_sub)
+                    : -1;
+  }
   for (int i = tid; i < G * C::kSlots; i += C::kThreads) perm[i] = -1;
   for (int i = tid; i < G * C::kChunks * C::kKeys; i += C::kThreads) wcnt[i] = 0;
   for (int i = tid; i < G * S * 16; i += C::kThreads) {
@@ -304,13 +351,12 @@ __global__ __launch_bounds__(C::kThreads, 1) void subtree_kernel(
 
   // ---- main loop: two stages, one barrier per K step ----
   // Iteration ks issues the loads of stage ks+1 into buffer (ks+1) % 2, then
-  // works on stage ks; iteration -1 only issues stage 0.  Each wave-wide
-  // load fills 16 rows of 64 bytes, chunks XOR-swizzled by row bits 1-2.
-  for (int ks = -1; ks < nk; ++ks) {
-    if (ks >= 0) {
-      wait_vmcnt<0>();   // this wave's loads of stage ks have landed
-      stage_barrier();   // everyone's have; everyone is done with stage ks-1
-    }
+  // works on stage ks (stage 0 was issued before the grouping).  Each
+  // wave-wide load fills 16 rows of 64 bytes, chunks XOR-swizzled by row
+  // bits 1-2.
+  for (int ks = 0; ks < nk; ++ks) {
+    wait_vmcnt<0>();   // this wave's loads of stage ks have landed
+    stage_barrier();   // everyone's have; everyone is done with stage ks-1
     if (ks + 1 < nk) {
       const int buf = (ks + 1) & 1;
       direct_load_rows_s<C, M, kSwz>(lds, C::kOffX + buf * C::kXBytes, x_row, (ks + 1) * 32, wave,
@@ -318,7 +364,6 @@ __global__ __launch_bounds__(C::kThreads, 1) void subtree_kernel(
       direct_load_rows_s<C, C::R, kSwz>(lds, C::kOffW + buf * C::kWBytes, w_row, (ks + 1) * 32,
                                         wave, lane);
     }
-    if (ks < 0) continue;
     const unsigned char* xs = lds + C::kOffX + (ks & 1) * C::kXBytes;
     const unsigned char* ws = lds + C::kOffW + (ks & 1) * C::kWBytes;
 #pragma unroll
@@ -401,7 +446,8 @@ template <> struct SubPick<32> { using C = Cfg<512, 1, 32>; };
 
 template <int S, int SL>
 hipError_t launch_sub(const Dims& s, int k, const void* x, const void* W, const void* b,
-                      float* rec_logit, int32_t* rec_next, hipStream_t st) {
+                      float* rec_logit, int32_t* rec_next, const float* part, int ncols,
+                      hipStream_t st) {
   using C = typename SubPick<S>::C;
   auto kern = subtree_kernel<C, SL>;
   {
@@ -415,18 +461,19 @@ hipError_t launch_sub(const Dims& s, int k, const void* x, const void* W, const 
   kern<<<dim3(static_cast<unsigned>(blocks)), dim3(C::kThreads), C::kLds, st>>>(
       static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(W),
       static_cast<const uint16_t*>(b), rec_logit, rec_next, s.prune ? s.prune->alive : nullptr,
-      static_cast<int>(s.T), s.d, s.P, s.D, k, s.N, tree_groups);
+      part, ncols, static_cast<int>(s.T), s.d, s.P, s.D, k, s.N, tree_groups);
   return hipGetLastError();
 }
 
 template <int S>
 hipError_t launch_sub_s(const Dims& s, int k, const void* x, const void* W, const void* b,
-                        float* rec_logit, int32_t* rec_next, hipStream_t st) {
+                        float* rec_logit, int32_t* rec_next, const float* part, int ncols,
+                        hipStream_t st) {
   switch (s.D - k + 1) {
-    case 1: return launch_sub<S, 1>(s, k, x, W, b, rec_logit, rec_next, st);
-    case 2: return launch_sub<S, 2>(s, k, x, W, b, rec_logit, rec_next, st);
-    case 3: return launch_sub<S, 3>(s, k, x, W, b, rec_logit, rec_next, st);
-    case 4: return launch_sub<S, 4>(s, k, x, W, b, rec_logit, rec_next, st);
+    case 1: return launch_sub<S, 1>(s, k, x, W, b, rec_logit, rec_next, part, ncols, st);
+    case 2: return launch_sub<S, 2>(s, k, x, W, b, rec_logit, rec_next, part, ncols, st);
+    case 3: return launch_sub<S, 3>(s, k, x, W, b, rec_logit, rec_next, part, ncols, st);
+    case 4: return launch_sub<S, 4>(s, k, x, W, b, rec_logit, rec_next, part, ncols, st);
     default: return hipErrorInvalidValue;
   }
 }
@@ -441,13 +488,14 @@ bool subtree_supported(const Dims& s, int k) {
 }
 
 hipError_t launch_subtree(const Dims& s, int k, const void* x, const void* W, const void* b,
-                          float* rec_logit, int32_t* rec_next, hipStream_t st) {
+                          float* rec_logit, int32_t* rec_next, const float* part, int ncols,
+                          hipStream_t st) {
   switch (k) {
-    case 1: return launch_sub_s<2>(s, k, x, W, b, rec_logit, rec_next, st);
-    case 2: return launch_sub_s<4>(s, k, x, W, b, rec_logit, rec_next, st);
-    case 3: return launch_sub_s<8>(s, k, x, W, b, rec_logit, rec_next, st);
-    case 4: return launch_sub_s<16>(s, k, x, W, b, rec_logit, rec_next, st);
-    case 5: return launch_sub_s<32>(s, k, x, W, b, rec_logit, rec_next, st);
+    case 1: return launch_sub_s<2>(s, k, x, W, b, rec_logit, rec_next, part, ncols, st);
+    case 2: return launch_sub_s<4>(s, k, x, W, b, rec_logit, rec_next, part, ncols, st);
+    case 3: return launch_sub_s<8>(s, k, x, W, b, rec_logit, rec_next, part, ncols, st);
+    case 4: return launch_sub_s<16>(s, k, x, W, b, rec_logit, rec_next, part, ncols, st);
+    case 5: return launch_sub_s<32>(s, k, x, W, b, rec_logit, rec_next, part, ncols, st);
     default: return hipErrorInvalidValue;
   }
 }

@@ -100,12 +100,26 @@ hipError_t launch_hbuild(const Dims& s, const float* rec_logit, const int32_t* r
                          const void* V, void* H, int32_t* path_out, bool blocked,
                          hipStream_t st);
 
+// Dense levels 0..L-1 as two K halves of raw fp32 logits, for the
+// token-tile plans of shapes with few column tiles (no walk: the token-tile
+// kernel below takes the halves).  part holds route_top_split_bytes():
+// part[(half * ncols + col) * T + t], ncols = route_top_split_cols().
+bool route_top_split_wanted(const Dims& s, int L);
+size_t route_top_split_bytes(const Dims& s, int L);
+int route_top_split_cols(const Dims& s, int L);
+hipError_t launch_route_top_split(const Dims& s, int L, const void* x, const void* W,
+                                  float* part, hipStream_t st);
+
 // Deep levels k..D per token tile (bf16; D-k <= 3, 1 <= k <= 5): for each
 // token and tree, the 16-node block of its own level-k subtree on the matrix
 // cores; completes rec_logit (levels k..D, stride D+1) and rec_next (leaf).
+// With `part` (launch_route_top_split's halves, ncols columns) it first
+// sums, biases and walks levels 0..k-1 itself and records them too; else it
+// starts from rec_next (the level-k node).
 bool subtree_supported(const Dims& s, int k);
 hipError_t launch_subtree(const Dims& s, int k, const void* x, const void* W, const void* b,
-                          float* rec_logit, int32_t* rec_next, hipStream_t st);
+                          float* rec_logit, int32_t* rec_next, const float* part, int ncols,
+                          hipStream_t st);
 
 // Deep levels k..D per token bucket (bf16; D-k <= 3).
 bool deep_supported(const Dims& s, int k);

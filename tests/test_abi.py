@@ -369,8 +369,16 @@ def test_token_tile_plans():
     s = _shape(T=T, d=d, P=P, D=6, h=h)
     r = fff.resolve_plan(s, fff.make_plan("prefill", 3, 0))
     assert (r.split_level, r.chunk_tokens) == (3, 0)
-    expect = up(T * P * 7 * 4) + up(T * P * 4) + up(T * P * h * 2)
+    # ... plus, at this shape (one 256-column tile of top-level columns, 128
+    # token tiles of 128), the two K halves of the dense levels' fp32 logits.
+    expect = up(T * P * 7 * 4) + up(T * P * 4) + up(T * P * h * 2) + up(2 * 256 * T * 4)
     assert fff.workspace_size(s, r) == expect
+    # Half the tokens: 64 token tiles, two halves still under 256 workgroups,
+    # so the dense levels keep their own walk and no halves are stored.
+    s2 = _shape(T=T // 2, d=d, P=P, D=6, h=h)
+    r2 = fff.resolve_plan(s2, fff.make_plan("prefill", 3, 0))
+    assert fff.workspace_size(s2, r2) == (up(T // 2 * P * 7 * 4) + up(T // 2 * P * 4) +
+                                          up(T // 2 * P * h * 2))
     r = fff.resolve_plan(s, fff.make_plan("prefill", 3, 4096))
     assert (r.split_level, r.chunk_tokens) == (3, 4096)
     # k = 6 > 5 at depth 6: bucketed
