@@ -138,7 +138,8 @@ __device__ __forceinline__ void gemm_mainloop(f32x16_t (&acc)[C::kTm][C::kTn], u
 }
 
 // ---------------------------------------------------------------------------
-// Direct-to-LDS main loop (both operands K-contiguous).
+// Direct-to-LDS main loop (A rows K-contiguous; B as K-contiguous rows of
+// the output columns, or k-major: KMajorBOp below).
 //
 // Each K step of 32 lives in one of kStages LDS buffers; the buffers are
 // filled with global_load_lds_dwordx4 (16 bytes per lane straight into LDS,
