@@ -90,11 +90,18 @@ KERNEL_SOURCES = {
 
 
 def kernel_source_hash(kernel: str):
+    """Hash of a kernel's device sources with comments and blank lines
+    dropped, so that editing a comment does not retire its counter figures."""
+    import re
+
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "sparse_tree_structured_amd", "csrc")
     for f in KERNEL_SOURCES[kernel]:
-        with open(os.path.join(csrc, f), "rb") as fh:
-            h.update(f.encode() + fh.read())
+        with open(os.path.join(csrc, f)) as fh:
+            text = fh.read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        code = [ln.split("//", 1)[0].rstrip() for ln in text.splitlines()]
+        h.update(f.encode() + "\n".join(ln for ln in code if ln).encode())
     return h.hexdigest()[:16]
 
 
