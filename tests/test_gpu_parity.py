@@ -74,13 +74,14 @@ def test_shape_sweep(shape):
 
 
 @needs_gpu
-@pytest.mark.parametrize("T", [16420, 32640])
-def test_split_top_levels(T):
+@pytest.mark.parametrize("T,P", [(16420, 32), (32640, 32), (16420, 30)])
+def test_split_top_levels(T, P):
     # Depth 6 takes the token-tile plan (k = 3); with one 256-column tile of
     # top-level columns and 129 or 255 token tiles of 128, the dense levels
     # run as two K halves that the token-tile kernel sums and walks.  T =
-    # 16420 leaves 36 tokens in the last tile.
-    inp = workloads.random_inputs(T, 256, 32, 6, 64, "bf16", seed=5, unit_rms_x=True)
+    # 16420 leaves 36 tokens in the last tile; P = 30 leaves the last group
+    # of four trees two short.
+    inp = workloads.random_inputs(T, 256, P, 6, 64, "bf16", seed=5, unit_rms_x=True)
     y, path = run(inp)
     check(inp, y, path)
 
