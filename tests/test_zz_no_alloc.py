@@ -19,12 +19,15 @@ CASES = [
     # T first, T second, d, P, D, h, algo
     ((64, 7), 2048, 32, 6, 128, "decode"),     # the decode workload's shape
     ((300, 100), 256, 8, 6, 128, "prefill"),   # every level dense, a ragged tile
+    # the direct-to-LDS projection on K-blocked H, then (1000 tokens: too few
+    # output tiles) the register-staged one on row-major H in the same region
+    ((4096, 1000), 1024, 8, 6, 64, "prefill"),
     ((200, 50), 96, 3, 4, 24, "generic"),
 ]
 
 
 @needs_gpu
-@pytest.mark.parametrize("case", CASES, ids=[c[-1] for c in CASES])
+@pytest.mark.parametrize("case", CASES, ids=[f"{c[-1]}-T{c[0][0]}" for c in CASES])
 def test_static_matches_workspace_forward(case):
     Ts, d, P, D, h, algo = case
     big = workloads.random_inputs(Ts[0], d, P, D, h, "bf16", seed=70 + D, unit_rms_x=True)
