@@ -333,7 +333,7 @@ fff_status_t fff_forward_pruned(const fff_shape_t *shape, const fff_plan_t *plan
  *   FFF-post  s = sum over the path of a v_n,      ds = GELU'(s) * dH_p,
  *             da = ds . v_n,                        dV_n += a ds
  *   db_n += da,  dW_n += da x_t,  dx_t += da w_n,   dW_out = H^T dy
- * (GELU' of the tanh form).  Not for pruned trees.
+ * (GELU' of the tanh form).  Pruned trees: fff_backward_pruned, below.
  *
  *   dy        [T,d] dtype (device)
  *   dx        [T,d] dtype out
@@ -354,6 +354,29 @@ fff_status_t fff_backward(const fff_shape_t *shape, const fff_plan_t *plan, cons
                           const void *W_out, const void *dy, void *dx, float *dW_node,
                           float *db_node, float *dV_node, float *dW_out, void *workspace,
                           size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * fff_backward on pruned trees (paper page, Figure 4: paths removed
+ * permanently): the same gradients with every token's paths as
+ * fff_forward_pruned takes them, a routed step into a subtree with no alive
+ * leaf going to the sibling.  Only visited nodes receive gradient (explainer
+ * page, section 3.B), so every pruned node's dW_node, db_node and dV_node
+ * come out 0.  Arguments, layouts, ownership and error codes as for
+ * fff_backward, plus the table fff_prune_prepare built for these trees (one
+ * prepared for another P, D or d is FFF_ERROR_INVALID_VALUE).  Plans: GENERIC
+ * takes any table; PREFILL needs a table prepared with every level dense
+ * (plan PREFILL, split_level D + 1), FFF_ERROR_NOT_SUPPORTED otherwise; AUTO
+ * picks PREFILL when the shape and the table allow it.  Workspace:
+ * fff_backward_pruned_workspace_size with the same plan and table.
+ */
+fff_status_t fff_backward_pruned_workspace_size(const fff_shape_t *shape, const fff_plan_t *plan,
+                                                const fff_pruning_t *pruning, size_t *bytes);
+fff_status_t fff_backward_pruned(const fff_shape_t *shape, const fff_plan_t *plan,
+                                 const fff_pruning_t *pruning, const void *x, const void *W_node,
+                                 const void *b_node, const void *V_node, const void *W_out,
+                                 const void *dy, void *dx, float *dW_node, float *db_node,
+                                 float *dV_node, float *dW_out, void *workspace,
+                                 size_t workspace_bytes, hipStream_t stream);
 
 /*
  * Allocation-free forward, for callers that cannot allocate device memory

@@ -75,7 +75,8 @@ EXPORTS = ("fff_plan_default", "fff_plan_resolve", "fff_workspace_size", "fff_fo
            "fff_route", "fff_project", "fff_project_workspace_size", "fff_project_ws",
            "fff_status_string", "fff_algo_name",
            "fff_prune_table_size", "fff_prune_prepare", "fff_forward_pruned",
-           "fff_backward_workspace_size", "fff_backward", "fff_forward_static")
+           "fff_backward_workspace_size", "fff_backward", "fff_forward_static",
+           "fff_backward_pruned_workspace_size", "fff_backward_pruned")
 STATIC_SCRATCH_BYTES = 32 << 20  # FFF_STATIC_SCRATCH_BYTES
 
 _lib: Optional[ctypes.CDLL] = None
@@ -109,6 +110,9 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
                                        ctypes.POINTER(StageEvents)]
     lib.fff_backward_workspace_size.argtypes = [SP, PP, ctypes.POINTER(sz)]
     lib.fff_backward.argtypes = [SP, PP, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.fff_backward_pruned_workspace_size.argtypes = [SP, PP, PrP, ctypes.POINTER(sz)]
+    lib.fff_backward_pruned.argtypes = [SP, PP, PrP, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                        vp, sz, vp]
     lib.fff_forward_static.argtypes = [SP, PP, vp, vp, vp, vp, vp, vp, vp, vp,
                                        ctypes.POINTER(StageEvents)]
     lib.fff_status_string.argtypes = [ctypes.c_int]
@@ -472,10 +476,35 @@ def backward_workspace_size(shape: Shape, plan: Optional[Plan] = None) -> int:
     return int(n.value)
 
 
+def backward_pruned_workspace_size(shape: Shape, plan: Optional[Plan], pruning: Pruning) -> int:
+    n = ctypes.c_size_t()
+    st = load_library().fff_backward_pruned_workspace_size(
+        ctypes.byref(shape), ctypes.byref(plan) if plan is not None else None,
+        ctypes.byref(pruning), ctypes.byref(n))
+    if st != SUCCESS:
+        raise FFFError(st, "fff_backward_pruned_workspace_size")
+    return int(n.value)
+
+
 def backward(x, W_node, b_node, V_node, W_out, dy, *, algo=ALGO_AUTO, split_level: int = -1,
              workspace=None, out=None, stream=None, variant=VARIANT_FFF):
     """Gradients of sum(y * dy) with the forward's paths held fixed.  Returns
     a dict: dx (dtype of x), dW_node, db_node, dV_node, dW_out (float32)."""
+    return _backward(x, W_node, b_node, V_node, W_out, dy, None, algo, split_level, workspace,
+                     out, stream, variant)
+
+
+def backward_pruned(x, W_node, b_node, V_node, W_out, dy, pruning: Pruning, *, algo=ALGO_AUTO,
+                    split_level: int = -1, workspace=None, out=None, stream=None,
+                    variant=VARIANT_FFF):
+    """fff_backward_pruned: the gradients of backward() with the paths
+    fff_forward_pruned takes on the prepared table."""
+    return _backward(x, W_node, b_node, V_node, W_out, dy, pruning, algo, split_level, workspace,
+                     out, stream, variant)
+
+
+def _backward(x, W_node, b_node, V_node, W_out, dy, pruning, algo, split_level, workspace, out,
+              stream, variant):
     torch = _torch()
     shape = shape_of(x, W_node, V_node, variant)
     N = (1 << (shape.D + 1)) - 1
@@ -493,7 +522,8 @@ def backward(x, W_node, b_node, V_node, W_out, dy, *, algo=ALGO_AUTO, split_leve
             _check([out[k]], dt, x.device)
     plan = make_plan(algo, split_level, 0)
     if workspace is None:
-        n = backward_workspace_size(shape, plan)
+        n = (backward_workspace_size(shape, plan) if pruning is None
+             else backward_pruned_workspace_size(shape, plan, pruning))
         workspace = torch.empty(max(n, 1), dtype=torch.uint8, device=x.device)
     nbytes = workspace.numel() * workspace.element_size()
     f32 = dict(dtype=torch.float32, device=x.device)
@@ -501,11 +531,18 @@ def backward(x, W_node, b_node, V_node, W_out, dy, *, algo=ALGO_AUTO, split_leve
                 "db_node": torch.empty(b_node.shape, **f32),
                 "dV_node": torch.empty(V_node.shape, **f32),
                 "dW_out": torch.empty(W_out.shape, **f32)}
-    st = load_library().fff_backward(
-        ctypes.byref(shape), ctypes.byref(plan), x.data_ptr(), W_node.data_ptr(), b_node.data_ptr(),
-        V_node.data_ptr(), W_out.data_ptr(), dy.data_ptr(), g["dx"].data_ptr(),
-        g["dW_node"].data_ptr(), g["db_node"].data_ptr(), g["dV_node"].data_ptr(),
-        g["dW_out"].data_ptr(), workspace.data_ptr(), nbytes, _stream_handle(stream))
+    ptrs = (x.data_ptr(), W_node.data_ptr(), b_node.data_ptr(), V_node.data_ptr(),
+            W_out.data_ptr(), dy.data_ptr(), g["dx"].data_ptr(), g["dW_node"].data_ptr(),
+            g["db_node"].data_ptr(), g["dV_node"].data_ptr(), g["dW_out"].data_ptr(),
+            workspace.data_ptr(), nbytes, _stream_handle(stream))
+    lib = load_library()
+    if pruning is None:
+        st = lib.fff_backward(ctypes.byref(shape), ctypes.byref(plan), *ptrs)
+        what = "fff_backward"
+    else:
+        st = lib.fff_backward_pruned(ctypes.byref(shape), ctypes.byref(plan),
+                                     ctypes.byref(pruning), *ptrs)
+        what = "fff_backward_pruned"
     if st != SUCCESS:
-        raise FFFError(st, "fff_backward")
+        raise FFFError(st, what)
     return g

@@ -379,20 +379,26 @@ fff_status_t forward_impl(const Dims& s, const fff_plan_t& p, const void* x, con
 
 bool bwd_mfma_fits(const Dims& s) { return fff::backward_mfma_supported(s); }
 
-fff_status_t resolve_bwd_plan(const Dims& s, const fff_plan_t* in, fff_plan_t* out) {
+// A pruned backward (pruning non-null) runs on the matrix cores only with a
+// table whose dense levels are all D + 1 levels: its routing is the dense
+// product over the packed alive rows.
+fff_status_t resolve_bwd_plan(const Dims& s, const fff_plan_t* in, fff_plan_t* out,
+                              const fff_pruning_t* pruning = nullptr) {
   fff_plan_t p;
   p.algo = in ? in->algo : FFF_ALGO_AUTO;
   p.split_level = in ? in->split_level : -1;
   p.chunk_tokens = 0;
   p.flags = in ? in->flags : 0;
   if (p.flags & ~kPlanFlags) return FFF_ERROR_INVALID_VALUE;
-  if (p.algo == FFF_ALGO_AUTO) p.algo = bwd_mfma_fits(s) ? FFF_ALGO_PREFILL : FFF_ALGO_GENERIC;
+  const bool table_ok = !pruning || pruning->split_level == s.D + 1;
+  if (p.algo == FFF_ALGO_AUTO)
+    p.algo = bwd_mfma_fits(s) && table_ok ? FFF_ALGO_PREFILL : FFF_ALGO_GENERIC;
   switch (p.algo) {
     case FFF_ALGO_GENERIC:
       p.split_level = 0;
       break;
     case FFF_ALGO_PREFILL:
-      if (!bwd_mfma_fits(s) || (p.split_level >= 0 && p.split_level != s.D + 1))
+      if (!bwd_mfma_fits(s) || !table_ok || (p.split_level >= 0 && p.split_level != s.D + 1))
         return FFF_ERROR_NOT_SUPPORTED;
       p.split_level = s.D + 1;
       break;
@@ -433,6 +439,72 @@ BwdLayout bwd_layout(const Dims& s, const fff_plan_t& p) {
   return B;
 }
 
+// The device views of a prepared pruning table, after checking that it was
+// prepared for this shape's trees.
+fff_status_t prune_view(const Dims& s, const fff_pruning_t* pruning, fff::PruneView* pv) {
+  if (!pruning || !pruning->table || !aligned(pruning->table, kWsAlign) || pruning->P != s.P ||
+      pruning->D != s.D || pruning->d != s.d || pruning->split_level < 0 ||
+      pruning->split_level > 8 || pruning->col_tiles < 0 || pruning->col_tiles > s.P)
+    return FFF_ERROR_INVALID_VALUE;
+  const PruneLayout PL = prune_layout(s, pruning->split_level);
+  const char* tb = static_cast<const char*>(pruning->table);
+  *pv = fff::PruneView{};
+  pv->alive = reinterpret_cast<const uint8_t*>(tb + PL.alive);
+  if (pruning->split_level > 0) {
+    pv->tree_base = reinterpret_cast<const int32_t*>(tb + PL.tree_base);
+    pv->tile_first = reinterpret_cast<const int32_t*>(tb + PL.tile_first);
+    pv->tile_count = reinterpret_cast<const int32_t*>(tb + PL.tile_count);
+    pv->colmap = reinterpret_cast<const int32_t*>(tb + PL.colmap);
+    pv->colinfo = reinterpret_cast<const uint32_t*>(tb + PL.colinfo);
+    pv->W_packed = reinterpret_cast<const uint16_t*>(tb + PL.packed);
+  }
+  pv->L = pruning->split_level;
+  pv->col_tiles = pruning->col_tiles;
+  return FFF_SUCCESS;
+}
+
+// The backward pass for a validated shape (s.prune set for pruned trees)
+// and resolved plan.
+fff_status_t backward_impl(const Dims& s, const fff_plan_t& p, const void* x, const void* W_node,
+                           const void* b_node, const void* V_node, const void* W_out,
+                           const void* dy, void* dx, float* dW_node, float* db_node,
+                           float* dV_node, float* dW_out, void* workspace,
+                           size_t workspace_bytes, hipStream_t stream) {
+  if (!dW_node || !db_node || !dV_node || !dW_out || !aligned(dW_node, 16) ||
+      !aligned(db_node, 4) || !aligned(dV_node, 16) || !aligned(dW_out, 16))
+    return FFF_ERROR_INVALID_VALUE;
+  const int64_t nW = int64_t(s.P) * s.N * s.d, nb = int64_t(s.P) * s.N;
+  const int64_t nV = int64_t(s.P) * s.N * s.h, nO = s.K * s.d;
+  if (s.T == 0) {  // no token: every gradient is zero
+    if (fff::launch_fill_f32(dW_node, nW, stream) != hipSuccess ||
+        fff::launch_fill_f32(db_node, nb, stream) != hipSuccess ||
+        fff::launch_fill_f32(dV_node, nV, stream) != hipSuccess ||
+        fff::launch_fill_f32(dW_out, nO, stream) != hipSuccess)
+      return FFF_ERROR_HIP;
+    return FFF_SUCCESS;
+  }
+  fff_status_t st = check_inputs(s, x, W_node, b_node, V_node);
+  if (st != FFF_SUCCESS) return st;
+  if (!W_out || !dy || !dx || !aligned(W_out, 16) || !aligned(dy, 16) || !aligned(dx, 16))
+    return FFF_ERROR_INVALID_VALUE;
+  const BwdLayout B = bwd_layout(s, p);
+  if (!workspace || workspace_bytes < B.total) return FFF_ERROR_WORKSPACE;
+  if (!aligned(workspace, kWsAlign)) return FFF_ERROR_INVALID_VALUE;
+  if (p.algo == FFF_ALGO_PREFILL)
+    return hip_status(fff::launch_backward_mfma(s, x, W_node, b_node, V_node, W_out, dy, dx,
+                                                dW_node, db_node, dV_node, dW_out, workspace,
+                                                stream));
+  char* ws = static_cast<char*>(workspace);
+  float* logits = reinterpret_cast<float*>(ws + B.logits);
+  int32_t* leaf = reinterpret_cast<int32_t*>(ws + B.leaf);
+  if (fff::launch_route_generic(s, x, W_node, b_node, logits, nullptr, leaf, stream) != hipSuccess)
+    return FFF_ERROR_HIP;
+  return hip_status(fff::launch_backward_generic(
+      s, x, W_node, V_node, W_out, dy, dx, dW_node, db_node, dV_node, dW_out, logits, leaf,
+      reinterpret_cast<float*>(ws + B.dH), reinterpret_cast<float*>(ws + B.H),
+      reinterpret_cast<float*>(ws + B.dxacc), stream));
+}
+
 }  // namespace
 
 extern "C" {
@@ -461,39 +533,44 @@ fff_status_t fff_backward(const fff_shape_t* shape, const fff_plan_t* plan, cons
   fff_plan_t p;
   st = resolve_bwd_plan(s, plan, &p);
   if (st != FFF_SUCCESS) return st;
-  if (!dW_node || !db_node || !dV_node || !dW_out || !aligned(dW_node, 16) ||
-      !aligned(db_node, 4) || !aligned(dV_node, 16) || !aligned(dW_out, 16))
-    return FFF_ERROR_INVALID_VALUE;
-  const int64_t nW = int64_t(s.P) * s.N * s.d, nb = int64_t(s.P) * s.N;
-  const int64_t nV = int64_t(s.P) * s.N * s.h, nO = s.K * s.d;
-  if (s.T == 0) {  // no token: every gradient is zero
-    if (fff::launch_fill_f32(dW_node, nW, stream) != hipSuccess ||
-        fff::launch_fill_f32(db_node, nb, stream) != hipSuccess ||
-        fff::launch_fill_f32(dV_node, nV, stream) != hipSuccess ||
-        fff::launch_fill_f32(dW_out, nO, stream) != hipSuccess)
-      return FFF_ERROR_HIP;
-    return FFF_SUCCESS;
-  }
-  st = check_inputs(s, x, W_node, b_node, V_node);
+  return backward_impl(s, p, x, W_node, b_node, V_node, W_out, dy, dx, dW_node, db_node, dV_node,
+                       dW_out, workspace, workspace_bytes, stream);
+}
+
+fff_status_t fff_backward_pruned_workspace_size(const fff_shape_t* shape, const fff_plan_t* plan,
+                                                const fff_pruning_t* pruning, size_t* bytes) {
+  Dims s;
+  fff_status_t st = check_shape(shape, &s);
   if (st != FFF_SUCCESS) return st;
-  if (!W_out || !dy || !dx || !aligned(W_out, 16) || !aligned(dy, 16) || !aligned(dx, 16))
-    return FFF_ERROR_INVALID_VALUE;
-  const BwdLayout B = bwd_layout(s, p);
-  if (!workspace || workspace_bytes < B.total) return FFF_ERROR_WORKSPACE;
-  if (!aligned(workspace, kWsAlign)) return FFF_ERROR_INVALID_VALUE;
-  if (p.algo == FFF_ALGO_PREFILL)
-    return hip_status(fff::launch_backward_mfma(s, x, W_node, b_node, V_node, W_out, dy, dx,
-                                                dW_node, db_node, dV_node, dW_out, workspace,
-                                                stream));
-  char* ws = static_cast<char*>(workspace);
-  float* logits = reinterpret_cast<float*>(ws + B.logits);
-  int32_t* leaf = reinterpret_cast<int32_t*>(ws + B.leaf);
-  if (fff::launch_route_generic(s, x, W_node, b_node, logits, nullptr, leaf, stream) != hipSuccess)
-    return FFF_ERROR_HIP;
-  return hip_status(fff::launch_backward_generic(
-      s, x, W_node, V_node, W_out, dy, dx, dW_node, db_node, dV_node, dW_out, logits, leaf,
-      reinterpret_cast<float*>(ws + B.dH), reinterpret_cast<float*>(ws + B.H),
-      reinterpret_cast<float*>(ws + B.dxacc), stream));
+  if (!bytes) return FFF_ERROR_INVALID_VALUE;
+  fff::PruneView pv;
+  st = prune_view(s, pruning, &pv);
+  if (st != FFF_SUCCESS) return st;
+  fff_plan_t p;
+  st = resolve_bwd_plan(s, plan, &p, pruning);
+  if (st != FFF_SUCCESS) return st;
+  *bytes = bwd_layout(s, p).total;
+  return FFF_SUCCESS;
+}
+
+fff_status_t fff_backward_pruned(const fff_shape_t* shape, const fff_plan_t* plan,
+                                 const fff_pruning_t* pruning, const void* x, const void* W_node,
+                                 const void* b_node, const void* V_node, const void* W_out,
+                                 const void* dy, void* dx, float* dW_node, float* db_node,
+                                 float* dV_node, float* dW_out, void* workspace,
+                                 size_t workspace_bytes, hipStream_t stream) {
+  Dims s;
+  fff_status_t st = check_shape(shape, &s);
+  if (st != FFF_SUCCESS) return st;
+  fff::PruneView pv;
+  st = prune_view(s, pruning, &pv);
+  if (st != FFF_SUCCESS) return st;
+  fff_plan_t p;
+  st = resolve_bwd_plan(s, plan, &p, pruning);
+  if (st != FFF_SUCCESS) return st;
+  s.prune = &pv;
+  return backward_impl(s, p, x, W_node, b_node, V_node, W_out, dy, dx, dW_node, db_node, dV_node,
+                       dW_out, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"
@@ -670,29 +747,14 @@ fff_status_t fff_forward_pruned(const fff_shape_t* shape, const fff_plan_t* plan
   Dims s;
   fff_status_t st = check_shape(shape, &s);
   if (st != FFF_SUCCESS) return st;
-  if (!pruning || !pruning->table || !aligned(pruning->table, kWsAlign) || pruning->P != s.P ||
-      pruning->D != s.D || pruning->d != s.d || pruning->split_level < 0 ||
-      pruning->split_level > 8 || pruning->col_tiles < 0 || pruning->col_tiles > s.P)
-    return FFF_ERROR_INVALID_VALUE;
+  fff::PruneView pv;
+  st = prune_view(s, pruning, &pv);
+  if (st != FFF_SUCCESS) return st;
   fff_plan_t p;
   st = resolve_plan(s, plan, &p);
   if (st != FFF_SUCCESS) return st;
   if (p.algo == FFF_ALGO_PREFILL && p.split_level != pruning->split_level)
     return FFF_ERROR_NOT_SUPPORTED;
-  const PruneLayout PL = prune_layout(s, pruning->split_level);
-  const char* tb = static_cast<const char*>(pruning->table);
-  fff::PruneView pv{};
-  pv.alive = reinterpret_cast<const uint8_t*>(tb + PL.alive);
-  if (pruning->split_level > 0) {
-    pv.tree_base = reinterpret_cast<const int32_t*>(tb + PL.tree_base);
-    pv.tile_first = reinterpret_cast<const int32_t*>(tb + PL.tile_first);
-    pv.tile_count = reinterpret_cast<const int32_t*>(tb + PL.tile_count);
-    pv.colmap = reinterpret_cast<const int32_t*>(tb + PL.colmap);
-    pv.colinfo = reinterpret_cast<const uint32_t*>(tb + PL.colinfo);
-    pv.W_packed = reinterpret_cast<const uint16_t*>(tb + PL.packed);
-  }
-  pv.L = pruning->split_level;
-  pv.col_tiles = pruning->col_tiles;
   s.prune = &pv;
   return forward_impl(s, p, x, W_node, b_node, V_node, W_out, y, path_out, workspace,
                       workspace_bytes, stream, events);

@@ -297,6 +297,44 @@ def test_backward_plans_and_workspace():
         fff.backward_workspace_size(s, fff.make_plan("prefill", 4))
 
 
+def test_backward_pruned_plans_and_validation(lib):
+    s = _shape(T=16384, d=2048, P=32, D=6, h=128)
+    dense = dict(table=FAKE, P=32, D=6, d=2048, split_level=7, col_tiles=16)
+    tile = dict(dense, split_level=3, col_tiles=1)
+    # A table with every level packed: AUTO takes the matrix-core backward,
+    # whose workspace is the unpruned one's.
+    full = fff.backward_workspace_size(s)
+    assert fff.backward_pruned_workspace_size(s, None, fff.Pruning(**dense)) == full
+    assert fff.backward_pruned_workspace_size(s, fff.make_plan("prefill"),
+                                              fff.Pruning(**dense)) == full
+    # Any other table: AUTO takes the generic backward; PREFILL is refused.
+    generic = fff.backward_workspace_size(s, fff.make_plan("generic"))
+    assert generic != full
+    assert fff.backward_pruned_workspace_size(s, None, fff.Pruning(**tile)) == generic
+    with pytest.raises(fff.FFFError) as err:
+        fff.backward_pruned_workspace_size(s, fff.make_plan("prefill"), fff.Pruning(**tile))
+    assert err.value.status == fff.ERROR_NOT_SUPPORTED
+
+    def run(pr, pl=None, nbytes=1 << 40, ws=FAKE, outs=FAKE):
+        return lib.fff_backward_pruned(
+            ctypes.byref(s), ctypes.byref(pl) if pl else None,
+            ctypes.byref(pr) if pr is not None else None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+            FAKE, outs, outs, outs, outs, ws, nbytes, None)
+
+    assert run(None) == fff.ERROR_INVALID_VALUE
+    for bad in (dict(table=None), dict(table=FAKE + 8), dict(P=4), dict(D=5), dict(d=64),
+                dict(split_level=9), dict(col_tiles=33)):
+        assert run(fff.Pruning(**dict(dense, **bad))) == fff.ERROR_INVALID_VALUE, bad
+        assert lib.fff_backward_pruned_workspace_size(
+            ctypes.byref(s), None, ctypes.byref(fff.Pruning(**dict(dense, **bad))),
+            ctypes.byref(ctypes.c_size_t())) == fff.ERROR_INVALID_VALUE, bad
+    assert run(fff.Pruning(**tile), fff.make_plan("prefill")) == fff.ERROR_NOT_SUPPORTED
+    assert run(fff.Pruning(**dense), fff.make_plan("decode")) == fff.ERROR_NOT_SUPPORTED
+    assert run(fff.Pruning(**dense), outs=None) == fff.ERROR_INVALID_VALUE
+    assert run(fff.Pruning(**dense), nbytes=full - 1) == fff.ERROR_WORKSPACE
+    assert run(fff.Pruning(**dense), ws=FAKE + 16) == fff.ERROR_INVALID_VALUE
+
+
 @pytest.mark.parametrize("D,k,chunk,slices", [(8, 5, 8192, 8), (11, 8, 16384, 16)])
 def test_bucketed_plan_workspace(D, k, chunk, slices):
     # Bucketed plans carve per-(chunk, tree) offsets and per-(chunk, tree,

@@ -204,3 +204,125 @@ def test_backward_full_size_sampled(variant):
     assert (g["dx"][np.setdiff1d(np.arange(s.T), rows)] == 0).all()
     g["dx"] = g["dx"][rows]
     assert_grads("bf16", g, ref, f, dy64[rows], rec, variant)
+
+
+def random_leaf_mask(rng, P, D, frac):
+    """A seeded fraction of each tree's leaves pruned; every tree keeps one."""
+    m = (rng.random((P, 1 << D)) >= frac).astype(np.uint8)
+    m[np.arange(P), rng.integers(0, 1 << D, size=P)] = 1
+    return m
+
+
+def run_backward_pruned(inp, mask, algo="auto", table_algo="generic", table_split=-1,
+                        variant=0, seed=7):
+    """fff_backward_pruned on a table prepared for (table_algo, table_split),
+    and the paths fff_forward_pruned takes on it (generic plan)."""
+    T = to_device(inp)
+    s = inp.shape
+    dy_t, dy64 = make_dy(inp, seed)
+    dy_t = dy_t.to(T["x"].device)
+    print(f"[gpu] backward pruned {s} algo={algo} table={table_algo}/{table_split} "
+          f"alive={mask.mean():.2f} variant={variant}", flush=True)
+    pr, table = fff.prune_prepare(mask, T["W_node"], T["V_node"], algo=table_algo,
+                                  split_level=table_split, T=max(s.T, 65536), variant=variant)
+    g = fff.backward_pruned(T["x"], T["W_node"], T["b_node"], T["V_node"], T["W_out"], dy_t, pr,
+                            algo=algo, variant=variant)
+    _, path = fff.forward_pruned(T["x"], T["W_node"], T["b_node"], T["V_node"], T["W_out"], pr,
+                                 algo="generic", variant=variant)
+    torch.cuda.synchronize()
+    del table
+    return {k: to_f64(v) for k, v in g.items()}, path.cpu().numpy(), dy64
+
+
+def check_grads_pruned(inp, mask, g, path, dy64, variant=0):
+    f = inp.as_f64()
+    rec = oracle.forward(f["x"], f["W_node"], f["b_node"], f["V_node"], f["W_out"],
+                         want_y=False, want_records=True, variant=variant, leaf_alive=mask)
+    np.testing.assert_array_equal(path, rec["path"])
+    ref = oracle.backward(f["x"], f["W_node"], f["b_node"], f["V_node"], f["W_out"], dy64,
+                          variant=variant, leaf_alive=mask)
+    # Nodes no token visits (every pruned node among them) get exactly 0.
+    s = inp.shape
+    visited = np.zeros((s.P, (1 << (s.D + 1)) - 1), bool)
+    nodes = np.asarray(rec["rec_node"]).reshape(s.T, s.P, s.D + 1)
+    for p in range(s.P):
+        visited[p, np.unique(nodes[:, p, :])] = True
+    assert (g["db_node"][~visited] == 0).all()
+    assert (g["dW_node"][~visited] == 0).all()
+    assert (g["dV_node"][~visited] == 0).all()
+    return assert_grads(s.dtype, g, ref, f, dy64, rec, variant)
+
+
+PRUNED_GENERIC = [
+    # T, d, P, D, h, dtype, pruned fraction
+    (50, 37, 3, 3, 5, "f32", 0.5),
+    (129, 96, 5, 2, 24, "f32", 0.7),
+    (40, 64, 4, 4, 16, "bf16", 0.6),
+    (33, 128, 3, 6, 64, "bf16", 0.8),
+]
+
+
+@needs_gpu
+@pytest.mark.parametrize("variant", [0, 1])
+@pytest.mark.parametrize("case", PRUNED_GENERIC, ids=[str(c) for c in PRUNED_GENERIC])
+def test_backward_pruned_generic(case, variant):
+    T, d, P, D, h, dt, frac = case
+    inp = workloads.random_inputs(T, d, P, D, h, dt, seed=90 + D, unit_rms_x=True)
+    mask = random_leaf_mask(np.random.default_rng(5 + D), P, D, frac)
+    g, path, dy = run_backward_pruned(inp, mask, algo="generic", variant=variant)
+    check_grads_pruned(inp, mask, g, path, dy, variant=variant)
+
+
+PRUNED_MFMA = [
+    # T, d, P, D, h, pruned fraction  (bf16, every level dense)
+    (300, 256, 4, 6, 64, 0.5),
+    (1000, 128, 8, 2, 64, 0.5),
+    (500, 512, 2, 7, 64, 0.7),
+    (257, 256, 16, 5, 128, 0.3),
+    (700, 256, 8, 6, 128, 0.9),   # a few paths left, packed into fewer column tiles
+]
+
+
+@needs_gpu
+@pytest.mark.parametrize("variant", [0, 1])
+@pytest.mark.parametrize("case", PRUNED_MFMA, ids=[str(c) for c in PRUNED_MFMA])
+def test_backward_pruned_mfma(case, variant):
+    T, d, P, D, h, frac = case
+    inp = workloads.random_inputs(T, d, P, D, h, "bf16", seed=110 + D, unit_rms_x=True)
+    mask = random_leaf_mask(np.random.default_rng(9 + D), P, D, frac)
+    g, path, dy = run_backward_pruned(inp, mask, algo="prefill", table_algo="prefill",
+                                      table_split=D + 1, variant=variant)
+    check_grads_pruned(inp, mask, g, path, dy, variant=variant)
+
+
+@needs_gpu
+def test_backward_pruned_token_tile_table():
+    # A table prepared for the token-tile forward (split level 3 of 7) has
+    # no packed rows for every level: AUTO takes the generic backward, and a
+    # forced matrix-core plan is refused.
+    inp = workloads.random_inputs(400, 256, 3, 6, 64, "bf16", seed=131, unit_rms_x=True)
+    mask = random_leaf_mask(np.random.default_rng(13), 3, 6, 0.5)
+    g, path, dy = run_backward_pruned(inp, mask, algo="auto", table_algo="prefill",
+                                      table_split=3)
+    check_grads_pruned(inp, mask, g, path, dy)
+    T = to_device(inp)
+    pr, table = fff.prune_prepare(mask, T["W_node"], T["V_node"], algo="prefill", split_level=3,
+                                  T=65536)
+    with pytest.raises(fff.FFFError) as err:
+        fff.backward_pruned(T["x"], T["W_node"], T["b_node"], T["V_node"], T["W_out"],
+                            T["x"].clone(), pr, algo="prefill")
+    assert err.value.status == fff.ERROR_NOT_SUPPORTED
+    del table
+
+
+@needs_gpu
+def test_backward_pruned_all_alive_equals_unpruned():
+    # With every leaf alive the pruned backward is the unpruned one, bit for
+    # bit on the matrix-core plan's deterministic gradients.
+    inp = workloads.random_inputs(300, 256, 4, 6, 64, "bf16", seed=141, unit_rms_x=True)
+    mask = np.ones((4, 64), np.uint8)
+    g, _, _ = run_backward_pruned(inp, mask, algo="prefill", table_algo="prefill",
+                                  table_split=7)
+    g0, _, _ = run_backward(inp, algo="prefill")
+    for k in ("dx", "dW_node", "dV_node", "dW_out"):
+        np.testing.assert_array_equal(g[k], g0[k])
