@@ -39,11 +39,14 @@ def to_f64(t: torch.Tensor) -> np.ndarray:
     return t.detach().float().cpu().numpy().astype(np.float64)
 
 
-def run(inp, algo="auto", split_level=-1, dev="cuda:0", variant=0, chunk_tokens=0):
+def run(inp, algo="auto", split_level=-1, dev="cuda:0", variant=0, chunk_tokens=0,
+        plan_flags=0):
     T = to_device(inp, dev)
-    print(f"[gpu] forward {inp.shape} algo={algo} k={split_level} variant={variant}", flush=True)
+    print(f"[gpu] forward {inp.shape} algo={algo} k={split_level} variant={variant} "
+          f"flags={plan_flags}", flush=True)
     y, path = fff.forward(T["x"], T["W_node"], T["b_node"], T["V_node"], T["W_out"], algo=algo,
-                          split_level=split_level, chunk_tokens=chunk_tokens, variant=variant)
+                          split_level=split_level, chunk_tokens=chunk_tokens, variant=variant,
+                          plan_flags=plan_flags)
     torch.cuda.synchronize()
     return to_f64(y), path.cpu().numpy()
 

@@ -15,6 +15,7 @@ import torch
 
 import oracle
 import workloads
+import sparse_tree_structured_amd as fff
 from gpu_helpers import check, run, to_device, to_f64
 
 pytestmark = pytest.mark.gpu
@@ -241,16 +242,41 @@ DECODE_SHAPES = [
     (64, 1024, 16, 7, 64),
     (8, 128, 4, 2, 128),       # narrowest model width
     (12, 256, 8, 4, 192),      # trees straddling K-chunk boundaries
+    # T <= 8 and 4 <= D <= 7: one subtree item per level-(D-3) node
+    (1, 128, 64, 4, 8),        # one top level, narrowest rows
+    (6, 512, 8, 5, 64),        # two top levels, ragged T
+    (8, 2048, 32, 6, 128),     # the decode workload's layer, unskewed
+    (2, 1024, 16, 7, 64),      # four top levels: 256 items, the most that fit
+    (8, 2048, 32, 7, 64),      # 512 items would not fit: round items instead
+    (3, 256, 4, 6, 256),       # widest node output
+    (7, 256, 24, 6, 64),       # eight trees per K chunk
+    (4, 256, 8, 6, 192),       # trees straddling K-chunk boundaries
 ]
 
 
 @needs_gpu
+@pytest.mark.parametrize("rounds", [False, True], ids=["auto", "rounds"])
 @pytest.mark.parametrize("shape", DECODE_SHAPES, ids=[str(s) for s in DECODE_SHAPES])
-def test_decode_shapes(shape):
+def test_decode_shapes(shape, rounds):
     T, d, P, D, h = shape
     inp = workloads.random_inputs(T, d, P, D, h, "bf16", seed=5, unit_rms_x=True)
-    y, path = run(inp, algo="decode")
+    y, path = run(inp, algo="decode", plan_flags=fff.PLAN_DECODE_ROUNDS if rounds else 0)
     check(inp, y, path)
+
+
+@needs_gpu
+@pytest.mark.parametrize("variant", [0, 1])
+@pytest.mark.parametrize("name", ["decode_skew_t1", "decode_skew_t8"])
+def test_decode_subtree_items_match_rounds(name, variant):
+    # Both item kinds evaluate every visited node with the same operands and
+    # summation order, and add the GELU(a) v_n terms in level order: paths
+    # and y agree bit for bit.
+    inp = wl(name)
+    ys, ps = run(inp, algo="decode", variant=variant)
+    yr, pr = run(inp, algo="decode", variant=variant, plan_flags=fff.PLAN_DECODE_ROUNDS)
+    np.testing.assert_array_equal(ps, pr)
+    np.testing.assert_array_equal(ys, yr)
+    check(inp, ys, ps, variant=variant)
 
 
 @needs_gpu
