@@ -165,13 +165,6 @@ typedef struct fff_plan {
  * the DECODE notes above).  Other algorithms ignore it. */
 #define FFF_PLAN_TEST_DECODE_NO_PUBLISH 1
 
-/* DECODE walks every tree in rounds of dependent node evaluations even where
- * it would otherwise route by subtree items (T <= 8, 4 <= D <= 7: one
- * workgroup per level-(D-3) node of each tree evaluates the tree's top rows
- * and its own subtree's rows in one round trip).  Both forms give the same
- * paths and y; other algorithms ignore the flag. */
-#define FFF_PLAN_DECODE_ROUNDS 2
-
 /* Optional events recorded on `stream` at stage boundaries (each may be
  * NULL), in this order:
  *   start     before the first kernel

@@ -32,7 +32,6 @@ ALGO_DECODE = 3
 ALGOS = {"auto": ALGO_AUTO, "generic": ALGO_GENERIC, "prefill": ALGO_PREFILL, "decode": ALGO_DECODE}
 # fff_plan_t flags
 PLAN_TEST_DECODE_NO_PUBLISH = 1
-PLAN_DECODE_ROUNDS = 2
 # fff_variant_t
 VARIANT_FFF = 0
 VARIANT_POST = 1
@@ -284,8 +283,7 @@ def forward(x, W_node, b_node, V_node, W_out, *, algo=ALGO_AUTO, split_level: in
 
     ``variant`` "fff" (0) applies GELU to each visited node's logit; "post"
     (1) applies it to each element of a tree's summed output instead.
-    ``plan_flags``: fff_plan_t flags (PLAN_DECODE_ROUNDS; PLAN_TEST_DECODE_NO_PUBLISH, tests
-    only)."""
+    ``plan_flags``: fff_plan_t flags (PLAN_TEST_DECODE_NO_PUBLISH, tests only)."""
     torch = _torch()
     shape = shape_of(x, W_node, V_node, variant)
     _check_layer(shape, x, W_node, b_node, V_node, W_out, y=y, path_out=path_out,

@@ -17,8 +17,7 @@ using fff::Dims;
 
 constexpr int64_t kMaxElems = int64_t(1) << 40;
 constexpr size_t kWsAlign = 256;
-constexpr int32_t kPlanFlags =
-    FFF_PLAN_TEST_DECODE_NO_PUBLISH | FFF_PLAN_DECODE_ROUNDS;  // every defined plan flag
+constexpr int32_t kPlanFlags = FFF_PLAN_TEST_DECODE_NO_PUBLISH;  // every defined plan flag
 
 bool mul_ok(int64_t a, int64_t b, int64_t limit) { return a == 0 || b <= limit / a; }
 

@@ -119,8 +119,7 @@ struct DecodeArgs {
   int T, d, P, D, h, K;
   int64_t N;
   int n_route_wg, n_proj_wg;
-  int tok;               // tokens per routing item (<= kDecTok; round items)
-  int kt;                // > 0: subtree items (below), one per level-kt node of each tree
+  int tok;               // tokens per routing item (<= kDecTok)
   int post;              // 1: GELU on the summed h-vector instead of on each node's logit
   const uint8_t* alive;  // static pruning: [P][N] 1 = node alive; null = every node
 };
@@ -196,23 +195,7 @@ struct RouteLds {
   static constexpr size_t meta = rsm + kDecTok * 4 * 4;             // R, rl
   static constexpr size_t total = meta + 16;
 };
-// Subtree items: the tokens' rows (copied straight from x, row-major), the
-// partial logits of waves 1-3, the logits of both row blocks, their V rows,
-// the tree's alive flags, each token's visited rows and its leaf.
-constexpr int kSubTok = 8;  // most tokens of a subtree item
-struct SubLds {
-  static constexpr size_t x = 0;                                        // [T][d] bf16
-  static constexpr size_t part = x + size_t(kSubTok) * kMaxD * 2;       // [3][2][16][16] f32
-  static constexpr size_t lgs = part + 3 * 2 * 256 * 4;                 // [32 rows][16] f32
-  static constexpr size_t vc = lgs + 32 * 16 * 4;                       // [32 rows][h] bf16
-  static constexpr size_t alive = vc + 32 * size_t(kMaxH) * 2;          // [256] u8
-  static constexpr size_t rsm = alive + 256;                            // [tok][8] i32 row
-  static constexpr size_t leaf = rsm + kSubTok * 8 * 4;                 // [tok] i32
-  static constexpr size_t total = leaf + kSubTok * 4;
-};
-constexpr size_t kRouteMax = RouteLds::total > SubLds::total ? RouteLds::total : SubLds::total;
-constexpr size_t kDecLds = ProjLds::total > kRouteMax ? ProjLds::total : kRouteMax;
-static_assert(SubLds::total <= ProjLds::total, "subtree items fit the projection's LDS");
+constexpr size_t kDecLds = ProjLds::total > RouteLds::total ? ProjLds::total : RouteLds::total;
 
 // Adds one round's GELU(a) * v_n terms (a * v_n when `post`) to the thread's
 // H pieces (token m, eight columns c0..c0+7; piece i is thread + 256 i).  rsm
@@ -475,228 +458,9 @@ __device__ void route_item(const DecodeArgs& a, unsigned char* lds, int item, in
     __hip_atomic_store(a.done + item, e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Routing of subtree item (tree p, level-kt node 2^kt - 1 + sub) for all
-// T <= kSubTok tokens, published with epoch e.  The item evaluates two
-// 16-row blocks at once: the top rows (heap ids 0 .. 2^kt - 2, the same in
-// every item of the tree) and the rows of its own subtree (the D + 1 - kt
-// <= 4 levels below its node).  Every load (token rows, both blocks, their
-// V rows and biases, the alive flags) is issued at entry, so the walk needs
-// no further round trip.  The top block's logits come out bit-identical in
-// every item of a tree (same operands, same summation order), so the items
-// agree on the subtree each token enters, and exactly one item writes each
-// token's H slice and path_out.
-__device__ void route_sub_item(const DecodeArgs& a, unsigned char* lds, int item, int p, int sub,
-                               uint64_t e) {
-  const uint16_t* xs = reinterpret_cast<const uint16_t*>(lds + SubLds::x);
-  float* part = reinterpret_cast<float*>(lds + SubLds::part);
-  float* lgs = reinterpret_cast<float*>(lds + SubLds::lgs);
-  uint16_t* vc = reinterpret_cast<uint16_t*>(lds + SubLds::vc);
-  uint8_t* alive = lds + SubLds::alive;
-  int32_t* rsm = reinterpret_cast<int32_t*>(lds + SubLds::rsm);
-  int32_t* leaf_s = reinterpret_cast<int32_t*>(lds + SubLds::leaf);
-  const int tid = threadIdx.x;
-  const int lane = tid & (kWave - 1);
-  const int wave = tid / kWave;
-  const int j = lane & 15;  // row of a block (A) / token (B)
-  const int q = lane >> 4;  // 8-wide k group within each 32-wide step
-  const int T = a.T;
-  const int kt = a.kt;
-  const int klen = a.d / kDecWaves;
-  const int nsteps = klen / 32;  // <= 16
-  const int hc = a.h / 8;
-  const int R = (1 << kt) - 1;                  // top rows
-  const int S = (1 << (a.D + 1 - kt)) - 1;     // subtree rows
-  const int root = R + sub;                     // heap id of the subtree's node
-  const __amdgpu_buffer_rsrc_t wbuf =
-      buffer_of(a.W + static_cast<int64_t>(p) * a.N * a.d, uint32_t(a.N) * a.d * 2);
-  const __amdgpu_buffer_rsrc_t bbuf = buffer_of(a.b + static_cast<int64_t>(p) * a.N, uint32_t(a.N) * 2);
-  const __amdgpu_buffer_rsrc_t abuf =
-      buffer_of(a.alive ? static_cast<const void*>(a.alive + static_cast<int64_t>(p) * a.N)
-                        : static_cast<const void*>(a.x),
-                a.alive ? uint32_t(a.N) : 0);
-  __syncthreads();  // LDS of a previous item is no longer read
-
-  // Token rows [0, T) of x straight into LDS: wave-wide 1 KB copies of the
-  // contiguous T * d block.
-  {
-    const unsigned char* src = reinterpret_cast<const unsigned char*>(a.x);
-    const int total = T * a.d * 2;
-    for (int base = wave * 1024; base < total; base += kDecWaves * 1024)
-      if (base + lane * 16 < total)
-        __builtin_amdgcn_global_load_lds(src + base + lane * 16,
-                                         lds + SubLds::x + base, 16, 0, 0);
-  }
-  // Both row blocks' slices: block 0 row j is heap id j (j < R), block 1
-  // row j the subtree's local node j (j < S); other rows load zeros.
-  uint4 wf0[16], wf1[16];
-  {
-    const uint32_t koff = uint32_t(wave * klen + q * 8) * 2;
-    const uint32_t o0 = j < R ? uint32_t(j * a.d) * 2 + koff : kOob;
-    const uint32_t o1 = j < S ? uint32_t(sub_global(root, j) * a.d) * 2 + koff : kOob;
-#pragma unroll
-    for (int u = 0; u < 16; ++u) {
-      wf0[u] = buffer_load16(wbuf, u < nsteps && o0 != kOob ? o0 + u * 64 : kOob);
-      wf1[u] = buffer_load16(wbuf, u < nsteps && o1 != kOob ? o1 + u * 64 : kOob);
-    }
-  }
-  // V rows straight into LDS (rows 0-15 the top block, 16-31 the subtree):
-  // the top rows are contiguous in V, and so is each level of the subtree,
-  // in the same order as its LDS rows.  Wave w copies segment w and w + 4
-  // (the top rows, then levels 0..3 of the subtree).
-  {
-    const int rb = a.h * 2;  // bytes per row
-    const unsigned char* vsrc = reinterpret_cast<const unsigned char*>(
-        a.V + static_cast<int64_t>(p) * a.N * a.h);
-    const int sl = a.D + 1 - kt;
-    for (int sg = wave; sg <= sl; sg += kDecWaves) {
-      // Segment 0: top rows 0 .. R-1; segment 1 + l: subtree level l.
-      const int first = sg == 0 ? 0 : static_cast<int>(sub_global(root, (1 << (sg - 1)) - 1));
-      const int rows = sg == 0 ? R : 1 << (sg - 1);
-      const int lrow = sg == 0 ? 0 : 16 + (1 << (sg - 1)) - 1;
-      const int bytes = rows * rb;
-      for (int base = 0; base < bytes; base += 1024)
-        if (base + lane * 16 < bytes)
-          __builtin_amdgcn_global_load_lds(vsrc + first * rb + base + lane * 16,
-                                           lds + SubLds::vc + lrow * rb + base, 16, 0, 0);
-    }
-  }
-  // Raw bias bits of rows 4q .. 4q+3 of both blocks (wave 0).
-  uint16_t braw[2][4];
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int row = 4 * q + r;
-    braw[0][r] = buffer_load2(bbuf, wave == 0 && row < R ? uint32_t(row) * 2 : kOob);
-    braw[1][r] = buffer_load2(
-        bbuf, wave == 0 && row < S ? uint32_t(sub_global(root, row)) * 2 : kOob);
-  }
-  const uint8_t alive_raw = buffer_load1(abuf, tid < a.N ? uint32_t(tid) : kOob);
-  wait_vmcnt<0>();
-  if (tid < a.N) alive[tid] = a.alive ? alive_raw : 1;
-  __syncthreads();
-
-  // Token j's fragment at k step u (tokens past T repeat the last one; k
-  // steps past the width are not taken).
-  f32x4_t acc0 = {0.0f, 0.0f, 0.0f, 0.0f}, acc1 = {0.0f, 0.0f, 0.0f, 0.0f};
-  {
-    const uint16_t* xrow = xs + (j < T ? j : T - 1) * a.d + wave * klen + q * 8;
-    // Four k steps at a time: their LDS reads, then their products (the
-    // barrier keeps the compiler from holding all sixteen fragments).
-#pragma unroll
-    for (int u0 = 0; u0 < 16; u0 += 4) {
-      uint4 xv[4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u)
-        if (u0 + u < nsteps) xv[u] = *reinterpret_cast<const uint4*>(xrow + (u0 + u) * 32);
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        if (u0 + u < nsteps) {
-          acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(wf0[u0 + u]), as_bf16x8(xv[u]),
-                                                         acc0, 0, 0, 0);
-          acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(wf1[u0 + u]), as_bf16x8(xv[u]),
-                                                         acc1, 0, 0, 0);
-        }
-      }
-      __builtin_amdgcn_sched_barrier(0);
-    }
-  }
-  // acc_b[r]: this wave's partial logit of block b's row 4q + r for token j.
-  if (wave != 0) {
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      part[(((wave - 1) * 2 + 0) * 16 + 4 * q + r) * 16 + j] = acc0[r];
-      part[(((wave - 1) * 2 + 1) * 16 + 4 * q + r) * 16 + j] = acc1[r];
-    }
-  }
-  __syncthreads();
-  if (wave == 0) {
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int row = 4 * q + r;
-      lgs[row * 16 + j] = acc0[r] + part[((0 * 2 + 0) * 16 + row) * 16 + j] +
-                          part[((1 * 2 + 0) * 16 + row) * 16 + j] +
-                          part[((2 * 2 + 0) * 16 + row) * 16 + j] + bf16_to_f32(braw[0][r]);
-      lgs[(16 + row) * 16 + j] = acc1[r] + part[((0 * 2 + 1) * 16 + row) * 16 + j] +
-                                 part[((1 * 2 + 1) * 16 + row) * 16 + j] +
-                                 part[((2 * 2 + 1) * 16 + row) * 16 + j] + bf16_to_f32(braw[1][r]);
-    }
-  }
-  __syncthreads();
-
-  // Walk of token m (thread m): the top levels by the top block's logits,
-  // then, if it enters this item's subtree, the subtree's levels.  A step
-  // into a pruned child goes to its sibling.
-  if (tid < T) {
-    const int m = tid;
-    int n = 0;
-    for (int lv = 0; lv < kt; ++lv) {
-      rsm[m * 8 + lv] = n;
-      int c = 2 * n + 1 + go_right(lgs[n * 16 + m]);
-      if (!alive[c]) c = (c & 1) ? c + 1 : c - 1;
-      n = c;
-    }
-    int leaf = -1;
-    if (n == root) {
-      int i = 0;
-      for (int lv = 0;; ++lv) {
-        rsm[m * 8 + kt + lv] = 16 + i;
-        if (kt + lv == a.D) break;
-        const int g = static_cast<int>(sub_global(root, i));
-        int bit = go_right(lgs[(16 + i) * 16 + m]);
-        if (!alive[2 * g + 1 + bit]) bit ^= 1;
-        i = 2 * i + 1 + bit;
-      }
-      leaf = static_cast<int>(sub_global(root, i)) - ((1 << a.D) - 1);
-    }
-    leaf_s[m] = leaf;
-  }
-  __syncthreads();
-
-  // H slices of this item's tokens: the GELU(a) v_n terms of all D + 1
-  // visited rows (a v_n, then GELU of the sum, for FFF-post).
-  const __amdgpu_buffer_rsrc_t hbuf = buffer_of(a.H, uint32_t(a.T) * a.K * 2);
-  for (int e2 = tid; e2 < T * hc; e2 += kDecThreads) {
-    const int m = e2 / hc;
-    if (leaf_s[m] < 0) continue;
-    const int c0 = (e2 - m * hc) * 8;
-    float hacc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    for (int lv = 0; lv <= a.D; ++lv) {
-      const int row = rsm[m * 8 + lv];
-      const float lg = lgs[row * 16 + m];
-      const float g = a.post ? lg : gelu_tanh(lg);
-      const uint4 v = *reinterpret_cast<const uint4*>(vc + row * a.h + c0);
-      hacc[0] += g * bf16lo(v.x);
-      hacc[1] += g * bf16hi(v.x);
-      hacc[2] += g * bf16lo(v.y);
-      hacc[3] += g * bf16hi(v.y);
-      hacc[4] += g * bf16lo(v.z);
-      hacc[5] += g * bf16hi(v.z);
-      hacc[6] += g * bf16lo(v.w);
-      hacc[7] += g * bf16hi(v.w);
-    }
-    if (a.post) {
-#pragma unroll
-      for (int u = 0; u < 8; ++u) hacc[u] = gelu_tanh(hacc[u]);
-    }
-    coherent_store16(hbuf, uint32_t(m * a.K + p * a.h + c0) * 2,
-                     make_uint4(pack_bf16x2(hacc[0], hacc[1]), pack_bf16x2(hacc[2], hacc[3]),
-                                pack_bf16x2(hacc[4], hacc[5]), pack_bf16x2(hacc[6], hacc[7])));
-  }
-  if (a.path_out && tid < T && leaf_s[tid] >= 0)
-    a.path_out[static_cast<int64_t>(tid) * a.P + p] = leaf_s[tid];
-
-  // Publish the item once every thread's stores have completed.
-  wait_vmcnt<0>();
-  __syncthreads();
-  if (tid == 0 && a.publish)
-    __hip_atomic_store(a.done + item, e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
 // W_out block (K chunk kc, column slice cs) into LDS as wt[n][k].  A thread
 // takes 4(k) x 8(n) pieces (four 16-byte row loads, byte permutes, eight
-// 8-byte LDS writes); eight lanes cover one 128-byte row segment.  PACED:
-// one piece per thread at a time (below); else every piece's loads are
-// issued at once.
-template <bool PACED>
+// 8-byte LDS writes); eight lanes cover one 128-byte row segment.
 __device__ void load_wout_block(const DecodeArgs& a, unsigned char* lds, int kc, int cs) {
   uint16_t* wt = reinterpret_cast<uint16_t*>(lds + ProjLds::wt);
   constexpr int kNb = kColSlice / 8;
@@ -704,18 +468,19 @@ __device__ void load_wout_block(const DecodeArgs& a, unsigned char* lds, int kc,
   constexpr int kPer = kPieces / kDecThreads;
   static_assert(kPieces % kDecThreads == 0, "pieces split evenly");
   const __amdgpu_buffer_rsrc_t obuf = buffer_of(a.Wout, uint32_t(a.K) * a.d * 2);
-  auto load = [&](int u, uint4 (&r)[4]) {
+  // One piece per thread at a time: the blocks of all projection
+  // workgroups together are the whole of W_out, and issuing them in
+  // batches keeps the memory queues short for the routing loads (measured:
+  // with all batches in flight at once, every routing round waits behind
+  // the W_out stream and the layer takes about 1.3 us longer).
+  for (int u = 0; u < kPer; ++u) {
     const int c = threadIdx.x + u * kDecThreads;
     const int nb = c % kNb;
     const int kb = c / kNb;
+    uint4 r[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
       r[i] = buffer_load16(obuf, uint32_t((kc * kKc + kb * 4 + i) * a.d + cs * kColSlice + nb * 8) * 2);
-  };
-  auto store = [&](int u, const uint4 (&r)[4]) {
-    const int c = threadIdx.x + u * kDecThreads;
-    const int nb = c % kNb;
-    const int kb = c / kNb;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const uint2 even = make_uint2(pack_lo(word(r[0], q), word(r[1], q)),
@@ -725,27 +490,9 @@ __device__ void load_wout_block(const DecodeArgs& a, unsigned char* lds, int kc,
       *reinterpret_cast<uint2*>(wt + (nb * 8 + 2 * q) * kWtPitch + kb * 4) = even;
       *reinterpret_cast<uint2*>(wt + (nb * 8 + 2 * q + 1) * kWtPitch + kb * 4) = odd;
     }
-  };
-  if constexpr (PACED) {
-    // The blocks of all projection workgroups together are the whole of
-    // W_out, and issuing them in batches keeps the memory queues short for
-    // the round items' dependent loads (measured: with all batches in
-    // flight at once, every routing round waits behind the W_out stream
-    // and the layer takes about 1.3 us longer).
-    for (int u = 0; u < kPer; ++u) {
-      uint4 r[4];
-      load(u, r);
-      store(u, r);
-      // Keeps the compiler from hoisting the next batch's loads above these
-      // stores (it would otherwise issue all of them at once).
-      __builtin_amdgcn_sched_barrier(0);
-    }
-  } else {
-    uint4 r[kPer][4];
-#pragma unroll
-    for (int u = 0; u < kPer; ++u) load(u, r[u]);
-#pragma unroll
-    for (int u = 0; u < kPer; ++u) store(u, r[u]);
+    // Keeps the compiler from hoisting the next batch's loads above these
+    // stores (it would otherwise issue all of them at once).
+    __builtin_amdgcn_sched_barrier(0);
   }
 }
 
@@ -819,13 +566,10 @@ __device__ void nan_slice(const DecodeArgs& a, int cs) {
   }
 }
 
-// SUB: the routing workgroups take subtree items (a.kt > 0), else round
-// items; one instantiation per kind keeps each within the register budget.
-template <bool SUB>
 __global__ __launch_bounds__(kDecThreads, 2) void decode_kernel(DecodeArgs a) {
   extern __shared__ __align__(16) unsigned char lds[];
   __shared__ int last, waited;
-  const int per_tree = a.kt ? (1 << a.kt) : (a.T + a.tok - 1) / a.tok;
+  const int per_tree = (a.T + a.tok - 1) / a.tok;
   const int nroute = a.P * per_tree;
   const int g = blockIdx.x;
   const int nkc = a.K / kKc;
@@ -854,20 +598,9 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_kernel(DecodeArgs a) {
   if (g < a.n_route_wg) {
     if (poisoned) return;
     for (int it = g; it < nroute; it += a.n_route_wg) {
-      if constexpr (SUB) {
-        // Workgroups go to the 8 XCDs in turn by block id: the items of a
-        // tree (consecutive ids) share one XCD, and so its L2 copy of the
-        // tree's top rows, when every item has a workgroup of its own.
-        const int item = nroute % 8 == 0 && a.n_route_wg == nroute
-                             ? (it % 8) * (nroute / 8) + it / 8
-                             : it;
-        const int p = item / per_tree;
-        route_sub_item(a, lds, item, p, item - p * per_tree, e);
-      } else {
-        const int p = it / per_tree;
-        const int t0 = (it - p * per_tree) * a.tok;
-        route_item(a, lds, it, p, t0, min(a.tok, a.T - t0), e);
-      }
+      const int p = it / per_tree;
+      const int t0 = (it - p * per_tree) * a.tok;
+      route_item(a, lds, it, p, t0, min(a.tok, a.T - t0), e);
     }
     return;
   }
@@ -881,9 +614,7 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_kernel(DecodeArgs a) {
       continue;
     }
     __syncthreads();  // LDS of a previous item is no longer read
-    // Subtree items load everything they need in one round trip, so the
-    // W_out stream is not paced for them.
-    load_wout_block<!SUB>(a, lds, kc, cs);
+    load_wout_block(a, lds, kc, cs);
     if (threadIdx.x < kWave) {
       // Routing items (consecutive ids) of the trees whose columns overlap
       // this K chunk.
@@ -940,7 +671,7 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_kernel(DecodeArgs a) {
 }
 
 struct DeviceInfo {
-  int cus = 0, per_cu[2] = {0, 0};  // per instantiation: round items, subtree items
+  int cus = 0, per_cu = 0;
   bool ready = false;
 };
 
@@ -993,25 +724,8 @@ static int tokens_per_item(const Dims& s) {
   return kDecTok;
 }
 
-// Subtree items: the top levels 0 .. kt-1 of every tree (kt = D - 3) and
-// the last four levels under one level-kt node per item, for T <= 8 and
-// 4 <= D <= 7, where both blocks have at most 15 rows.  0 where they do not
-// apply.  They are taken at launch when the items fit half of the grid.
-static int subtree_top_levels(const Dims& s) {
-  if (s.T > kSubTok || s.D < 4 || s.D > 7) return 0;
-  return s.D - 3;
-}
-
-// Publication slots: enough for either kind of routing item.
-static size_t routing_items(const Dims& s) {
-  size_t items = size_t(s.P) * ((s.T + tokens_per_item(s) - 1) / tokens_per_item(s));
-  const int kt = subtree_top_levels(s);
-  if (kt) items = std::max(items, size_t(s.P) << kt);
-  return items;
-}
-
 size_t decode_workspace(const Dims& s) {
-  const size_t items = routing_items(s);
+  const size_t items = size_t(s.P) * ((s.T + tokens_per_item(s) - 1) / tokens_per_item(s));
   return 256 + up256(items * 8) + up256(size_t(s.T) * s.K * 2) +
          up256(size_t(s.d / kColSlice) * (s.K / kKc) * 8) + up256(size_t(s.K / kKc) * s.T * s.d * 4);
 }
@@ -1028,11 +742,12 @@ hipError_t launch_decode(const Dims& s, const void* x, const void* W, const void
   a.y = static_cast<uint16_t*>(y);
   a.path_out = path_out;
   a.tok = tokens_per_item(s);
+  const int nroute = s.P * static_cast<int>((s.T + a.tok - 1) / a.tok);
   char* w = static_cast<char*>(ws);
   a.hdr = reinterpret_cast<uint64_t*>(w);
   w += 256;
   a.done = reinterpret_cast<uint64_t*>(w);
-  w += up256(routing_items(s) * 8);
+  w += up256(size_t(nroute) * 8);
   a.H = reinterpret_cast<uint16_t*>(w);
   w += up256(size_t(s.T) * s.K * 2);
   a.arrive = reinterpret_cast<uint64_t*>(w);
@@ -1056,31 +771,18 @@ hipError_t launch_decode(const Dims& s, const void* x, const void* W, const void
   if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
   DeviceInfo& di = info[dev];
   if (!di.ready) {
-    e = hipDeviceGetAttribute(&di.cus, hipDeviceAttributeMultiprocessorCount, dev);
-    int k = 0;
-    for (const void* f : {reinterpret_cast<const void*>(decode_kernel<false>),
-                          reinterpret_cast<const void*>(decode_kernel<true>)}) {
-      if (e == hipSuccess)
-        e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, int(kDecLds));
-      if (e == hipSuccess)
-        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&di.per_cu[k], f, kDecThreads, kDecLds);
-      ++k;
-    }
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(decode_kernel),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, int(kDecLds));
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&di.cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e == hipSuccess)
+      e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&di.per_cu, decode_kernel, kDecThreads, kDecLds);
     if (e != hipSuccess) return e;
-    if (di.cus < 1 || di.per_cu[0] < 1 || di.per_cu[1] < 1) return hipErrorInvalidConfiguration;
+    if (di.cus < 1 || di.per_cu < 1) return hipErrorInvalidConfiguration;
     di.ready = true;
   }
-  // Grid no larger than what the device holds at once (the smaller of the
-  // two instantiations' limits, so that the choice below does not depend on
-  // it); items beyond it are looped over.  Routing gets at most half of the
-  // slots.
-  const int cap = di.cus * std::min(di.per_cu[0], di.per_cu[1]);
-  // Subtree items where they apply and every item has a workgroup of its
-  // own (and not for FFF_PLAN_DECODE_ROUNDS); else round items.
-  a.kt = subtree_top_levels(s);
-  if ((flags & FFF_PLAN_DECODE_ROUNDS) || (int64_t(s.P) << a.kt) > cap / 2) a.kt = 0;
-  const int nroute =
-      a.kt ? (s.P << a.kt) : s.P * static_cast<int>((s.T + a.tok - 1) / a.tok);
+  // Grid no larger than what the device holds at once; items beyond it are
+  // looped over.  Routing gets at most half of the slots.
+  const int cap = di.cus * di.per_cu;
   const int nproj = static_cast<int>(s.K / kKc) * (s.d / kColSlice);
   a.n_route_wg = nroute < cap / 2 ? nroute : cap / 2;
   a.n_proj_wg = nproj < cap - a.n_route_wg ? nproj : cap - a.n_route_wg;
@@ -1094,12 +796,8 @@ hipError_t launch_decode(const Dims& s, const void* x, const void* W, const void
   const bool test_no_publish = (flags & FFF_PLAN_TEST_DECODE_NO_PUBLISH) != 0;
   a.publish = test_no_publish ? 0 : 1;
   a.spin_limit = test_no_publish ? kTestSpinLimit : kSpinLimit;
-  if (a.kt)
-    hipLaunchKernelGGL(decode_kernel<true>, dim3(a.n_route_wg + a.n_proj_wg), dim3(kDecThreads),
-                       kDecLds, st, a);
-  else
-    hipLaunchKernelGGL(decode_kernel<false>, dim3(a.n_route_wg + a.n_proj_wg), dim3(kDecThreads),
-                       kDecLds, st, a);
+  hipLaunchKernelGGL(decode_kernel, dim3(a.n_route_wg + a.n_proj_wg), dim3(kDecThreads), kDecLds,
+                     st, a);
   return hipGetLastError();
 }
 

@@ -141,14 +141,12 @@ def test_plans(lib):
     assert _forward(lib, _shape(dtype=fff.DTYPE_F32), plan=bad) == fff.ERROR_NOT_SUPPORTED
     assert _forward(lib, _shape(d=72), plan=bad) == fff.ERROR_NOT_SUPPORTED
     assert _forward(lib, _shape(), plan=fff.make_plan(9)) == fff.ERROR_INVALID_VALUE
-    # Plan flags: the defined bits pass through resolution; others are invalid.
+    # Plan flags: the defined bit passes through resolution; others are invalid.
     dec = _shape(T=8, d=2048, P=32, D=6, h=128)
-    for flags in (fff.PLAN_TEST_DECODE_NO_PUBLISH, fff.PLAN_DECODE_ROUNDS,
-                  fff.PLAN_TEST_DECODE_NO_PUBLISH | fff.PLAN_DECODE_ROUNDS):
-        r = fff.resolve_plan(dec, fff.make_plan("decode", flags=flags))
-        assert r.algo == fff.ALGO_DECODE and r.flags == flags
+    r = fff.resolve_plan(dec, fff.make_plan("decode", flags=fff.PLAN_TEST_DECODE_NO_PUBLISH))
+    assert r.algo == fff.ALGO_DECODE and r.flags == fff.PLAN_TEST_DECODE_NO_PUBLISH
     assert fff.resolve_plan(dec, fff.make_plan()).flags == 0
-    for flags in (4, 1 << 30, -1):
+    for flags in (2, 1 << 30, -1):
         assert _forward(lib, dec, plan=fff.make_plan(flags=flags)) == fff.ERROR_INVALID_VALUE
         assert lib.fff_plan_resolve(ctypes.byref(dec), ctypes.byref(fff.make_plan(flags=flags)),
                                     ctypes.byref(fff.Plan())) == fff.ERROR_INVALID_VALUE
@@ -202,12 +200,11 @@ def test_decode_workspace_covers_route(lib):
     dec = fff.workspace_size(s, fff.make_plan("decode"))
     pre = fff.workspace_size(s, fff.make_plan("prefill"))
     assert auto >= dec > 0 and auto >= pre > 0
-    # A 256-byte epoch header, 256 routing-item slots (64-bit each: one
-    # subtree item per level-3 node of each tree, more than the 128 round
-    # items of 2 tokens), H [8, 4096] bf16, 32 x 8 arrival slots and 8
+    # A 256-byte epoch header, 128 routing-item slots (2 tokens per item at
+    # 8 tokens; 64-bit each), H [8, 4096] bf16, 32 x 8 arrival slots and 8
     # K-chunk partials of y [8, 2048] fp32.
-    assert dec == 256 + 32 * 8 * 8 + 8 * 4096 * 2 + 32 * 8 * 8 + 8 * 8 * 2048 * 4
-    # 9 tokens: round items only (2 tokens each, 5 per tree).
+    assert dec == 256 + 32 * 4 * 8 + 8 * 4096 * 2 + 32 * 8 * 8 + 8 * 8 * 2048 * 4
+    # 9 tokens: 2 tokens per item, 5 items per tree.
     s9 = _shape(T=9, d=2048, P=32, D=6, h=128)
     assert fff.workspace_size(s9, fff.make_plan("decode")) == \
         256 + 32 * 5 * 8 + 9 * 4096 * 2 + 32 * 8 * 8 + 8 * 9 * 2048 * 4

@@ -255,28 +255,12 @@ DECODE_SHAPES = [
 
 
 @needs_gpu
-@pytest.mark.parametrize("rounds", [False, True], ids=["auto", "rounds"])
 @pytest.mark.parametrize("shape", DECODE_SHAPES, ids=[str(s) for s in DECODE_SHAPES])
-def test_decode_shapes(shape, rounds):
+def test_decode_shapes(shape):
     T, d, P, D, h = shape
     inp = workloads.random_inputs(T, d, P, D, h, "bf16", seed=5, unit_rms_x=True)
-    y, path = run(inp, algo="decode", plan_flags=fff.PLAN_DECODE_ROUNDS if rounds else 0)
+    y, path = run(inp, algo="decode")
     check(inp, y, path)
-
-
-@needs_gpu
-@pytest.mark.parametrize("variant", [0, 1])
-@pytest.mark.parametrize("name", ["decode_skew_t1", "decode_skew_t8"])
-def test_decode_subtree_items_match_rounds(name, variant):
-    # Both item kinds evaluate every visited node with the same operands and
-    # summation order, and add the GELU(a) v_n terms in level order: paths
-    # and y agree bit for bit.
-    inp = wl(name)
-    ys, ps = run(inp, algo="decode", variant=variant)
-    yr, pr = run(inp, algo="decode", variant=variant, plan_flags=fff.PLAN_DECODE_ROUNDS)
-    np.testing.assert_array_equal(ps, pr)
-    np.testing.assert_array_equal(ys, yr)
-    check(inp, ys, ps, variant=variant)
 
 
 @needs_gpu
