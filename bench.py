@@ -49,7 +49,8 @@ def parse():
     ap.add_argument("--rotate", type=int, default=0, help="input sets (0 = by footprint)")
     ap.add_argument("--prune", type=float, default=0.0,
                     help="statically prune this fraction of each tree's paths (seeded random "
-                         "leaf mask) and run fff_forward_pruned")
+                         "leaf mask) and run fff_forward_pruned (with --backward: "
+                         "fff_backward_pruned)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="oracle budget: three timed runs of about a third of this each")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -365,7 +366,18 @@ def backward_bench(args):
     variant = fff.VARIANTS[args.variant]
     fshape = fff.shape_of(sets[0][0], sets[0][1], sets[0][3], variant)
     plan = fff.make_plan(args.algo)
-    nbytes = fff.backward_workspace_size(fshape, plan)
+    prunings = None
+    if args.prune > 0:
+        # One table per input set, packed for every level dense (the
+        # matrix-core backward's routing); each tree keeps at least one path.
+        rng = np.random.default_rng(0)
+        mask = (rng.random((shape.P, 1 << shape.D)) >= args.prune).astype(np.uint8)
+        mask[np.arange(shape.P), rng.integers(0, 1 << shape.D, size=shape.P)] = 1
+        prunings = [fff.prune_prepare(mask, st[1], st[3], algo="prefill", split_level=shape.D + 1,
+                                      T=shape.T) for st in sets]
+        nbytes = fff.backward_pruned_workspace_size(fshape, plan, prunings[0][0])
+    else:
+        nbytes = fff.backward_workspace_size(fshape, plan)
     ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
     f32 = dict(dtype=torch.float32, device=dev)
     out = {"dx": torch.empty_like(sets[0][0]), "dW_node": torch.empty(sets[0][1].shape, **f32),
@@ -375,6 +387,10 @@ def backward_bench(args):
 
     def step(i):
         x, W, b, V, Wo, dy = sets[i % rotate]
+        if prunings is not None:
+            fff.backward_pruned(x, W, b, V, Wo, dy, prunings[i % rotate][0], algo=args.algo,
+                                workspace=ws, out=out, variant=variant)
+            return
         fff.backward(x, W, b, V, Wo, dy, algo=args.algo, workspace=ws, out=out, variant=variant)
 
     t_ms = _events_ms(torch, step, args.steps, args.warmup)
@@ -391,7 +407,10 @@ def backward_bench(args):
         "ms_per_step": t_ms, "higher_is_better": True, "dtype": "bf16" if s.dtype == "bf16" else "f32",
         "data": "synthetic", "config": {"workload": args.workload, "T": s.T, "d": s.d, "P": s.P,
                                         "D": s.D, "h": s.h, "variant": args.variant,
-                                        "algo": args.algo, "rotated_sets": rotate},
+                                        "algo": args.algo, "rotated_sets": rotate,
+                                        **({"pruning": {"ratio": args.prune,
+                                                        "alive_leaves": float(mask.mean())}}
+                                           if prunings is not None else {})},
         "flops": {"algorithmic": alg, "executed": executed,
                   "executed_tflops": executed / (t_ms * 1e-3) / 1e12}}), flush=True)
 

@@ -326,3 +326,45 @@ def test_backward_pruned_all_alive_equals_unpruned():
     g0, _, _ = run_backward(inp, algo="prefill")
     for k in ("dx", "dW_node", "dV_node", "dW_out"):
         np.testing.assert_array_equal(g[k], g0[k])
+
+
+@needs_gpu
+def test_backward_pruned_full_size_sampled():
+    # The OPT-1.3B-shaped depth-6 layer with half of each tree's leaves
+    # pruned, on the matrix-core plan, with dy nonzero on a sample of tokens
+    # only (the oracle's pruned backward over the sample is then the exact
+    # reference).
+    inp = workloads.workload("opt1p3b_d6")
+    s = inp.shape
+    T = to_device(inp)
+    mask = random_leaf_mask(np.random.default_rng(21), s.P, s.D, 0.5)
+    print("[gpu] pruned backward full size", flush=True)
+    pr, table = fff.prune_prepare(mask, T["W_node"], T["V_node"], algo="prefill",
+                                  split_level=s.D + 1, T=s.T)
+    _, path = fff.forward_pruned(T["x"], T["W_node"], T["b_node"], T["V_node"], T["W_out"], pr,
+                                 algo="prefill", split_level=s.D + 1)
+    torch.cuda.synchronize()
+    path = path.cpu().numpy()
+    cand = np.sort(np.random.default_rng(6).choice(s.T, size=48, replace=False))
+    fc = inp.subset_tokens(cand).as_f64()
+    ok = (oracle.forward(fc["x"], fc["W_node"], fc["b_node"], fc["V_node"], fc["W_out"],
+                         want_y=False, leaf_alive=mask)["path"] == path[cand]).all(axis=1)
+    rows = cand[ok][:24]
+    assert len(rows) == 24
+    dy = np.zeros((s.T, s.d))
+    dy[rows] = np.random.default_rng(8).standard_normal((len(rows), s.d))
+    dy_t = torch.from_numpy(dy).to(torch.bfloat16)
+    dy64 = dy_t.double().numpy()
+    g = fff.backward_pruned(T["x"], T["W_node"], T["b_node"], T["V_node"], T["W_out"],
+                            dy_t.to(T["x"].device), pr)
+    torch.cuda.synchronize()
+    del table
+    g = {k: to_f64(v) for k, v in g.items()}
+    f = inp.subset_tokens(rows).as_f64()
+    ref = oracle.backward(f["x"], f["W_node"], f["b_node"], f["V_node"], f["W_out"], dy64[rows],
+                          leaf_alive=mask)
+    rec = oracle.forward(f["x"], f["W_node"], f["b_node"], f["V_node"], f["W_out"],
+                         want_y=False, want_records=True, leaf_alive=mask)
+    assert (g["dx"][np.setdiff1d(np.arange(s.T), rows)] == 0).all()
+    g["dx"] = g["dx"][rows]
+    assert_grads("bf16", g, ref, f, dy64[rows], rec, 0)
