@@ -286,7 +286,9 @@ typedef struct fff_pruning {
     const void *table;   /* device table written by fff_prune_prepare */
     int32_t P, D, d;     /* the shape it was prepared for */
     int32_t split_level; /* PREFILL split level whose rows are packed; 0 = none */
-    int32_t col_tiles;   /* 256-column tiles of packed rows */
+    int32_t col_tiles;   /* 256-column tiles of packed rows (at least 1 when
+                            split_level > 0; a table whose fields do not fit
+                            the shape is FFF_ERROR_INVALID_VALUE) */
 } fff_pruning_t;
 
 /* Device bytes of the table for this shape and plan (plan NULL = the

@@ -444,7 +444,8 @@ BwdLayout bwd_layout(const Dims& s, const fff_plan_t& p) {
 fff_status_t prune_view(const Dims& s, const fff_pruning_t* pruning, fff::PruneView* pv) {
   if (!pruning || !pruning->table || !aligned(pruning->table, kWsAlign) || pruning->P != s.P ||
       pruning->D != s.D || pruning->d != s.d || pruning->split_level < 0 ||
-      pruning->split_level > 8 || pruning->col_tiles < 0 || pruning->col_tiles > s.P)
+      pruning->split_level > 8 || pruning->col_tiles < 0 || pruning->col_tiles > s.P ||
+      (pruning->split_level > 0 && pruning->col_tiles < 1))  // packed levels need a tile
     return FFF_ERROR_INVALID_VALUE;
   const PruneLayout PL = prune_layout(s, pruning->split_level);
   const char* tb = static_cast<const char*>(pruning->table);

@@ -271,7 +271,7 @@ def test_forward_pruned_validation(lib):
     good = dict(table=FAKE, P=3, D=4, d=128, split_level=5, col_tiles=1)
     assert run(None) == fff.ERROR_INVALID_VALUE
     for bad in (dict(table=None), dict(table=FAKE + 8), dict(P=4), dict(D=3), dict(d=64),
-                dict(split_level=9), dict(col_tiles=4)):
+                dict(split_level=9), dict(col_tiles=4), dict(col_tiles=0)):
         assert run(fff.Pruning(**dict(good, **bad))) == fff.ERROR_INVALID_VALUE, bad
     # A PREFILL plan must use the split level the table packed.
     assert run(fff.Pruning(**dict(good, split_level=3))) == fff.ERROR_NOT_SUPPORTED
@@ -327,7 +327,7 @@ def test_backward_pruned_plans_and_validation(lib):
 
     assert run(None) == fff.ERROR_INVALID_VALUE
     for bad in (dict(table=None), dict(table=FAKE + 8), dict(P=4), dict(D=5), dict(d=64),
-                dict(split_level=9), dict(col_tiles=33)):
+                dict(split_level=9), dict(col_tiles=33), dict(col_tiles=0)):
         assert run(fff.Pruning(**dict(dense, **bad))) == fff.ERROR_INVALID_VALUE, bad
         assert lib.fff_backward_pruned_workspace_size(
             ctypes.byref(s), None, ctypes.byref(fff.Pruning(**dict(dense, **bad))),
