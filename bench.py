@@ -226,6 +226,14 @@ def _events_ms(torch, fn, steps, warmup):
     return float(np.median([a.elapsed_time(b) for a, b in evs]))
 
 
+def event_floor_us(torch, steps=200):
+    """Median interval between two events on the current stream around the
+    smallest kernel (a one-element add): the floor under any per-launch time
+    taken this way, whatever the kernel does."""
+    x = torch.zeros(1, device="cuda:0")
+    return 1e3 * _events_ms(torch, lambda i: x.add_(1.0), steps, 20)
+
+
 def depth_sweep(args):
     """Speed against tree depth, the MI355X counterpart of the paper page's
     Figure 5 and Table 5: the headline workload's T, d, P and h at depths
@@ -659,7 +667,8 @@ def main():
                   "rotated": True,
                   "staged_pass_us_per_step": 1e6 * staged_elapsed / args.steps,
                   "warm_t_us_median": float(np.median(warm_ms)) * 1e3,
-                  "warm_tokens_per_s": shape.T / (float(np.median(warm_ms)) * 1e-3)},
+                  "warm_tokens_per_s": shape.T / (float(np.median(warm_ms)) * 1e-3),
+                  "event_floor_us": event_floor_us(torch)},
         "host": platform.node(),
     }
     if not args.no_cpu_baseline:
